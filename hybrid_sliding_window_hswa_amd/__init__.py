@@ -1,0 +1,295 @@
+"""Hybrid Sliding-Window Attention hot path for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of libhswa.so (include/hswa.h).  The
+functions keep the C names; they only marshal arguments (torch tensors ->
+device pointers, Python sequences -> host int32 arrays) and turn a non-zero
+status into an exception.  Every step of the path runs in the library's HIP
+kernels and host C++; torch provides device memory and streams only.
+
+Sources: "MiMo-V2.5 Series Inference Full-Link Optimization: Pushing Hybrid
+SWA Efficiency to the Extreme" (sec. 1.1 layer mix and window, sec. 1.2
+decode cost, sec. 2.1 KVCache Dual Pool and SWA-aware prefix cache tree)
+and "Following the Bottleneck: Optimizing MiniMax M3 on AMD Instinct
+MI355X" (sec. 3, 16-token pages behind a page table).
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import _capi
+from ._capi import (HSWA_E_HIP, HSWA_E_INVAL, HSWA_E_NOSPC, HSWA_E_UNSUPPORTED,
+                    HSWA_LAYER_FULL, HSWA_LAYER_SWA, HSWA_OK)
+
+PAGE_SIZE = 16
+FULL = HSWA_LAYER_FULL
+SWA = HSWA_LAYER_SWA
+
+__all__ = [
+    "HswaError", "NoSpace", "FULL", "SWA", "PAGE_SIZE",
+    "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view", "hswa_pool_alloc",
+    "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_read_tables",
+    "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
+    "hswa_last_error", "hswa_version", "kv_cache_shapes", "library",
+]
+
+
+class HswaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_capi.load().hswa_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+class NoSpace(HswaError):
+    """The joint Full/SWA capacity check failed; the pool is unchanged."""
+
+
+def library():
+    return _capi.load()
+
+
+def hswa_last_error() -> str:
+    return library().hswa_last_error().decode()
+
+
+def hswa_version() -> int:
+    return library().hswa_version()
+
+
+def _check(rc: int):
+    if rc != HSWA_OK:
+        msg = hswa_last_error()
+        if rc == HSWA_E_NOSPC:
+            raise NoSpace(rc, msg)
+        raise HswaError(rc, msg)
+
+
+def _i32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(_capi.I32P)
+
+
+def _dptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Pool
+
+
+class Pool:
+    """A pool handle plus the device tables it mirrors (kept alive here)."""
+
+    def __init__(self, handle, tables, desc):
+        self.handle = handle
+        self.tables = tables  # dict of torch int32 tensors or None
+        self.desc = desc
+
+    def __del__(self):
+        try:
+            hswa_pool_destroy(self)
+        except Exception:
+            pass
+
+
+def hswa_pool_create(window: int, ring_slots: int, max_seqs: int, max_pages_per_seq: int,
+                     num_full_pages: int, full_free_order, ring_pages, device=None) -> Pool:
+    """Creates a pool.  With ``device`` (e.g. "cuda:0") the four device
+    tables are allocated there as int32 torch tensors and mirrored by the
+    library; without it the pool keeps host bookkeeping only."""
+    lib = library()
+    free = _i32(full_free_order)
+    ring = _i32(ring_pages)
+    tables = None
+    desc = _capi.PoolDesc()
+    desc.page_size = PAGE_SIZE
+    desc.window = window
+    desc.ring_slots = ring_slots
+    desc.max_seqs = max_seqs
+    desc.max_pages_per_seq = max_pages_per_seq
+    desc.num_full_pages = num_full_pages
+    if free.size != num_full_pages or ring.size != max_seqs * (ring_slots // PAGE_SIZE):
+        raise ValueError("full_free_order / ring_pages have the wrong length")
+    desc.full_free_order = _p(free)
+    desc.ring_pages = _p(ring)
+    if device is not None:
+        import torch
+        tables = {
+            "seq_len": torch.empty(max_seqs, dtype=torch.int32, device=device),
+            "fpt": torch.empty(max_seqs * max_pages_per_seq, dtype=torch.int32, device=device),
+            "rpt": torch.empty(ring.size, dtype=torch.int32, device=device),
+            "map": torch.empty(num_full_pages * PAGE_SIZE, dtype=torch.int32, device=device),
+        }
+        desc.dev_seq_len = tables["seq_len"].data_ptr()
+        desc.dev_fpt = tables["fpt"].data_ptr()
+        desc.dev_rpt = tables["rpt"].data_ptr()
+        desc.dev_map = tables["map"].data_ptr()
+    h = C.c_void_p()
+    _check(lib.hswa_pool_create(C.byref(desc), C.byref(h)))
+    info = dict(window=window, ring_slots=ring_slots, max_seqs=max_seqs,
+                max_pages_per_seq=max_pages_per_seq, num_full_pages=num_full_pages)
+    return Pool(h, tables, info)
+
+
+def hswa_pool_destroy(pool: Pool) -> None:
+    if pool.handle is not None and pool.handle.value:
+        library().hswa_pool_destroy(pool.handle)
+    pool.handle = None
+
+
+def hswa_pool_get_view(pool: Pool) -> _capi.PoolView:
+    v = _capi.PoolView()
+    _check(library().hswa_pool_get_view(pool.handle, C.byref(v)))
+    return v
+
+
+def hswa_pool_alloc(pool: Pool, seq_ids: Sequence[int], n_new: Sequence[int],
+                    want_slots: bool = True, stream=None):
+    """Returns (full_slots, swa_slots) as int32 arrays (None if not wanted)."""
+    ids, n = _i32(seq_ids), _i32(n_new)
+    tot = int(np.clip(n, 0, None).sum()) if n.size else 0
+    full = np.empty(tot, np.int32) if want_slots else None
+    swa = np.empty(tot, np.int32) if want_slots else None
+    _check(library().hswa_pool_alloc(pool.handle, ids.size, _p(ids), _p(n), _p(full), _p(swa),
+                                     _stream(stream)))
+    return full, swa
+
+
+def hswa_pool_import(pool: Pool, seq_ids: Sequence[int], n_new: Sequence[int],
+                     want_slots: bool = True, stream=None):
+    ids, n = _i32(seq_ids), _i32(n_new)
+    tot = int(np.clip(n, 0, None).sum()) if n.size else 0
+    full = np.empty(tot, np.int32) if want_slots else None
+    swa = np.empty(tot, np.int32) if want_slots else None
+    _check(library().hswa_pool_import(pool.handle, ids.size, _p(ids), _p(n), _p(full),
+                                      _p(swa), _stream(stream)))
+    return full, swa
+
+
+def hswa_pool_evict(pool: Pool, seq_ids: Sequence[int], want_slots: bool = True,
+                    capacity: Optional[int] = None, stream=None):
+    """Returns (evicted_full_slots, counts) (None, counts if not wanted)."""
+    ids = _i32(seq_ids)
+    cap = capacity if capacity is not None else ids.size * pool.desc["ring_slots"]
+    ev = np.empty(max(cap, 1), np.int32) if want_slots else None
+    cnt = np.empty(max(ids.size, 1), np.int32)
+    _check(library().hswa_pool_evict(pool.handle, ids.size, _p(ids), _p(ev), cap, _p(cnt),
+                                     _stream(stream)))
+    cnt = cnt[:ids.size]
+    if ev is not None:
+        ev = ev[:int(cnt.sum())]
+    return ev, cnt
+
+
+def hswa_pool_release(pool: Pool, seq_ids: Sequence[int], stream=None) -> None:
+    ids = _i32(seq_ids)
+    _check(library().hswa_pool_release(pool.handle, ids.size, _p(ids), _stream(stream)))
+
+
+def hswa_pool_read_tables(pool: Pool) -> dict:
+    d = pool.desc
+    seq_len = np.empty(d["max_seqs"], np.int32)
+    fpt = np.empty(d["max_seqs"] * d["max_pages_per_seq"], np.int32)
+    mp = np.empty(d["num_full_pages"] * PAGE_SIZE, np.int32)
+    free = np.empty(d["num_full_pages"], np.int32)
+    nfree = np.zeros(1, np.int32)
+    _check(library().hswa_pool_read_tables(pool.handle, _p(seq_len), _p(fpt), _p(mp), _p(free),
+                                           _p(nfree)))
+    return {"seq_len": seq_len, "fpt": fpt.reshape(d["max_seqs"], d["max_pages_per_seq"]),
+            "map": mp, "free": free[:int(nfree[0])]}
+
+
+# ---------------------------------------------------------------------------
+# Attention
+
+
+def kv_cache_shapes(num_pages: int, num_kv_heads: int, head_dim: int):
+    """Shapes of one layer's K and V page buffers (bf16)."""
+    return ((num_pages, num_kv_heads, PAGE_SIZE, head_dim),
+            (num_pages, num_kv_heads, head_dim, PAGE_SIZE))
+
+
+def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_seq_len,
+          view, k_cache, v_cache, out, vlen, scale) -> _capi.AttnArgs:
+    a = _capi.AttnArgs()
+    a.kind = kind
+    a.window = window
+    hq, d = (q.shape[-2], q.shape[-1]) if q is not None else (k_new.shape[-2], k_new.shape[-1])
+    a.num_q_heads = hq
+    a.num_kv_heads = k_cache.shape[1]
+    a.head_dim = d
+    a.scale = scale
+    a.num_seqs = seq_ids.shape[0]
+    a.seq_ids = _dptr(seq_ids)
+    a.cu_q = _dptr(cu_q)
+    a.total_q = total_q
+    a.max_q_len = max_q_len
+    a.max_seq_len = max_seq_len
+    a.q = _dptr(q)
+    a.k_new = _dptr(k_new)
+    a.v_new = _dptr(v_new)
+    a.pool = view
+    a.k_cache = _dptr(k_cache)
+    a.v_cache = _dptr(v_cache)
+    a.out = _dptr(out)
+    a.vlen_out = _dptr(vlen)
+    return a
+
+
+def hswa_prefill_chunk(kind: int, window: int, q, k_new, v_new, seq_ids, cu_q,
+                       max_q_len: int, view, k_cache, v_cache, out, vlen=None,
+                       scale: float = 0.0, stream=None) -> None:
+    """q [T, Hq, d] bf16; k_new/v_new [T, Hkv, d] bf16 or None; seq_ids [B] and
+    cu_q [B+1] int32 device tensors; out [T, Hq, d] fp32; vlen [T] int32."""
+    a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0], max_q_len, 0, view,
+              k_cache, v_cache, out, vlen, scale)
+    _check(library().hswa_prefill_chunk(C.byref(a), _stream(stream)))
+
+
+def hswa_decode_workspace_bytes(kind: int, window: int, num_seqs: int, num_q_heads: int,
+                                num_kv_heads: int, head_dim: int, max_seq_len: int) -> int:
+    a = _capi.AttnArgs()
+    a.kind, a.window, a.num_seqs = kind, window, num_seqs
+    a.num_q_heads, a.num_kv_heads, a.head_dim = num_q_heads, num_kv_heads, head_dim
+    a.max_seq_len = max_seq_len
+    return int(library().hswa_decode_workspace_bytes(C.byref(a)))
+
+
+def hswa_decode(kind: int, window: int, q, k_new, v_new, seq_ids, max_seq_len: int, view,
+                k_cache, v_cache, out, workspace=None, vlen=None, scale: float = 0.0,
+                stream=None) -> None:
+    """One query row per sequence (q [B, Hq, d]) at position seq_len - 1."""
+    a = _args(kind, window, q, k_new, v_new, seq_ids, None, q.shape[0], 1, max_seq_len, view,
+              k_cache, v_cache, out, vlen, scale)
+    ws = _dptr(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().hswa_decode(C.byref(a), ws, nbytes, _stream(stream)))
+
+
+def hswa_append_kv(kind: int, k_new, v_new, seq_ids, view, k_cache, v_cache, cu_q=None,
+                   max_q_len: int = 1, stream=None) -> None:
+    """Writes k_new/v_new rows into this layer's pages (no attention)."""
+    a = _args(kind, 1, None, k_new, v_new, seq_ids, cu_q, k_new.shape[0], max_q_len, 1, view,
+              k_cache, v_cache, None, None, 0.0)
+    a.num_q_heads = k_new.shape[1]
+    _check(library().hswa_append_kv(C.byref(a), _stream(stream)))

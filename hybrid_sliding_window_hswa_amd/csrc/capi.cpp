@@ -1,0 +1,281 @@
+// C ABI entry points for attention (prefill, decode, KV append), argument
+// validation and the thread-local error text.  Kernels live in the .hip
+// files; this file only checks arguments and dispatches.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/hswa.h"
+#include "internal.h"
+
+namespace hswa {
+
+static thread_local std::string g_err;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+}
+
+void clear_error() { g_err.clear(); }
+
+int hip_fail(hipError_t e, const char* what) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return HSWA_E_HIP;
+}
+
+}  // namespace hswa
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared validation of an attention call.  `decode` selects the one-row-
+// per-sequence form (cu_q ignored).
+int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnParams* p) {
+  if (!a) {
+    hswa::set_error("args is NULL");
+    return HSWA_E_INVAL;
+  }
+  if (a->kind != HSWA_LAYER_FULL && a->kind != HSWA_LAYER_SWA) {
+    hswa::set_error("kind must be HSWA_LAYER_FULL or HSWA_LAYER_SWA (got %d)", a->kind);
+    return HSWA_E_INVAL;
+  }
+  if (a->head_dim != 64 && a->head_dim != 128) {
+    hswa::set_error("head_dim must be 64 or 128 (got %d)", a->head_dim);
+    return HSWA_E_INVAL;
+  }
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1 || a->num_q_heads % a->num_kv_heads) {
+    hswa::set_error("num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    a->num_q_heads, a->num_kv_heads);
+    return HSWA_E_INVAL;
+  }
+  int g = a->num_q_heads / a->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) {
+    hswa::set_error("query heads per KV head must be 1, 2, 4 or 8 (got %d)", g);
+    return HSWA_E_UNSUPPORTED;
+  }
+  if (a->num_seqs < 0) {
+    hswa::set_error("num_seqs must be >= 0");
+    return HSWA_E_INVAL;
+  }
+  const hswa_pool_view& v = a->pool;
+  if (!v.seq_len || !v.fpt || !v.rpt) {
+    hswa::set_error("pool view has NULL device tables");
+    return HSWA_E_INVAL;
+  }
+  if (v.ring_slots < 16 || v.ring_slots % 16 || v.max_pages_per_seq < 1 || v.window < 1 ||
+      v.max_seqs < 1) {
+    hswa::set_error("pool view geometry is invalid");
+    return HSWA_E_INVAL;
+  }
+  if (a->kind == HSWA_LAYER_SWA && (a->window < 1 || a->window > v.window)) {
+    hswa::set_error("SWA window %d must be in [1, pool window %d]", a->window, v.window);
+    return HSWA_E_INVAL;
+  }
+  if (decode) {
+    if (a->total_q != a->num_seqs) {
+      hswa::set_error("decode: total_q (%d) must equal num_seqs (%d)", a->total_q,
+                      a->num_seqs);
+      return HSWA_E_INVAL;
+    }
+    if (need_attn && a->max_seq_len < 1 && a->num_seqs > 0) {
+      hswa::set_error("decode: max_seq_len must be >= 1");
+      return HSWA_E_INVAL;
+    }
+  } else {
+    if (a->num_seqs > 0 && !a->cu_q) {
+      hswa::set_error("prefill: cu_q is NULL");
+      return HSWA_E_INVAL;
+    }
+    if (a->total_q < 0 || a->max_q_len < 0 || (a->total_q > 0 && a->max_q_len < 1)) {
+      hswa::set_error("prefill: total_q and max_q_len must be >= 0 (max_q_len >= 1 "
+                      "when there are rows)");
+      return HSWA_E_INVAL;
+    }
+  }
+  if (a->num_seqs > 0 && !a->seq_ids) {
+    hswa::set_error("seq_ids is NULL");
+    return HSWA_E_INVAL;
+  }
+  if ((a->k_new == nullptr) != (a->v_new == nullptr)) {
+    hswa::set_error("k_new and v_new must both be set or both be NULL");
+    return HSWA_E_INVAL;
+  }
+  if (!a->k_cache || !a->v_cache) {
+    hswa::set_error("k_cache and v_cache must be set");
+    return HSWA_E_INVAL;
+  }
+  if (need_attn && a->total_q > 0 && (!a->q || !a->out)) {
+    hswa::set_error("q and out must be set");
+    return HSWA_E_INVAL;
+  }
+  const void* ptrs[] = {a->q, a->k_new, a->v_new, a->k_cache, a->v_cache, a->out};
+  for (const void* q : ptrs) {
+    if (q && !aligned16(q)) {
+      hswa::set_error("device buffers must be 16-byte aligned");
+      return HSWA_E_INVAL;
+    }
+  }
+  if ((int64_t)a->total_q * a->num_q_heads * a->head_dim > INT32_MAX) {
+    hswa::set_error("q has more than 2^31 elements");
+    return HSWA_E_UNSUPPORTED;
+  }
+  float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->head_dim);
+  *p = hswa::AttnParams{};
+  p->kind = a->kind;
+  p->window = a->kind == HSWA_LAYER_SWA ? a->window : 0;
+  p->hq = a->num_q_heads;
+  p->hkv = a->num_kv_heads;
+  p->d = a->head_dim;
+  p->scale_log2 = scale * 1.4426950408889634f;
+  p->num_seqs = a->num_seqs;
+  p->seq_ids = a->seq_ids;
+  p->cu_q = decode ? nullptr : a->cu_q;
+  p->total_q = a->total_q;
+  p->max_q_len = decode ? 1 : a->max_q_len;
+  p->max_seq_len = a->max_seq_len;
+  p->q = (const uint16_t*)a->q;
+  p->k_new = (const uint16_t*)a->k_new;
+  p->v_new = (const uint16_t*)a->v_new;
+  p->k_cache = (uint16_t*)a->k_cache;
+  p->v_cache = (uint16_t*)a->v_cache;
+  p->t.seq_len = v.seq_len;
+  p->t.fpt = v.fpt;
+  p->t.rpt = v.rpt;
+  p->t.max_pages = v.max_pages_per_seq;
+  p->t.ring_slots = v.ring_slots;
+  p->t.max_seqs = v.max_seqs;
+  p->out = a->out;
+  p->vlen = a->vlen_out;
+  return HSWA_OK;
+}
+
+}  // namespace
+
+namespace hswa {
+
+// Split-K plan for a decode call.  FULL layers cut each sequence's context
+// into chunks of split_len keys (a multiple of 64) so that the grid has
+// enough workgroups for 256 CUs while the partial results stay small next
+// to the KV bytes; SWA layers read at most W keys and use one split.
+DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d,
+                       int32_t window, int32_t max_seq_len) {
+  DecodePlan pl{1, 0, 0};
+  if (num_seqs <= 0) return pl;
+  if (kind == HSWA_LAYER_SWA) {
+    pl.split_len = ((window + 63) / 64) * 64;
+    return pl;
+  }
+  const int64_t min_split = 1024;
+  const int64_t target_units = 16384;  // (sequence, kv head, split) workgroups
+  int64_t units = (int64_t)num_seqs * hkv;
+  int64_t want = (target_units + units - 1) / units;
+  int64_t max_by_len = (max_seq_len + min_split - 1) / min_split;
+  int64_t n = want < max_by_len ? want : max_by_len;
+  if (n < 1) n = 1;
+  if (n > 128) n = 128;
+  int64_t sl = (max_seq_len + n - 1) / n;
+  sl = ((sl + 63) / 64) * 64;
+  n = (max_seq_len + sl - 1) / sl;
+  pl.n_splits = (int32_t)n;
+  pl.split_len = (int32_t)sl;
+  if (n > 1) pl.ws_bytes = (size_t)num_seqs * hq * n * (d + 2) * sizeof(float);
+  return pl;
+}
+
+}  // namespace hswa
+
+extern "C" {
+
+const char* hswa_last_error(void) { return hswa::g_err.c_str(); }
+
+const char* hswa_status_string(int s) {
+  switch (s) {
+    case HSWA_OK: return "HSWA_OK";
+    case HSWA_E_INVAL: return "HSWA_E_INVAL";
+    case HSWA_E_NOSPC: return "HSWA_E_NOSPC";
+    case HSWA_E_HIP: return "HSWA_E_HIP";
+    case HSWA_E_UNSUPPORTED: return "HSWA_E_UNSUPPORTED";
+    default: return "unknown hswa status";
+  }
+}
+
+int hswa_version(void) { return 100; }
+
+int hswa_append_kv(const hswa_attn_args* a, void* stream) {
+  hswa::clear_error();
+  hswa::AttnParams p;
+  bool decode = a && a->cu_q == nullptr;
+  int rc = validate(a, decode, false, &p);
+  if (rc) return rc;
+  if (!a->k_new) {
+    hswa::set_error("append: k_new and v_new are required");
+    return HSWA_E_INVAL;
+  }
+  if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;
+  hipError_t e = hswa::launch_append(p, (hipStream_t)stream);
+  return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "append launch");
+}
+
+int hswa_prefill_chunk(const hswa_attn_args* a, void* stream) {
+  hswa::clear_error();
+  hswa::AttnParams p;
+  int rc = validate(a, false, true, &p);
+  if (rc) return rc;
+  if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (p.k_new) {
+    e = hswa::launch_append(p, s);
+    if (e != hipSuccess) return hswa::hip_fail(e, "append launch");
+  }
+  e = hswa::launch_prefill(p, s);
+  return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "prefill launch");
+}
+
+size_t hswa_decode_workspace_bytes(const hswa_attn_args* a) {
+  if (!a) return 0;
+  return hswa::plan_decode(a->kind, a->num_seqs, a->num_q_heads, a->num_kv_heads,
+                           a->head_dim, a->window, a->max_seq_len)
+      .ws_bytes;
+}
+
+int hswa_decode(const hswa_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
+  hswa::clear_error();
+  hswa::AttnParams p;
+  int rc = validate(a, true, true, &p);
+  if (rc) return rc;
+  if (p.num_seqs == 0) return HSWA_OK;
+  hswa::DecodePlan pl = hswa::plan_decode(p.kind, p.num_seqs, p.hq, p.hkv, p.d, p.window,
+                                          p.max_seq_len);
+  if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) {
+    hswa::set_error("decode workspace: %zu bytes given, %zu needed", ws_bytes, pl.ws_bytes);
+    return HSWA_E_INVAL;
+  }
+  if (ws && !aligned16(ws)) {
+    hswa::set_error("workspace must be 16-byte aligned");
+    return HSWA_E_INVAL;
+  }
+  p.n_splits = pl.n_splits;
+  p.split_len = pl.split_len;
+  p.ws = (float*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (p.k_new) {
+    e = hswa::launch_append(p, s);
+    if (e != hipSuccess) return hswa::hip_fail(e, "append launch");
+  }
+  e = hswa::launch_decode(p, s);
+  return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "decode launch");
+}
+
+}  // extern "C"

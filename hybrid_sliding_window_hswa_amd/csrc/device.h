@@ -1,0 +1,59 @@
+// Device-side helpers for the gfx950 kernels: vector types for the MFMA
+// builtins, bf16/fp16 conversions, cross-lane reductions and page lookups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hswa {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 16;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two bf16 (packed in one dword) -> two fp16 (packed).  Exact for
+// |x| < 65504 and |x| >= 2^-14; smaller magnitudes round to fp16 subnormals.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  f16x2 h = {(_Float16)bf16_lo(w), (_Float16)bf16_hi(w)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Lane exchange inside a wavefront (ds_bpermute based).
+__device__ __forceinline__ float xor_lane(float v, int mask) {
+  int lane = __lane_id();
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane ^ mask) & 63) << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Physical page holding the 16-aligned key tile that starts at `pos` for
+// sequence `sid`: Full layers read the Full page table, SWA layers the ring
+// page table (position taken modulo the ring size).
+template <int KIND>
+__device__ __forceinline__ int32_t page_of(const int32_t* __restrict__ fpt,
+                                           const int32_t* __restrict__ rpt, int32_t sid,
+                                           int32_t pos, int32_t max_pages, int32_t ring) {
+  if (KIND == 0) return fpt[(int64_t)sid * max_pages + pos / kPage];
+  int32_t r = pos % ring;
+  return rpt[(int64_t)sid * (ring / kPage) + r / kPage];
+}
+
+}  // namespace dev
+}  // namespace hswa

@@ -1,0 +1,100 @@
+// Internal declarations shared by the host code and the HIP kernels of the
+// Hybrid SWA library.  Not part of the public ABI (include/hswa.h is).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace hswa {
+
+// ---------------------------------------------------------------------------
+// Errors: thread-local text of the last failure (hswa_last_error).
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+int hip_fail(hipError_t e, const char* what);
+
+// ---------------------------------------------------------------------------
+// Device-table update of the dual pool.  One record per sequence touched by
+// a pool operation; the kernel applies all records of one operation.
+struct PoolRec {
+  int32_t seq;       // sequence id
+  int32_t new_len;   // seq_len after the operation
+  int32_t clr_lo;    // positions [clr_lo, clr_hi) lose their SWA entry
+  int32_t clr_hi;
+  int32_t set_lo;    // positions [set_lo, set_hi) get map = their SWA slot
+  int32_t set_hi;
+  int32_t pg_lo;     // logical page of pages[pg_off]
+  int32_t pg_off;    // offset of this record's pages in the page list
+  int32_t fpt_lo;    // fpt entries [fpt_lo, fpt_hi) of the row are written
+  int32_t fpt_hi;
+  int32_t fpt_clear; // 1: write -1, 0: write the listed physical page
+  int32_t pad;
+};
+
+struct PoolDev {
+  int32_t* seq_len;
+  int32_t* fpt;
+  const int32_t* rpt;
+  int32_t* map;
+  int32_t max_pages;
+  int32_t ring_slots;
+};
+
+// recs/pages live in pinned host memory readable by the device.
+hipError_t launch_pool_apply(const PoolDev& dev, const PoolRec* recs, int n_recs,
+                             const int32_t* pages, int64_t max_range,
+                             hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Attention kernels.
+struct Tables {
+  const int32_t* seq_len;
+  const int32_t* fpt;
+  const int32_t* rpt;
+  int32_t max_pages;
+  int32_t ring_slots;
+  int32_t max_seqs;
+};
+
+struct AttnParams {
+  int32_t kind;          // 0 FULL, 1 SWA
+  int32_t window;
+  int32_t hq, hkv, d;
+  float scale_log2;      // softmax scale * log2(e)
+  int32_t num_seqs;
+  const int32_t* seq_ids;
+  const int32_t* cu_q;   // nullptr: one row per sequence
+  int32_t total_q;
+  int32_t max_q_len;
+  int32_t max_seq_len;
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  Tables t;
+  float* out;
+  int32_t* vlen;
+  // decode split-K
+  int32_t n_splits;
+  int32_t split_len;
+  float* ws;             // [num_seqs][hq][n_splits][d] partial sums, then
+                         // [num_seqs][hq][n_splits][2] (max, sum)
+};
+
+hipError_t launch_append(const AttnParams& p, hipStream_t stream);
+hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);
+hipError_t launch_decode(const AttnParams& p, hipStream_t stream);
+
+// Split-K plan for decode: shared by the workspace query and the launch.
+struct DecodePlan {
+  int32_t n_splits;
+  int32_t split_len;
+  size_t ws_bytes;
+};
+DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t hq, int32_t hkv,
+                       int32_t d, int32_t window, int32_t max_seq_len);
+
+}  // namespace hswa

@@ -1,0 +1,255 @@
+// Paged decode attention over the dual pool, one query row per sequence.
+//
+// "MiMo-V2.5 Series Inference Full-Link Optimization" sec. 1.2: decode is
+// bound by the bytes of KV it reads.  A Full layer reads the whole prefix
+// through the Full page table; a SWA layer reads at most W keys from the
+// sequence's ring (sec. 2.1 "KVCache Dual Pool").
+//
+// Design (gfx950):
+//  - One workgroup = 4 wavefronts per (sequence, KV head, split).  Full
+//    layers split the context in split_len-key pieces so the grid fills 256
+//    CUs; pieces are merged by log-sum-exp in decode_combine_kernel.
+//  - The G query heads that share a KV head ride in the N dimension of a
+//    16x16x32 MFMA: S^T[key][head] = K[key][:] . Q[head][:], so every K/V
+//    byte is read from HBM once for all G heads.
+//  - K rows (token-major pages) are the A operand loaded straight from HBM,
+//    16 bytes per lane.  V pages are dim-major, so the PV product
+//    O^T[d][head] = V^T[d][key] . P^T[key][head] reads 8 contiguous bytes per
+//    lane per page.  P and V enter the PV MFMA as fp16 (V converted in
+//    registers), keeping the weights to 11 significant bits.
+//  - Online softmax in fp32 in the log2 domain (exp2 of prescaled scores).
+//  - Wave w takes 32-key steps w, w+4, ...; the four partial states merge
+//    through LDS in a fixed order, so results depend only on logical key
+//    positions, never on where pages sit in memory.
+#include <hip/hip_runtime.h>
+
+#include "device.h"
+#include "internal.h"
+
+namespace hswa {
+
+using namespace dev;
+
+namespace {
+
+constexpr int kDecWaves = 4;
+
+template <int D, int KIND, int G>
+__global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
+  constexpr int NB = D / 16;  // 16-row d blocks of O^T
+  constexpr int NC = D / 32;  // 32-wide d chunks of the QK reduction
+  __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][G][D];
+  __shared__ float red_ml[kDecWaves][G][2];
+
+  const int i = blockIdx.x / p.n_splits;
+  const int split = blockIdx.x % p.n_splits;
+  const int kvh = blockIdx.y;
+  const int sid = p.seq_ids[i];
+  if (sid < 0 || sid >= p.t.max_seqs) return;
+  const int L = p.t.seq_len[sid];
+  int klo, khi;  // keys [klo, khi) of this workgroup
+  if (KIND == 0) {
+    klo = split * p.split_len;
+    khi = min(L, klo + p.split_len);
+  } else {
+    klo = max(0, L - p.window);
+    khi = L;
+  }
+  if (klo >= khi) return;  // whole workgroup idle: no barrier reached
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;  // query head within the group (N index)
+  const int q4 = lane >> 4;   // which 8-wide k slice / 4-row group
+  const int hq = p.hq;
+  const int hkv = p.hkv;
+
+  // Q^T fragments: lane holds Q[head col][32c + 8*q4 .. +8]
+  bf16x8 qf[NC];
+  {
+    const bool has = col < G;
+    const uint16_t* qrow = p.q + ((int64_t)i * hq + kvh * G + (has ? col : 0)) * D;
+    for (int c = 0; c < NC; ++c) {
+      u32x4 w = has ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
+      qf[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  f32x4 o[NB];
+  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;
+  float lsum = 0.f;
+  const float sl2 = p.scale_log2;
+
+  const int s0 = (klo / 32) * 32;
+  const int nsteps = (khi - 1 - s0) / 32 + 1;
+  const int64_t head_stride = (int64_t)kPage * D;  // elements per (page, head) block
+
+  for (int st = wave; st < nsteps; st += kDecWaves) {
+    const int kp0 = s0 + 32 * st;
+    const bool has1 = kp0 + 16 < khi;
+    const int32_t pg0 = page_of<KIND>(p.t.fpt, p.t.rpt, sid, kp0, p.t.max_pages, p.t.ring_slots);
+    const int32_t pg1 =
+        has1 ? page_of<KIND>(p.t.fpt, p.t.rpt, sid, kp0 + 16, p.t.max_pages, p.t.ring_slots) : 0;
+    if (pg0 < 0 || pg1 < 0) break;  // positions without pages: the caller skipped alloc
+    const uint16_t* kb0 = p.k_cache + ((int64_t)pg0 * hkv + kvh) * head_stride;
+    const uint16_t* kb1 = p.k_cache + ((int64_t)pg1 * hkv + kvh) * head_stride;
+    const uint16_t* vb0 = p.v_cache + ((int64_t)pg0 * hkv + kvh) * head_stride;
+    const uint16_t* vb1 = p.v_cache + ((int64_t)pg1 * hkv + kvh) * head_stride;
+
+    // issue every load of the step first
+    u32x4 kr[2][NC];
+    for (int c = 0; c < NC; ++c) {
+      kr[0][c] = *(const u32x4*)(kb0 + col * D + 32 * c + 8 * q4);
+      kr[1][c] = has1 ? *(const u32x4*)(kb1 + col * D + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
+    }
+    u32x2 vr[NB][2];
+    for (int nb = 0; nb < NB; ++nb) {
+      vr[nb][0] = *(const u32x2*)(vb0 + (16 * nb + col) * kPage + 4 * q4);
+      vr[nb][1] = has1 ? *(const u32x2*)(vb1 + (16 * nb + col) * kPage + 4 * q4) : u32x2{0, 0};
+    }
+
+    // S^T for the two 16-key tiles
+    f32x4 s[2];
+    for (int t = 0; t < 2; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[t][c]), qf[c],
+                                                      acc, 0, 0, 0);
+      s[t] = acc;
+    }
+    // mask: lane value (t, r) is key kp0 + 16t + 4*q4 + r
+    unsigned valid = 0;
+    float mx = -INFINITY;
+    float sv[8];
+    for (int t = 0; t < 2; ++t)
+      for (int r = 0; r < 4; ++r) {
+        const int kp = kp0 + 16 * t + 4 * q4 + r;
+        const bool ok = kp >= klo && kp < khi;
+        valid |= (unsigned)ok << (4 * t + r);
+        const float x = ok ? s[t][r] * sl2 : -INFINITY;
+        sv[4 * t + r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float pv[8];
+    float ps = 0.f;
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = fast_exp2(sv[j] - m_use);
+      ps += pv[j];
+    }
+    lsum = lsum * alpha + ps;
+    m = m_new;
+    f16x8 pf;
+    for (int j = 0; j < 8; ++j) pf[j] = (_Float16)pv[j];
+    const bool full = valid == 0xffu;
+    for (int nb = 0; nb < NB; ++nb) {
+      uint32_t w[4] = {bf16x2_to_f16x2(vr[nb][0][0]), bf16x2_to_f16x2(vr[nb][0][1]),
+                       bf16x2_to_f16x2(vr[nb][1][0]), bf16x2_to_f16x2(vr[nb][1][1])};
+      if (!full) {
+        // zero V of masked keys: their slots may hold stale or unwritten data
+        for (int j = 0; j < 8; ++j)
+          if (!((valid >> j) & 1u)) w[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
+      }
+      f16x8 vf = __builtin_bit_cast(f16x8, u32x4{w[0], w[1], w[2], w[3]});
+      o[nb] *= alpha;
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[nb], 0, 0, 0);
+    }
+  }
+
+  // merge the four waves' states (fixed order)
+  lsum += xor_lane(lsum, 16);
+  lsum += xor_lane(lsum, 32);
+  if (col < G) {
+    for (int nb = 0; nb < NB; ++nb)
+      *(f32x4*)(&red_o[wave][col][16 * nb + 4 * q4]) = o[nb];
+    if (q4 == 0) {
+      red_ml[wave][col][0] = m;
+      red_ml[wave][col][1] = lsum;
+    }
+  }
+  __syncthreads();
+  const int hq_base = kvh * G;
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int c = idx / D;
+    const int d = idx % D;
+    float M = -INFINITY;
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_ml[w][c][0]);
+    float num = 0.f, den = 0.f;
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = red_ml[w][c][0];
+      const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      num += sc * red_o[w][c][d];
+      den += sc * red_ml[w][c][1];
+    }
+    const int64_t hrow = (int64_t)i * hq + hq_base + c;
+    if (p.n_splits == 1) {
+      p.out[hrow * D + d] = num / den;
+    } else {
+      const int64_t slot = hrow * p.n_splits + split;
+      p.ws[slot * D + d] = num;
+      if (d == 0) {
+        float* ml = p.ws + (int64_t)p.num_seqs * hq * p.n_splits * D;
+        ml[2 * slot] = M;
+        ml[2 * slot + 1] = den;
+      }
+    }
+  }
+  if (p.vlen && split == 0 && kvh == 0 && threadIdx.x == 0)
+    p.vlen[i] = KIND == 0 ? L : min(L, p.window);
+}
+
+// Log-sum-exp merge of the split partial states of one (sequence, head).
+template <int D>
+__global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p) {
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int d = threadIdx.x;
+  const int sid = p.seq_ids[i];
+  if (sid < 0 || sid >= p.t.max_seqs) return;
+  const int L = p.t.seq_len[sid];
+  const int ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
+  const int64_t hrow = (int64_t)i * p.hq + h;
+  const float* ml = p.ws + (int64_t)p.num_seqs * p.hq * p.n_splits * D;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * (hrow * p.n_splits + s)]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const int64_t slot = hrow * p.n_splits + s;
+    const float sc = fast_exp2(ml[2 * slot] - M);
+    num += sc * p.ws[slot * D + d];
+    den += sc * ml[2 * slot + 1];
+  }
+  p.out[hrow * D + d] = num / den;
+}
+
+template <int D, int KIND>
+hipError_t launch_decode_g(const AttnParams& p, hipStream_t s) {
+  dim3 grid((unsigned)(p.num_seqs * p.n_splits), (unsigned)p.hkv);
+  const int g = p.hq / p.hkv;
+  switch (g) {
+    case 1: hipLaunchKernelGGL((decode_kernel<D, KIND, 1>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, KIND, 2>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, KIND, 4>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, KIND, 8>), grid, dim3(256), 0, s, p); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_splits == 1) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.num_seqs, p.hq), dim3(D), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const AttnParams& p, hipStream_t s) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  if (p.d == 128)
+    return p.kind == 0 ? launch_decode_g<128, 0>(p, s) : launch_decode_g<128, 1>(p, s);
+  return p.kind == 0 ? launch_decode_g<64, 0>(p, s) : launch_decode_g<64, 1>(p, s);
+}
+
+}  // namespace hswa

@@ -1,0 +1,137 @@
+// Pool table updates and the KV append (scatter of new K/V into pages).
+//
+// Page layout of a layer's pool (Full pool and SWA ring alike), per
+// "Following the Bottleneck: Optimizing MiniMax M3 on AMD Instinct MI355X"
+// sec. 3 (16-token pages behind a page table):
+//   K: [page][Hkv][16][d]   token-major: a key row is d contiguous bf16
+//   V: [page][Hkv][d][16]   dim-major:  the 16 tokens of one dim are
+//                           contiguous, which is the operand order of the
+//                           PV matrix product (keys are its reduction dim)
+#include <hip/hip_runtime.h>
+
+#include "device.h"
+#include "internal.h"
+
+namespace hswa {
+
+using namespace dev;
+
+// ---------------------------------------------------------------------------
+// Applies one pool operation's records to the device tables.  Block x is a
+// record (one sequence); blocks along y and threads stride over its ranges.
+__global__ void __launch_bounds__(256) pool_apply_kernel(PoolDev d, const PoolRec* recs,
+                                                         const int32_t* pages) {
+  const PoolRec r = recs[blockIdx.x];
+  const int tid = blockIdx.y * blockDim.x + threadIdx.x;
+  const int stride = gridDim.y * blockDim.x;
+  if (tid == 0) d.seq_len[r.seq] = r.new_len;
+  int32_t* row = d.fpt + (int64_t)r.seq * d.max_pages;
+  const int32_t* pg = pages + r.pg_off;
+  for (int lp = r.fpt_lo + tid; lp < r.fpt_hi; lp += stride)
+    row[lp] = r.fpt_clear ? -1 : pg[lp - r.pg_lo];
+  for (int pos = r.clr_lo + tid; pos < r.clr_hi; pos += stride) {
+    int32_t fs = pg[pos / kPage - r.pg_lo] * kPage + pos % kPage;
+    d.map[fs] = -1;
+  }
+  const int rp = d.ring_slots / kPage;
+  for (int pos = r.set_lo + tid; pos < r.set_hi; pos += stride) {
+    int32_t fs = pg[pos / kPage - r.pg_lo] * kPage + pos % kPage;
+    int32_t q = pos % d.ring_slots;
+    d.map[fs] = d.rpt[(int64_t)r.seq * rp + q / kPage] * kPage + q % kPage;
+  }
+}
+
+hipError_t launch_pool_apply(const PoolDev& d, const PoolRec* recs, int n_recs,
+                             const int32_t* pages, int64_t max_range, hipStream_t s) {
+  if (n_recs <= 0) return hipSuccess;
+  int64_t y = (max_range + 2047) / 2048;
+  if (y < 1) y = 1;
+  if (y > 64) y = 64;
+  hipLaunchKernelGGL(pool_apply_kernel, dim3(n_recs, (unsigned)y), dim3(256), 0, s, d, recs,
+                     pages);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// KV append.  One workgroup per (sequence, 16-position page tile, KV head).
+// The rows of sequence i are its last n_i positions [L - n_i, L).  Full
+// page tiles are written with 16-byte stores (K rows straight, V through
+// an LDS transpose); tiles shared with positions outside this call are
+// written element by element so those positions are untouched.
+template <int D, int KIND>
+__global__ void __launch_bounds__(256) append_kernel(AttnParams p, int tiles_per_seq) {
+  __shared__ uint16_t vt[kPage][D + 8];
+  const int i = blockIdx.x / tiles_per_seq;
+  const int t = blockIdx.x % tiles_per_seq;
+  const int h = blockIdx.y;
+  const int sid = p.seq_ids[i];
+  if (sid < 0 || sid >= p.t.max_seqs) return;  // invalid id: nothing to write
+  const int row0 = p.cu_q ? p.cu_q[i] : i;
+  const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
+  const int L = p.t.seq_len[sid];
+  const int p0 = L - n;
+  const int tile_pos = (p0 / kPage + t) * kPage;
+  if (n <= 0 || n > L || tile_pos >= L) return;
+  const int lo = max(tile_pos, p0);
+  const int hi = min(tile_pos + kPage, L);
+  const bool whole = (lo == tile_pos) && (hi == tile_pos + kPage);
+  const int32_t page = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile_pos, p.t.max_pages,
+                                     p.t.ring_slots);
+  if (page < 0) return;  // position without a page: the caller skipped alloc
+  const int hkv = p.hkv;
+  uint16_t* kdst = p.k_cache + ((int64_t)page * hkv + h) * kPage * D;
+  uint16_t* vdst = p.v_cache + ((int64_t)page * hkv + h) * D * kPage;
+  constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  const int tid = threadIdx.x;
+  // K rows and the V tile into LDS
+  if (tid < kPage * kChunks) {
+    const int tok = tid / kChunks;
+    const int c = tid % kChunks;
+    const int pos = tile_pos + tok;
+    if (pos >= lo && pos < hi) {
+      const int64_t row = row0 + (pos - p0);
+      const u32x4 kv = *(const u32x4*)(p.k_new + (row * hkv + h) * D + c * 8);
+      *(u32x4*)(kdst + tok * D + c * 8) = kv;
+      const u32x4 vv = *(const u32x4*)(p.v_new + (row * hkv + h) * D + c * 8);
+      *(u32x4*)(&vt[tok][c * 8]) = vv;
+    }
+  }
+  __syncthreads();
+  // V^T: thread (e, half) owns 8 tokens of dim e
+  if (tid < D * 2) {
+    const int e = tid >> 1;
+    const int half = tid & 1;
+    uint16_t* dst = vdst + e * kPage + half * 8;
+    if (whole) {
+      u32x4 w;
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)vt[half * 8 + 2 * j][e] | ((uint32_t)vt[half * 8 + 2 * j + 1][e] << 16);
+      *(u32x4*)dst = w;
+    } else {
+      for (int j = 0; j < 8; ++j) {
+        const int pos = tile_pos + half * 8 + j;
+        if (pos >= lo && pos < hi) dst[j] = vt[half * 8 + j][e];
+      }
+    }
+  }
+}
+
+hipError_t launch_append(const AttnParams& p, hipStream_t s) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  const int tiles = (p.max_q_len + 14) / kPage + 1;
+  dim3 grid((unsigned)(p.num_seqs * tiles), (unsigned)p.hkv);
+  if (p.d == 128) {
+    if (p.kind == 0)
+      hipLaunchKernelGGL((append_kernel<128, 0>), grid, dim3(256), 0, s, p, tiles);
+    else
+      hipLaunchKernelGGL((append_kernel<128, 1>), grid, dim3(256), 0, s, p, tiles);
+  } else {
+    if (p.kind == 0)
+      hipLaunchKernelGGL((append_kernel<64, 0>), grid, dim3(256), 0, s, p, tiles);
+    else
+      hipLaunchKernelGGL((append_kernel<64, 1>), grid, dim3(256), 0, s, p, tiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hswa

@@ -1,0 +1,546 @@
+// Dual KV pool bookkeeping: Full page allocator, per-sequence SWA rings,
+// the Full-to-SWA map and window eviction.
+//
+// Follows "MiMo-V2.5 Series Inference Full-Link Optimization" sec. 2.1
+// ("KVCache Dual Pool": Full pool O(N) and SWA pool O(W); Full index
+// authoritative with a Full-to-SWA map; joint capacity check; "SWA-aware
+// prefix cache tree" point 2: release out-of-window SWA entries per chunk,
+// per request end and as decode advances) and the 16-token page tables of
+// "Following the Bottleneck: Optimizing MiniMax M3 on AMD Instinct MI355X"
+// sec. 3.
+//
+// The host keeps the authoritative metadata.  Each operation computes its
+// effect on the host, then enqueues one small kernel that applies the same
+// effect to the caller's device tables.  The kernel reads a compact record
+// list (position ranges and page ids, not per-slot values) straight from a
+// pinned, device-readable staging buffer; a ring of staging buffers with
+// one event each keeps the host from overwriting a buffer the device has
+// not read yet.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/hswa.h"
+#include "internal.h"
+
+using hswa::PoolRec;
+
+namespace {
+
+constexpr int kPage = HSWA_PAGE_SIZE;
+constexpr int kStages = 4;
+
+struct Stage {
+  void* buf = nullptr;       // pinned host memory, device-readable
+  size_t cap = 0;
+  hipEvent_t done = nullptr; // recorded after the apply kernel that read it
+  bool pending = false;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct hswa_pool {
+  int32_t W = 0, C = 0, max_seqs = 0, max_pages = 0, num_pages = 0;
+  int32_t ring_pages_per_seq = 0;
+  // host metadata
+  std::vector<int32_t> len;        // tokens per sequence
+  std::vector<int32_t> res_start;  // first position still in the SWA ring
+  std::vector<int32_t> npages;     // Full pages held per sequence
+  std::vector<int32_t> fpt;        // [max_seqs][max_pages]
+  std::vector<int32_t> rpt;        // [max_seqs][C/16]
+  std::vector<int32_t> map;        // [num_pages*16]
+  std::vector<int32_t> freeq;      // FIFO ring of free pages
+  int64_t fhead = 0, fcount = 0;
+  std::vector<uint32_t> mark;      // per-sequence epoch for duplicate checks
+  uint32_t epoch = 0;
+  // device mirror
+  bool has_dev = false;
+  hswa::PoolDev dev{};
+  Stage stage[kStages];
+  int next_stage = 0;
+  std::vector<void*> retired;      // outgrown staging buffers, freed at destroy
+
+  int32_t pop_page() {
+    int32_t p = freeq[fhead];
+    fhead = (fhead + 1) % num_pages;
+    --fcount;
+    return p;
+  }
+  void push_page(int32_t p) {
+    freeq[(fhead + fcount) % num_pages] = p;
+    ++fcount;
+  }
+  int32_t full_slot(int32_t b, int32_t pos) const {
+    return fpt[(size_t)b * max_pages + pos / kPage] * kPage + pos % kPage;
+  }
+  int32_t swa_slot(int32_t b, int32_t pos) const {
+    int32_t r = pos % C;
+    return rpt[(size_t)b * ring_pages_per_seq + r / kPage] * kPage + r % kPage;
+  }
+};
+
+namespace {
+
+// Validates a list of sequence ids (range, no repeats).
+int check_ids(hswa_pool* p, int32_t n, const int32_t* ids) {
+  if (n < 0) {
+    hswa::set_error("n_seqs must be >= 0 (got %d)", n);
+    return HSWA_E_INVAL;
+  }
+  if (n > 0 && !ids) {
+    hswa::set_error("seq_ids is NULL");
+    return HSWA_E_INVAL;
+  }
+  if (++p->epoch == 0) {
+    std::fill(p->mark.begin(), p->mark.end(), 0u);
+    p->epoch = 1;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = ids[i];
+    if (b < 0 || b >= p->max_seqs) {
+      hswa::set_error("sequence id %d out of range [0, %d)", b, p->max_seqs);
+      return HSWA_E_INVAL;
+    }
+    if (p->mark[b] == p->epoch) {
+      hswa::set_error("sequence id %d listed twice", b);
+      return HSWA_E_INVAL;
+    }
+    p->mark[b] = p->epoch;
+  }
+  return HSWA_OK;
+}
+
+// Builds a record covering the given position ranges and fpt writes; the
+// record's page list spans every logical page any of them touches.
+struct RecBuilder {
+  std::vector<PoolRec> recs;
+  std::vector<int32_t> pages;
+  int64_t max_range = 0;
+
+  void add(const hswa_pool* p, int32_t b, int32_t new_len, int32_t clr_lo,
+           int32_t clr_hi, int32_t set_lo, int32_t set_hi, int32_t fpt_lo,
+           int32_t fpt_hi, int32_t fpt_clear, const int32_t* page_src) {
+    PoolRec r{};
+    r.seq = b;
+    r.new_len = new_len;
+    r.clr_lo = clr_lo;
+    r.clr_hi = std::max(clr_lo, clr_hi);
+    r.set_lo = set_lo;
+    r.set_hi = std::max(set_lo, set_hi);
+    r.fpt_lo = fpt_lo;
+    r.fpt_hi = std::max(fpt_lo, fpt_hi);
+    r.fpt_clear = fpt_clear;
+    int64_t lo = INT64_MAX, hi = INT64_MIN;  // logical pages [lo, hi)
+    if (r.clr_hi > r.clr_lo) {
+      lo = std::min<int64_t>(lo, r.clr_lo / kPage);
+      hi = std::max<int64_t>(hi, (r.clr_hi - 1) / kPage + 1);
+    }
+    if (r.set_hi > r.set_lo) {
+      lo = std::min<int64_t>(lo, r.set_lo / kPage);
+      hi = std::max<int64_t>(hi, (r.set_hi - 1) / kPage + 1);
+    }
+    if (r.fpt_hi > r.fpt_lo && !fpt_clear) {
+      lo = std::min<int64_t>(lo, r.fpt_lo);
+      hi = std::max<int64_t>(hi, r.fpt_hi);
+    }
+    if (hi <= lo) {
+      lo = 0;
+      hi = 0;
+    }
+    r.pg_lo = (int32_t)lo;
+    r.pg_off = (int32_t)pages.size();
+    for (int64_t lp = lo; lp < hi; ++lp) pages.push_back(page_src[lp]);
+    recs.push_back(r);
+    max_range = std::max<int64_t>(max_range, r.clr_hi - r.clr_lo);
+    max_range = std::max<int64_t>(max_range, r.set_hi - r.set_lo);
+    max_range = std::max<int64_t>(max_range, r.fpt_hi - r.fpt_lo);
+  }
+};
+
+// Copies the records into a staging buffer and enqueues the apply kernel.
+int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
+  if (!p->has_dev || rb.recs.empty()) return HSWA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  size_t rec_bytes = rb.recs.size() * sizeof(PoolRec);
+  size_t bytes = rec_bytes + rb.pages.size() * sizeof(int32_t);
+  Stage& st = p->stage[p->next_stage];
+  p->next_stage = (p->next_stage + 1) % kStages;
+  if (st.pending) {
+    hipError_t e = hipEventSynchronize(st.done);
+    if (e != hipSuccess) return hswa::hip_fail(e, "waiting for a pool staging buffer");
+    st.pending = false;
+  }
+  if (st.cap < bytes) {
+    if (st.buf) p->retired.push_back(st.buf);
+    st.buf = nullptr;
+    size_t cap = std::max<size_t>(bytes + bytes / 2, 64 << 10);
+    hipError_t e = hipHostMalloc(&st.buf, cap, hipHostMallocCoherent | hipHostMallocMapped);
+    if (e != hipSuccess) {
+      st.cap = 0;
+      return hswa::hip_fail(e, "hipHostMalloc of a pool staging buffer");
+    }
+    st.cap = cap;
+  }
+  memcpy(st.buf, rb.recs.data(), rec_bytes);
+  if (!rb.pages.empty())
+    memcpy((char*)st.buf + rec_bytes, rb.pages.data(), rb.pages.size() * sizeof(int32_t));
+  void* dptr = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&dptr, st.buf, 0);
+  if (e != hipSuccess) return hswa::hip_fail(e, "hipHostGetDevicePointer");
+  e = hswa::launch_pool_apply(p->dev, (const PoolRec*)dptr, (int)rb.recs.size(),
+                              (const int32_t*)((char*)dptr + rec_bytes), rb.max_range, s);
+  if (e != hipSuccess) return hswa::hip_fail(e, "pool table update launch");
+  e = hipEventRecord(st.done, s);
+  if (e != hipSuccess) return hswa::hip_fail(e, "hipEventRecord");
+  st.pending = true;
+  return HSWA_OK;
+}
+
+// Shared body of alloc (ring checked) and import (ring not checked; only
+// in-window positions get SWA slots).
+int alloc_impl(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new,
+               int32_t* full_out, int32_t* swa_out, void* stream, bool importing) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  int rc = check_ids(p, n, ids);
+  if (rc) return rc;
+  if (n > 0 && !n_new) {
+    hswa::set_error("n_new is NULL");
+    return HSWA_E_INVAL;
+  }
+  // Joint capacity check before any change ([MiMo] 2.1 Scheduling
+  // Constraints): Full pages for all listed sequences together, the page
+  // table row of each, and (alloc only) each SWA ring.
+  int64_t need_pages = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = ids[i];
+    int64_t k = n_new[i];
+    if (k < 0) {
+      hswa::set_error("n_new[%d] = %lld is negative", i, (long long)k);
+      return HSWA_E_INVAL;
+    }
+    int64_t new_len = (int64_t)p->len[b] + k;
+    if (new_len > (int64_t)INT32_MAX - kPage) {
+      hswa::set_error("sequence %d would exceed the int32 position range", b);
+      return HSWA_E_INVAL;
+    }
+    int64_t pages = ceil_div(new_len, kPage);
+    if (pages > p->max_pages) {
+      hswa::set_error("sequence %d needs %lld pages, its table row holds %d", b,
+                      (long long)pages, p->max_pages);
+      return HSWA_E_NOSPC;
+    }
+    need_pages += pages - p->npages[b];
+    if (!importing && (int64_t)(p->len[b] - p->res_start[b]) + k > p->C) {
+      hswa::set_error("SWA ring of sequence %d: %d resident + %lld new > %d slots", b,
+                      p->len[b] - p->res_start[b], (long long)k, p->C);
+      return HSWA_E_NOSPC;
+    }
+  }
+  if (need_pages > p->fcount) {
+    hswa::set_error("Full pool: %lld pages needed, %lld free", (long long)need_pages,
+                    (long long)p->fcount);
+    return HSWA_E_NOSPC;
+  }
+  RecBuilder rb;
+  size_t o = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = ids[i];
+    int32_t L = p->len[b];
+    int32_t k = n_new[i];
+    int32_t new_len = L + k;
+    int32_t old_pages = p->npages[b];
+    int32_t keep_from = importing ? std::max(0, new_len - p->W + 1) : 0;
+    int32_t clr_lo = p->res_start[b], clr_hi = clr_lo;
+    if (importing) {
+      clr_hi = std::max(clr_lo, std::min(keep_from, L));
+      for (int32_t pos = clr_lo; pos < clr_hi; ++pos) p->map[p->full_slot(b, pos)] = -1;
+      p->res_start[b] = std::max(p->res_start[b], keep_from);
+    }
+    int32_t* row = &p->fpt[(size_t)b * p->max_pages];
+    for (int32_t pos = L; pos < new_len; ++pos) {
+      if (pos % kPage == 0) row[pos / kPage] = p->pop_page();
+      int32_t fs = p->full_slot(b, pos);
+      int32_t ss = -1;
+      if (pos >= keep_from) {
+        ss = p->swa_slot(b, pos);
+        p->map[fs] = ss;
+      }
+      if (full_out) full_out[o] = fs;
+      if (swa_out) swa_out[o] = ss;
+      ++o;
+    }
+    p->npages[b] = (int32_t)ceil_div(new_len, kPage);
+    p->len[b] = new_len;
+    if (p->has_dev)
+      rb.add(p, b, new_len, clr_lo, clr_hi, std::max(L, keep_from), new_len, old_pages,
+             p->npages[b], 0, row);
+  }
+  return flush(p, rb, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int hswa_pool_create(const hswa_pool_desc* d, hswa_pool** out) {
+  hswa::clear_error();
+  if (!d || !out) {
+    hswa::set_error("desc and out must be non-NULL");
+    return HSWA_E_INVAL;
+  }
+  *out = nullptr;
+  if (d->page_size != kPage) {
+    hswa::set_error("page_size must be 16 (got %d)", d->page_size);
+    return HSWA_E_INVAL;
+  }
+  if (d->window < 1 || d->ring_slots < d->window || d->ring_slots % kPage != 0) {
+    hswa::set_error("need window >= 1 and ring_slots >= window, a multiple of 16 "
+                    "(window %d, ring_slots %d)", d->window, d->ring_slots);
+    return HSWA_E_INVAL;
+  }
+  if (d->max_seqs < 1 || d->max_pages_per_seq < 1 || d->num_full_pages < 1) {
+    hswa::set_error("max_seqs, max_pages_per_seq and num_full_pages must be >= 1");
+    return HSWA_E_INVAL;
+  }
+  if ((int64_t)d->num_full_pages * kPage > INT32_MAX ||
+      (int64_t)d->max_seqs * (d->ring_slots / kPage) * kPage > INT32_MAX ||
+      (int64_t)d->max_pages_per_seq * kPage > INT32_MAX) {
+    hswa::set_error("pool too large for int32 slot ids");
+    return HSWA_E_INVAL;
+  }
+  if (!d->full_free_order || !d->ring_pages) {
+    hswa::set_error("full_free_order and ring_pages must be given");
+    return HSWA_E_INVAL;
+  }
+  int ndev = (d->dev_seq_len != nullptr) + (d->dev_fpt != nullptr) +
+             (d->dev_rpt != nullptr) + (d->dev_map != nullptr);
+  if (ndev != 0 && ndev != 4) {
+    hswa::set_error("give all four device tables or none");
+    return HSWA_E_INVAL;
+  }
+  hswa_pool* p = new (std::nothrow) hswa_pool();
+  if (!p) {
+    hswa::set_error("out of host memory");
+    return HSWA_E_INVAL;
+  }
+  p->W = d->window;
+  p->C = d->ring_slots;
+  p->max_seqs = d->max_seqs;
+  p->max_pages = d->max_pages_per_seq;
+  p->num_pages = d->num_full_pages;
+  p->ring_pages_per_seq = d->ring_slots / kPage;
+  try {
+    // both page lists must be permutations
+    std::vector<uint8_t> seen((size_t)p->num_pages, 0);
+    for (int32_t i = 0; i < p->num_pages; ++i) {
+      int32_t v = d->full_free_order[i];
+      if (v < 0 || v >= p->num_pages || seen[v]) {
+        hswa::set_error("full_free_order is not a permutation of 0..%d", p->num_pages - 1);
+        delete p;
+        return HSWA_E_INVAL;
+      }
+      seen[v] = 1;
+    }
+    int64_t nring = (int64_t)p->max_seqs * p->ring_pages_per_seq;
+    std::vector<uint8_t> rseen((size_t)nring, 0);
+    for (int64_t i = 0; i < nring; ++i) {
+      int32_t v = d->ring_pages[i];
+      if (v < 0 || v >= nring || rseen[v]) {
+        hswa::set_error("ring_pages is not a permutation of 0..%lld", (long long)nring - 1);
+        delete p;
+        return HSWA_E_INVAL;
+      }
+      rseen[v] = 1;
+    }
+    p->len.assign(p->max_seqs, 0);
+    p->res_start.assign(p->max_seqs, 0);
+    p->npages.assign(p->max_seqs, 0);
+    p->mark.assign(p->max_seqs, 0);
+    p->fpt.assign((size_t)p->max_seqs * p->max_pages, -1);
+    p->rpt.assign(d->ring_pages, d->ring_pages + nring);
+    p->map.assign((size_t)p->num_pages * kPage, -1);
+    p->freeq.assign(d->full_free_order, d->full_free_order + p->num_pages);
+    p->fhead = 0;
+    p->fcount = p->num_pages;
+  } catch (const std::bad_alloc&) {
+    hswa::set_error("out of host memory");
+    delete p;
+    return HSWA_E_INVAL;
+  }
+  if (ndev == 4) {
+    p->has_dev = true;
+    p->dev.seq_len = d->dev_seq_len;
+    p->dev.fpt = d->dev_fpt;
+    p->dev.rpt = d->dev_rpt;
+    p->dev.map = d->dev_map;
+    p->dev.max_pages = p->max_pages;
+    p->dev.ring_slots = p->C;
+    struct {
+      void* dst;
+      const void* src;
+      size_t bytes;
+    } copies[] = {
+        {d->dev_seq_len, p->len.data(), p->len.size() * 4},
+        {d->dev_fpt, p->fpt.data(), p->fpt.size() * 4},
+        {d->dev_rpt, p->rpt.data(), p->rpt.size() * 4},
+        {d->dev_map, p->map.data(), p->map.size() * 4},
+    };
+    for (auto& c : copies) {
+      hipError_t e = hipMemcpy(c.dst, c.src, c.bytes, hipMemcpyHostToDevice);
+      if (e != hipSuccess) {
+        int rc = hswa::hip_fail(e, "initial device table copy");
+        delete p;
+        return rc;
+      }
+    }
+    for (auto& st : p->stage) {
+      hipError_t e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        int rc = hswa::hip_fail(e, "hipEventCreate");
+        hswa_pool_destroy(p);
+        return rc;
+      }
+    }
+  }
+  *out = p;
+  return HSWA_OK;
+}
+
+void hswa_pool_destroy(hswa_pool* p) {
+  if (!p) return;
+  for (auto& st : p->stage) {
+    if (st.pending) hipEventSynchronize(st.done);
+    if (st.done) hipEventDestroy(st.done);
+    if (st.buf) hipHostFree(st.buf);
+  }
+  for (void* b : p->retired) hipHostFree(b);
+  delete p;
+}
+
+int hswa_pool_get_view(const hswa_pool* p, hswa_pool_view* out) {
+  hswa::clear_error();
+  if (!p || !out) {
+    hswa::set_error("pool and out must be non-NULL");
+    return HSWA_E_INVAL;
+  }
+  if (!p->has_dev) {
+    hswa::set_error("pool has no device tables");
+    return HSWA_E_INVAL;
+  }
+  out->seq_len = p->dev.seq_len;
+  out->fpt = p->dev.fpt;
+  out->rpt = p->dev.rpt;
+  out->map = p->dev.map;
+  out->max_seqs = p->max_seqs;
+  out->max_pages_per_seq = p->max_pages;
+  out->ring_slots = p->C;
+  out->window = p->W;
+  return HSWA_OK;
+}
+
+int hswa_pool_alloc(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new,
+                    int32_t* full_out, int32_t* swa_out, void* stream) {
+  return alloc_impl(p, n, ids, n_new, full_out, swa_out, stream, false);
+}
+
+int hswa_pool_import(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new,
+                     int32_t* full_out, int32_t* swa_out, void* stream) {
+  return alloc_impl(p, n, ids, n_new, full_out, swa_out, stream, true);
+}
+
+int hswa_pool_evict(hswa_pool* p, int32_t n, const int32_t* ids, int32_t* evicted_out,
+                    int64_t evicted_cap, int32_t* counts_out, void* stream) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  int rc = check_ids(p, n, ids);
+  if (rc) return rc;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = ids[i];
+    int32_t keep_from = std::max(0, p->len[b] - p->W + 1);
+    total += std::max(0, keep_from - p->res_start[b]);
+  }
+  if (evicted_out && total > evicted_cap) {
+    hswa::set_error("evicted_out holds %lld entries, %lld needed", (long long)evicted_cap,
+                    (long long)total);
+    return HSWA_E_INVAL;
+  }
+  RecBuilder rb;
+  int64_t o = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = ids[i];
+    int32_t keep_from = std::max(0, p->len[b] - p->W + 1);
+    int32_t lo = p->res_start[b];
+    int32_t cnt = std::max(0, keep_from - lo);
+    for (int32_t pos = lo; pos < lo + cnt; ++pos) {
+      int32_t fs = p->full_slot(b, pos);
+      p->map[fs] = -1;
+      if (evicted_out) evicted_out[o] = fs;
+      ++o;
+    }
+    if (counts_out) counts_out[i] = cnt;
+    p->res_start[b] = std::max(lo, keep_from);
+    if (p->has_dev && cnt > 0)
+      rb.add(p, b, p->len[b], lo, lo + cnt, 0, 0, 0, 0, 0,
+             &p->fpt[(size_t)b * p->max_pages]);
+  }
+  return flush(p, rb, stream);
+}
+
+int hswa_pool_release(hswa_pool* p, int32_t n, const int32_t* ids, void* stream) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  int rc = check_ids(p, n, ids);
+  if (rc) return rc;
+  RecBuilder rb;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = ids[i];
+    int32_t* row = &p->fpt[(size_t)b * p->max_pages];
+    int32_t lo = p->res_start[b], hi = p->len[b];
+    for (int32_t pos = lo; pos < hi; ++pos) p->map[p->full_slot(b, pos)] = -1;
+    if (p->has_dev) rb.add(p, b, 0, lo, hi, 0, 0, 0, p->npages[b], 1, row);
+    for (int32_t lp = 0; lp < p->npages[b]; ++lp) {
+      p->push_page(row[lp]);
+      row[lp] = -1;
+    }
+    p->npages[b] = 0;
+    p->len[b] = 0;
+    p->res_start[b] = 0;
+  }
+  return flush(p, rb, stream);
+}
+
+int hswa_pool_read_tables(const hswa_pool* p, int32_t* seq_len, int32_t* fpt,
+                          int32_t* map, int32_t* free_pages, int32_t* n_free) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  if (seq_len) memcpy(seq_len, p->len.data(), p->len.size() * 4);
+  if (fpt) memcpy(fpt, p->fpt.data(), p->fpt.size() * 4);
+  if (map) memcpy(map, p->map.data(), p->map.size() * 4);
+  if (free_pages)
+    for (int64_t i = 0; i < p->fcount; ++i)
+      free_pages[i] = p->freeq[(p->fhead + i) % p->num_pages];
+  if (n_free) *n_free = (int32_t)p->fcount;
+  return HSWA_OK;
+}
+
+}  // extern "C"

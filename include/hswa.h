@@ -1,0 +1,257 @@
+/*
+ * hswa.h -- C ABI of the Hybrid Sliding-Window Attention hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (sources, cited by page title and section):
+ *
+ *   [MiMo]  "MiMo-V2.5 Series Inference Full-Link Optimization: Pushing
+ *           Hybrid SWA Efficiency to the Extreme" (mimo.mi.com).
+ *           Sec. 1.1: most layers are SWA layers that attend only to the last
+ *           W = 128 tokens, a few Full layers attend to the whole prefix;
+ *           chunked prefill is roughly compute-bound.  Sec. 1.2: decode is
+ *           roughly bound by the bytes of KV it reads.  Sec. 2.1 "KVCache
+ *           Dual Pool": a Full pool of O(N) and a SWA pool of O(W) with its
+ *           own window eviction, one logical sequence view in which the Full
+ *           index is authoritative plus a Full-to-SWA map, and a joint
+ *           capacity check on admission.  Sec. 2.1 "SWA-aware prefix cache
+ *           tree", point 2: out-of-window SWA entries are released when a
+ *           prefill chunk completes and as decode advances.
+ *   [vLLM]  "Following the Bottleneck: Optimizing MiniMax M3 on AMD Instinct
+ *           MI355X" (vLLM blog), sec. 3 "Which bytes move?": KV addressed as
+ *           16-token pages through a per-sequence page table.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every function returns HSWA_OK (0) or a negative hswa_status.  The
+ *    text of the last failure on the calling thread is hswa_last_error().
+ *    No C++ exception crosses this boundary.
+ *  - "host" pointers are ordinary CPU memory; "device" pointers are GPU
+ *    memory of the current HIP device, owned by the caller.  The library
+ *    allocates no device memory.  Device pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    All device work is enqueued on it, asynchronously; nothing waits for
+ *    the device except where a function says so.
+ *  - Outputs never alias inputs.  Calls that use one pool, or one layer's
+ *    K/V buffers, from several host threads at once are not supported.
+ *  - bf16 tensors are passed as raw 16-bit words (void*).
+ *
+ * Memory layout of a layer's K/V pool (Full pool or SWA ring alike):
+ *    K: [num_pages][Hkv][16][head_dim]  bf16   (token-major in a page)
+ *    V: [num_pages][Hkv][head_dim][16]  bf16   (dim-major in a page)
+ *  A token's slot is page * 16 + offset.  One (page, head) block is
+ *  16 * head_dim * 2 bytes contiguous for K and for V.  V values must be
+ *  finite with |v| < 65504: the PV product runs in fp16 (bf16 -> fp16 is
+ *  exact in that range).
+ */
+#ifndef HSWA_H
+#define HSWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hswa_status {
+  HSWA_OK = 0,
+  HSWA_E_INVAL = -1,       /* bad argument, size, alignment or shape       */
+  HSWA_E_NOSPC = -2,       /* joint Full/SWA capacity check failed; the
+                              pool is unchanged                             */
+  HSWA_E_HIP = -3,         /* a HIP runtime call or kernel launch failed    */
+  HSWA_E_UNSUPPORTED = -4  /* valid request outside what is built          */
+} hswa_status;
+
+typedef enum hswa_layer_kind {
+  HSWA_LAYER_FULL = 0,     /* keys 0..i of query position i ([MiMo] 1.1)  */
+  HSWA_LAYER_SWA = 1       /* keys max(0, i-W+1)..i, W keys counting the
+                              query itself ([MiMo] 1.1; 2.1 prefix tree,
+                              point 1 counts the window the same way)     */
+} hswa_layer_kind;
+
+#define HSWA_PAGE_SIZE 16
+
+/* Text of the last failure on this thread ("" if none).  Never NULL. */
+const char* hswa_last_error(void);
+/* Static name of a status code. */
+const char* hswa_status_string(int status);
+/* Library version as major*10000 + minor*100 + patch. */
+int hswa_version(void);
+
+/* ------------------------------------------------------------------------
+ * Dual KV pool: slot bookkeeping ([MiMo] 2.1 "KVCache Dual Pool")
+ *
+ * The pool owns host metadata only.  It mirrors four caller-owned device
+ * tables that the attention kernels read:
+ *   seq_len [max_seqs]                       tokens stored per sequence
+ *   fpt     [max_seqs * max_pages_per_seq]   Full page table, -1 = none
+ *   rpt     [max_seqs * ring_slots/16]       SWA ring page table (fixed)
+ *   map     [num_full_pages * 16]            Full slot -> SWA slot, -1 = no
+ *                                            SWA entry (evicted or never)
+ * Slot rules (integer, exact):
+ *   full_slot(b, pos) = fpt[b][pos / 16] * 16 + pos % 16
+ *   swa_slot(b, pos)  = rpt[b][(pos mod C) / 16] * 16 + (pos mod C) % 16
+ * A sequence's Full page for position pos is taken from the head of a FIFO
+ * free list when pos % 16 == 0; within a call sequences are served in the
+ * order listed, positions ascending.  The SWA pool of a sequence is a ring
+ * of C = ring_slots slots; after eviction at length L exactly the last
+ * min(L, W-1) positions stay resident, which is what the next query needs.
+ * -------------------------------------------------------------------- */
+
+typedef struct hswa_pool hswa_pool;
+
+typedef struct hswa_pool_desc {
+  int32_t page_size;          /* must be 16                                  */
+  int32_t window;             /* W >= 1                                      */
+  int32_t ring_slots;         /* C: multiple of 16, C >= W                   */
+  int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1            */
+  int32_t max_pages_per_seq;  /* row length of fpt                           */
+  int32_t num_full_pages;     /* Full pool size in pages                     */
+  const int32_t* full_free_order; /* host [num_full_pages]: initial free list,
+                                     a permutation of 0..num_full_pages-1   */
+  const int32_t* ring_pages;  /* host [max_seqs * C/16]: ring page ids of
+                                 each sequence, a permutation of
+                                 0..max_seqs*C/16-1                          */
+  /* Device tables (caller-owned, int32).  All four NULL gives a host-only
+     pool (bookkeeping without a device mirror); otherwise all four must be
+     set.  hswa_pool_create fills them synchronously.                        */
+  int32_t* dev_seq_len;
+  int32_t* dev_fpt;
+  int32_t* dev_rpt;
+  int32_t* dev_map;
+} hswa_pool_desc;
+
+/* Device-table view of a pool, read by the attention entry points. */
+typedef struct hswa_pool_view {
+  const int32_t* seq_len;
+  const int32_t* fpt;
+  const int32_t* rpt;
+  const int32_t* map;
+  int32_t max_seqs;
+  int32_t max_pages_per_seq;
+  int32_t ring_slots;
+  int32_t window;
+} hswa_pool_view;
+
+/* Validates desc, copies it, writes the initial device tables (seq_len = 0,
+   fpt = -1, rpt = ring_pages, map = -1) with a blocking copy.  *out owns
+   host memory only; release it with hswa_pool_destroy. */
+int hswa_pool_create(const hswa_pool_desc* desc, hswa_pool** out);
+/* Waits for the pool's pending table updates, then frees host state.
+   NULL is a no-op. */
+void hswa_pool_destroy(hswa_pool* pool);
+/* Fills *out with the device tables and geometry ([MiMo] 2.1). */
+int hswa_pool_get_view(const hswa_pool* pool, hswa_pool_view* out);
+
+/* Step "alloc" ([MiMo] 2.1 Dual Pool; Scheduling Constraints): gives Full
+ * and SWA slots to n_new[i] >= 0 new positions of sequence seq_ids[i]
+ * (host arrays of length n_seqs, ids distinct).  The joint check runs first
+ * and nothing changes if it fails (HSWA_E_NOSPC): the Full free list must
+ * hold every page the call needs, each sequence's page-table row must fit,
+ * and each ring must hold resident_b + n_new_b <= C.
+ * full_slots_out / swa_slots_out (host, nullable) receive sum(n_new)
+ * entries: sequences in the order listed, positions ascending.  The device
+ * tables (seq_len, fpt, map) are updated on `stream`. */
+int hswa_pool_alloc(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
+                    const int32_t* n_new, int32_t* full_slots_out,
+                    int32_t* swa_slots_out, void* stream);
+
+/* Step "evict" ([MiMo] 2.1 prefix tree, point 2): for each listed sequence
+ * of length L, releases the SWA entry of every resident position
+ * pos <= L - W (map[full_slot] = -1).  The library computes the set itself,
+ * so an in-window position can never be evicted.  evicted_out (host,
+ * nullable, capacity evicted_cap entries) receives the Full slots released,
+ * ascending position per sequence, sequences in the order listed;
+ * counts_out (host, nullable, n_seqs entries) the number per sequence.
+ * HSWA_E_INVAL, with nothing changed, if evicted_cap is too small. */
+int hswa_pool_evict(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
+                    int32_t* evicted_out, int64_t evicted_cap,
+                    int32_t* counts_out, void* stream);
+
+/* Appends n_new[i] positions whose K/V the caller stores directly, e.g. a
+ * context restored from another cache tier where only the in-window SWA KV
+ * moves ([MiMo] 2.1 Dual Pool, "Data Transfer").  Every new position gets a
+ * Full slot; only positions inside the window of the new length get SWA
+ * slots (others report -1), and resident positions that leave the window are
+ * released as by hswa_pool_evict.  The ring check does not apply; the Full
+ * check does (HSWA_E_NOSPC, nothing changed). */
+int hswa_pool_import(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
+                     const int32_t* n_new, int32_t* full_slots_out,
+                     int32_t* swa_slots_out, void* stream);
+
+/* Ends the listed requests ([MiMo] 2.1 prefix tree, point 2, "request
+ * end"): their Full pages return to the tail of the free list in logical
+ * page order, their SWA entries are dropped, their length becomes 0. */
+int hswa_pool_release(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
+                      void* stream);
+
+/* Host copies of the pool's metadata for inspection (each pointer nullable):
+ * seq_len [max_seqs], fpt [max_seqs*max_pages_per_seq], map
+ * [num_full_pages*16], free_pages [num_full_pages] (free list head first)
+ * with its length in *n_free. */
+int hswa_pool_read_tables(const hswa_pool* pool, int32_t* seq_len, int32_t* fpt,
+                          int32_t* map, int32_t* free_pages, int32_t* n_free);
+
+/* ------------------------------------------------------------------------
+ * Attention over the dual pool
+ * -------------------------------------------------------------------- */
+
+typedef struct hswa_attn_args {
+  int32_t kind;             /* hswa_layer_kind                              */
+  int32_t window;           /* SWA: 1 <= window <= pool window; FULL: unused */
+  int32_t num_q_heads;      /* Hq                                           */
+  int32_t num_kv_heads;     /* Hkv; Hq / Hkv in {1, 2, 4, 8}                 */
+  int32_t head_dim;         /* 64 or 128                                    */
+  float scale;              /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t num_seqs;         /* sequences in this call                       */
+  const int32_t* seq_ids;   /* device [num_seqs], distinct pool sequence ids */
+  const int32_t* cu_q;      /* device [num_seqs+1], row offsets of each
+                               sequence's query rows (prefill only)         */
+  int32_t total_q;          /* rows of q / out (prefill: cu_q[num_seqs];
+                               decode: num_seqs)                            */
+  int32_t max_q_len;        /* prefill: max rows of one sequence (host hint
+                               sizing the grid; must be >= the true max)     */
+  int32_t max_seq_len;      /* decode: >= every listed sequence's length     */
+  const void* q;            /* device bf16 [total_q][Hq][head_dim]          */
+  const void* k_new;        /* device bf16 [total_q][Hkv][head_dim] or NULL  */
+  const void* v_new;        /* device bf16 [total_q][Hkv][head_dim] or NULL  */
+  hswa_pool_view pool;      /* from hswa_pool_get_view                      */
+  void* k_cache;            /* this layer's K pages: the Full pool for FULL
+                               layers, the SWA ring pool for SWA layers     */
+  void* v_cache;            /* this layer's V pages (layout above)          */
+  float* out;               /* device fp32 [total_q][Hq][head_dim]          */
+  int32_t* vlen_out;        /* device int32 [total_q] or NULL: number of keys
+                               each query row attended to                   */
+} hswa_attn_args;
+
+/* Chunked prefill of one layer ([MiMo] 1.1 chunked prefill; 2.1 prefix
+ * tree, point 2).  The query rows of sequence i are its LAST
+ * (cu_q[i+1]-cu_q[i]) positions, i.e. the tokens just given slots by
+ * hswa_pool_alloc: row r is position seq_len - n_i + (r - cu_q[i]).  When
+ * k_new/v_new are set they are first written into k_cache/v_cache at those
+ * positions' slots (Full slots for FULL layers, SWA ring slots for SWA
+ * layers); then each row attends to its keys through the page tables.
+ * Every needed key must be resident, which holds when the caller allocates
+ * the chunk after evicting the previous one.  Output fp32. */
+int hswa_prefill_chunk(const hswa_attn_args* args, void* stream);
+
+/* Decode step of one layer ([MiMo] 1.2): one query row per listed
+ * sequence at position seq_len - 1 (cu_q is ignored).  Appends k_new/v_new
+ * when set, then attends; FULL layers split the context across workgroups
+ * and merge the parts (log-sum-exp) in a second kernel.  `workspace` is a
+ * caller-owned device buffer of at least hswa_decode_workspace_bytes(args)
+ * bytes (may be NULL when that is 0); HSWA_E_INVAL if it is smaller. */
+int hswa_decode(const hswa_attn_args* args, void* workspace, size_t ws_bytes,
+                void* stream);
+size_t hswa_decode_workspace_bytes(const hswa_attn_args* args);
+
+/* KV append alone: writes k_new/v_new (both required) of the query rows
+ * described as for hswa_prefill_chunk (cu_q given) or hswa_decode (cu_q
+ * NULL: one row per sequence) into k_cache/v_cache.  No attention. */
+int hswa_append_kv(const hswa_attn_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSWA_H */

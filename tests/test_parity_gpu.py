@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar (fixed by the workload statement): slot maps, eviction sets and valid
+window lengths bit-exact; attention outputs from bf16 inputs within max-abs
+4e-3 of the oracle.
+"""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_sliding_window_hswa_amd as H
+import synth
+from oracle import attention as OA
+from oracle.pool import NoSpace, PoolSim
+
+from harness import TOL, SeqData, Setup, chunked_prefill, dev, make_seqs, oracle_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_seq(outs, vlens, seqs, kind, W, scale=None, sample=None):
+    worst = 0.0
+    for b, s in enumerate(seqs):
+        L = s.q.shape[0]
+        pos = list(range(L)) if sample is None else sorted(set(p for p in sample(L)))
+        exp = oracle_rows(s, pos, kind, W, scale)
+        got = outs[b][pos].double().numpy()
+        assert np.all(np.isfinite(got)), f"non-finite output in sequence {b}"
+        err = float(np.max(np.abs(got - exp)))
+        worst = max(worst, err)
+        assert err < TOL, f"sequence {b}: max-abs error {err:.3e}"
+        vl = vlens[b][pos].numpy()
+        want = np.array([OA.valid_length(p, kind, W) for p in pos])
+        assert np.array_equal(vl, want)
+    return worst
+
+
+# ---------------------------------------------------------------------------
+# Pool tables on the device are bit-exact against the oracle simulator
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_pool_device_tables_match_oracle(gpu, seed):
+    rnd = random.Random(seed)
+    W, C, S, maxp, npages = [(4, 16, 3, 6, 12), (128, 384, 4, 40, 100), (17, 48, 5, 9, 30)][seed]
+    free = synth.permutation(npages, seed, 1)
+    ring = synth.permutation(S * C // 16, seed, 2)
+    pool = H.hswa_pool_create(W, C, S, maxp, npages, free, ring, device=dev())
+    sim = PoolSim(W, C, S, maxp, npages, free, ring)
+    t = pool.tables
+    for step in range(80):
+        ids = rnd.sample(range(S), rnd.randint(1, S))
+        r = rnd.random()
+        if r < 0.45:
+            n = [rnd.choice([0, 1, 3, 16, 40, rnd.randint(0, C)]) for _ in ids]
+            try:
+                exp = sim.alloc(ids, n)
+            except NoSpace:
+                with pytest.raises(H.NoSpace):
+                    H.hswa_pool_alloc(pool, ids, n)
+                continue
+            got = H.hswa_pool_alloc(pool, ids, n)
+            assert list(got[0]) == exp[0] and list(got[1]) == exp[1]
+        elif r < 0.8:
+            exp = sim.evict(ids)
+            got = H.hswa_pool_evict(pool, ids)
+            assert list(got[0]) == exp[0] and list(got[1]) == exp[1]
+        elif r < 0.92:
+            n = [rnd.randint(0, 3 * W) for _ in ids]
+            try:
+                exp = sim.import_context(ids, n)
+            except NoSpace:
+                with pytest.raises(H.NoSpace):
+                    H.hswa_pool_import(pool, ids, n)
+                continue
+            got = H.hswa_pool_import(pool, ids, n)
+            assert list(got[0]) == exp[0] and list(got[1]) == exp[1]
+        else:
+            sim.release(ids)
+            H.hswa_pool_release(pool, ids)
+        torch.cuda.synchronize()
+        assert t["seq_len"].cpu().tolist() == sim.seq_len_table()
+        assert t["fpt"].cpu().view(S, maxp).tolist() == sim.fpt_table()
+        assert t["map"].cpu().tolist() == sim.map_table()
+        assert t["rpt"].cpu().view(S, C // 16).tolist() == sim.rpt_table()
+
+
+# ---------------------------------------------------------------------------
+# SWA single-chunk prefill then decode steps (one sequence, d = 64, g = 4)
+
+
+def test_swa_single_chunk_then_decode(gpu):
+    wl = synth.C1
+    L0, steps = wl.prefill_len, wl.decode_steps
+    total = L0 + steps
+    hq, hkv, d, W = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window
+    seqs = make_seqs([total], hq, hkv, d, wl.seed)
+    C = W + L0
+    # contiguous slot tables: identity page orders
+    st = Setup(H.SWA, W, C, 1, total // 16 + 2, total // 16 + 2, hkv, d, wl.seed)
+    H.hswa_pool_destroy(st.pool)
+    st.pool = H.hswa_pool_create(W, C, 1, total // 16 + 2, total // 16 + 2,
+                                 np.arange(total // 16 + 2), np.arange(C // 16), device=dev())
+    st.view = H.hswa_pool_get_view(st.pool)
+    st.ring_pages = np.arange(C // 16).reshape(1, -1)
+    pre = [SeqData(seqs[0].q[:L0], seqs[0].k[:L0], seqs[0].v[:L0])]
+    outs, vlens, _ = chunked_prefill(st, pre, L0, hq)
+    _check_seq(outs, vlens, pre, OA.SWA, W)
+    sid = torch.zeros(1, dtype=torch.int32, device=dev())
+    for t in range(steps):
+        pos = L0 + t
+        H.hswa_pool_alloc(st.pool, [0], [1])
+        q = seqs[0].q[pos:pos + 1].to(dev())
+        kn = seqs[0].k[pos:pos + 1].to(dev())
+        vn = seqs[0].v[pos:pos + 1].to(dev())
+        out = torch.full((1, hq, d), float("nan"), dtype=torch.float32, device=dev())
+        vl = torch.full((1,), -1, dtype=torch.int32, device=dev())
+        ws_bytes = H.hswa_decode_workspace_bytes(H.SWA, W, 1, hq, hkv, d, pos + 1)
+        assert ws_bytes == 0
+        H.hswa_decode(H.SWA, W, q, kn, vn, sid, pos + 1, st.view, st.kc, st.vc, out, None, vl)
+        ev, cnt = H.hswa_pool_evict(st.pool, [0])
+        exp = oracle_rows(seqs[0], [pos], OA.SWA, W)
+        err = float(np.max(np.abs(out.cpu().double().numpy() - exp)))
+        assert err < TOL, f"decode step {t}: {err:.3e}"
+        assert int(vl.item()) == W
+        assert list(cnt) == [1]
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill, several sequences, ragged tails, permuted pages, NaN-poisoned
+# evicted and unwritten slots
+
+
+@pytest.mark.parametrize("kind", [H.SWA, H.FULL])
+def test_chunked_prefill_ragged(gpu, kind):
+    hq, hkv, d, W, chunk = 64, 8, 128, 128, 256
+    lens = [700, 333, 1029, 1]
+    seqs = make_seqs(lens, hq, hkv, d, 11)
+    maxp = max(lens) // 16 + 2
+    st = Setup(kind, W, W + chunk, len(lens), maxp, len(lens) * maxp + 5, hkv, d, 11)
+    outs, vlens, _ = chunked_prefill(st, seqs, chunk, hq)
+    _check_seq(outs, vlens, seqs, kind, W)
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind", [H.SWA, H.FULL])
+def test_gqa_and_head_dims(gpu, g, d, kind):
+    hkv = 2
+    hq = g * hkv
+    W, chunk = 48, 96
+    lens = [200, 77]
+    seqs = make_seqs(lens, hq, hkv, d, 100 + g + d)
+    maxp = max(lens) // 16 + 2
+    st = Setup(kind, W, W + chunk, 2, maxp, 2 * maxp, hkv, d, 5)
+    outs, vlens, _ = chunked_prefill(st, seqs, chunk, hq)
+    _check_seq(outs, vlens, seqs, kind, W)
+
+
+def test_window_one_returns_value(gpu):
+    hq, hkv, d = 8, 2, 64
+    seqs = make_seqs([90], hq, hkv, d, 21)
+    st = Setup(H.SWA, 1, 64, 1, 8, 8, hkv, d, 21)
+    outs, vlens, _ = chunked_prefill(st, seqs, 32, hq)
+    v = seqs[0].v.float()
+    for h in range(hq):
+        # exact except where bf16 -> fp16 lands in the fp16 subnormal range
+        err = (outs[0][:, h] - v[:, h // (hq // hkv)]).abs().max().item()
+        assert err <= 2.0 ** -25
+    assert torch.all(vlens[0] == 1)
+
+
+def test_large_window_equals_full_bitwise(gpu):
+    """A SWA layer whose window covers the sequence reads the same logical
+    keys as a Full layer; the reduction order depends on logical positions
+    only, so the outputs agree bit for bit."""
+    hq, hkv, d = 16, 2, 128
+    L = 300
+    seqs = make_seqs([L], hq, hkv, d, 31)
+    a = Setup(H.SWA, 512, 512 + 64, 1, 20, 20, hkv, d, 31)
+    oa, va, _ = chunked_prefill(a, seqs, 64, hq)
+    b = Setup(H.FULL, 512, 512 + 64, 1, 20, 20, hkv, d, 77)
+    ob, vb, _ = chunked_prefill(b, seqs, 64, hq)
+    assert torch.equal(oa[0], ob[0])
+    assert torch.equal(va[0], vb[0])
+    _check_seq(oa, va, seqs, OA.FULL, 0)
+
+
+@pytest.mark.parametrize("kind", [H.SWA, H.FULL])
+def test_page_permutation_bitwise(gpu, kind):
+    hq, hkv, d, W = 64, 8, 128, 128
+    seqs = make_seqs([450, 260], hq, hkv, d, 41)
+    res = []
+    for perm_seed in (1, 2):
+        st = Setup(kind, W, W + 128, 2, 40, 80, hkv, d, perm_seed)
+        outs, vlens, _ = chunked_prefill(st, seqs, 128, hq)
+        res.append(outs)
+    for x, y in zip(*res):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("chunk", [1, 16, 100])
+def test_chunk_sizes_agree_with_oracle(gpu, chunk):
+    hq, hkv, d, W = 16, 2, 64, 32
+    seqs = make_seqs([130, 45], hq, hkv, d, 51)
+    st = Setup(H.SWA, W, W + chunk + 16 - (W + chunk) % 16, 2, 20, 40, hkv, d, 51)
+    outs, vlens, _ = chunked_prefill(st, seqs, chunk, hq)
+    _check_seq(outs, vlens, seqs, OA.SWA, W)
+
+
+def test_empty_batch_is_noop(gpu):
+    st = Setup(H.SWA, 16, 32, 1, 4, 4, 2, 64, 1)
+    q = torch.empty((0, 8, 64), dtype=torch.bfloat16, device=dev())
+    cu = torch.zeros(1, dtype=torch.int32, device=dev())
+    sid = torch.empty(0, dtype=torch.int32, device=dev())
+    out = torch.empty((0, 8, 64), dtype=torch.float32, device=dev())
+    H.hswa_prefill_chunk(H.SWA, 16, q, None, None, sid, cu, 0, st.view, st.kc, st.vc, out)
+    H.hswa_decode(H.SWA, 16, q, None, None, sid, 1, st.view, st.kc, st.vc, out)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Decode over a Full and a SWA layer (mixed batch), contexts restored with
+# hswa_pool_import, new token appended each step, eviction each step
+
+
+def _decode_scenario(ctxs, steps, hq, hkv, d, W, seed, C=None):
+    B = len(ctxs)
+    total = [c + steps for c in ctxs]
+    seqs = make_seqs(total, hq, hkv, d, seed)
+    C = C or W
+    maxp = max(total) // 16 + 2
+    nfull = B * maxp + 8
+    full = Setup(H.FULL, W, C, B, maxp, nfull, hkv, d, seed)
+    # the SWA layer shares the pool's tables; it only needs its own ring buffers
+    ks, vs = H.kv_cache_shapes(B * C // 16, hkv, d)
+    skc = torch.full(ks, float("nan"), dtype=torch.bfloat16, device=dev())
+    svc = torch.full(vs, float("nan"), dtype=torch.bfloat16, device=dev())
+    pool, view = full.pool, full.view
+    ids = list(range(B))
+    H.hswa_pool_import(pool, ids, ctxs)
+    sid = torch.tensor(ids, dtype=torch.int32, device=dev())
+    # place the restored context: every position in the Full layer, the
+    # in-window positions in the SWA ring
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(ctxs)]), dtype=torch.int32, device=dev())
+    kf = torch.cat([s.k[:c] for s, c in zip(seqs, ctxs)]).to(dev())
+    vf = torch.cat([s.v[:c] for s, c in zip(seqs, ctxs)]).to(dev())
+    H.hswa_append_kv(H.FULL, kf, vf, sid, view, full.kc, full.vc, cu, max(ctxs))
+    nw = [min(c, W - 1) for c in ctxs]
+    cuw = torch.tensor(np.concatenate([[0], np.cumsum(nw)]), dtype=torch.int32, device=dev())
+    ksw = torch.cat([s.k[c - k:c] for s, c, k in zip(seqs, ctxs, nw)]).to(dev())
+    vsw = torch.cat([s.v[c - k:c] for s, c, k in zip(seqs, ctxs, nw)]).to(dev())
+    H.hswa_append_kv(H.SWA, ksw, vsw, sid, view, skc, svc, cuw, max(nw))
+    errs = []
+    for t in range(steps):
+        H.hswa_pool_alloc(pool, ids, [1] * B)
+        pos = [c + t for c in ctxs]
+        q = torch.stack([s.q[p] for s, p in zip(seqs, pos)]).to(dev())
+        kn = torch.stack([s.k[p] for s, p in zip(seqs, pos)]).to(dev())
+        vn = torch.stack([s.v[p] for s, p in zip(seqs, pos)]).to(dev())
+        maxlen = max(pos) + 1
+        for kind, kc, vc in ((H.FULL, full.kc, full.vc), (H.SWA, skc, svc)):
+            out = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device=dev())
+            vl = torch.full((B,), -1, dtype=torch.int32, device=dev())
+            nb = H.hswa_decode_workspace_bytes(kind, W, B, hq, hkv, d, maxlen)
+            ws = torch.empty(max(nb // 4, 1), dtype=torch.float32, device=dev())
+            H.hswa_decode(kind, W, q, kn, vn, sid, maxlen, view, kc, vc, out, ws, vl)
+            got = out.cpu().double().numpy()
+            for b in range(B):
+                exp = oracle_rows(seqs[b], [pos[b]], kind, W)[0]
+                err = float(np.max(np.abs(got[b] - exp)))
+                errs.append(err)
+                assert err < TOL, f"step {t} kind {kind} seq {b}: {err:.3e}"
+            assert vl.cpu().tolist() == [OA.valid_length(p, kind, W) for p in pos]
+        ev, cnt = H.hswa_pool_evict(pool, ids)
+        assert list(cnt) == [1 if p + 1 >= W else 0 for p in pos]
+    return max(errs)
+
+
+def test_decode_mixed_full_and_swa(gpu):
+    rng = np.random.default_rng(3)
+    ctxs = [int(x) for x in rng.integers(1, 3000, size=12)] + [1, 127, 128, 129]
+    _decode_scenario(ctxs, 4, 64, 8, 128, 128, 61)
+
+
+def test_decode_long_context_splits(gpu):
+    """Long contexts force the split-K path (several splits + merge)."""
+    _decode_scenario([20000, 7000, 33], 2, 64, 8, 128, 128, 71, C=128 + 256)
+
+
+def test_decode_small_heads_d64(gpu):
+    _decode_scenario([1500, 90, 700], 3, 8, 2, 64, 128, 81)

@@ -1,0 +1,523 @@
+"""Benchmark of the Hybrid SWA attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: SWA-only chunked prefill, 8 sequences with lengths uniform
+in [2048, 16384], chunk 2048, 64 query / 8 KV heads, head_dim 128, W = 128,
+ring of W + chunk slots per sequence in 16-token pages placed by a seeded
+random permutation.  One step = the whole chunked prefill of the batch: for
+every chunk, pool alloc (joint capacity check + device table update), KV
+append, SWA attention, out-of-window eviction; then release of the
+sequences.  `value` is prefill tokens per second over the whole step.
+
+The same run also times a mixed decode batch (256 sequences, contexts
+uniform in [4096, 32768], one Full and one SWA layer, one new token per
+sequence per step with append and eviction) and reports its algorithmic HBM
+GB/s under "decode".
+
+Other workloads (--workload): swa_single_chunk, hybrid_stack, long_decode.
+
+All inputs are seeded synthetic N(0,1) values rounded to bf16, resident in
+HBM before the timed region starts.  The attention kernel's duration is
+measured with HIP events on the stream it is launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2516.6    # 256 CU * 2.4 GHz * 4096 flop/clk (dense)
+PEAKS = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (MFMA_BF16_PEAK_TFS, "TFLOP/s")}
+METRIC = "Hybrid-SWA attn prefill tok/s + decode HBM GB/s (% of MI355X peak)"
+
+KV_TOKEN_BYTES = lambda hkv, d: 2 * hkv * d * 2  # K and V, bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+
+
+class Ctx:
+    """Holds torch, the binding and a stream for the run."""
+
+    def __init__(self):
+        import torch
+        import hybrid_sliding_window_hswa_amd as H
+        self.torch = torch
+        self.H = H
+        self.lib = H.library()
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+        self.sptr = C.c_void_p(self.stream.cuda_stream)
+
+    def i32(self, x):
+        return self.torch.tensor(np.asarray(x, dtype=np.int32), device=self.dev)
+
+
+def _arr(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _attn_args(cx, kind, window, hq, hkv, d, seq_ids, cu_q, total_q, max_q_len, max_seq_len,
+               view, q, k_new, v_new, kc, vc, out):
+    from hybrid_sliding_window_hswa_amd import _capi
+    a = _capi.AttnArgs()
+    a.kind, a.window = kind, window
+    a.num_q_heads, a.num_kv_heads, a.head_dim = hq, hkv, d
+    a.scale = 0.0
+    a.num_seqs = seq_ids.shape[0]
+    a.seq_ids = seq_ids.data_ptr()
+    a.cu_q = cu_q.data_ptr() if cu_q is not None else None
+    a.total_q, a.max_q_len, a.max_seq_len = total_q, max_q_len, max_seq_len
+    a.q = q.data_ptr() if q is not None else None
+    a.k_new = k_new.data_ptr() if k_new is not None else None
+    a.v_new = v_new.data_ptr() if v_new is not None else None
+    a.pool = view
+    a.k_cache, a.v_cache = kc.data_ptr(), vc.data_ptr()
+    a.out = out.data_ptr() if out is not None else None
+    a.vlen_out = None
+    return a
+
+
+def _check(cx, rc):
+    if rc != 0:
+        raise RuntimeError(f"hswa call failed ({rc}): {cx.H.hswa_last_error()}")
+
+
+# ---------------------------------------------------------------------------
+# SWA / Full chunked prefill over a batch of sequences
+
+
+class ChunkedPrefill:
+    """Precomputes every chunk step's batch; run() replays the whole
+    chunked prefill of the batch through the C ABI."""
+
+    def __init__(self, cx, lens, chunk, hq, hkv, d, W, seed, kinds=("S",), ring=None):
+        torch, H = cx.torch, cx.H
+        import synth
+        self.cx = cx
+        self.lens, self.chunk, self.hq, self.hkv, self.d, self.W = lens, chunk, hq, hkv, d, W
+        B = len(lens)
+        self.B = B
+        C_ = ring or W + chunk
+        C_ = -(-C_ // 16) * 16
+        maxp = max(lens) // 16 + 2
+        nfull = B * maxp + 16
+        free = synth.permutation(nfull, seed, 1)
+        ringp = synth.permutation(B * C_ // 16, seed, 2)
+        self.pool = H.hswa_pool_create(W, C_, B, maxp, nfull, free, ringp, device=cx.dev)
+        self.view = H.hswa_pool_get_view(self.pool)
+        self.layers = []
+        for li, kind in enumerate(kinds):
+            npages = nfull if kind == "F" else B * C_ // 16
+            ks, vs = H.kv_cache_shapes(npages, hkv, d)
+            kc = torch.zeros(ks, dtype=torch.bfloat16, device=cx.dev)
+            vc = torch.zeros(vs, dtype=torch.bfloat16, device=cx.dev)
+            self.layers.append((H.FULL if kind == "F" else H.SWA, kc, vc))
+        # inputs per sequence, generated on the device
+        self.q, self.k, self.v = [], [], []
+        for b, L in enumerate(lens):
+            self.q.append(synth.bf16_normal((L, hq, d), seed, 0, b, synth.ROLE_Q, device=cx.dev))
+            self.k.append(synth.bf16_normal((L, hkv, d), seed, 0, b, synth.ROLE_K, device=cx.dev))
+            self.v.append(synth.bf16_normal((L, hkv, d), seed, 0, b, synth.ROLE_V, device=cx.dev))
+        # chunk steps
+        self.steps = []
+        done = [0] * B
+        max_rows = 0
+        while True:
+            act = [b for b in range(B) if done[b] < lens[b]]
+            if not act:
+                break
+            n = [min(chunk, lens[b] - done[b]) for b in act]
+            rows = [(b, done[b], done[b] + k) for b, k in zip(act, n)]
+            st = {
+                "ids": _arr(act), "n": _arr(n), "nseq": len(act), "max_n": max(n),
+                "sid": cx.i32(act),
+                "cu": cx.i32(np.concatenate([[0], np.cumsum(n)])),
+                "q": torch.cat([self.q[b][a:e] for b, a, e in rows]),
+                "k": torch.cat([self.k[b][a:e] for b, a, e in rows]),
+                "v": torch.cat([self.v[b][a:e] for b, a, e in rows]),
+                "rows": rows,
+                "halo": [min(W - 1, a) for b, a, e in rows],
+            }
+            max_rows = max(max_rows, st["q"].shape[0])
+            self.steps.append(st)
+            for b, k in zip(act, n):
+                done[b] += k
+        self.out = torch.empty((max_rows, hq, d), dtype=torch.float32, device=cx.dev)
+        self.all_ids = _arr(list(range(B)))
+        for st in self.steps:
+            T = st["q"].shape[0]
+            st["args"] = []
+            for kind, kc, vc in self.layers:
+                app = _attn_args(cx, kind, W, hkv, hkv, d, st["sid"], st["cu"], T, st["max_n"],
+                                 0, self.view, None, st["k"], st["v"], kc, vc, None)
+                att = _attn_args(cx, kind, W, hq, hkv, d, st["sid"], st["cu"], T, st["max_n"],
+                                 0, self.view, st["q"], None, None, kc, vc, self.out)
+                st["args"].append((app, att))
+        self.tokens = sum(lens)
+
+    def run(self, events=None):
+        lib, cx = self.cx.lib, self.cx
+        h = self.pool.handle
+        for st in self.steps:
+            ids, idp = st["ids"]
+            n, np_ = st["n"]
+            _check(cx, lib.hswa_pool_alloc(h, st["nseq"], idp, np_, None, None, cx.sptr))
+            for app, att in st["args"]:
+                _check(cx, lib.hswa_append_kv(C.byref(app), cx.sptr))
+                if events is not None:
+                    e0, e1 = cx.torch.cuda.Event(enable_timing=True), cx.torch.cuda.Event(
+                        enable_timing=True)
+                    e0.record(cx.stream)
+                _check(cx, lib.hswa_prefill_chunk(C.byref(att), cx.sptr))
+                if events is not None:
+                    e1.record(cx.stream)
+                    events.append((att.kind, st, e0, e1))
+            _check(cx, lib.hswa_pool_evict(h, st["nseq"], idp, None, 0, None, cx.sptr))
+        ids, idp = self.all_ids
+        _check(cx, lib.hswa_pool_release(h, self.B, idp, cx.sptr))
+
+    def attn_bytes(self, st):
+        """Algorithmic HBM bytes of one attention launch: Q read, O written
+        (fp32), and each needed key's K/V read once (chunk + window halo)."""
+        T = st["q"].shape[0]
+        kvb = KV_TOKEN_BYTES(self.hkv, self.d)
+        qb = T * self.hq * self.d * 2
+        ob = T * self.hq * self.d * 4
+        keys = sum((e - a) + h for (b, a, e), h in zip(st["rows"], st["halo"]))
+        return qb + ob + keys * kvb
+
+    def attn_flops(self, st, kind):
+        """4 * d * Hq flops per scored (query, key) pair."""
+        pairs = 0
+        for b, a, e in st["rows"]:
+            if kind == self.cx.H.SWA:
+                pairs += _pairs_swa(e, self.W) - _pairs_swa(a, self.W)
+            else:
+                pairs += e * (e + 1) // 2 - a * (a + 1) // 2
+        return 4 * self.d * self.hq * pairs
+
+
+def _pairs_swa(n, W):
+    return n * (n + 1) // 2 if n <= W else n * W - W * (W - 1) // 2
+
+
+# ---------------------------------------------------------------------------
+# Decode over Full + SWA layers
+
+
+class Decode:
+    def __init__(self, cx, ctxs, pattern, hq, hkv, d, W, ring, seed, steps_total):
+        torch, H = cx.torch, cx.H
+        import synth
+        self.cx, self.hq, self.hkv, self.d, self.W = cx, hq, hkv, d, W
+        B = len(ctxs)
+        self.B = B
+        self.ctx0 = list(ctxs)
+        maxlen = max(ctxs) + steps_total + 1
+        maxp = maxlen // 16 + 2
+        nfull = int(sum(c // 16 + 2 for c in ctxs) * 1.1) + B * (steps_total // 16 + 2) + 64
+        free = synth.permutation(nfull, seed, 1)
+        ringp = synth.permutation(B * ring // 16, seed, 2)
+        self.pool = H.hswa_pool_create(W, ring, B, maxp, nfull, free, ringp, device=cx.dev)
+        self.view = H.hswa_pool_get_view(self.pool)
+        ids = list(range(B))
+        self.ids = _arr(ids)
+        self.sid = cx.i32(ids)
+        H.hswa_pool_import(self.pool, ids, ctxs, want_slots=False)
+        self.layers = []
+        kvb = KV_TOKEN_BYTES(hkv, d)
+        for li, kind in enumerate(pattern):
+            if kind == "F":
+                ks, vs = H.kv_cache_shapes(nfull, hkv, d)
+            else:
+                ks, vs = H.kv_cache_shapes(B * ring // 16, hkv, d)
+            kc = torch.empty(ks, dtype=torch.bfloat16, device=cx.dev)
+            vc = torch.empty(vs, dtype=torch.bfloat16, device=cx.dev)
+            # restore the context: generated per sequence on the device and
+            # appended (Full: every position, SWA: the last W-1)
+            for b, c in enumerate(ctxs):
+                n = c if kind == "F" else min(c, W - 1)
+                kk = synth.bf16_normal((n, hkv, d), seed, li, b, synth.ROLE_K, device=cx.dev)
+                vv = synth.bf16_normal((n, hkv, d), seed, li, b, synth.ROLE_V, device=cx.dev)
+                H.hswa_append_kv(H.FULL if kind == "F" else H.SWA, kk, vv, cx.i32([b]), self.view,
+                                 kc, vc, cx.i32([0, n]), n)
+                del kk, vv
+            self.layers.append((H.FULL if kind == "F" else H.SWA, kc, vc))
+        torch.cuda.synchronize()
+        # per-step inputs (one new token per sequence per layer)
+        g = lambda shape, *s: synth.bf16_normal(shape, seed, 900, *s, device=cx.dev)
+        self.q = [g((B, hq, d), li, synth.ROLE_Q) for li in range(len(pattern))]
+        self.kn = [g((B, hkv, d), li, synth.ROLE_K) for li in range(len(pattern))]
+        self.vn = [g((B, hkv, d), li, synth.ROLE_V) for li in range(len(pattern))]
+        self.out = torch.empty((B, hq, d), dtype=torch.float32, device=cx.dev)
+        self.max_seq_len = maxlen
+        nb = max(H.hswa_decode_workspace_bytes(H.FULL, W, B, hq, hkv, d, maxlen), 16)
+        self.ws = torch.empty(nb // 4 + 4, dtype=torch.float32, device=cx.dev)
+        self.nbytes_ws = self.ws.numel() * 4
+        self.args = []
+        for li, (kind, kc, vc) in enumerate(self.layers):
+            a = _attn_args(cx, kind, W, hq, hkv, d, self.sid, None, B, 1, maxlen, self.view,
+                           self.q[li], self.kn[li], self.vn[li], kc, vc, self.out)
+            self.args.append(a)
+        self.lens = list(ctxs)
+        self.ones = _arr([1] * B)
+
+    def step(self, events=None):
+        lib, cx = self.cx.lib, self.cx
+        h = self.pool.handle
+        ids, idp = self.ids
+        _, onep = self.ones
+        _check(cx, lib.hswa_pool_alloc(h, self.B, idp, onep, None, None, cx.sptr))
+        self.lens = [x + 1 for x in self.lens]
+        for a in self.args:
+            if events is not None:
+                e0, e1 = cx.torch.cuda.Event(enable_timing=True), cx.torch.cuda.Event(
+                    enable_timing=True)
+                e0.record(cx.stream)
+            _check(cx, lib.hswa_decode(C.byref(a), C.c_void_p(self.ws.data_ptr()),
+                                       self.nbytes_ws, cx.sptr))
+            if events is not None:
+                e1.record(cx.stream)
+                events.append((a.kind, list(self.lens), e0, e1))
+        _check(cx, lib.hswa_pool_evict(h, self.B, idp, None, 0, None, cx.sptr))
+
+    def layer_bytes(self, kind, lens):
+        """Algorithmic HBM bytes of one decode layer call: the K/V of every
+        key the new token attends to, Q read, O written (fp32), and the new
+        token's K/V read and written by the append."""
+        kvb = KV_TOKEN_BYTES(self.hkv, self.d)
+        keys = sum(L if kind == self.cx.H.FULL else min(L, self.W) for L in lens)
+        B = len(lens)
+        return keys * kvb + B * (self.hq * self.d * 2 + self.hq * self.d * 4 + 2 * kvb)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle, untuned)
+
+
+def cpu_baseline_prefill(cx, cp: ChunkedPrefill, budget_s: float, seed=7):
+    """The oracle (fp64 NumPy, one thread) on a bounded sample of the same
+    prefill: query rows drawn uniformly from the batch, each with all heads
+    and its full window of keys.  Inputs are copied to the host first; only
+    the oracle is timed."""
+    import synth
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    rng = np.random.default_rng(seed)
+    W = cp.W
+
+    def draw(k):
+        out = []
+        for _ in range(k):
+            b = int(rng.integers(cp.B))
+            pos = int(rng.integers(cp.lens[b]))
+            lo = max(0, pos - W + 1)
+            out.append((pos - lo, synth.to_f64(cp.q[b][pos:pos + 1]),
+                        synth.to_f64(cp.k[b][lo:pos + 1]), synth.to_f64(cp.v[b][lo:pos + 1])))
+        return out
+
+    def run(sample):
+        t0 = time.perf_counter()
+        for rel, q, k, v in sample:
+            OA.attend(q, [rel], k, v, OA.SWA, W)
+        return time.perf_counter() - t0
+
+    per_row = run(draw(32)) / 32
+    n = max(64, int(budget_s / max(per_row, 1e-6)))
+    sample = draw(n)
+    dt = run(sample)
+    return {"value": round(n / dt, 2), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} query rows (each with all {cp.hq} heads and its {W}-key window) "
+                      f"drawn uniformly from the {cp.B} sequences; fp64 NumPy on 1 thread, "
+                      f"{dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+
+
+def timed(cx, fn, steps, warmup):
+    torch = cx.torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def roofline(bound, achieved, traffic=None):
+    peak, unit = PEAKS[bound]
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def bench_prefill(cx, args):
+    import synth
+    wl = synth.C2
+    lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
+    cp = ChunkedPrefill(cx, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                        wl.window, wl.seed)
+    cx.torch.cuda.synchronize()
+    log(f"prefill: {cp.tokens} tokens in {len(cp.steps)} chunk steps")
+    sec = timed(cx, cp.run, args.steps, args.warmup)
+    # kernel time with events, over a separate pass
+    ev = []
+    for _ in range(max(1, min(args.steps, 5))):
+        cp.run(ev)
+    cx.torch.cuda.synchronize()
+    ktime = sum(e0.elapsed_time(e1) for _, _, e0, e1 in ev) / 1e3
+    kbytes = sum(cp.attn_bytes(st) for _, st, _, _ in ev)
+    kflops = sum(cp.attn_flops(st, kind) for kind, st, _, _ in ev)
+    res = {
+        "tok_s": cp.tokens / sec,
+        "ms_per_step": sec * 1e3,
+        "kernel_avg_us": ktime / len(ev) * 1e6,
+        "kernel_gbs": kbytes / ktime / 1e9,
+        "kernel_tflops": kflops / ktime / 1e12,
+        "launches": len(ev),
+        "lens": lens,
+    }
+    return cp, res
+
+
+def bench_decode(cx, args):
+    import synth
+    wl = synth.C3
+    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
+    steps, warm = args.decode_steps, 2
+    dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                wl.ring_slots, wl.seed, steps + warm + 8)
+    lens0 = list(dc.lens)
+    torch = cx.torch
+    for _ in range(warm):
+        dc.step()
+    torch.cuda.synchronize()
+    lens_start = list(dc.lens)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dc.step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    # bytes of the timed steps (lengths grow by one per step)
+    tot = 0
+    for s in range(steps):
+        lens = [x + s + 1 for x in lens_start]
+        tot += dc.layer_bytes(cx.H.FULL, lens) + dc.layer_bytes(cx.H.SWA, lens)
+    step_bytes = tot / steps
+    ev = []
+    for _ in range(3):
+        dc.step(ev)
+    torch.cuda.synchronize()
+    full = [(l, e0.elapsed_time(e1) / 1e3) for k, l, e0, e1 in ev if k == cx.H.FULL]
+    swa = [(l, e0.elapsed_time(e1) / 1e3) for k, l, e0, e1 in ev if k == cx.H.SWA]
+    fb = sum(dc.layer_bytes(cx.H.FULL, l) for l, _ in full)
+    ft = sum(t for _, t in full)
+    sb = sum(dc.layer_bytes(cx.H.SWA, l) for l, _ in swa)
+    st_ = sum(t for _, t in swa)
+    res = {
+        "gbs": step_bytes / sec / 1e9,
+        "ms_per_step": sec * 1e3,
+        "bytes_per_step": step_bytes,
+        "full_kernel_us": ft / len(full) * 1e6,
+        "full_gbs": fb / ft / 1e9,
+        "swa_call_us": st_ / len(swa) * 1e6,
+        "swa_gbs": sb / st_ / 1e9,
+    }
+    return dc, res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    cx = Ctx()
+    import synth
+    cp, pre = bench_prefill(cx, args)
+    log(f"prefill: {pre}")
+    dec = None
+    if not args.no_decode:
+        dc, dec = bench_decode(cx, args)
+        log(f"decode: {dec}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_prefill(cx, cp, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+    wl = synth.C2
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tok_s"], 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "swa_chunked_prefill",
+            "num_seqs": wl.num_seqs, "seq_len_range": [wl.len_lo, wl.len_hi],
+            "seq_lens": pre["lens"], "chunk": wl.chunk, "window": wl.window,
+            "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim, "page_size": 16, "ring_slots": wl.window + wl.chunk,
+            "output_dtype": "fp32", "seed": wl.seed,
+        },
+        "roofline": roofline("hbm", pre["kernel_gbs"]),
+        "kernel": {"name": "prefill_kernel<128,SWA,8>", "avg_us": round(pre["kernel_avg_us"], 2),
+                   "launches_timed": pre["launches"],
+                   "tflops": round(pre["kernel_tflops"], 2),
+                   "mfma_frac": round(pre["kernel_tflops"] / MFMA_BF16_PEAK_TFS, 4)},
+        "cpu_baseline": cpu,
+    }
+    if dec is not None:
+        w3 = synth.C3
+        line["decode"] = {
+            "workload": "mixed_decode", "num_seqs": w3.num_seqs,
+            "ctx_range": [w3.ctx_lo, w3.ctx_hi], "layers": "1 Full + 1 SWA",
+            "value": round(dec["gbs"], 1), "unit": "GB/s",
+            "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(dec["ms_per_step"], 4),
+            "roofline": roofline("hbm", dec["full_gbs"]),
+            "full_kernel_us": round(dec["full_kernel_us"], 1),
+            "swa_call_us": round(dec["swa_call_us"], 1),
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@ using hswa::PoolRec;
 namespace {
 
 constexpr int kPage = HSWA_PAGE_SIZE;
-constexpr int kStages = 4;
+constexpr int kStages = 16;
 
 struct Stage {
   void* buf = nullptr;       // pinned host memory, device-readable

@@ -136,16 +136,14 @@ __global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
     const float m_new = fmaxf(m, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
-    float pv[8];
+    f16x8 pf;
     float ps = 0.f;
     for (int j = 0; j < 8; ++j) {
-      pv[j] = fast_exp2(sv[j] - m_use);
-      ps += pv[j];
+      pf[j] = (_Float16)fast_exp2(sv[j] - m_use);
+      ps += (float)pf[j];  // sum the fp16 weights the PV product uses
     }
     lsum = lsum * alpha + ps;
     m = m_new;
-    f16x8 pf;
-    for (int j = 0; j < 8; ++j) pf[j] = (_Float16)pv[j];
     const bool full = valid == 0xffu;
     for (int nb = 0; nb < NB; ++nb) {
       uint32_t w[4] = {bf16x2_to_f16x2(vr[nb][0][0]), bf16x2_to_f16x2(vr[nb][0][1]),

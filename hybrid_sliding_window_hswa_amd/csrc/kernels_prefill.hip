@@ -7,10 +7,11 @@
 // ring) or [0, i] (Full, through the Full page table).
 //
 // Design (gfx950):
-//  - Workgroup = 8 wavefronts for one (sequence, query block, KV head).
-//    Wave w owns 32 query positions of one query head of the group, so the
-//    G heads sharing a KV head (and, for G < 8, several 32-position groups)
-//    share every K/V tile the workgroup stages.
+//  - Workgroup = 4 wavefronts for one (sequence, query block, KV head,
+//    head group).  Wave w owns 32 query positions of one query head, so up
+//    to four heads sharing a KV head (and, for G < 4, several 32-position
+//    groups) share every K/V tile the workgroup stages.  Small workgroups
+//    let three of them share a CU, so one's loads overlap another's math.
 //  - Scores use the 32x32x16 bf16 MFMA as S^T[key][row] = K . Q^T, with the
 //    Q^T fragments held in registers for the whole key loop and K read from
 //    LDS.  The output uses the 32x32x16 fp16 MFMA as O^T[d][row] = V^T . P^T.
@@ -34,21 +35,42 @@ using namespace dev;
 
 namespace {
 
-constexpr int kPreWaves = 8;
+constexpr int kPreWaves = 4;
 constexpr int kPreThreads = kPreWaves * 64;
+// Lazy softmax rescaling: the running max is only moved when a new score
+// exceeds it by more than 2^kLazy, so unnormalised weights stay <= 2^kLazy
+// (exact in fp16 with the same relative precision) and the O rescale runs
+// rarely.  The final division by the row sum makes the result independent
+// of where the max was taken.
+constexpr float kLazy = 8.0f;
 
 template <int D, int KIND, int G>
-__global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnParams p, int qblocks) {
-  constexpr int QB = 32 * kPreWaves / G;  // query positions per workgroup
-  constexpr int KROW = D + 8;             // LDS K row in bf16 (16-byte pad)
-  constexpr int NC = D / 16;              // k steps of the QK product
-  constexpr int NM = D / 32;              // 32-row d blocks of O^T
+__global__ void __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(3, 4)))
+prefill_kernel(AttnParams p, int qblocks,
+                                                              int total_tiles) {
+  constexpr int HPW = G < kPreWaves ? G : kPreWaves;  // heads per workgroup
+  constexpr int HG = G / HPW;                         // workgroups per KV head
+  constexpr int PG = kPreWaves / HPW;                 // 32-position groups
+  constexpr int QB = 32 * PG;                         // query positions per workgroup
+  constexpr int KROW = D + 8;                         // LDS K row in bf16 (16-byte pad)
+  constexpr int NC = D / 16;                          // k steps of the QK product
+  constexpr int NM = D / 32;                          // 32-row d blocks of O^T
   __shared__ __attribute__((aligned(16))) uint16_t kl[2][32 * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t vl[2][2 * D * 16];
 
-  const int i = blockIdx.x / qblocks;
-  const int qb = blockIdx.x % qblocks;
-  const int kvh = blockIdx.y;
+  // XCD-aware tile order: workgroup g runs on XCD g % 8; give each XCD a
+  // contiguous range of tiles so neighbouring query blocks of one
+  // (sequence, head group) share that XCD's L2 (their K/V windows overlap).
+  const int g = blockIdx.x;
+  const int per = gridDim.x / 8;
+  const int t = (g % 8) * per + g / 8;
+  if (t >= total_tiles) return;
+  const int qb = t % qblocks;
+  const int i = (t / qblocks) % p.num_seqs;
+  const int yh = t / (qblocks * p.num_seqs);
+  const int kvh = yh / HG;
+  const int hg = yh % HG;
+
   const int row0 = p.cu_q[i];
   const int n = p.cu_q[i + 1] - row0;
   if (qb * QB >= n) return;  // whole workgroup idle: no barrier reached
@@ -65,8 +87,8 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnParams p, int 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hl = wave % G;
-  const int r0 = (wave / G) * 32;        // first workgroup row of this wave
+  const int hl = hg * HPW + wave % HPW;
+  const int r0 = (wave / HPW) * 32;      // first workgroup row of this wave
   const int head = kvh * G + hl;
   const int qr = lane & 31;              // query row within the wave (N index)
   const int h2 = lane >> 5;              // k half of the MFMA operands
@@ -92,69 +114,74 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnParams p, int 
   f32x16 o[NM];
   for (int mb = 0; mb < NM; ++mb)
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
-  float m = -INFINITY;
-  float lsum = 0.f;
+  float m = -INFINITY;   // running max of scaled scores (log2 domain)
+  float lsum = 0.f;      // this lane's share of the row sum
   const float sl2 = p.scale_log2;
 
   const int kstart = (wg_klo / 32) * 32;
   const int nsteps = (wg_khi - kstart) / 32 + 1;
   const int64_t head_stride = (int64_t)kPage * D;
 
-  // staging roles: K thread (key sk, 16-byte chunk sc); V thread (page st,
-  // dim sd, 8-key half sh)
-  constexpr int KCH = D / 8;
-  const bool k_role = tid < 32 * KCH;
-  const int sk = tid / KCH;
-  const int sc = tid % KCH;
-  const bool v_role = tid < 2 * D * 2;
-  const int st = tid / (2 * D);
-  const int sd = (tid / 2) % D;
-  const int sh = tid & 1;
-
-  u32x4 kreg, vreg;
+  // Staging.  One 16-token page block of one head is 16*D*2 contiguous
+  // bytes for K (token-major) and for V (dim-major), so thread t copies the
+  // 16-byte chunk(s) at t*8 (+ j*kPreThreads*8) of each of the step's two
+  // page blocks.  For K the chunk is row (t*8)/D, columns (t*8)%D; for V it
+  // is dim (t*8)/16, keys 8*(t&1) .. +8.
+  constexpr int EPB = kPage * D;                    // elements per page block
+  constexpr int NCH = EPB / 8;                      // 16-byte chunks per block
+  constexpr int CPT = (NCH + kPreThreads - 1) / kPreThreads;
+  u32x4 kreg[2][CPT], vreg[2][CPT];
   auto stage_load = [&](int kp0) {
-    kreg = u32x4{0, 0, 0, 0};
-    vreg = u32x4{0, 0, 0, 0};
-    if (k_role) {
-      const int tile = kp0 + (sk / 16) * 16;
-      const int kp = kp0 + sk;
-      if (tile <= wg_khi && kp >= wg_klo && kp <= wg_khi) {
-        const int32_t pg = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile, p.t.max_pages,
-                                         p.t.ring_slots);
-        if (pg >= 0)
-          kreg = *(const u32x4*)(p.k_cache + ((int64_t)pg * hkv + kvh) * head_stride +
-                               (sk % 16) * D + sc * 8);
-      }
-    }
-    if (v_role) {
-      const int tile = kp0 + 16 * st;
-      const int k8 = tile + 8 * sh;
-      if (tile <= wg_khi && k8 + 7 >= wg_klo && k8 <= wg_khi) {
-        const int32_t pg = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile, p.t.max_pages,
-                                         p.t.ring_slots);
-        if (pg >= 0)
-          vreg = *(const u32x4*)(p.v_cache + ((int64_t)pg * hkv + kvh) * head_stride +
-                                 sd * kPage + 8 * sh);
-        if (k8 < wg_klo || k8 + 7 > wg_khi) {
-          for (int j = 0; j < 8; ++j) {
-            const int kp = k8 + j;
-            if (kp < wg_klo || kp > wg_khi) vreg[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
+    // wave-uniform: the two page blocks of this step and whether every key
+    // in them lies inside the workgroup's key range
+    const bool inner = kp0 >= wg_klo && kp0 + 31 <= wg_khi;
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int tile = kp0 + 16 * t2;
+      int32_t pg = -1;
+      if (tile <= wg_khi)
+        pg = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile, p.t.max_pages, p.t.ring_slots);
+      pg = __builtin_amdgcn_readfirstlane(pg);
+      const uint16_t* kb = p.k_cache + ((int64_t)pg * hkv + kvh) * head_stride;
+      const uint16_t* vb = p.v_cache + ((int64_t)pg * hkv + kvh) * head_stride;
+      for (int j = 0; j < CPT; ++j) {
+        const int e = (tid + j * kPreThreads) * 8;  // element offset in the block
+        if (e >= EPB) break;
+        if (pg < 0) {
+          kreg[t2][j] = u32x4{0, 0, 0, 0};
+          vreg[t2][j] = u32x4{0, 0, 0, 0};
+          continue;
+        }
+        kreg[t2][j] = *(const u32x4*)(kb + e);
+        vreg[t2][j] = *(const u32x4*)(vb + e);
+        if (!inner) {
+          // keys outside [wg_klo, wg_khi] may hold evicted or unwritten data
+          const int kk = tile + e / D;
+          if (kk < wg_klo || kk > wg_khi) kreg[t2][j] = u32x4{0, 0, 0, 0};
+          const int k8 = tile + (e % 16);
+          for (int x = 0; x < 8; ++x) {
+            const int kp = k8 + x;
+            if (kp < wg_klo || kp > wg_khi)
+              vreg[t2][j][x >> 1] &= (x & 1) ? 0x0000ffffu : 0xffff0000u;
           }
         }
       }
     }
   };
   auto stage_store = [&](int buf) {
-    if (k_role) *(u32x4*)(&kl[buf][sk * KROW + sc * 8]) = kreg;
-    if (v_role) {
-      // page-local keys 8*sh + 0..3 go to slots 4*sh + 0..3 and keys
-      // 8*sh + 4..7 to slots 8 + 4*sh + 0..3 (the PV operand order)
-      uint16_t* dst = &vl[buf][(st * D + sd) * 16];
-      u32x2 a = {bf16x2_to_f16x2(vreg[0]), bf16x2_to_f16x2(vreg[1])};
-      u32x2 b = {bf16x2_to_f16x2(vreg[2]), bf16x2_to_f16x2(vreg[3])};
-      *(u32x2*)(dst + 4 * sh) = a;
-      *(u32x2*)(dst + 8 + 4 * sh) = b;
-    }
+    for (int t2 = 0; t2 < 2; ++t2)
+      for (int j = 0; j < CPT; ++j) {
+        const int e = (tid + j * kPreThreads) * 8;
+        if (e >= EPB) break;
+        *(u32x4*)(&kl[buf][(16 * t2 + e / D) * KROW + e % D]) = kreg[t2][j];
+        // page-local keys 0..3 / 4..7 of this 8-key half go to slots
+        // 4*h + 0..3 / 8 + 4*h + 0..3 (h = which half): the PV operand order
+        const int dd = e / 16, h = (e % 16) / 8;
+        uint16_t* dst = &vl[buf][(t2 * D + dd) * 16];
+        u32x2 a = {bf16x2_to_f16x2(vreg[t2][j][0]), bf16x2_to_f16x2(vreg[t2][j][1])};
+        u32x2 b = {bf16x2_to_f16x2(vreg[t2][j][2]), bf16x2_to_f16x2(vreg[t2][j][3])};
+        *(u32x2*)(dst + 4 * h) = a;
+        *(u32x2*)(dst + 8 + 4 * h) = b;
+      }
   };
 
   stage_load(kstart);
@@ -174,33 +201,43 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnParams p, int 
         bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * c));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc, 0, 0, 0);
       }
-      // lane value r is key kp0 + 8*(r/4) + 4*h2 + r%4 for query row qr
-      float sv[16];
+      // every key of the step valid for every row of the wave?
+      const bool interior = kp0 + 31 <= w_pos_lo && (KIND == 0 || kp0 > w_pos_hi - W);
       float mx = -INFINITY;
-      for (int r = 0; r < 16; ++r) {
-        const int kp = kp0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const bool ok = kp <= my_pos && (KIND == 0 || kp > my_pos - W);
-        sv[r] = ok ? sacc[r] * sl2 : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
+      if (interior) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      } else {
+        // lane value r is key kp0 + 8*(r/4) + 4*h2 + r%4 for query row qr
+        const int rel = kp0 + 4 * h2 - my_pos;  // key - query of value 0
+        for (int r = 0; r < 16; ++r) {
+          const int dk = rel + 8 * (r >> 2) + (r & 3);
+          const bool ok = dk <= 0 && (KIND == 0 || dk > -W);
+          sacc[r] = ok ? sacc[r] : -INFINITY;
+          mx = fmaxf(mx, sacc[r]);
+        }
       }
       mx = fmaxf(mx, xor_lane(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
+      const float mxs = mx * sl2;
+      if (__builtin_amdgcn_ballot_w64(mxs > m + kLazy) != 0) {  // wave-uniform branch
+        const float m_new = fmaxf(m, mxs);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+        for (int mb = 0; mb < NM; ++mb) o[mb] *= alpha;
+        lsum *= alpha;
+        m = m_new;
+      }
+      const float mo = m == -INFINITY ? 0.f : m;
       float ps = 0.f;
       f16x8 pf0, pf1;
       for (int r = 0; r < 8; ++r) {
-        const float e0 = fast_exp2(sv[r] - m_use);
-        const float e1 = fast_exp2(sv[r + 8] - m_use);
+        const float e0 = fast_exp2(__builtin_fmaf(sacc[r], sl2, -mo));
+        const float e1 = fast_exp2(__builtin_fmaf(sacc[r + 8], sl2, -mo));
         ps += e0 + e1;
         pf0[r] = (_Float16)e0;
         pf1[r] = (_Float16)e1;
       }
-      lsum = lsum * alpha + ps;
-      m = m_new;
+      lsum += ps;
       const uint16_t* v0 = &vl[buf][0];
       for (int mb = 0; mb < NM; ++mb) {
-        o[mb] *= alpha;
         const int d = 32 * mb + qr;
         f16x8 va = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + d * 16 + 8 * h2));
         f16x8 vb = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + (D + d) * 16 + 8 * h2));
@@ -227,27 +264,27 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnParams p, int 
   }
 }
 
-template <int D, int KIND>
+template <int D, int KIND, int G>
 hipError_t launch_prefill_g(const AttnParams& p, hipStream_t s) {
-  const int g = p.hq / p.hkv;
-  const int qb_pos = 32 * kPreWaves / g;
-  const int qblocks = (p.max_q_len + qb_pos - 1) / qb_pos;
-  dim3 grid((unsigned)(p.num_seqs * qblocks), (unsigned)p.hkv);
-  switch (g) {
-    case 1:
-      hipLaunchKernelGGL((prefill_kernel<D, KIND, 1>), grid, dim3(kPreThreads), 0, s, p, qblocks);
-      break;
-    case 2:
-      hipLaunchKernelGGL((prefill_kernel<D, KIND, 2>), grid, dim3(kPreThreads), 0, s, p, qblocks);
-      break;
-    case 4:
-      hipLaunchKernelGGL((prefill_kernel<D, KIND, 4>), grid, dim3(kPreThreads), 0, s, p, qblocks);
-      break;
-    default:
-      hipLaunchKernelGGL((prefill_kernel<D, KIND, 8>), grid, dim3(kPreThreads), 0, s, p, qblocks);
-      break;
-  }
+  constexpr int HPW = G < kPreWaves ? G : kPreWaves;
+  constexpr int QB = 32 * (kPreWaves / HPW);
+  const int qblocks = (p.max_q_len + QB - 1) / QB;
+  const int64_t tiles = (int64_t)p.num_seqs * qblocks * p.hkv * (G / HPW);
+  if (tiles > INT32_MAX - 8) return hipErrorInvalidValue;
+  const int grid = (int)((tiles + 7) / 8 * 8);
+  hipLaunchKernelGGL((prefill_kernel<D, KIND, G>), dim3(grid), dim3(kPreThreads), 0, s, p,
+                     qblocks, (int)tiles);
   return hipGetLastError();
+}
+
+template <int D, int KIND>
+hipError_t launch_prefill_k(const AttnParams& p, hipStream_t s) {
+  switch (p.hq / p.hkv) {
+    case 1: return launch_prefill_g<D, KIND, 1>(p, s);
+    case 2: return launch_prefill_g<D, KIND, 2>(p, s);
+    case 4: return launch_prefill_g<D, KIND, 4>(p, s);
+    default: return launch_prefill_g<D, KIND, 8>(p, s);
+  }
 }
 
 }  // namespace
@@ -255,8 +292,8 @@ hipError_t launch_prefill_g(const AttnParams& p, hipStream_t s) {
 hipError_t launch_prefill(const AttnParams& p, hipStream_t s) {
   if (p.num_seqs <= 0 || p.total_q <= 0) return hipSuccess;
   if (p.d == 128)
-    return p.kind == 0 ? launch_prefill_g<128, 0>(p, s) : launch_prefill_g<128, 1>(p, s);
-  return p.kind == 0 ? launch_prefill_g<64, 0>(p, s) : launch_prefill_g<64, 1>(p, s);
+    return p.kind == 0 ? launch_prefill_k<128, 0>(p, s) : launch_prefill_k<128, 1>(p, s);
+  return p.kind == 0 ? launch_prefill_k<64, 0>(p, s) : launch_prefill_k<64, 1>(p, s);
 }
 
 }  // namespace hswa

@@ -166,9 +166,11 @@ def test_window_one_returns_value(gpu):
     outs, vlens, _ = chunked_prefill(st, seqs, 32, hq)
     v = seqs[0].v.float()
     for h in range(hq):
-        # exact except where bf16 -> fp16 lands in the fp16 subnormal range
-        err = (outs[0][:, h] - v[:, h // (hq // hkv)]).abs().max().item()
-        assert err <= 2.0 ** -25
+        # one key of weight 1: the value itself, up to fp32 rounding of the
+        # normaliser and the fp16 subnormal range of the PV operand
+        vv = v[:, h // (hq // hkv)]
+        err = (outs[0][:, h] - vv).abs() - 1e-6 * vv.abs()
+        assert err.max().item() <= 2.0 ** -24
     assert torch.all(vlens[0] == 1)
 
 

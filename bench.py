@@ -125,9 +125,7 @@ class ChunkedPrefill:
         self.layers = []
         for li, kind in enumerate(kinds):
             npages = nfull if kind == "F" else B * C_ // 16
-            ks, vs = H.kv_cache_shapes(npages, hkv, d)
-            kc = torch.zeros(ks, dtype=torch.bfloat16, device=cx.dev)
-            vc = torch.zeros(vs, dtype=torch.bfloat16, device=cx.dev)
+            kc, vc = H.kv_cache_alloc(npages, hkv, d, cx.dev, 0.0)
             self.layers.append((H.FULL if kind == "F" else H.SWA, kc, vc))
         # inputs per sequence, generated on the device
         self.q, self.k, self.v = [], [], []
@@ -244,12 +242,7 @@ class Decode:
         self.layers = []
         kvb = KV_TOKEN_BYTES(hkv, d)
         for li, kind in enumerate(pattern):
-            if kind == "F":
-                ks, vs = H.kv_cache_shapes(nfull, hkv, d)
-            else:
-                ks, vs = H.kv_cache_shapes(B * ring // 16, hkv, d)
-            kc = torch.empty(ks, dtype=torch.bfloat16, device=cx.dev)
-            vc = torch.empty(vs, dtype=torch.bfloat16, device=cx.dev)
+            kc, vc = H.kv_cache_alloc(nfull if kind == "F" else B * ring // 16, hkv, d, cx.dev)
             # restore the context: generated per sequence on the device and
             # appended (Full: every position, SWA: the last W-1)
             for b, c in enumerate(ctxs):

@@ -32,7 +32,7 @@ __all__ = [
     "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view", "hswa_pool_alloc",
     "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
-    "hswa_last_error", "hswa_version", "kv_cache_shapes", "library",
+    "hswa_last_error", "hswa_version", "kv_cache_shapes", "kv_cache_alloc", "library",
 ]
 
 
@@ -224,9 +224,22 @@ def hswa_pool_read_tables(pool: Pool) -> dict:
 
 
 def kv_cache_shapes(num_pages: int, num_kv_heads: int, head_dim: int):
-    """Shapes of one layer's K and V page buffers (bf16)."""
+    """Shapes of one layer's K pages (bf16, token-major) and V pages (fp16,
+    dim-major)."""
     return ((num_pages, num_kv_heads, PAGE_SIZE, head_dim),
             (num_pages, num_kv_heads, head_dim, PAGE_SIZE))
+
+
+def kv_cache_alloc(num_pages: int, num_kv_heads: int, head_dim: int, device, fill=None):
+    """Allocates one layer's K (bf16) and V (fp16) page buffers on `device`,
+    uninitialised or filled with `fill`."""
+    import torch
+    ks, vs = kv_cache_shapes(num_pages, num_kv_heads, head_dim)
+    if fill is None:
+        return (torch.empty(ks, dtype=torch.bfloat16, device=device),
+                torch.empty(vs, dtype=torch.float16, device=device))
+    return (torch.full(ks, fill, dtype=torch.bfloat16, device=device),
+            torch.full(vs, fill, dtype=torch.float16, device=device))
 
 
 def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_seq_len,

@@ -13,10 +13,13 @@
 //    16x16x32 MFMA: S^T[key][head] = K[key][:] . Q[head][:], so every K/V
 //    byte is read from HBM once for all G heads.
 //  - K rows (token-major pages) are the A operand loaded straight from HBM,
-//    16 bytes per lane.  V pages are dim-major, so the PV product
-//    O^T[d][head] = V^T[d][key] . P^T[key][head] reads 8 contiguous bytes per
-//    lane per page.  P and V enter the PV MFMA as fp16 (V converted in
-//    registers), keeping the weights to 11 significant bits.
+//    16 bytes per lane.  The 32 keys of a step are dealt to the two 16-row
+//    score tiles so that each lane's eight scores are eight consecutive keys
+//    of one page (tile 0 row 4a+r is key 8a+r, tile 1 row 4a+r is key
+//    8a+4+r); with V pages dim-major and in fp16, the PV product
+//    O^T[d][head] = V^T[d][key] . P^T[key][head] then reads each lane's V
+//    fragment as 16 contiguous bytes and needs no conversion.  P enters the
+//    PV MFMA as fp16, keeping the weights to 11 significant bits.
 //  - Online softmax in fp32 in the log2 domain (exp2 of prescaled scores).
 //  - Wave w takes 32-key steps w, w+4, ...; the four partial states merge
 //    through LDS in a fixed order, so results depend only on logical key
@@ -89,25 +92,30 @@ __global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
     const int kp0 = s0 + 32 * st;
     const bool has1 = kp0 + 16 < khi;
     const int32_t pg0 = page_of<KIND>(p.t.fpt, p.t.rpt, sid, kp0, p.t.max_pages, p.t.ring_slots);
+    // a page past the last key: read page 0 again (those keys are masked)
     const int32_t pg1 =
-        has1 ? page_of<KIND>(p.t.fpt, p.t.rpt, sid, kp0 + 16, p.t.max_pages, p.t.ring_slots) : 0;
+        has1 ? page_of<KIND>(p.t.fpt, p.t.rpt, sid, kp0 + 16, p.t.max_pages, p.t.ring_slots)
+             : pg0;
     if (pg0 < 0 || pg1 < 0) break;  // positions without pages: the caller skipped alloc
     const uint16_t* kb0 = p.k_cache + ((int64_t)pg0 * hkv + kvh) * head_stride;
     const uint16_t* kb1 = p.k_cache + ((int64_t)pg1 * hkv + kvh) * head_stride;
     const uint16_t* vb0 = p.v_cache + ((int64_t)pg0 * hkv + kvh) * head_stride;
     const uint16_t* vb1 = p.v_cache + ((int64_t)pg1 * hkv + kvh) * head_stride;
 
-    // issue every load of the step first
+    // issue every load of the step first.  K: this lane's row `col` of
+    // score tile t is key 8*(col/4) + 4t + col%4 (page col/8).  V: keys
+    // 8*q4 .. +8 are page q4/2, offset 8*(q4%2).
+    const int kpage = col >> 3;
+    const uint16_t* kb = kpage ? kb1 : kb0;
+    const int krow0 = (8 * (col >> 2) + (col & 3)) & 15;
     u32x4 kr[2][NC];
     for (int c = 0; c < NC; ++c) {
-      kr[0][c] = *(const u32x4*)(kb0 + col * D + 32 * c + 8 * q4);
-      kr[1][c] = has1 ? *(const u32x4*)(kb1 + col * D + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
+      kr[0][c] = *(const u32x4*)(kb + krow0 * D + 32 * c + 8 * q4);
+      kr[1][c] = *(const u32x4*)(kb + (krow0 + 4) * D + 32 * c + 8 * q4);
     }
-    u32x2 vr[NB][2];
-    for (int nb = 0; nb < NB; ++nb) {
-      vr[nb][0] = *(const u32x2*)(vb0 + (16 * nb + col) * kPage + 4 * q4);
-      vr[nb][1] = has1 ? *(const u32x2*)(vb1 + (16 * nb + col) * kPage + 4 * q4) : u32x2{0, 0};
-    }
+    const uint16_t* vb = ((q4 >> 1) ? vb1 : vb0) + 8 * (q4 & 1);
+    u32x4 vr[NB];
+    for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(vb + (16 * nb + col) * kPage);
 
     // S^T for the two 16-key tiles
     f32x4 s[2];
@@ -118,13 +126,13 @@ __global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
                                                       acc, 0, 0, 0);
       s[t] = acc;
     }
-    // mask: lane value (t, r) is key kp0 + 16t + 4*q4 + r
+    // mask: lane value (t, r) is key kp0 + 8*q4 + 4t + r
     unsigned valid = 0;
     float mx = -INFINITY;
     float sv[8];
     for (int t = 0; t < 2; ++t)
       for (int r = 0; r < 4; ++r) {
-        const int kp = kp0 + 16 * t + 4 * q4 + r;
+        const int kp = kp0 + 8 * q4 + 4 * t + r;
         const bool ok = kp >= klo && kp < khi;
         valid |= (unsigned)ok << (4 * t + r);
         const float x = ok ? s[t][r] * sl2 : -INFINITY;
@@ -144,16 +152,14 @@ __global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
     }
     lsum = lsum * alpha + ps;
     m = m_new;
-    const bool full = valid == 0xffu;
+    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+    if (valid != 0xffu) {
+      // zero V of masked keys: their slots may hold stale or unwritten data
+      for (int j = 0; j < 8; ++j)
+        if (!((valid >> j) & 1u)) vmask[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
+    }
     for (int nb = 0; nb < NB; ++nb) {
-      uint32_t w[4] = {bf16x2_to_f16x2(vr[nb][0][0]), bf16x2_to_f16x2(vr[nb][0][1]),
-                       bf16x2_to_f16x2(vr[nb][1][0]), bf16x2_to_f16x2(vr[nb][1][1])};
-      if (!full) {
-        // zero V of masked keys: their slots may hold stale or unwritten data
-        for (int j = 0; j < 8; ++j)
-          if (!((valid >> j) & 1u)) w[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
-      }
-      f16x8 vf = __builtin_bit_cast(f16x8, u32x4{w[0], w[1], w[2], w[3]});
+      const f16x8 vf = __builtin_bit_cast(f16x8, vr[nb] & vmask);
       o[nb] *= alpha;
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[nb], 0, 0, 0);
     }

@@ -3,10 +3,13 @@
 // Page layout of a layer's pool (Full pool and SWA ring alike), per
 // "Following the Bottleneck: Optimizing MiniMax M3 on AMD Instinct MI355X"
 // sec. 3 (16-token pages behind a page table):
-//   K: [page][Hkv][16][d]   token-major: a key row is d contiguous bf16
-//   V: [page][Hkv][d][16]   dim-major:  the 16 tokens of one dim are
-//                           contiguous, which is the operand order of the
-//                           PV matrix product (keys are its reduction dim)
+//   K: [page][Hkv][16][d]   bf16, token-major: a key row is d contiguous
+//   V: [page][Hkv][d][16]   fp16, dim-major: the 16 tokens of one dim are
+//                           contiguous, the operand order of the PV matrix
+//                           product (keys are its reduction dim).  V is
+//                           stored in fp16 because that product runs on the
+//                           fp16 MFMA; bf16 -> fp16 is exact for
+//                           2^-14 <= |v| < 65504.
 #include <hip/hip_runtime.h>
 
 #include "device.h"
@@ -105,12 +108,13 @@ __global__ void __launch_bounds__(256) append_kernel(AttnParams p, int tiles_per
     if (whole) {
       u32x4 w;
       for (int j = 0; j < 4; ++j)
-        w[j] = (uint32_t)vt[half * 8 + 2 * j][e] | ((uint32_t)vt[half * 8 + 2 * j + 1][e] << 16);
+        w[j] = pack_f16x2(bf16_lo(vt[half * 8 + 2 * j][e]), bf16_lo(vt[half * 8 + 2 * j + 1][e]));
       *(u32x4*)dst = w;
     } else {
       for (int j = 0; j < 8; ++j) {
         const int pos = tile_pos + half * 8 + j;
-        if (pos >= lo && pos < hi) dst[j] = vt[half * 8 + j][e];
+        if (pos >= lo && pos < hi)
+          dst[j] = __builtin_bit_cast(uint16_t, (_Float16)bf16_lo(vt[half * 8 + j][e]));
       }
     }
   }

@@ -14,16 +14,19 @@
 //    let three of them share a CU, so one's loads overlap another's math.
 //  - Scores use the 32x32x16 bf16 MFMA as S^T[key][row] = K . Q^T, with the
 //    Q^T fragments held in registers for the whole key loop and K read from
-//    LDS.  The output uses the 32x32x16 fp16 MFMA as O^T[d][row] = V^T . P^T.
-//    The score layout puts each lane's probabilities exactly where the PV
-//    product wants them, so P never goes through LDS.
+//    LDS.  The output uses the 32x32x16 fp16 MFMA as O^T[d][row] = V^T . P^T
+//    on the fp16 V pages.  K rows are staged with bits 2 and 3 of the
+//    in-page key index swapped, which makes the eight scores a lane holds per
+//    page eight consecutive keys: each lane's probabilities are then exactly
+//    the B operand of the PV product and its V fragment is 16 contiguous
+//    bytes of the page, so P never goes through LDS and V is copied verbatim.
 //  - K/V move through LDS in 32-key steps (two 16-token pages), double
 //    buffered: global loads of step s+1 are in flight while step s computes.
-//    V is converted to fp16 once, at staging, and stored in the key order the
-//    PV fragments read (16 contiguous bytes per lane).
 //  - Keys outside the workgroup's range are staged as zeros (their slots can
 //    hold evicted or unwritten data); per-row masks select -inf scores.
-//  - Online softmax in fp32, log2 domain; output fp32.
+//  - Online softmax in fp32, log2 domain, with lazy rescaling: the two lanes
+//    of a row exchange their maxima only when the running max must move;
+//    output fp32.
 #include <hip/hip_runtime.h>
 
 #include "device.h"
@@ -172,15 +175,11 @@ prefill_kernel(AttnParams p, int qblocks,
       for (int j = 0; j < CPT; ++j) {
         const int e = (tid + j * kPreThreads) * 8;
         if (e >= EPB) break;
-        *(u32x4*)(&kl[buf][(16 * t2 + e / D) * KROW + e % D]) = kreg[t2][j];
-        // page-local keys 0..3 / 4..7 of this 8-key half go to slots
-        // 4*h + 0..3 / 8 + 4*h + 0..3 (h = which half): the PV operand order
-        const int dd = e / 16, h = (e % 16) / 8;
-        uint16_t* dst = &vl[buf][(t2 * D + dd) * 16];
-        u32x2 a = {bf16x2_to_f16x2(vreg[t2][j][0]), bf16x2_to_f16x2(vreg[t2][j][1])};
-        u32x2 b = {bf16x2_to_f16x2(vreg[t2][j][2]), bf16x2_to_f16x2(vreg[t2][j][3])};
-        *(u32x2*)(dst + 4 * h) = a;
-        *(u32x2*)(dst + 8 + 4 * h) = b;
+        // key row kr of the page goes to LDS row swap23(kr) of the page half
+        const int kr = e / D;
+        const int rho = ((kr >> 2) & 1) * 8 + ((kr >> 3) & 1) * 4 + (kr & 3);
+        *(u32x4*)(&kl[buf][(16 * t2 + rho) * KROW + e % D]) = kreg[t2][j];
+        *(u32x4*)(&vl[buf][t2 * EPB + e]) = vreg[t2][j];
       }
   };
 
@@ -207,19 +206,19 @@ prefill_kernel(AttnParams p, int qblocks,
       if (interior) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
       } else {
-        // lane value r is key kp0 + 8*(r/4) + 4*h2 + r%4 for query row qr
-        const int rel = kp0 + 4 * h2 - my_pos;  // key - query of value 0
+        // lane value r = 4j + i is key kp0 + 16(j/2) + 8*h2 + 4(j%2) + i
+        const int rel = kp0 + 8 * h2 - my_pos;  // key - query of value 0
         for (int r = 0; r < 16; ++r) {
-          const int dk = rel + 8 * (r >> 2) + (r & 3);
+          const int dk = rel + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
           const bool ok = dk <= 0 && (KIND == 0 || dk > -W);
           sacc[r] = ok ? sacc[r] : -INFINITY;
           mx = fmaxf(mx, sacc[r]);
         }
       }
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      const float mxs = mx * sl2;
-      if (__builtin_amdgcn_ballot_w64(mxs > m + kLazy) != 0) {  // wave-uniform branch
-        const float m_new = fmaxf(m, mxs);
+      // the running max moves only when some score exceeds it by 2^kLazy;
+      // then the two lanes of a row agree on the new one through one exchange
+      if (__builtin_amdgcn_ballot_w64(mx * sl2 > m + kLazy) != 0) {  // wave-uniform
+        const float m_new = fmaxf(m, fmaxf(mx, xor_lane(mx, 32)) * sl2);
         const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
         for (int mb = 0; mb < NM; ++mb) o[mb] *= alpha;
         lsum *= alpha;
@@ -236,11 +235,11 @@ prefill_kernel(AttnParams p, int qblocks,
         pf1[r] = (_Float16)e1;
       }
       lsum += ps;
-      const uint16_t* v0 = &vl[buf][0];
+      // V fragment: dim 32mb + qr, keys 8*h2 .. +8 of each page
+      const uint16_t* v0 = &vl[buf][qr * 16 + 8 * h2];
       for (int mb = 0; mb < NM; ++mb) {
-        const int d = 32 * mb + qr;
-        f16x8 va = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + d * 16 + 8 * h2));
-        f16x8 vb = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + (D + d) * 16 + 8 * h2));
+        f16x8 va = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + 512 * mb));
+        f16x8 vb = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + EPB + 512 * mb));
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf0, o[mb], 0, 0, 0);
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb, pf1, o[mb], 0, 0, 0);
       }

@@ -37,11 +37,13 @@
  *
  * Memory layout of a layer's K/V pool (Full pool or SWA ring alike):
  *    K: [num_pages][Hkv][16][head_dim]  bf16   (token-major in a page)
- *    V: [num_pages][Hkv][head_dim][16]  bf16   (dim-major in a page)
+ *    V: [num_pages][Hkv][head_dim][16]  fp16   (dim-major in a page)
  *  A token's slot is page * 16 + offset.  One (page, head) block is
- *  16 * head_dim * 2 bytes contiguous for K and for V.  V values must be
- *  finite with |v| < 65504: the PV product runs in fp16 (bf16 -> fp16 is
- *  exact in that range).
+ *  16 * head_dim * 2 bytes contiguous for K and for V.  V is kept in fp16
+ *  because the PV product runs on the fp16 MFMA: the append converts the
+ *  bf16 input, exactly for 2^-14 <= |v| < 65504 (smaller magnitudes round to
+ *  fp16 subnormals, error < 2^-25); V values must be finite with
+ *  |v| < 65504.  Callers that write pages themselves write V in fp16.
  */
 #ifndef HSWA_H
 #define HSWA_H

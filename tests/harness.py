@@ -60,10 +60,8 @@ class Setup:
                                        free, ring, device=dev())
         self.view = H.hswa_pool_get_view(self.pool)
         npages = num_full_pages if kind == H.FULL else max_seqs * ring_slots // 16
-        ks, vs = H.kv_cache_shapes(npages, hkv, d)
-        fill = float("nan") if poison else 0.0
-        self.kc = torch.full(ks, fill, dtype=torch.bfloat16, device=dev())
-        self.vc = torch.full(vs, fill, dtype=torch.bfloat16, device=dev())
+        self.kc, self.vc = H.kv_cache_alloc(npages, hkv, d, dev(),
+                                            float("nan") if poison else 0.0)
         self.ring_pages = ring.reshape(max_seqs, ring_slots // 16)
 
     def poison_ring_positions(self, b, positions):

@@ -237,9 +237,7 @@ def _decode_scenario(ctxs, steps, hq, hkv, d, W, seed, C=None):
     nfull = B * maxp + 8
     full = Setup(H.FULL, W, C, B, maxp, nfull, hkv, d, seed)
     # the SWA layer shares the pool's tables; it only needs its own ring buffers
-    ks, vs = H.kv_cache_shapes(B * C // 16, hkv, d)
-    skc = torch.full(ks, float("nan"), dtype=torch.bfloat16, device=dev())
-    svc = torch.full(vs, float("nan"), dtype=torch.bfloat16, device=dev())
+    skc, svc = H.kv_cache_alloc(B * C // 16, hkv, d, dev(), float("nan"))
     pool, view = full.pool, full.view
     ids = list(range(B))
     H.hswa_pool_import(pool, ids, ctxs)

@@ -38,7 +38,8 @@ namespace {
 constexpr int kDecWaves = 4;
 
 template <int D, int KIND, int G>
-__global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 4)))
+decode_kernel(AttnParams p) {
   constexpr int NB = D / 16;  // 16-row d blocks of O^T
   constexpr int NC = D / 32;  // 32-wide d chunks of the QK reduction
   __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][G][D];
@@ -88,36 +89,55 @@ __global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
   const int nsteps = (khi - 1 - s0) / 32 + 1;
   const int64_t head_stride = (int64_t)kPage * D;  // elements per (page, head) block
 
+  // Page-table row of the sequence, read through the constant address space
+  // so the lookups are scalar loads (the tables do not change while the
+  // kernel runs).
+  typedef const __attribute__((address_space(4))) int32_t* ctab_t;
+  const ctab_t ptab = (ctab_t)(KIND == 0 ? p.t.fpt + (int64_t)sid * p.t.max_pages
+                                         : p.t.rpt + (int64_t)sid * (p.t.ring_slots / kPage));
+  auto page_at = [&](int pos) {
+    const int idx = KIND == 0 ? pos / kPage : (pos % p.t.ring_slots) / kPage;
+    return ptab[__builtin_amdgcn_readfirstlane(idx)];
+  };
+  // K: this lane's row `col` of score tile t is key 8*(col/4) + 4t + col%4,
+  // on page col/8.  V: keys 8*q4 .. +8 are page q4/2, offset 8*(q4%2).
+  const int kpage = col >> 3;
+  const int krow0 = (8 * (col >> 2) + (col & 3)) & 15;
+  const int k_lane = krow0 * D + 8 * q4;
+  const int v_lane = col * kPage + 8 * (q4 & 1);
+  auto step_pages = [&](int kp0, const uint16_t*& kb, const uint16_t*& vb) {
+    int32_t pg0 = page_at(kp0);
+    // a page past the last key: read page 0 again (those keys are masked)
+    int32_t pg1 = kp0 + 16 < khi ? page_at(kp0 + 16) : pg0;
+    // a missing page means the caller skipped alloc: read page 0 of the pool
+    // instead of faulting (the result of such a call is undefined)
+    pg0 = pg0 < 0 ? 0 : pg0;
+    pg1 = pg1 < 0 ? 0 : pg1;
+    kb = p.k_cache + ((int64_t)(kpage ? pg1 : pg0) * hkv + kvh) * head_stride + k_lane;
+    vb = p.v_cache + ((int64_t)((q4 >> 1) ? pg1 : pg0) * hkv + kvh) * head_stride + v_lane;
+  };
+
+  // Software pipeline, register-neutral: the K loads of this wave's next
+  // step are issued as soon as the score MFMAs have consumed the current K
+  // fragments, the V loads as soon as the PV MFMAs have consumed V; so each
+  // wave keeps a step's worth of bytes in flight through its math.
+  u32x4 kr[2][NC], vr[NB];
+  const uint16_t *kb, *vb;
+  if (wave < nsteps) {
+    step_pages(s0 + 32 * wave, kb, vb);
+    for (int c = 0; c < NC; ++c) {
+      kr[0][c] = *(const u32x4*)(kb + 32 * c);
+      kr[1][c] = *(const u32x4*)(kb + 4 * D + 32 * c);
+    }
+    for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(vb + 16 * nb * kPage);
+  }
   for (int st = wave; st < nsteps; st += kDecWaves) {
     const int kp0 = s0 + 32 * st;
-    const bool has1 = kp0 + 16 < khi;
-    const int32_t pg0 = page_of<KIND>(p.t.fpt, p.t.rpt, sid, kp0, p.t.max_pages, p.t.ring_slots);
-    // a page past the last key: read page 0 again (those keys are masked)
-    const int32_t pg1 =
-        has1 ? page_of<KIND>(p.t.fpt, p.t.rpt, sid, kp0 + 16, p.t.max_pages, p.t.ring_slots)
-             : pg0;
-    if (pg0 < 0 || pg1 < 0) break;  // positions without pages: the caller skipped alloc
-    const uint16_t* kb0 = p.k_cache + ((int64_t)pg0 * hkv + kvh) * head_stride;
-    const uint16_t* kb1 = p.k_cache + ((int64_t)pg1 * hkv + kvh) * head_stride;
-    const uint16_t* vb0 = p.v_cache + ((int64_t)pg0 * hkv + kvh) * head_stride;
-    const uint16_t* vb1 = p.v_cache + ((int64_t)pg1 * hkv + kvh) * head_stride;
+    const bool more = st + kDecWaves < nsteps;
+    const uint16_t *kbn = kb, *vbn = vb;
+    if (more) step_pages(kp0 + 32 * kDecWaves, kbn, vbn);
 
-    // issue every load of the step first.  K: this lane's row `col` of
-    // score tile t is key 8*(col/4) + 4t + col%4 (page col/8).  V: keys
-    // 8*q4 .. +8 are page q4/2, offset 8*(q4%2).
-    const int kpage = col >> 3;
-    const uint16_t* kb = kpage ? kb1 : kb0;
-    const int krow0 = (8 * (col >> 2) + (col & 3)) & 15;
-    u32x4 kr[2][NC];
-    for (int c = 0; c < NC; ++c) {
-      kr[0][c] = *(const u32x4*)(kb + krow0 * D + 32 * c + 8 * q4);
-      kr[1][c] = *(const u32x4*)(kb + (krow0 + 4) * D + 32 * c + 8 * q4);
-    }
-    const uint16_t* vb = ((q4 >> 1) ? vb1 : vb0) + 8 * (q4 & 1);
-    u32x4 vr[NB];
-    for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(vb + (16 * nb + col) * kPage);
-
-    // S^T for the two 16-key tiles
+    // S^T for the two 16-key tiles, then refill K
     f32x4 s[2];
     for (int t = 0; t < 2; ++t) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -126,6 +146,11 @@ __global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
                                                       acc, 0, 0, 0);
       s[t] = acc;
     }
+    if (more)
+      for (int c = 0; c < NC; ++c) {
+        kr[0][c] = *(const u32x4*)(kbn + 32 * c);
+        kr[1][c] = *(const u32x4*)(kbn + 4 * D + 32 * c);
+      }
     // mask: lane value (t, r) is key kp0 + 8*q4 + 4t + r
     unsigned valid = 0;
     float mx = -INFINITY;
@@ -163,6 +188,11 @@ __global__ void __launch_bounds__(256) decode_kernel(AttnParams p) {
       o[nb] *= alpha;
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[nb], 0, 0, 0);
     }
+    // refill V
+    if (more)
+      for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(vbn + 16 * nb * kPage);
+    kb = kbn;
+    vb = vbn;
   }
 
   // merge the four waves' states (fixed order)

@@ -45,9 +45,12 @@ decode_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][G][D];
   __shared__ float red_ml[kDecWaves][G][2];
 
-  const int i = blockIdx.x / p.n_splits;
-  const int split = blockIdx.x % p.n_splits;
-  const int kvh = blockIdx.y;
+  // KV head fastest in the grid: workgroups running at the same time then
+  // read all KV heads' slices of the pages, which spreads their traffic over
+  // all HBM channels (one head's 4 KB slices alone concentrate on a few).
+  const int kvh = blockIdx.x % p.hkv;
+  const int i = (blockIdx.x / p.hkv) / p.n_splits;
+  const int split = (blockIdx.x / p.hkv) % p.n_splits;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
   const int L = p.t.seq_len[sid];
@@ -263,7 +266,7 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p) {
 
 template <int D, int KIND>
 hipError_t launch_decode_g(const AttnParams& p, hipStream_t s) {
-  dim3 grid((unsigned)(p.num_seqs * p.n_splits), (unsigned)p.hkv);
+  dim3 grid((unsigned)(p.num_seqs * p.n_splits * p.hkv), 1);
   const int g = p.hq / p.hkv;
   switch (g) {
     case 1: hipLaunchKernelGGL((decode_kernel<D, KIND, 1>), grid, dim3(256), 0, s, p); break;

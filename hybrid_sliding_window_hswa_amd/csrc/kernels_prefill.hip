@@ -8,7 +8,7 @@
 //
 // Design (gfx950):
 //  - Workgroup = 4 wavefronts for one (sequence, query block, KV head,
-//    head group).  Wave w owns 32 query positions of one query head, so up
+//    head group); the grid runs head groups fastest (HBM channel spread).  Wave w owns 32 query positions of one query head, so up
 //    to four heads sharing a KV head (and, for G < 4, several 32-position
 //    groups) share every K/V tile the workgroup stages.  Small workgroups
 //    let three of them share a CU, so one's loads overlap another's math.
@@ -61,16 +61,17 @@ prefill_kernel(AttnParams p, int qblocks,
   __shared__ __attribute__((aligned(16))) uint16_t kl[2][32 * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t vl[2][2 * D * 16];
 
-  // XCD-aware tile order: workgroup g runs on XCD g % 8; give each XCD a
-  // contiguous range of tiles so neighbouring query blocks of one
-  // (sequence, head group) share that XCD's L2 (their K/V windows overlap).
-  const int g = blockIdx.x;
-  const int per = gridDim.x / 8;
-  const int t = (g % 8) * per + g / 8;
+  // Tile order: head group fastest.  Workgroups running at the same time
+  // then cover every KV head's slice of the K/V pages and every head's slice
+  // of the Q/O rows, which spreads their traffic over all HBM channels (one
+  // head's slices alone concentrate on a few).  Neighbouring query blocks of
+  // one head, whose K/V windows overlap, still run close together in time.
+  const int t = blockIdx.x;
   if (t >= total_tiles) return;
-  const int qb = t % qblocks;
-  const int i = (t / qblocks) % p.num_seqs;
-  const int yh = t / (qblocks * p.num_seqs);
+  const int NY = p.hkv * HG;
+  const int yh = t % NY;
+  const int qb = (t / NY) % qblocks;
+  const int i = (t / NY) / qblocks;
   const int kvh = yh / HG;
   const int hg = yh % HG;
 
@@ -270,7 +271,7 @@ hipError_t launch_prefill_g(const AttnParams& p, hipStream_t s) {
   const int qblocks = (p.max_q_len + QB - 1) / QB;
   const int64_t tiles = (int64_t)p.num_seqs * qblocks * p.hkv * (G / HPW);
   if (tiles > INT32_MAX - 8) return hipErrorInvalidValue;
-  const int grid = (int)((tiles + 7) / 8 * 8);
+  const int grid = (int)tiles;
   hipLaunchKernelGGL((prefill_kernel<D, KIND, G>), dim3(grid), dim3(kPreThreads), 0, s, p,
                      qblocks, (int)tiles);
   return hipGetLastError();

@@ -2,31 +2,46 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Default workload: SWA-only chunked prefill, 8 sequences with lengths uniform
-in [2048, 16384], chunk 2048, 64 query / 8 KV heads, head_dim 128, W = 128,
-ring of W + chunk slots per sequence in 16-token pages placed by a seeded
-random permutation.  One step = the whole chunked prefill of the batch: for
-every chunk, pool alloc (joint capacity check + device table update), KV
-append, SWA attention, out-of-window eviction; then release of the
-sequences.  `value` is prefill tokens per second over the whole step.
+Workloads (all inputs seeded synthetic N(0,1) values rounded to bf16,
+resident in HBM before the timed region starts):
 
-The same run also times a mixed decode batch (256 sequences, contexts
-uniform in [4096, 32768], one Full and one SWA layer, one new token per
-sequence per step with append and eviction) and reports its algorithmic HBM
-GB/s under "decode".
+  swa_chunked_prefill (default)
+      SWA-only chunked prefill: 8 sequences with lengths uniform in
+      [2048, 16384], chunk 2048, 64 query / 8 KV heads, head_dim 128, W = 128,
+      a ring of W + chunk slots per sequence in 16-token pages placed by a
+      seeded random permutation.  One step = the whole chunked prefill of the
+      batch: for every chunk, pool alloc (joint capacity check + device table
+      update), KV append, SWA attention, out-of-window eviction; then release.
+      `value` = prefill tokens/s.  The same run times the mixed decode below
+      and reports it under "decode".
+  mixed_decode
+      256 sequences, contexts uniform in [4096, 32768], one Full layer (paged
+      Full pool, 16-token pages in random order) and one SWA layer (ring of
+      W = 128 slots); one step = alloc one token per sequence, append + attend
+      both layers, evict.  `value` = algorithmic HBM GB/s.
+  hybrid_stack
+      70 attention-only layers (6 SWA then 1 Full, repeated), one 65536-token
+      sequence prefilled in 4096-token chunks, and the same with all 70 layers
+      Full.  `value` = stack tokens/s; the Full-layer kernel is MFMA-bound.
+  long_decode
+      64 sequences, contexts uniform in [131072, 262144], 14 layers (6 SWA then
+      1 Full, twice), SWA ring of W + 256 slots.  `value` = HBM GB/s.
+  swa_single_chunk
+      One SWA layer, one 1024-token sequence (8 query / 2 KV heads, head_dim
+      64) prefilled in one chunk, then 16 decode steps.  `value` = tok/s.
 
-Other workloads (--workload): swa_single_chunk, hybrid_stack, long_decode.
-
-All inputs are seeded synthetic N(0,1) values rounded to bf16, resident in
-HBM before the timed region starts.  The attention kernel's duration is
-measured with HIP events on the stream it is launched on.
+The dominant kernel's duration is measured with HIP events recorded on the
+stream it is launched on; `roofline.achieved` = algorithmic bytes (or flops)
+per launch / that duration.  `roofline.traffic` is the measured HBM bytes
+per launch from rocprofv3 counters (profiles/traffic.json), given only when
+they were taken on the current kernel source, else null.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes as C
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -41,7 +56,30 @@ MFMA_BF16_PEAK_TFS = 2516.6    # 256 CU * 2.4 GHz * 4096 flop/clk (dense)
 PEAKS = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (MFMA_BF16_PEAK_TFS, "TFLOP/s")}
 METRIC = "Hybrid-SWA attn prefill tok/s + decode HBM GB/s (% of MI355X peak)"
 
-KV_TOKEN_BYTES = lambda hkv, d: 2 * hkv * d * 2  # K and V, bf16
+CSRC = os.path.join(ROOT, "hybrid_sliding_window_hswa_amd", "csrc")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def KV_TOKEN_BYTES(hkv, d):
+    return 2 * hkv * d * 2  # K (bf16) and V (fp16) of one token
+
+
+def source_sha(fname):
+    with open(os.path.join(CSRC, fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(key, fname):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current source of the kernel; else None."""
+    try:
+        with open(TRAFFIC) as f:
+            t = json.load(f)["kernels"][key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha(fname):
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def log(*a):
@@ -104,10 +142,12 @@ def _check(cx, rc):
 
 
 class ChunkedPrefill:
-    """Precomputes every chunk step's batch; run() replays the whole
-    chunked prefill of the batch through the C ABI."""
+    """Precomputes every chunk step's batch; run() replays the whole chunked
+    prefill of the batch through every layer via the C ABI.  `pattern` lists
+    the layers ('S' SWA, 'F' Full), each with K/V buffers of its own; all
+    layers see the same synthetic Q/K/V (an attention-only stack)."""
 
-    def __init__(self, cx, lens, chunk, hq, hkv, d, W, seed, kinds=("S",), ring=None):
+    def __init__(self, cx, lens, chunk, hq, hkv, d, W, seed, pattern="S", ring=None):
         torch, H = cx.torch, cx.H
         import synth
         self.cx = cx
@@ -123,7 +163,7 @@ class ChunkedPrefill:
         self.pool = H.hswa_pool_create(W, C_, B, maxp, nfull, free, ringp, device=cx.dev)
         self.view = H.hswa_pool_get_view(self.pool)
         self.layers = []
-        for li, kind in enumerate(kinds):
+        for kind in pattern:
             npages = nfull if kind == "F" else B * C_ // 16
             kc, vc = H.kv_cache_alloc(npages, hkv, d, cx.dev, 0.0)
             self.layers.append((H.FULL if kind == "F" else H.SWA, kc, vc))
@@ -143,15 +183,15 @@ class ChunkedPrefill:
                 break
             n = [min(chunk, lens[b] - done[b]) for b in act]
             rows = [(b, done[b], done[b] + k) for b, k in zip(act, n)]
+            cat = (lambda xs: xs[0]) if len(rows) == 1 else torch.cat
             st = {
                 "ids": _arr(act), "n": _arr(n), "nseq": len(act), "max_n": max(n),
                 "sid": cx.i32(act),
                 "cu": cx.i32(np.concatenate([[0], np.cumsum(n)])),
-                "q": torch.cat([self.q[b][a:e] for b, a, e in rows]),
-                "k": torch.cat([self.k[b][a:e] for b, a, e in rows]),
-                "v": torch.cat([self.v[b][a:e] for b, a, e in rows]),
+                "q": cat([self.q[b][a:e] for b, a, e in rows]),
+                "k": cat([self.k[b][a:e] for b, a, e in rows]),
+                "v": cat([self.v[b][a:e] for b, a, e in rows]),
                 "rows": rows,
-                "halo": [min(W - 1, a) for b, a, e in rows],
             }
             max_rows = max(max_rows, st["q"].shape[0])
             self.steps.append(st)
@@ -191,15 +231,17 @@ class ChunkedPrefill:
         ids, idp = self.all_ids
         _check(cx, lib.hswa_pool_release(h, self.B, idp, cx.sptr))
 
-    def attn_bytes(self, st):
-        """Algorithmic HBM bytes of one attention launch: Q read, O written
-        (fp32), and each needed key's K/V read once (chunk + window halo)."""
+    def attn_bytes(self, st, kind):
+        """Algorithmic HBM bytes of one attention launch: Q read (bf16), O
+        written (fp32), and the K/V of each key the chunk needs read once
+        (SWA: the chunk plus its W-1 halo; Full: the whole prefix)."""
         T = st["q"].shape[0]
         kvb = KV_TOKEN_BYTES(self.hkv, self.d)
-        qb = T * self.hq * self.d * 2
-        ob = T * self.hq * self.d * 4
-        keys = sum((e - a) + h for (b, a, e), h in zip(st["rows"], st["halo"]))
-        return qb + ob + keys * kvb
+        if kind == self.cx.H.FULL:
+            keys = sum(e for b, a, e in st["rows"])
+        else:
+            keys = sum((e - a) + min(self.W - 1, a) for b, a, e in st["rows"])
+        return T * self.hq * self.d * (2 + 4) + keys * kvb
 
     def attn_flops(self, st, kind):
         """4 * d * Hq flops per scored (query, key) pair."""
@@ -367,44 +409,23 @@ def roofline(bound, achieved, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
-def bench_prefill(cx, args):
-    import synth
-    wl = synth.C2
-    lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
-    cp = ChunkedPrefill(cx, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                        wl.window, wl.seed)
-    cx.torch.cuda.synchronize()
-    log(f"prefill: {cp.tokens} tokens in {len(cp.steps)} chunk steps")
-    sec = timed(cx, cp.run, args.steps, args.warmup)
-    # kernel time with events, over a separate pass
-    ev = []
-    for _ in range(max(1, min(args.steps, 5))):
-        cp.run(ev)
-    cx.torch.cuda.synchronize()
-    ktime = sum(e0.elapsed_time(e1) for _, _, e0, e1 in ev) / 1e3
-    kbytes = sum(cp.attn_bytes(st) for _, st, _, _ in ev)
-    kflops = sum(cp.attn_flops(st, kind) for kind, st, _, _ in ev)
-    res = {
-        "tok_s": cp.tokens / sec,
-        "ms_per_step": sec * 1e3,
-        "kernel_avg_us": ktime / len(ev) * 1e6,
-        "kernel_gbs": kbytes / ktime / 1e9,
-        "kernel_tflops": kflops / ktime / 1e12,
-        "launches": len(ev),
-        "lens": lens,
-    }
-    return cp, res
+def kernel_stats(cp, ev, kind):
+    """Average duration, algorithmic GB/s and TFLOP/s of the attention
+    launches of one layer kind, from the events recorded around them."""
+    sel = [(st, e0.elapsed_time(e1) / 1e3) for k, st, e0, e1 in ev if k == kind]
+    if not sel:
+        return None
+    t = sum(x for _, x in sel)
+    return {"avg_us": t / len(sel) * 1e6,
+            "gbs": sum(cp.attn_bytes(st, kind) for st, _ in sel) / t / 1e9,
+            "tflops": sum(cp.attn_flops(st, kind) for st, _ in sel) / t / 1e12,
+            "launches": len(sel)}
 
 
-def bench_decode(cx, args):
-    import synth
-    wl = synth.C3
-    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
-    steps, warm = args.decode_steps, 2
-    dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
-                wl.ring_slots, wl.seed, steps + warm + 8)
-    lens0 = list(dc.lens)
-    torch = cx.torch
+def run_decode(cx, dc, pattern, steps, warm):
+    """Times `steps` decode steps; returns the step's algorithmic GB/s and
+    per-kind call durations from events."""
+    torch, H = cx.torch, cx.H
     for _ in range(warm):
         dc.step()
     torch.cuda.synchronize()
@@ -414,32 +435,214 @@ def bench_decode(cx, args):
         dc.step()
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / steps
-    # bytes of the timed steps (lengths grow by one per step)
+    # bytes of the timed steps (every length grows by one per step)
     tot = 0
     for s in range(steps):
         lens = [x + s + 1 for x in lens_start]
-        tot += dc.layer_bytes(cx.H.FULL, lens) + dc.layer_bytes(cx.H.SWA, lens)
+        for kind in pattern:
+            tot += dc.layer_bytes(H.FULL if kind == "F" else H.SWA, lens)
     step_bytes = tot / steps
     ev = []
-    for _ in range(3):
+    for _ in range(2):
         dc.step(ev)
     torch.cuda.synchronize()
-    full = [(l, e0.elapsed_time(e1) / 1e3) for k, l, e0, e1 in ev if k == cx.H.FULL]
-    swa = [(l, e0.elapsed_time(e1) / 1e3) for k, l, e0, e1 in ev if k == cx.H.SWA]
-    fb = sum(dc.layer_bytes(cx.H.FULL, l) for l, _ in full)
-    ft = sum(t for _, t in full)
-    sb = sum(dc.layer_bytes(cx.H.SWA, l) for l, _ in swa)
-    st_ = sum(t for _, t in swa)
-    res = {
-        "gbs": step_bytes / sec / 1e9,
-        "ms_per_step": sec * 1e3,
-        "bytes_per_step": step_bytes,
-        "full_kernel_us": ft / len(full) * 1e6,
-        "full_gbs": fb / ft / 1e9,
-        "swa_call_us": st_ / len(swa) * 1e6,
-        "swa_gbs": sb / st_ / 1e9,
+    res = {"gbs": step_bytes / sec / 1e9, "ms_per_step": sec * 1e3, "bytes_per_step": step_bytes}
+    for kind, name in ((H.FULL, "full"), (H.SWA, "swa")):
+        sel = [(l, e0.elapsed_time(e1) / 1e3) for k, l, e0, e1 in ev if k == kind]
+        if sel:
+            t = sum(x for _, x in sel)
+            res[name + "_call_us"] = t / len(sel) * 1e6
+            res[name + "_gbs"] = sum(dc.layer_bytes(kind, l) for l, _ in sel) / t / 1e9
+    return res
+
+
+def base_line(args, value, unit, ms, config, rl):
+    return {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": config, "roofline": rl}
+
+
+def copy_calibration(cx):
+    """A plain 1 GiB device-to-device copy, three times: the reference that
+    scales the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of a counter run."""
+    torch = cx.torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=cx.dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+
+
+def wl_swa_chunked_prefill(cx, args):
+    import synth
+    H = cx.H
+    wl = synth.C2
+    lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
+    cp = ChunkedPrefill(cx, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                        wl.window, wl.seed)
+    cx.torch.cuda.synchronize()
+    log(f"prefill: {cp.tokens} tokens in {len(cp.steps)} chunk steps")
+    sec = timed(cx, cp.run, args.steps, args.warmup)
+    ev = []
+    for _ in range(max(1, min(args.steps, 5))):
+        cp.run(ev)
+    cx.torch.cuda.synchronize()
+    ks = kernel_stats(cp, ev, H.SWA)
+    log(f"prefill: {cp.tokens / sec:.4g} tok/s, {sec * 1e3:.3f} ms/step, kernel {ks}")
+    config = {
+        "workload": "swa_chunked_prefill", "num_seqs": wl.num_seqs,
+        "seq_len_range": [wl.len_lo, wl.len_hi], "seq_lens": lens, "chunk": wl.chunk,
+        "window": wl.window, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+        "head_dim": wl.head_dim, "page_size": 16, "ring_slots": wl.window + wl.chunk,
+        "output_dtype": "fp32", "seed": wl.seed,
     }
-    return dc, res
+    rl = roofline("hbm", ks["gbs"], measured_traffic("prefill_swa", "kernels_prefill.hip"))
+    line = base_line(args, round(cp.tokens / sec, 1), "tok/s", sec * 1e3, config, rl)
+    line["kernel"] = {"name": "prefill_kernel<128,SWA>", "avg_us": round(ks["avg_us"], 2),
+                      "launches_timed": ks["launches"], "tflops": round(ks["tflops"], 2),
+                      "mfma_frac": round(ks["tflops"] / MFMA_BF16_PEAK_TFS, 4)}
+    if not args.no_decode:
+        d = wl_mixed_decode(cx, args)
+        line["decode"] = {**d["config"], "value": d["value"], "unit": d["unit"],
+                          "frac": d["step_frac_of_hbm_peak"], "ms_per_step": d["ms_per_step"],
+                          "roofline": d["roofline"], "full_call_us": d["full_call_us"],
+                          "swa_call_us": d["swa_call_us"]}
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(cx, cp, args.cpu_seconds)
+        log(f"cpu baseline: {line['cpu_baseline']}")
+    return line
+
+
+def wl_mixed_decode(cx, args):
+    import synth
+    wl = synth.C3
+    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
+    steps, warm = args.decode_steps, 2
+    dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                wl.ring_slots, wl.seed, steps + warm + 8)
+    r = run_decode(cx, dc, "FS", steps, warm)
+    log(f"decode: {r}")
+    config = {"workload": "mixed_decode", "num_seqs": wl.num_seqs,
+              "ctx_range": [wl.ctx_lo, wl.ctx_hi], "layers": "1 Full + 1 SWA",
+              "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+              "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
+              "seed": wl.seed}
+    rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full", "kernels_decode.hip"))
+    line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
+    line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+    line["full_call_us"] = round(r["full_call_us"], 1)
+    line["swa_call_us"] = round(r["swa_call_us"], 1)
+    return line
+
+
+def wl_hybrid_stack(cx, args):
+    import synth
+    H = cx.H
+    wl = synth.C4
+    res = {}
+    steps = max(1, min(args.steps, 3))
+    for variant, pattern in (("hybrid", wl.pattern), ("all_full", "F" * len(wl.pattern))):
+        cp = ChunkedPrefill(cx, [wl.seq_len], wl.chunk, wl.num_q_heads, wl.num_kv_heads,
+                            wl.head_dim, wl.window, wl.seed, pattern=pattern)
+        cx.torch.cuda.synchronize()
+        n = steps if variant == "hybrid" else 1
+        sec = timed(cx, cp.run, n, min(args.warmup, 1))
+        ev = []
+        cp.run(ev)
+        cx.torch.cuda.synchronize()
+        res[variant] = {"sec": sec, "full": kernel_stats(cp, ev, H.FULL),
+                        "swa": kernel_stats(cp, ev, H.SWA)}
+        log(f"stack {variant}: {wl.seq_len / sec:.4g} tok/s, {sec:.3f} s/step, "
+            f"full {res[variant]['full']}, swa {res[variant]['swa']}")
+        del cp, ev
+        cx.torch.cuda.empty_cache()
+    hy, af = res["hybrid"], res["all_full"]
+    fk = hy["full"]
+    config = {"workload": "hybrid_stack", "layers": len(wl.pattern),
+              "pattern": "6 SWA then 1 Full, x10", "seq_len": wl.seq_len, "chunk": wl.chunk,
+              "window": wl.window, "num_q_heads": wl.num_q_heads,
+              "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "seed": wl.seed}
+    rl = roofline("mfma", fk["tflops"], measured_traffic("prefill_full", "kernels_prefill.hip"))
+    line = base_line(args, round(wl.seq_len / hy["sec"], 1), "tok/s", hy["sec"] * 1e3, config,
+                     rl)
+    line["steps"] = steps
+    line["kernel"] = {"name": "prefill_kernel<128,FULL>", "avg_us": round(fk["avg_us"], 2),
+                      "launches_timed": fk["launches"], "gbs": round(fk["gbs"], 1)}
+    line["swa_kernel"] = {"avg_us": round(hy["swa"]["avg_us"], 2),
+                          "gbs": round(hy["swa"]["gbs"], 1)}
+    line["all_full"] = {"value": round(wl.seq_len / af["sec"], 1), "unit": "tok/s",
+                        "ms_per_step": round(af["sec"] * 1e3, 3),
+                        "full_kernel_tflops": round(af["full"]["tflops"], 1)}
+    line["time_ratio_hybrid_over_all_full"] = round(hy["sec"] / af["sec"], 5)
+    return line
+
+
+def wl_long_decode(cx, args):
+    import synth
+    wl = synth.C5
+    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
+    steps, warm = max(2, min(args.decode_steps, 10)), 2
+    t0 = time.perf_counter()
+    dc = Decode(cx, ctxs, wl.pattern, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                wl.ring_slots, wl.seed, steps + warm + 4)
+    log(f"long decode: setup {time.perf_counter() - t0:.1f} s")
+    r = run_decode(cx, dc, wl.pattern, steps, warm)
+    log(f"long decode: {r}")
+    config = {"workload": "long_decode", "num_seqs": wl.num_seqs,
+              "ctx_range": [wl.ctx_lo, wl.ctx_hi], "layers": len(wl.pattern),
+              "pattern": "6 SWA then 1 Full, x2", "ring_slots": wl.ring_slots,
+              "window": wl.window, "num_q_heads": wl.num_q_heads,
+              "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "seed": wl.seed}
+    rl = roofline("hbm", r["full_gbs"], None)
+    line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
+    line["steps"] = steps
+    line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+    line["full_call_us"] = round(r["full_call_us"], 1)
+    line["swa_call_us"] = round(r["swa_call_us"], 1)
+    return line
+
+
+def wl_swa_single_chunk(cx, args):
+    import synth
+    H = cx.H
+    wl = synth.C1
+    L = wl.prefill_len
+    cp = ChunkedPrefill(cx, [L], L, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                        wl.seed)
+    sec = timed(cx, cp.run, args.steps, args.warmup)
+    ev = []
+    cp.run(ev)
+    cx.torch.cuda.synchronize()
+    ks = kernel_stats(cp, ev, H.SWA)
+    config = {"workload": "swa_single_chunk", "seq_len": L, "decode_steps": wl.decode_steps,
+              "window": wl.window, "num_q_heads": wl.num_q_heads,
+              "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "seed": wl.seed}
+    line = base_line(args, round(L / sec, 1), "tok/s", sec * 1e3, config,
+                     roofline("hbm", ks["gbs"], None))
+    line["kernel"] = {"name": "prefill_kernel<64,SWA>", "avg_us": round(ks["avg_us"], 2)}
+    dc = Decode(cx, [L], "S", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                wl.window + 16, wl.seed, wl.decode_steps + 8)
+    r = run_decode(cx, dc, "S", wl.decode_steps, 2)
+    line["decode_step_us"] = round(r["ms_per_step"] * 1e3, 2)
+    return line
+
+
+WORKLOADS = {
+    "swa_chunked_prefill": wl_swa_chunked_prefill,
+    "mixed_decode": wl_mixed_decode,
+    "hybrid_stack": wl_hybrid_stack,
+    "long_decode": wl_long_decode,
+    "swa_single_chunk": wl_swa_single_chunk,
+}
 
 
 def main():
@@ -447,68 +650,23 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="swa_chunked_prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy first, as the reference for the "
+                         "HBM byte counters of a rocprofv3 --pmc run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     cx = Ctx()
-    import synth
-    cp, pre = bench_prefill(cx, args)
-    log(f"prefill: {pre}")
-    dec = None
-    if not args.no_decode:
-        dc, dec = bench_decode(cx, args)
-        log(f"decode: {dec}")
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline_prefill(cx, cp, args.cpu_seconds)
-        log(f"cpu baseline: {cpu}")
-    wl = synth.C2
-    line = {
-        "metric": METRIC,
-        "value": round(pre["tok_s"], 1),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(pre["ms_per_step"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "swa_chunked_prefill",
-            "num_seqs": wl.num_seqs, "seq_len_range": [wl.len_lo, wl.len_hi],
-            "seq_lens": pre["lens"], "chunk": wl.chunk, "window": wl.window,
-            "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
-            "head_dim": wl.head_dim, "page_size": 16, "ring_slots": wl.window + wl.chunk,
-            "output_dtype": "fp32", "seed": wl.seed,
-        },
-        "roofline": roofline("hbm", pre["kernel_gbs"]),
-        "kernel": {"name": "prefill_kernel<128,SWA,8>", "avg_us": round(pre["kernel_avg_us"], 2),
-                   "launches_timed": pre["launches"],
-                   "tflops": round(pre["kernel_tflops"], 2),
-                   "mfma_frac": round(pre["kernel_tflops"] / MFMA_BF16_PEAK_TFS, 4)},
-        "cpu_baseline": cpu,
-    }
-    if dec is not None:
-        w3 = synth.C3
-        line["decode"] = {
-            "workload": "mixed_decode", "num_seqs": w3.num_seqs,
-            "ctx_range": [w3.ctx_lo, w3.ctx_hi], "layers": "1 Full + 1 SWA",
-            "value": round(dec["gbs"], 1), "unit": "GB/s",
-            "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
-            "ms_per_step": round(dec["ms_per_step"], 4),
-            "roofline": roofline("hbm", dec["full_gbs"]),
-            "full_kernel_us": round(dec["full_kernel_us"], 1),
-            "swa_call_us": round(dec["swa_call_us"], 1),
-        }
+    if args.copy_calibration:
+        copy_calibration(cx)
+    line = WORKLOADS[args.workload](cx, args)
     print(json.dumps(line), flush=True)
 
 

@@ -526,7 +526,7 @@ def wl_mixed_decode(cx, args):
     import synth
     wl = synth.C3
     ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
-    steps, warm = args.decode_steps, 2
+    steps, warm = args.decode_steps, 4
     dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
                 wl.ring_slots, wl.seed, steps + warm + 8)
     r = run_decode(cx, dc, "FS", steps, warm)
@@ -590,7 +590,7 @@ def wl_long_decode(cx, args):
     import synth
     wl = synth.C5
     ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
-    steps, warm = max(2, min(args.decode_steps, 10)), 2
+    steps, warm = max(2, args.decode_steps // 2), 2
     t0 = time.perf_counter()
     dc = Decode(cx, ctxs, wl.pattern, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
                 wl.ring_slots, wl.seed, steps + warm + 4)
@@ -651,7 +651,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="swa_chunked_prefill", choices=sorted(WORKLOADS))
-    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")

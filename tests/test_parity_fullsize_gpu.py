@@ -1,0 +1,229 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration that
+bench.py times (KV append as its own call, then attention; decode with the
+new token's append inside the call and the same split plan).
+
+The oracle cannot evaluate every output at these sizes, so each test checks
+sampled query rows (all heads) against it: chunk edges, the rows where the
+window halo ends, the longest and shortest sequences, and seeded random
+rows.  Pool results are checked in full: the slots handed out and the
+eviction sets against the oracle's pool simulator (prefill) or against the
+slot formulas applied to the slots the pool returned (decode), and every
+valid-window length the kernels report.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_sliding_window_hswa_amd as H
+import synth
+from oracle import attention as OA
+from oracle.pool import PoolSim
+
+from harness import TOL, Setup, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(shape, seed, layer, b, role):
+    return synth.bf16_normal(shape, seed, layer, b, role, device=dev())
+
+
+class _Host:
+    """fp64 copies of one sequence's K/V rows from position `lo` on (moved
+    from the device once)."""
+
+    def __init__(self, k, v, lo=0):
+        self.k, self.v, self.lo = synth.to_f64(k), synth.to_f64(v), lo
+
+    def attend(self, q, positions, kind, W):
+        # rows before `lo` are outside every window asked for (SWA only)
+        assert self.lo == 0 or all(p - W + 1 >= self.lo for p in positions)
+        return OA.attend(q, [p - self.lo for p in positions], self.k, self.v, kind, W)
+
+
+def _sample_chunk_rows(a, e, W, rng, k_random):
+    """Row positions in [a, e) to check for a chunk: its edges, the end of
+    the window halo and seeded random rows."""
+    cand = {a, a + 1, e - 1, e - 2, a + W - 2, a + W - 1, a + W}
+    cand |= set(int(x) for x in rng.integers(a, e, size=k_random))
+    return sorted(p for p in cand if a <= p < e)
+
+
+def _prefill_fullsize(kind, lens, chunk, hq, hkv, d, W, C, seed, rows_per_chunk, layer=0):
+    B = len(lens)
+    maxp = max(lens) // 16 + 2
+    nfull = B * maxp + 16
+    su = Setup(kind, W, C, B, maxp, nfull, hkv, d, seed)
+    sim = PoolSim(W, C, B, maxp, nfull, synth.permutation(nfull, seed, 1),
+                  synth.permutation(B * C // 16, seed, 2))
+    Q = [_draw((L, hq, d), seed, layer, b, synth.ROLE_Q) for b, L in enumerate(lens)]
+    K = [_draw((L, hkv, d), seed, layer, b, synth.ROLE_K) for b, L in enumerate(lens)]
+    V = [_draw((L, hkv, d), seed, layer, b, synth.ROLE_V) for b, L in enumerate(lens)]
+    host = [_Host(k, v) for k, v in zip(K, V)]
+    rng = np.random.default_rng(seed + 17)
+    done = [0] * B
+    worst, checked = 0.0, 0
+    while True:
+        act = [b for b in range(B) if done[b] < lens[b]]
+        if not act:
+            break
+        n = [min(chunk, lens[b] - done[b]) for b in act]
+        rows = [(b, done[b], done[b] + k) for b, k in zip(act, n)]
+        full, swa = H.hswa_pool_alloc(su.pool, act, n)
+        efull, eswa = sim.alloc(act, n)
+        assert np.array_equal(full, efull) and np.array_equal(swa, eswa)
+        q = torch.cat([Q[b][a:e] for b, a, e in rows])
+        kn = torch.cat([K[b][a:e] for b, a, e in rows])
+        vn = torch.cat([V[b][a:e] for b, a, e in rows])
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(n)]), dtype=torch.int32, device=dev())
+        sid = torch.tensor(act, dtype=torch.int32, device=dev())
+        H.hswa_append_kv(kind, kn, vn, sid, su.view, su.kc, su.vc, cu, max(n))
+        out = torch.full((q.shape[0], hq, d), float("nan"), dtype=torch.float32, device=dev())
+        vl = torch.full((q.shape[0],), -7, dtype=torch.int32, device=dev())
+        H.hswa_prefill_chunk(kind, W, q, None, None, sid, cu, max(n), su.view, su.kc, su.vc,
+                             out, vl)
+        ev, cnt = H.hswa_pool_evict(su.pool, act)
+        eev, ecnt = sim.evict(act)
+        assert list(cnt) == list(ecnt) and np.array_equal(ev, eev)
+        # every valid length, then the sampled rows
+        want_vl = np.concatenate([[OA.valid_length(p, kind, W) for p in range(a, e)]
+                                  for b, a, e in rows])
+        assert np.array_equal(vl.cpu().numpy(), want_vl)
+        off = np.concatenate([[0], np.cumsum(n)])
+        for j, (b, a, e) in enumerate(rows):
+            pos = _sample_chunk_rows(a, e, W, rng, rows_per_chunk)
+            idx = torch.tensor([off[j] + p - a for p in pos], dtype=torch.int64, device=dev())
+            got = out.index_select(0, idx).cpu().double().numpy()
+            exp = host[b].attend(synth.to_f64(Q[b][pos]), pos, kind, W)
+            assert np.all(np.isfinite(got)), f"non-finite output, sequence {b} chunk at {a}"
+            err = float(np.max(np.abs(got - exp)))
+            assert err < TOL, f"sequence {b} chunk at {a}: max-abs error {err:.3e}"
+            worst, checked = max(worst, err), checked + len(pos)
+        # out-of-window ring slots become NaN: a read of them would show
+        for (b, a, e), c in zip(rows, cnt):
+            if c > 0:
+                first = e - W + 1 - int(c)
+                su.poison_ring_positions(b, list(range(first, first + int(c))))
+        for b, k in zip(act, n):
+            done[b] += k
+    H.hswa_pool_release(su.pool, list(range(B)))
+    return worst, checked
+
+
+def test_swa_chunked_prefill_fullsize(gpu):
+    """8 sequences of 2048..16384 tokens, chunk 2048, Hq 64 / Hkv 8, d 128,
+    W 128, ring of W + chunk slots."""
+    wl = synth.C2
+    lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
+    worst, n = _prefill_fullsize(H.SWA, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads,
+                                 wl.head_dim, wl.window, wl.window + wl.chunk, wl.seed, 12)
+    print(f"C2 full size: {n} rows checked, worst max-abs {worst:.3e}")
+
+
+@pytest.mark.parametrize("kind", [H.FULL, H.SWA])
+def test_hybrid_stack_layer_fullsize(gpu, kind):
+    """One Full and one SWA layer of the 70-layer stack: a 65536-token
+    sequence in 4096-token chunks (ring of W + 4096 slots)."""
+    wl = synth.C4
+    layer = 6 if kind == H.FULL else 0
+    worst, n = _prefill_fullsize(kind, [wl.seq_len], wl.chunk, wl.num_q_heads, wl.num_kv_heads,
+                                 wl.head_dim, wl.window, wl.window + wl.chunk, wl.seed, 3,
+                                 layer=layer)
+    print(f"C4 layer kind {kind}: {n} rows checked, worst max-abs {worst:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# Decode at full size: contexts restored directly into the pools (every
+# position in the Full layer, the last W - 1 in the SWA ring), then decode
+# steps with alloc, append + attention per layer, eviction.
+
+
+def _decode_fullsize(ctxs, hq, hkv, d, W, C, seed, steps, sampled, bench_steps_total):
+    B = len(ctxs)
+    maxlen = max(ctxs) + bench_steps_total + 1  # bench.py's max_seq_len: same split plan
+    maxp = maxlen // 16 + 2
+    nfull = int(sum(c // 16 + 2 for c in ctxs) * 1.1) + B * (bench_steps_total // 16 + 2) + 64
+    su = Setup(H.FULL, W, C, B, maxp, nfull, hkv, d, seed)
+    skc, svc = H.kv_cache_alloc(B * C // 16, hkv, d, dev(), float("nan"))
+    layers = ((H.FULL, su.kc, su.vc), (H.SWA, skc, svc))
+    ids = list(range(B))
+    sid = torch.tensor(ids, dtype=torch.int32, device=dev())
+    full_slots, _ = H.hswa_pool_import(su.pool, ids, ctxs)
+    starts = np.concatenate([[0], np.cumsum(ctxs)])
+    ctx_slots = [full_slots[starts[b]:starts[b + 1]] for b in ids]
+    # per layer: the stored context (every position for the Full layer, the
+    # last W - 1 for the SWA ring) plus the rows of the decode steps
+    new_k, new_v, step_q, host = {}, {}, {}, {}
+    for li, (kind, kc, vc) in enumerate(layers):
+        for b, c in enumerate(ctxs):
+            lo = 0 if kind == H.FULL else c - min(c, W - 1)
+            k = _draw((c + steps - lo, hkv, d), seed, li, b, synth.ROLE_K)
+            v = _draw((c + steps - lo, hkv, d), seed, li, b, synth.ROLE_V)
+            n = c - lo
+            one = torch.tensor([b], dtype=torch.int32, device=dev())
+            cu = torch.tensor([0, n], dtype=torch.int32, device=dev())
+            H.hswa_append_kv(kind, k[:n], v[:n], one, su.view, kc, vc, cu, n)
+            new_k[li, b], new_v[li, b] = k[n:].clone(), v[n:].clone()
+            if b in sampled:
+                host[li, b] = _Host(k, v, lo)
+            del k, v
+        step_q[li] = _draw((steps, B, hq, d), seed, li, 999, synth.ROLE_Q)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for t in range(steps):
+        H.hswa_pool_alloc(su.pool, ids, [1] * B)
+        pos = [c + t for c in ctxs]
+        for li, (kind, kc, vc) in enumerate(layers):
+            q = step_q[li][t]
+            kn = torch.stack([new_k[li, b][t] for b in ids])
+            vn = torch.stack([new_v[li, b][t] for b in ids])
+            out = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device=dev())
+            vl = torch.full((B,), -1, dtype=torch.int32, device=dev())
+            nb = H.hswa_decode_workspace_bytes(kind, W, B, hq, hkv, d, maxlen)
+            ws = torch.empty(max(nb // 4, 1), dtype=torch.float32, device=dev())
+            H.hswa_decode(kind, W, q, kn, vn, sid, maxlen, su.view, kc, vc, out, ws, vl)
+            assert vl.cpu().tolist() == [OA.valid_length(p, kind, W) for p in pos]
+            got = out.cpu().double().numpy()
+            qh = synth.to_f64(q)
+            for b in sampled:
+                exp = host[li, b].attend(qh[b:b + 1], [pos[b]], kind, W)[0]
+                assert np.all(np.isfinite(got[b]))
+                err = float(np.max(np.abs(got[b] - exp)))
+                worst = max(worst, err)
+                assert err < TOL, f"step {t} kind {kind} sequence {b}: max-abs {err:.3e}"
+        ev, cnt = H.hswa_pool_evict(su.pool, ids)
+        # one eviction per sequence per step once the window is full: the
+        # position that just left it, at the Full slot the import gave it
+        want_cnt = [1 if p + 1 >= W else 0 for p in pos]
+        assert list(cnt) == want_cnt
+        want_ev = [int(ctx_slots[b][pos[b] + 1 - W]) for b in ids if want_cnt[b]]
+        assert [int(x) for x in ev] == want_ev
+    return worst
+
+
+def test_mixed_decode_fullsize(gpu):
+    """256 sequences with 4096..32768 tokens of context, one Full and one
+    SWA layer (ring of W slots); 3 steps; 16 sequences checked in full,
+    including the shortest and the longest context."""
+    wl = synth.C3
+    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
+    rng = np.random.default_rng(wl.seed + 5)
+    sampled = {int(np.argmin(ctxs)), int(np.argmax(ctxs))}
+    sampled |= set(int(x) for x in rng.choice(len(ctxs), size=14, replace=False))
+    worst = _decode_fullsize(ctxs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                             wl.ring_slots, wl.seed, 3, sorted(sampled), 32 + 4 + 8)
+    print(f"C3 full size: worst max-abs {worst:.3e}")
+
+
+def test_long_decode_fullsize(gpu):
+    """64 sequences with 131072..262144 tokens of context, one Full and one
+    SWA layer of the 14-layer stack (ring of W + 256 slots); 2 steps; the
+    shortest, the longest and two seeded sequences checked in full."""
+    wl = synth.C5
+    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
+    rng = np.random.default_rng(wl.seed + 5)
+    sampled = {int(np.argmin(ctxs)), int(np.argmax(ctxs))}
+    sampled |= set(int(x) for x in rng.choice(len(ctxs), size=2, replace=False))
+    worst = _decode_fullsize(ctxs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                             wl.ring_slots, wl.seed, 2, sorted(sampled), 16 + 2 + 4)
+    print(f"C5 full size: worst max-abs {worst:.3e}")

@@ -43,6 +43,13 @@ __device__ __forceinline__ float xor_lane(float v, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Waits until every vector memory load of the wave has returned (gfx9
+// s_waitcnt encoding: vmcnt = 0, expcnt and lgkmcnt left at their maxima).
+// Used once after loads whose registers stay live across a loop, so the
+// compiler's wait insertion need not assume they are still in flight inside
+// the loop.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Physical page holding the 16-aligned key tile that starts at `pos` for
 // sequence `sid`: Full layers read the Full page table, SWA layers the ring
 // page table (position taken modulo the ring size).
@@ -53,6 +60,26 @@ __device__ __forceinline__ int32_t page_of(const int32_t* __restrict__ fpt,
   if (KIND == 0) return fpt[(int64_t)sid * max_pages + pos / kPage];
   int32_t r = pos % ring;
   return rpt[(int64_t)sid * (ring / kPage) + r / kPage];
+}
+
+// The same lookup for a wave-uniform (sid, pos), as a scalar load: the
+// entry arrives in a scalar register and only the scalar-memory counter is
+// waited on, so vector loads already in flight (a prefetch of K/V) are not
+// waited for.  A read through the scalar cache; the pool tables hold fewer
+// than 2^31 entries (pool creation checks it).
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* base, int32_t idx) {
+  const int32_t* ptr = base + __builtin_amdgcn_readfirstlane(idx);
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+template <int KIND>
+__device__ __forceinline__ int32_t page_of_uniform(const int32_t* __restrict__ fpt,
+                                                   const int32_t* __restrict__ rpt, int32_t sid,
+                                                   int32_t pos, int32_t max_pages,
+                                                   int32_t ring) {
+  return KIND == 0 ? scalar_load_i32(fpt, sid * max_pages + pos / kPage)
+                   : scalar_load_i32(rpt, sid * (ring / kPage) + (pos % ring) / kPage);
 }
 
 }  // namespace dev

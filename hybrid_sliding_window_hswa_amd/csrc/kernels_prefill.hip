@@ -130,122 +130,131 @@ prefill_kernel(AttnParams p, int qblocks,
   // bytes for K (token-major) and for V (dim-major), so thread t copies the
   // 16-byte chunk(s) at t*8 (+ j*kPreThreads*8) of each of the step's two
   // page blocks.  For K the chunk is row (t*8)/D, columns (t*8)%D; for V it
-  // is dim (t*8)/16, keys 8*(t&1) .. +8.
+  // is dim (t*8)/16, keys 8*(t&1) .. +8.  Loads are issued one step ahead
+  // and unconditionally (a tile past the range reads page 0, which every
+  // pool has); masking and the LDS write happen after the step's math, when
+  // the data has arrived anyway.  Page ids come by scalar loads, so waiting
+  // for them never waits for the K/V loads in flight.
   constexpr int EPB = kPage * D;                    // elements per page block
   constexpr int NCH = EPB / 8;                      // 16-byte chunks per block
   constexpr int CPT = (NCH + kPreThreads - 1) / kPreThreads;
   u32x4 kreg[2][CPT], vreg[2][CPT];
   auto stage_load = [&](int kp0) {
-    // wave-uniform: the two page blocks of this step and whether every key
-    // in them lies inside the workgroup's key range
+    // both page ids first: their wait then covers no K/V load
+    int32_t pgs[2];
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int tile = kp0 + 16 * t2;
+      pgs[t2] = tile <= wg_khi ? page_of_uniform<KIND>(p.t.fpt, p.t.rpt, sid, tile,
+                                                       p.t.max_pages, p.t.ring_slots)
+                               : 0;
+    }
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const uint16_t* kb = p.k_cache + ((int64_t)pgs[t2] * hkv + kvh) * head_stride;
+      const uint16_t* vb = p.v_cache + ((int64_t)pgs[t2] * hkv + kvh) * head_stride;
+      for (int j = 0; j < CPT; ++j) {
+        const int e = (tid + j * kPreThreads) * 8;  // element offset in the block
+        if (NCH % kPreThreads != 0 && e >= EPB) break;
+        kreg[t2][j] = *(const u32x4*)(kb + e);
+        vreg[t2][j] = *(const u32x4*)(vb + e);
+      }
+    }
+  };
+  auto stage_store = [&](int buf, int kp0) {
+    // wave-uniform: whether every key of the step's two page blocks lies
+    // inside the workgroup's key range
     const bool inner = kp0 >= wg_klo && kp0 + 31 <= wg_khi;
     for (int t2 = 0; t2 < 2; ++t2) {
       const int tile = kp0 + 16 * t2;
-      int32_t pg = -1;
-      if (tile <= wg_khi)
-        pg = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile, p.t.max_pages, p.t.ring_slots);
-      pg = __builtin_amdgcn_readfirstlane(pg);
-      const uint16_t* kb = p.k_cache + ((int64_t)pg * hkv + kvh) * head_stride;
-      const uint16_t* vb = p.v_cache + ((int64_t)pg * hkv + kvh) * head_stride;
       for (int j = 0; j < CPT; ++j) {
-        const int e = (tid + j * kPreThreads) * 8;  // element offset in the block
-        if (e >= EPB) break;
-        if (pg < 0) {
-          kreg[t2][j] = u32x4{0, 0, 0, 0};
-          vreg[t2][j] = u32x4{0, 0, 0, 0};
-          continue;
-        }
-        kreg[t2][j] = *(const u32x4*)(kb + e);
-        vreg[t2][j] = *(const u32x4*)(vb + e);
+        const int e = (tid + j * kPreThreads) * 8;
+        if (NCH % kPreThreads != 0 && e >= EPB) break;
+        u32x4 kv = kreg[t2][j], vv = vreg[t2][j];
         if (!inner) {
           // keys outside [wg_klo, wg_khi] may hold evicted or unwritten data
           const int kk = tile + e / D;
-          if (kk < wg_klo || kk > wg_khi) kreg[t2][j] = u32x4{0, 0, 0, 0};
+          if (kk < wg_klo || kk > wg_khi) kv = u32x4{0, 0, 0, 0};
           const int k8 = tile + (e % 16);
           for (int x = 0; x < 8; ++x) {
             const int kp = k8 + x;
-            if (kp < wg_klo || kp > wg_khi)
-              vreg[t2][j][x >> 1] &= (x & 1) ? 0x0000ffffu : 0xffff0000u;
+            if (kp < wg_klo || kp > wg_khi) vv[x >> 1] &= (x & 1) ? 0x0000ffffu : 0xffff0000u;
           }
         }
-      }
-    }
-  };
-  auto stage_store = [&](int buf) {
-    for (int t2 = 0; t2 < 2; ++t2)
-      for (int j = 0; j < CPT; ++j) {
-        const int e = (tid + j * kPreThreads) * 8;
-        if (e >= EPB) break;
         // key row kr of the page goes to LDS row swap23(kr) of the page half
         const int kr = e / D;
         const int rho = ((kr >> 2) & 1) * 8 + ((kr >> 3) & 1) * 4 + (kr & 3);
-        *(u32x4*)(&kl[buf][(16 * t2 + rho) * KROW + e % D]) = kreg[t2][j];
-        *(u32x4*)(&vl[buf][t2 * EPB + e]) = vreg[t2][j];
+        *(u32x4*)(&kl[buf][(16 * t2 + rho) * KROW + e % D]) = kv;
+        *(u32x4*)(&vl[buf][t2 * EPB + e]) = vv;
       }
+    }
+  };
+
+  // One 32-key step of scores, softmax and PV from LDS buffer `buf`.
+  auto compute = [&](int buf, int kp0) {
+    // does this wave have any unmasked key in the step?
+    if (!(wave_on && kp0 <= w_pos_hi && kp0 + 31 >= w_klo)) return;
+    f32x16 sacc;
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    const uint16_t* krow = &kl[buf][qr * KROW + 8 * h2];
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * c));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc, 0, 0, 0);
+    }
+    // every key of the step valid for every row of the wave?
+    const bool interior = kp0 + 31 <= w_pos_lo && (KIND == 0 || kp0 > w_pos_hi - W);
+    float mx = -INFINITY;
+    if (interior) {
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    } else {
+      // lane value r = 4j + i is key kp0 + 16(j/2) + 8*h2 + 4(j%2) + i
+      const int rel = kp0 + 8 * h2 - my_pos;  // key - query of value 0
+      for (int r = 0; r < 16; ++r) {
+        const int dk = rel + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
+        const bool ok = dk <= 0 && (KIND == 0 || dk > -W);
+        sacc[r] = ok ? sacc[r] : -INFINITY;
+        mx = fmaxf(mx, sacc[r]);
+      }
+    }
+    // the running max moves only when some score exceeds it by 2^kLazy;
+    // then the two lanes of a row agree on the new one through one exchange
+    if (__builtin_amdgcn_ballot_w64(mx * sl2 > m + kLazy) != 0) {  // wave-uniform
+      const float m_new = fmaxf(m, fmaxf(mx, xor_lane(mx, 32)) * sl2);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+      for (int mb = 0; mb < NM; ++mb) o[mb] *= alpha;
+      lsum *= alpha;
+      m = m_new;
+    }
+    const float mo = m == -INFINITY ? 0.f : m;
+    float ps = 0.f;
+    f16x8 pf0, pf1;
+    for (int r = 0; r < 8; ++r) {
+      const float e0 = fast_exp2(__builtin_fmaf(sacc[r], sl2, -mo));
+      const float e1 = fast_exp2(__builtin_fmaf(sacc[r + 8], sl2, -mo));
+      ps += e0 + e1;
+      pf0[r] = (_Float16)e0;
+      pf1[r] = (_Float16)e1;
+    }
+    lsum += ps;
+    // V fragment: dim 32mb + qr, keys 8*h2 .. +8 of each page
+    const uint16_t* v0 = &vl[buf][qr * 16 + 8 * h2];
+    for (int mb = 0; mb < NM; ++mb) {
+      f16x8 va = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + 512 * mb));
+      f16x8 vb = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + EPB + 512 * mb));
+      o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf0, o[mb], 0, 0, 0);
+      o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb, pf1, o[mb], 0, 0, 0);
+    }
   };
 
   stage_load(kstart);
-  stage_store(0);
+  stage_store(0, kstart);
+  wait_vm_all();  // Q fragments have arrived
   __syncthreads();
-
+  // every iteration loads and stores (the last one a masked tile past the
+  // range), so the loads never merge with other values in registers
   for (int s = 0; s < nsteps; ++s) {
     const int kp0 = kstart + 32 * s;
-    const int buf = s & 1;
-    if (s + 1 < nsteps) stage_load(kp0 + 32);
-    // does this wave have any unmasked key in the step?
-    if (wave_on && kp0 <= w_pos_hi && kp0 + 31 >= w_klo) {
-      f32x16 sacc;
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-      const uint16_t* krow = &kl[buf][qr * KROW + 8 * h2];
-      for (int c = 0; c < NC; ++c) {
-        bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * c));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc, 0, 0, 0);
-      }
-      // every key of the step valid for every row of the wave?
-      const bool interior = kp0 + 31 <= w_pos_lo && (KIND == 0 || kp0 > w_pos_hi - W);
-      float mx = -INFINITY;
-      if (interior) {
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-      } else {
-        // lane value r = 4j + i is key kp0 + 16(j/2) + 8*h2 + 4(j%2) + i
-        const int rel = kp0 + 8 * h2 - my_pos;  // key - query of value 0
-        for (int r = 0; r < 16; ++r) {
-          const int dk = rel + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
-          const bool ok = dk <= 0 && (KIND == 0 || dk > -W);
-          sacc[r] = ok ? sacc[r] : -INFINITY;
-          mx = fmaxf(mx, sacc[r]);
-        }
-      }
-      // the running max moves only when some score exceeds it by 2^kLazy;
-      // then the two lanes of a row agree on the new one through one exchange
-      if (__builtin_amdgcn_ballot_w64(mx * sl2 > m + kLazy) != 0) {  // wave-uniform
-        const float m_new = fmaxf(m, fmaxf(mx, xor_lane(mx, 32)) * sl2);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
-        for (int mb = 0; mb < NM; ++mb) o[mb] *= alpha;
-        lsum *= alpha;
-        m = m_new;
-      }
-      const float mo = m == -INFINITY ? 0.f : m;
-      float ps = 0.f;
-      f16x8 pf0, pf1;
-      for (int r = 0; r < 8; ++r) {
-        const float e0 = fast_exp2(__builtin_fmaf(sacc[r], sl2, -mo));
-        const float e1 = fast_exp2(__builtin_fmaf(sacc[r + 8], sl2, -mo));
-        ps += e0 + e1;
-        pf0[r] = (_Float16)e0;
-        pf1[r] = (_Float16)e1;
-      }
-      lsum += ps;
-      // V fragment: dim 32mb + qr, keys 8*h2 .. +8 of each page
-      const uint16_t* v0 = &vl[buf][qr * 16 + 8 * h2];
-      for (int mb = 0; mb < NM; ++mb) {
-        f16x8 va = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + 512 * mb));
-        f16x8 vb = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + EPB + 512 * mb));
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf0, o[mb], 0, 0, 0);
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb, pf1, o[mb], 0, 0, 0);
-      }
-    }
-    if (s + 1 < nsteps) stage_store(buf ^ 1);
+    stage_load(kp0 + 32);
+    compute(s & 1, kp0);
+    stage_store((s & 1) ^ 1, kp0 + 32);
     __syncthreads();
   }
 

@@ -314,8 +314,9 @@ int hswa_pool_create(const hswa_pool_desc* d, hswa_pool** out) {
   }
   if ((int64_t)d->num_full_pages * kPage > INT32_MAX ||
       (int64_t)d->max_seqs * (d->ring_slots / kPage) * kPage > INT32_MAX ||
-      (int64_t)d->max_pages_per_seq * kPage > INT32_MAX) {
-    hswa::set_error("pool too large for int32 slot ids");
+      (int64_t)d->max_pages_per_seq * kPage > INT32_MAX ||
+      (int64_t)d->max_seqs * d->max_pages_per_seq > INT32_MAX) {
+    hswa::set_error("pool too large for int32 slot ids and table indices");
     return HSWA_E_INVAL;
   }
   if (!d->full_free_order || !d->ring_pages) {

@@ -8,22 +8,29 @@
 //
 // Design (gfx950):
 //  - Workgroup = 4 wavefronts for one (sequence, query block, KV head,
-//    head group); the grid runs head groups fastest (HBM channel spread).  Wave w owns 32 query positions of one query head, so up
+//    head group).  Wave w owns 32 query positions of one query head, so up
 //    to four heads sharing a KV head (and, for G < 4, several 32-position
 //    groups) share every K/V tile the workgroup stages.  Small workgroups
 //    let three of them share a CU, so one's loads overlap another's math.
+//    The grid runs KV heads fastest: workgroups resident at the same time
+//    then cover all KV heads' slices of the pages (all HBM channels).
 //  - Scores use the 32x32x16 bf16 MFMA as S^T[key][row] = K . Q^T, with the
 //    Q^T fragments held in registers for the whole key loop and K read from
 //    LDS.  The output uses the 32x32x16 fp16 MFMA as O^T[d][row] = V^T . P^T
-//    on the fp16 V pages.  K rows are staged with bits 2 and 3 of the
+//    on the fp16 V pages.  K rows are placed in LDS with bits 2 and 3 of the
 //    in-page key index swapped, which makes the eight scores a lane holds per
 //    page eight consecutive keys: each lane's probabilities are then exactly
 //    the B operand of the PV product and its V fragment is 16 contiguous
 //    bytes of the page, so P never goes through LDS and V is copied verbatim.
-//  - K/V move through LDS in 32-key steps (two 16-token pages), double
-//    buffered: global loads of step s+1 are in flight while step s computes.
-//  - Keys outside the workgroup's range are staged as zeros (their slots can
-//    hold evicted or unwritten data); per-row masks select -inf scores.
+//  - K/V move global -> LDS by DMA (global_load_lds_dwordx4: each lane's 16
+//    bytes land at the LDS base + 16 * lane), in 32-key steps (two 16-token
+//    pages) through three LDS buffers: the loads of steps s+1 and s+2 are in
+//    flight while step s computes, and no registers hold staged data.  The
+//    K rows' 16-byte chunks are XOR-swizzled by row so that the QK operand
+//    reads are free of bank conflicts without padding.
+//  - Keys outside the workgroup's range (their slots can hold evicted or
+//    unwritten data) get -inf scores through the per-row masks, and their V
+//    is zeroed in LDS before use so that 0 * V stays 0.
 //  - Online softmax in fp32, log2 domain, with lazy rescaling: the two lanes
 //    of a row exchange their maxima only when the running max must move;
 //    output fp32.
@@ -40,6 +47,7 @@ namespace {
 
 constexpr int kPreWaves = 4;
 constexpr int kPreThreads = kPreWaves * 64;
+constexpr int kBufs = 3;  // LDS buffers: the step computed plus two in flight
 // Lazy softmax rescaling: the running max is only moved when a new score
 // exceeds it by more than 2^kLazy, so unnormalised weights stay <= 2^kLazy
 // (exact in fp16 with the same relative precision) and the O rescale runs
@@ -47,33 +55,47 @@ constexpr int kPreThreads = kPreWaves * 64;
 // of where the max was taken.
 constexpr float kLazy = 8.0f;
 
+// 16 bytes per lane from sbase + voff (the lane's byte offset) into LDS at
+// lds_base + 16 * lane.  The transfer counts on the vector-memory counter;
+// the kernel waits for it explicitly (the compiler does not see it).
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+// Wait until at most N vector-memory operations of the wave are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm_at_most() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int D, int KIND, int G>
 __global__ void __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(3, 4)))
-prefill_kernel(AttnParams p, int qblocks,
-                                                              int total_tiles) {
+prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   constexpr int HPW = G < kPreWaves ? G : kPreWaves;  // heads per workgroup
   constexpr int HG = G / HPW;                         // workgroups per KV head
   constexpr int PG = kPreWaves / HPW;                 // 32-position groups
   constexpr int QB = 32 * PG;                         // query positions per workgroup
-  constexpr int KROW = D + 8;                         // LDS K row in bf16 (16-byte pad)
   constexpr int NC = D / 16;                          // k steps of the QK product
   constexpr int NM = D / 32;                          // 32-row d blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t kl[2][32 * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[2][2 * D * 16];
+  constexpr int CPR = D / 8;                          // 16-byte chunks per K row
+  constexpr int KBYTES = 32 * D * 2;                  // K bytes per 32-key step
+  constexpr int VPAGE = 16 * D * 2;                   // V bytes per page block
+  constexpr int SBYTES = 2 * KBYTES;                  // K + V bytes per step
+  constexpr int NI = SBYTES / 1024;                   // 1 KB transfers per step
+  constexpr int NIW = NI / kPreWaves;                 // per wave
+  static_assert(NI % kPreWaves == 0 && NIW >= 1, "a step's transfers split over the waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBufs * SBYTES];
 
-  // Tile order: head group fastest.  Workgroups running at the same time
-  // then cover every KV head's slice of the K/V pages and every head's slice
-  // of the Q/O rows, which spreads their traffic over all HBM channels (one
-  // head's slices alone concentrate on a few).  Neighbouring query blocks of
-  // one head, whose K/V windows overlap, still run close together in time.
   const int t = blockIdx.x;
   if (t >= total_tiles) return;
   const int NY = p.hkv * HG;
   const int yh = t % NY;
   const int qb = (t / NY) % qblocks;
   const int i = (t / NY) / qblocks;
-  const int kvh = yh / HG;
-  const int hg = yh % HG;
+  const int kvh = yh % p.hkv;
+  const int hg = yh / p.hkv;
 
   const int row0 = p.cu_q[i];
   const int n = p.cu_q[i + 1] - row0;
@@ -90,7 +112,7 @@ prefill_kernel(AttnParams p, int qblocks,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hl = hg * HPW + wave % HPW;
   const int r0 = (wave / HPW) * 32;      // first workgroup row of this wave
   const int head = kvh * G + hl;
@@ -124,66 +146,50 @@ prefill_kernel(AttnParams p, int qblocks,
 
   const int kstart = (wg_klo / 32) * 32;
   const int nsteps = (wg_khi - kstart) / 32 + 1;
-  const int64_t head_stride = (int64_t)kPage * D;
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)(lds));
 
-  // Staging.  One 16-token page block of one head is 16*D*2 contiguous
-  // bytes for K (token-major) and for V (dim-major), so thread t copies the
-  // 16-byte chunk(s) at t*8 (+ j*kPreThreads*8) of each of the step's two
-  // page blocks.  For K the chunk is row (t*8)/D, columns (t*8)%D; for V it
-  // is dim (t*8)/16, keys 8*(t&1) .. +8.  Loads are issued one step ahead
-  // and unconditionally (a tile past the range reads page 0, which every
-  // pool has); masking and the LDS write happen after the step's math, when
-  // the data has arrived anyway.  Page ids come by scalar loads, so waiting
-  // for them never waits for the K/V loads in flight.
-  constexpr int EPB = kPage * D;                    // elements per page block
-  constexpr int NCH = EPB / 8;                      // 16-byte chunks per block
-  constexpr int CPT = (NCH + kPreThreads - 1) / kPreThreads;
-  u32x4 kreg[2][CPT], vreg[2][CPT];
-  auto stage_load = [&](int kp0) {
-    // both page ids first: their wait then covers no K/V load
-    int32_t pgs[2];
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int tile = kp0 + 16 * t2;
-      pgs[t2] = tile <= wg_khi ? page_of_uniform<KIND>(p.t.fpt, p.t.rpt, sid, tile,
-                                                       p.t.max_pages, p.t.ring_slots)
-                               : 0;
+  // Transfers of one step.  Transfers 0 .. NI/2-1 fill the K region: LDS row
+  // r (of 32) holds key swap23(r % 16) of page r / 16, its chunk j at
+  // position j ^ (r % CPR).  Transfers NI/2 .. NI-1 copy the two V page
+  // blocks verbatim.  Each transfer reads within one page block, so its
+  // source is a scalar base plus a per-lane offset fixed for the kernel.
+  uint32_t voff[NIW];
+  for (int ii = 0; ii < NIW; ++ii) {
+    const int inst = wave * NIW + ii;
+    if (inst < NI / 2) {
+      const int slot = inst * 64 + lane;
+      const int row = slot / CPR;
+      const int rr = row & 15;
+      const int kr = ((rr >> 2) & 1) * 8 + ((rr >> 3) & 1) * 4 + (rr & 3);
+      const int j = (slot % CPR) ^ (row & (CPR - 1));
+      voff[ii] = (kr * D + j * 8) * 2;
+    } else {
+      voff[ii] = ((inst - NI / 2) * 1024 + lane * 16) % VPAGE;
     }
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const uint16_t* kb = p.k_cache + ((int64_t)pgs[t2] * hkv + kvh) * head_stride;
-      const uint16_t* vb = p.v_cache + ((int64_t)pgs[t2] * hkv + kvh) * head_stride;
-      for (int j = 0; j < CPT; ++j) {
-        const int e = (tid + j * kPreThreads) * 8;  // element offset in the block
-        if (NCH % kPreThreads != 0 && e >= EPB) break;
-        kreg[t2][j] = *(const u32x4*)(kb + e);
-        vreg[t2][j] = *(const u32x4*)(vb + e);
-      }
-    }
-  };
-  auto stage_store = [&](int buf, int kp0) {
-    // wave-uniform: whether every key of the step's two page blocks lies
-    // inside the workgroup's key range
-    const bool inner = kp0 >= wg_klo && kp0 + 31 <= wg_khi;
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int tile = kp0 + 16 * t2;
-      for (int j = 0; j < CPT; ++j) {
-        const int e = (tid + j * kPreThreads) * 8;
-        if (NCH % kPreThreads != 0 && e >= EPB) break;
-        u32x4 kv = kreg[t2][j], vv = vreg[t2][j];
-        if (!inner) {
-          // keys outside [wg_klo, wg_khi] may hold evicted or unwritten data
-          const int kk = tile + e / D;
-          if (kk < wg_klo || kk > wg_khi) kv = u32x4{0, 0, 0, 0};
-          const int k8 = tile + (e % 16);
-          for (int x = 0; x < 8; ++x) {
-            const int kp = k8 + x;
-            if (kp < wg_klo || kp > wg_khi) vv[x >> 1] &= (x & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-        }
-        // key row kr of the page goes to LDS row swap23(kr) of the page half
-        const int kr = e / D;
-        const int rho = ((kr >> 2) & 1) * 8 + ((kr >> 3) & 1) * 4 + (kr & 3);
-        *(u32x4*)(&kl[buf][(16 * t2 + rho) * KROW + e % D]) = kv;
-        *(u32x4*)(&vl[buf][t2 * EPB + e]) = vv;
+  }
+  const int64_t blk = (int64_t)kPage * D;  // elements per (page, KV head) block
+  // tiles past the range read page 0 (present in every pool); their keys
+  // are masked like any other key outside the range
+  auto issue = [&](int kp0, int buf) {
+    const int32_t pg0 = kp0 <= wg_khi ? page_of_uniform<KIND>(p.t.fpt, p.t.rpt, sid, kp0,
+                                                              p.t.max_pages, p.t.ring_slots)
+                                      : 0;
+    const int32_t pg1 = kp0 + 16 <= wg_khi
+                            ? page_of_uniform<KIND>(p.t.fpt, p.t.rpt, sid, kp0 + 16,
+                                                    p.t.max_pages, p.t.ring_slots)
+                            : 0;
+    const uint32_t base = lds0 + buf * SBYTES;
+    for (int ii = 0; ii < NIW; ++ii) {
+      const int inst = wave * NIW + ii;  // wave-uniform
+      if (inst < NI / 2) {
+        const int t2 = (inst * 64 / CPR) >> 4;
+        dma16(voff[ii], p.k_cache + ((int64_t)(t2 ? pg1 : pg0) * hkv + kvh) * blk,
+              base + inst * 1024);
+      } else {
+        const int vi = inst - NI / 2;
+        const int t2 = (vi * 1024) / VPAGE;
+        dma16(voff[ii], p.v_cache + ((int64_t)(t2 ? pg1 : pg0) * hkv + kvh) * blk,
+              base + KBYTES + vi * 1024);
       }
     }
   };
@@ -192,11 +198,12 @@ prefill_kernel(AttnParams p, int qblocks,
   auto compute = [&](int buf, int kp0) {
     // does this wave have any unmasked key in the step?
     if (!(wave_on && kp0 <= w_pos_hi && kp0 + 31 >= w_klo)) return;
+    const uint8_t* kb = lds + buf * SBYTES;
     f32x16 sacc;
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    const uint16_t* krow = &kl[buf][qr * KROW + 8 * h2];
     for (int c = 0; c < NC; ++c) {
-      bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * c));
+      const int pos = (2 * c + h2) ^ (qr & (CPR - 1));
+      bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + qr * (CPR * 16) + pos * 16));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc, 0, 0, 0);
     }
     // every key of the step valid for every row of the wave?
@@ -235,28 +242,46 @@ prefill_kernel(AttnParams p, int qblocks,
     }
     lsum += ps;
     // V fragment: dim 32mb + qr, keys 8*h2 .. +8 of each page
-    const uint16_t* v0 = &vl[buf][qr * 16 + 8 * h2];
+    const uint8_t* v0 = kb + KBYTES + qr * 32 + h2 * 16;
     for (int mb = 0; mb < NM; ++mb) {
-      f16x8 va = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + 512 * mb));
-      f16x8 vb = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + EPB + 512 * mb));
+      f16x8 va = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + mb * 1024));
+      f16x8 vb = __builtin_bit_cast(f16x8, *(const u32x4*)(v0 + VPAGE + mb * 1024));
       o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf0, o[mb], 0, 0, 0);
       o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb, pf1, o[mb], 0, 0, 0);
     }
   };
 
-  stage_load(kstart);
-  stage_store(0, kstart);
-  wait_vm_all();  // Q fragments have arrived
-  __syncthreads();
-  // every iteration loads and stores (the last one a masked tile past the
-  // range), so the loads never merge with other values in registers
+  wait_vm_all();  // Q fragments have arrived: from here on only transfers count
+  issue(kstart, 0);
+  issue(kstart + 32, 1);
+  int bc = 0, bn = 2;  // buffers of step s and of step s+2
   for (int s = 0; s < nsteps; ++s) {
     const int kp0 = kstart + 32 * s;
-    stage_load(kp0 + 32);
-    compute(s & 1, kp0);
-    stage_store((s & 1) ^ 1, kp0 + 32);
-    __syncthreads();
+    wait_vm_at_most<NIW>();  // this wave's part of step s has landed
+    __syncthreads();         // every part has; step s-1's buffer is free
+    if (!(kp0 >= wg_klo && kp0 + 31 <= wg_khi)) {
+      // keys of the step outside the workgroup's range: zero their V
+      uint8_t* vz = lds + bc * SBYTES + KBYTES;
+      for (int e = tid; e < 2 * D; e += kPreThreads) {  // (page block, dim) rows
+        const int key0 = kp0 + 16 * (e / D);
+        u32x4* rowp = (u32x4*)(vz + (e / D) * VPAGE + (e % D) * 32);
+        for (int hf = 0; hf < 2; ++hf) {
+          u32x4 w = rowp[hf];
+          for (int x = 0; x < 8; ++x) {
+            const int k = key0 + 8 * hf + x;
+            if (k < wg_klo || k > wg_khi) w[x >> 1] &= (x & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+          rowp[hf] = w;
+        }
+      }
+      __syncthreads();
+    }
+    issue(kp0 + 64, bn);  // into step s-1's buffer
+    compute(bc, kp0);
+    bc = bc == kBufs - 1 ? 0 : bc + 1;
+    bn = bn == kBufs - 1 ? 0 : bn + 1;
   }
+  wait_vm_at_most<0>();  // no transfer may land after the workgroup leaves
 
   lsum += xor_lane(lsum, 32);
   if (row_ok) {

@@ -32,8 +32,8 @@
 //    unwritten data) get -inf scores through the per-row masks, and their V
 //    is zeroed in LDS before use so that 0 * V stays 0.
 //  - Online softmax in fp32, log2 domain, with lazy rescaling: the two lanes
-//    of a row exchange their maxima only when the running max must move;
-//    output fp32.
+//    of a row exchange their maxima only when the running max must move.
+//  - Output fp32, passed through LDS so that stores write whole row pieces.
 #include <hip/hip_runtime.h>
 
 #include "device.h"
@@ -86,7 +86,10 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   constexpr int NI = SBYTES / 1024;                   // 1 KB transfers per step
   constexpr int NIW = NI / kPreWaves;                 // per wave
   static_assert(NI % kPreWaves == 0 && NIW >= 1, "a step's transfers split over the waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBufs * SBYTES];
+  constexpr int OROW = 64 * 4 + 16;  // LDS bytes per row of a 64-dim output piece (padded)
+  constexpr int OBYTES = kPreWaves * 32 * OROW;
+  constexpr int LBYTES = kBufs * SBYTES > OBYTES ? kBufs * SBYTES : OBYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LBYTES];
 
   const int t = blockIdx.x;
   if (t >= total_tiles) return;
@@ -283,19 +286,37 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   }
   wait_vm_at_most<0>();  // no transfer may land after the workgroup leaves
 
+  // Output.  A lane holds 4 consecutive dims per (mb, j) of its row, so
+  // storing straight from registers would write 32 bytes to each of 32 rows
+  // per instruction.  Instead each wave passes its 32 x D tile through LDS
+  // (the K/V buffers are free once every wave has left the loop), 64 dims at
+  // a time, and stores whole rows: every store instruction writes 4
+  // contiguous 256-byte row pieces.
   lsum += xor_lane(lsum, 32);
-  if (row_ok) {
-    const float inv = 1.0f / lsum;
-    float* orow = p.out + (grow * hq + head) * D;
-    for (int mb = 0; mb < NM; ++mb)
+  const float inv = 1.0f / lsum;
+  __syncthreads();
+  uint8_t* ot = lds + wave * 32 * OROW;
+  for (int ps = 0; ps < NM / 2; ++ps) {
+    for (int mh = 0; mh < 2; ++mh) {
+      const int mb = 2 * ps + mh;
       for (int j = 0; j < 4; ++j) {
         f32x4 v = {o[mb][4 * j] * inv, o[mb][4 * j + 1] * inv, o[mb][4 * j + 2] * inv,
                    o[mb][4 * j + 3] * inv};
-        *(f32x4*)(orow + 32 * mb + 8 * j + 4 * h2) = v;
+        *(f32x4*)(ot + qr * OROW + (32 * mh + 8 * j + 4 * h2) * 4) = v;
       }
-    if (p.vlen && kvh == 0 && hl == 0 && h2 == 0)
-      p.vlen[grow] = KIND == 0 ? my_pos + 1 : min(my_pos + 1, W);
+    }
+    // lane l stores 16 bytes of row 4k + l / 16 (dims 64 ps + 4 (l % 16) ..)
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + (lane >> 4);
+      const f32x4 v = *(const f32x4*)(ot + r * OROW + (lane & 15) * 16);
+      if (r0 + r < nrows) {
+        const int64_t gr = (int64_t)row0 + qb * QB + r0 + r;
+        *(f32x4*)(p.out + (gr * hq + head) * D + 64 * ps + 4 * (lane & 15)) = v;
+      }
+    }
   }
+  if (row_ok && p.vlen && kvh == 0 && hl == 0 && h2 == 0)
+    p.vlen[grow] = KIND == 0 ? my_pos + 1 : min(my_pos + 1, W);
 }
 
 template <int D, int KIND, int G>

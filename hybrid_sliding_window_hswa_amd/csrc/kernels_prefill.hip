@@ -305,13 +305,15 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
         *(f32x4*)(ot + qr * OROW + (32 * mh + 8 * j + 4 * h2) * 4) = v;
       }
     }
-    // lane l stores 16 bytes of row 4k + l / 16 (dims 64 ps + 4 (l % 16) ..)
+    // lane l stores 16 bytes of row 4k + l / 16 (dims 64 ps + 4 (l % 16) ..);
+    // the output is not read again here, so the stores are non-temporal
     for (int k = 0; k < 8; ++k) {
       const int r = 4 * k + (lane >> 4);
       const f32x4 v = *(const f32x4*)(ot + r * OROW + (lane & 15) * 16);
       if (r0 + r < nrows) {
         const int64_t gr = (int64_t)row0 + qb * QB + r0 + r;
-        *(f32x4*)(p.out + (gr * hq + head) * D + 64 * ps + 4 * (lane & 15)) = v;
+        __builtin_nontemporal_store(v, (f32x4*)(p.out + (gr * hq + head) * D + 64 * ps +
+                                                4 * (lane & 15)));
       }
     }
   }

@@ -42,10 +42,14 @@ struct PoolDev {
   int32_t ring_slots;
 };
 
-// recs/pages live in pinned host memory readable by the device.
+// recs/pages live in pinned host memory readable by the device.  Every
+// block of the launch writes `seq` into done[its index] (pinned host memory)
+// once it has read everything it needs from the staging buffer, so the host
+// knows when the buffer may be reused without recording an event.
+int pool_apply_blocks(int n_recs, int64_t max_range);
 hipError_t launch_pool_apply(const PoolDev& dev, const PoolRec* recs, int n_recs,
-                             const int32_t* pages, int64_t max_range,
-                             hipStream_t stream);
+                             const int32_t* pages, int64_t max_range, int32_t* done,
+                             int32_t seq, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Attention kernels.

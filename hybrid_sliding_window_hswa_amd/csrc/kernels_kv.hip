@@ -22,9 +22,16 @@ using namespace dev;
 // ---------------------------------------------------------------------------
 // Applies one pool operation's records to the device tables.  Block x is a
 // record (one sequence); blocks along y and threads stride over its ranges.
+// Records and page lists sit in pinned host memory, read over the bus: the
+// record is read once per block, and each listed page id once per thread
+// that needs it (map entries are written a whole page at a time).
 __global__ void __launch_bounds__(256) pool_apply_kernel(PoolDev d, const PoolRec* recs,
-                                                         const int32_t* pages) {
-  const PoolRec r = recs[blockIdx.x];
+                                                         const int32_t* pages, int32_t* done,
+                                                         int32_t seq) {
+  __shared__ PoolRec rs;
+  if (threadIdx.x == 0) rs = recs[blockIdx.x];
+  __syncthreads();
+  const PoolRec r = rs;
   const int tid = blockIdx.y * blockDim.x + threadIdx.x;
   const int stride = gridDim.y * blockDim.x;
   if (tid == 0) d.seq_len[r.seq] = r.new_len;
@@ -32,26 +39,50 @@ __global__ void __launch_bounds__(256) pool_apply_kernel(PoolDev d, const PoolRe
   const int32_t* pg = pages + r.pg_off;
   for (int lp = r.fpt_lo + tid; lp < r.fpt_hi; lp += stride)
     row[lp] = r.fpt_clear ? -1 : pg[lp - r.pg_lo];
-  for (int pos = r.clr_lo + tid; pos < r.clr_hi; pos += stride) {
-    int32_t fs = pg[pos / kPage - r.pg_lo] * kPage + pos % kPage;
-    d.map[fs] = -1;
+  if (r.clr_hi > r.clr_lo) {
+    for (int lp = r.clr_lo / kPage + tid; lp <= (r.clr_hi - 1) / kPage; lp += stride) {
+      int32_t* m = d.map + pg[lp - r.pg_lo] * kPage;
+      for (int x = 0; x < kPage; ++x) {
+        const int pos = lp * kPage + x;
+        if (pos >= r.clr_lo && pos < r.clr_hi) m[x] = -1;
+      }
+    }
   }
-  const int rp = d.ring_slots / kPage;
-  for (int pos = r.set_lo + tid; pos < r.set_hi; pos += stride) {
-    int32_t fs = pg[pos / kPage - r.pg_lo] * kPage + pos % kPage;
-    int32_t q = pos % d.ring_slots;
-    d.map[fs] = d.rpt[(int64_t)r.seq * rp + q / kPage] * kPage + q % kPage;
+  if (r.set_hi > r.set_lo) {
+    const int rp = d.ring_slots / kPage;
+    const int32_t* rring = d.rpt + (int64_t)r.seq * rp;
+    for (int lp = r.set_lo / kPage + tid; lp <= (r.set_hi - 1) / kPage; lp += stride) {
+      int32_t* m = d.map + pg[lp - r.pg_lo] * kPage;
+      for (int x = 0; x < kPage; ++x) {
+        const int pos = lp * kPage + x;
+        if (pos >= r.set_lo && pos < r.set_hi) {
+          const int32_t q = pos % d.ring_slots;
+          m[x] = rring[q / kPage] * kPage + q % kPage;
+        }
+      }
+    }
   }
+  // every read of the staging buffer by this block is complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(done + blockIdx.y * gridDim.x + blockIdx.x, seq, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+int pool_apply_blocks(int n_recs, int64_t max_range) {
+  int64_t y = (max_range / kPage + 255) / 256;  // one page per thread
+  if (y < 1) y = 1;
+  if (y > 64) y = 64;
+  return n_recs * (int)y;
 }
 
 hipError_t launch_pool_apply(const PoolDev& d, const PoolRec* recs, int n_recs,
-                             const int32_t* pages, int64_t max_range, hipStream_t s) {
+                             const int32_t* pages, int64_t max_range, int32_t* done,
+                             int32_t seq, hipStream_t s) {
   if (n_recs <= 0) return hipSuccess;
-  int64_t y = (max_range + 2047) / 2048;
-  if (y < 1) y = 1;
-  if (y > 64) y = 64;
+  const int y = pool_apply_blocks(n_recs, max_range) / n_recs;
   hipLaunchKernelGGL(pool_apply_kernel, dim3(n_recs, (unsigned)y), dim3(256), 0, s, d, recs,
-                     pages);
+                     pages, done, seq);
   return hipGetLastError();
 }
 

@@ -21,7 +21,10 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <new>
+#include <thread>
 #include <vector>
 
 #include "../../include/hswa.h"
@@ -37,9 +40,43 @@ constexpr int kStages = 16;
 struct Stage {
   void* buf = nullptr;       // pinned host memory, device-readable
   size_t cap = 0;
-  hipEvent_t done = nullptr; // recorded after the apply kernel that read it
+  // the apply kernel that last read the buffer: its blocks write `seq` into
+  // done[0 .. nblk) when they no longer need the buffer
+  volatile int32_t* done = nullptr;
+  int32_t nblk = 0;
+  int32_t seq = 0;
   bool pending = false;
 };
+
+// Waits until every block of the kernel that last read the stage is done
+// with it.  After a second of polling the device is synchronised once, so a
+// failed or aborted kernel surfaces as an error instead of a hang.
+int wait_stage(Stage& st) {
+  if (!st.pending) return HSWA_OK;
+  auto all_done = [&]() {
+    for (int32_t i = 0; i < st.nblk; ++i)
+      if (st.done[i] != st.seq) return false;
+    return true;
+  };
+  const auto t0 = std::chrono::steady_clock::now();
+  bool synced = false;
+  while (!all_done()) {
+    if (!synced && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(1)) {
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hswa::hip_fail(e, "waiting for a pool staging buffer");
+      synced = true;
+      if (!all_done()) {
+        hswa::set_error("pool table update did not report completion");
+        return HSWA_E_HIP;
+      }
+      break;
+    }
+    std::this_thread::yield();
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  st.pending = false;
+  return HSWA_OK;
+}
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -64,6 +101,7 @@ struct hswa_pool {
   hswa::PoolDev dev{};
   Stage stage[kStages];
   int next_stage = 0;
+  int32_t flush_seq = 0;
   std::vector<void*> retired;      // outgrown staging buffers, freed at destroy
 
   int32_t pop_page() {
@@ -164,18 +202,19 @@ struct RecBuilder {
 };
 
 // Copies the records into a staging buffer and enqueues the apply kernel.
+// Buffer layout: records, page list, then one completion word per block.
 int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
   if (!p->has_dev || rb.recs.empty()) return HSWA_OK;
   hipStream_t s = (hipStream_t)stream;
+  const int n_recs = (int)rb.recs.size();
+  const int nblk = hswa::pool_apply_blocks(n_recs, rb.max_range);
   size_t rec_bytes = rb.recs.size() * sizeof(PoolRec);
-  size_t bytes = rec_bytes + rb.pages.size() * sizeof(int32_t);
+  size_t done_off = (rec_bytes + rb.pages.size() * sizeof(int32_t) + 63) / 64 * 64;
+  size_t bytes = done_off + (size_t)nblk * sizeof(int32_t);
   Stage& st = p->stage[p->next_stage];
   p->next_stage = (p->next_stage + 1) % kStages;
-  if (st.pending) {
-    hipError_t e = hipEventSynchronize(st.done);
-    if (e != hipSuccess) return hswa::hip_fail(e, "waiting for a pool staging buffer");
-    st.pending = false;
-  }
+  int rc = wait_stage(st);
+  if (rc) return rc;
   if (st.cap < bytes) {
     if (st.buf) p->retired.push_back(st.buf);
     st.buf = nullptr;
@@ -193,11 +232,15 @@ int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
   void* dptr = nullptr;
   hipError_t e = hipHostGetDevicePointer(&dptr, st.buf, 0);
   if (e != hipSuccess) return hswa::hip_fail(e, "hipHostGetDevicePointer");
-  e = hswa::launch_pool_apply(p->dev, (const PoolRec*)dptr, (int)rb.recs.size(),
-                              (const int32_t*)((char*)dptr + rec_bytes), rb.max_range, s);
+  st.seq = ++p->flush_seq;
+  if (st.seq <= 0) st.seq = p->flush_seq = 1;  // positive, never a stale value
+  st.nblk = nblk;
+  st.done = (volatile int32_t*)((char*)st.buf + done_off);
+  for (int i = 0; i < nblk; ++i) st.done[i] = 0;
+  e = hswa::launch_pool_apply(p->dev, (const PoolRec*)dptr, n_recs,
+                              (const int32_t*)((char*)dptr + rec_bytes), rb.max_range,
+                              (int32_t*)((char*)dptr + done_off), st.seq, s);
   if (e != hipSuccess) return hswa::hip_fail(e, "pool table update launch");
-  e = hipEventRecord(st.done, s);
-  if (e != hipSuccess) return hswa::hip_fail(e, "hipEventRecord");
   st.pending = true;
   return HSWA_OK;
 }
@@ -404,14 +447,6 @@ int hswa_pool_create(const hswa_pool_desc* d, hswa_pool** out) {
         return rc;
       }
     }
-    for (auto& st : p->stage) {
-      hipError_t e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
-      if (e != hipSuccess) {
-        int rc = hswa::hip_fail(e, "hipEventCreate");
-        hswa_pool_destroy(p);
-        return rc;
-      }
-    }
   }
   *out = p;
   return HSWA_OK;
@@ -420,8 +455,7 @@ int hswa_pool_create(const hswa_pool_desc* d, hswa_pool** out) {
 void hswa_pool_destroy(hswa_pool* p) {
   if (!p) return;
   for (auto& st : p->stage) {
-    if (st.pending) hipEventSynchronize(st.done);
-    if (st.done) hipEventDestroy(st.done);
+    wait_stage(st);
     if (st.buf) hipHostFree(st.buf);
   }
   for (void* b : p->retired) hipHostFree(b);

@@ -40,6 +40,13 @@ Readings taken where the pages leave a step open:
   as section 2.1 "Data Transfer" asks for transfers.
 * ``release`` ends a request: its Full pages go back to the tail of the free
   list in logical-page order and its remaining SWA entries are dropped.
+* ``truncate`` drops a sequence's newest positions, e.g. draft tokens that a
+  multi-token (MTP) verification step rejected (section 5.2 of the page runs
+  three MTP layers, so a step appends up to four tokens).  The window of the
+  new length must still be resident, so it runs before the step's eviction.
+  Dropped positions lose their SWA entry; Full pages that no longer hold a
+  position go back to the head of the free list, lowest logical page first,
+  so the next allocation takes them again.
 * -1 marks "no slot" in every table.
 """
 from __future__ import annotations
@@ -210,6 +217,26 @@ class PoolSim:
             self.pages[b] = []
             self.length[b] = 0
             self.res_start[b] = 0
+
+    def truncate(self, seq_ids, new_lens) -> None:
+        """Cut sequence seq_ids[i] back to new_lens[i] positions."""
+        ids = self._check_ids(seq_ids)
+        lens = [int(x) for x in new_lens]
+        if len(lens) != len(ids):
+            raise ValueError("one new length per sequence")
+        for b, n in zip(ids, lens):
+            if not 0 <= n <= self.length[b]:
+                raise ValueError("new length outside [0, current length]")
+            if self.res_start[b] > max(0, n - self.W + 1):
+                raise ValueError("the window of the new length was already evicted")
+        for b, n in zip(ids, lens):
+            for pos in range(n, self.length[b]):
+                del self.map[self.full_slot(b, pos)]
+            keep = self._pages_for(n)
+            freed = self.pages[b][keep:]
+            self.pages[b] = self.pages[b][:keep]
+            self.free.extendleft(reversed(freed))
+            self.length[b] = n
 
     # -- table views (what the device tables must hold) ---------------------
     def seq_len_table(self) -> List[int]:

@@ -46,6 +46,16 @@ def _run_fixture(sc):
             assert ev == op["evicted"] and cnt == op["counts"], op
         elif op["op"] == "release":
             p.release(op["seq_ids"])
+        elif op["op"] == "truncate":
+            if op.get("invalid"):
+                before = _state(p)
+                with pytest.raises(ValueError):
+                    p.truncate(op["seq_ids"], op["new_len"])
+                assert _state(p) == before
+            else:
+                p.truncate(op["seq_ids"], op["new_len"])
+        else:
+            raise AssertionError(f"unknown fixture op {op['op']}")
     f = sc["final"]
     assert p.seq_len_table() == f["seq_len"]
     assert p.fpt_table() == f["fpt"]
@@ -131,6 +141,17 @@ class DictPool:
             self.alive[b] = set()
             self.n[b] = 0
 
+    def truncate(self, ids, lens):
+        for b, n in zip(ids, lens):
+            lo = min(self.alive[b]) if self.alive[b] else self.n[b]
+            if n < 0 or n > self.n[b] or lo > max(0, n - self.W + 1):
+                raise ValueError()
+        for b, n in zip(ids, lens):
+            self.alive[b] = {p for p in self.alive[b] if p < n}
+            gone = sorted(lp for lp in self.page_of[b] if lp * 16 >= n)
+            self.free = [self.page_of[b].pop(lp) for lp in gone] + self.free
+            self.n[b] = n
+
     def map_table(self):
         t = [-1] * (self.npages * 16)
         for b in self.alive:
@@ -199,7 +220,20 @@ def test_random_operations_against_second_simulator(seed):
         elif r < 0.8:
             assert a.evict(ids) == b.evict(ids)
             just_evicted = set(ids)
-        elif r < 0.92:
+        elif r < 0.86:
+            # cut back by up to 4 positions (rejected drafts), sometimes far
+            # below the resident window (refused, nothing changes)
+            lens = [max(0, a.length[i] - rnd.choice([0, 1, 3, 4, W + 5])) for i in ids]
+            try:
+                b.truncate(ids, lens)
+            except ValueError:
+                before = _state(a)
+                with pytest.raises(ValueError):
+                    a.truncate(ids, lens)
+                assert _state(a) == before
+                continue
+            a.truncate(ids, lens)
+        elif r < 0.94:
             ns = [rnd.randint(0, 3 * W + 20) for _ in ids]
             try:
                 exp = b.alloc(ids, ns, importing=True)

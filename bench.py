@@ -263,16 +263,24 @@ def _pairs_swa(n, W):
 
 
 class Decode:
-    def __init__(self, cx, ctxs, pattern, hq, hkv, d, W, ring, seed, steps_total):
+    """Decode steps over a layer pattern ("F" Full, "S" SWA).  rows = 1 is a
+    plain decode step; rows > 1 verifies one token plus rows-1 drafts per
+    sequence (multi-token decode), then keeps a seeded accepted prefix
+    (hswa_pool_truncate) before the eviction."""
+
+    def __init__(self, cx, ctxs, pattern, hq, hkv, d, W, ring, seed, steps_total, rows=1):
         torch, H = cx.torch, cx.H
         import synth
         self.cx, self.hq, self.hkv, self.d, self.W = cx, hq, hkv, d, W
         B = len(ctxs)
         self.B = B
+        self.rows = rows
+        self.seed = seed
         self.ctx0 = list(ctxs)
-        maxlen = max(ctxs) + steps_total + 1
+        maxlen = max(ctxs) + steps_total * rows + 1
         maxp = maxlen // 16 + 2
-        nfull = int(sum(c // 16 + 2 for c in ctxs) * 1.1) + B * (steps_total // 16 + 2) + 64
+        nfull = (int(sum(c // 16 + 2 for c in ctxs) * 1.1) + B * (steps_total * rows // 16 + 2)
+                 + 64)
         free = synth.permutation(nfull, seed, 1)
         ringp = synth.permutation(B * ring // 16, seed, 2)
         self.pool = H.hswa_pool_create(W, ring, B, maxp, nfull, free, ringp, device=cx.dev)
@@ -282,7 +290,6 @@ class Decode:
         self.sid = cx.i32(ids)
         H.hswa_pool_import(self.pool, ids, ctxs, want_slots=False)
         self.layers = []
-        kvb = KV_TOKEN_BYTES(hkv, d)
         for li, kind in enumerate(pattern):
             kc, vc = H.kv_cache_alloc(nfull if kind == "F" else B * ring // 16, hkv, d, cx.dev)
             # restore the context: generated per sequence on the device and
@@ -296,31 +303,36 @@ class Decode:
                 del kk, vv
             self.layers.append((H.FULL if kind == "F" else H.SWA, kc, vc))
         torch.cuda.synchronize()
-        # per-step inputs (one new token per sequence per layer)
+        # per-step inputs (rows new tokens per sequence per layer)
+        T = B * rows
         g = lambda shape, *s: synth.bf16_normal(shape, seed, 900, *s, device=cx.dev)
-        self.q = [g((B, hq, d), li, synth.ROLE_Q) for li in range(len(pattern))]
-        self.kn = [g((B, hkv, d), li, synth.ROLE_K) for li in range(len(pattern))]
-        self.vn = [g((B, hkv, d), li, synth.ROLE_V) for li in range(len(pattern))]
-        self.out = torch.empty((B, hq, d), dtype=torch.float32, device=cx.dev)
+        self.q = [g((T, hq, d), li, synth.ROLE_Q) for li in range(len(pattern))]
+        self.kn = [g((T, hkv, d), li, synth.ROLE_K) for li in range(len(pattern))]
+        self.vn = [g((T, hkv, d), li, synth.ROLE_V) for li in range(len(pattern))]
+        self.out = torch.empty((T, hq, d), dtype=torch.float32, device=cx.dev)
         self.max_seq_len = maxlen
-        nb = max(H.hswa_decode_workspace_bytes(H.FULL, W, B, hq, hkv, d, maxlen), 16)
+        self.cu = cx.i32(np.arange(0, T + 1, rows)) if rows > 1 else None
+        nb = max(H.hswa_decode_workspace_bytes(H.FULL, W, B, hq, hkv, d, maxlen, total_q=T), 16)
         self.ws = torch.empty(nb // 4 + 4, dtype=torch.float32, device=cx.dev)
         self.nbytes_ws = self.ws.numel() * 4
         self.args = []
         for li, (kind, kc, vc) in enumerate(self.layers):
-            a = _attn_args(cx, kind, W, hq, hkv, d, self.sid, None, B, 1, maxlen, self.view,
-                           self.q[li], self.kn[li], self.vn[li], kc, vc, self.out)
+            a = _attn_args(cx, kind, W, hq, hkv, d, self.sid, self.cu, T, rows, maxlen,
+                           self.view, self.q[li], self.kn[li], self.vn[li], kc, vc, self.out)
             self.args.append(a)
         self.lens = list(ctxs)
-        self.ones = _arr([1] * B)
+        self.nrows = _arr([rows] * B)
+        self.step_no = 0
+        self.step_bytes = []     # algorithmic bytes of every step run
+        self.accepted = []       # tokens kept by every step
 
     def step(self, events=None):
-        lib, cx = self.cx.lib, self.cx
+        lib, cx, H = self.cx.lib, self.cx, self.cx.H
         h = self.pool.handle
         ids, idp = self.ids
-        _, onep = self.ones
-        _check(cx, lib.hswa_pool_alloc(h, self.B, idp, onep, None, None, cx.sptr))
-        self.lens = [x + 1 for x in self.lens]
+        _, np_ = self.nrows
+        _check(cx, lib.hswa_pool_alloc(h, self.B, idp, np_, None, None, cx.sptr))
+        self.lens = [x + self.rows for x in self.lens]
         for a in self.args:
             if events is not None:
                 e0, e1 = cx.torch.cuda.Event(enable_timing=True), cx.torch.cuda.Event(
@@ -331,16 +343,31 @@ class Decode:
             if events is not None:
                 e1.record(cx.stream)
                 events.append((a.kind, list(self.lens), e0, e1))
+        self.step_bytes.append(sum(self.layer_bytes(a.kind, self.lens) for a in self.args))
+        if self.rows > 1:
+            import synth
+            acc = synth.uniform_ints(self.B, 1, self.rows, self.seed, 700, self.step_no)
+            self.lens = [x - self.rows + k for x, k in zip(self.lens, acc)]
+            keep, kp = _arr(self.lens)
+            _check(cx, lib.hswa_pool_truncate(h, self.B, idp, kp, cx.sptr))
+            self.accepted.append(sum(acc))
+        else:
+            self.accepted.append(self.B)
+        self.step_no += 1
         _check(cx, lib.hswa_pool_evict(h, self.B, idp, None, 0, None, cx.sptr))
 
     def layer_bytes(self, kind, lens):
-        """Algorithmic HBM bytes of one decode layer call: the K/V of every
-        key the new token attends to, Q read, O written (fp32), and the new
-        token's K/V read and written by the append."""
+        """Algorithmic HBM bytes of one decode layer call at lengths `lens`
+        (after the step's rows were allocated): the K/V of every key some row
+        attends to, read once for all rows of the sequence (Full: L keys; SWA:
+        the first row's window through the last row, min(L, W - 1 + rows)),
+        Q read, O written (fp32), and the rows' K/V read and written by the
+        append."""
         kvb = KV_TOKEN_BYTES(self.hkv, self.d)
-        keys = sum(L if kind == self.cx.H.FULL else min(L, self.W) for L in lens)
-        B = len(lens)
-        return keys * kvb + B * (self.hq * self.d * 2 + self.hq * self.d * 4 + 2 * kvb)
+        r = self.rows
+        keys = sum(L if kind == self.cx.H.FULL else min(L, self.W - 1 + r) for L in lens)
+        T = len(lens) * r
+        return keys * kvb + T * (self.hq * self.d * 2 + self.hq * self.d * 4 + 2 * kvb)
 
 
 # ---------------------------------------------------------------------------
@@ -423,30 +450,26 @@ def kernel_stats(cp, ev, kind):
 
 
 def run_decode(cx, dc, pattern, steps, warm):
-    """Times `steps` decode steps; returns the step's algorithmic GB/s and
-    per-kind call durations from events."""
+    """Times `steps` decode steps; returns the step's algorithmic GB/s, the
+    tokens kept per second and per-kind call durations from events."""
     torch, H = cx.torch, cx.H
     for _ in range(warm):
         dc.step()
     torch.cuda.synchronize()
-    lens_start = list(dc.lens)
+    first = len(dc.step_bytes)
     t0 = time.perf_counter()
     for _ in range(steps):
         dc.step()
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / steps
-    # bytes of the timed steps (every length grows by one per step)
-    tot = 0
-    for s in range(steps):
-        lens = [x + s + 1 for x in lens_start]
-        for kind in pattern:
-            tot += dc.layer_bytes(H.FULL if kind == "F" else H.SWA, lens)
-    step_bytes = tot / steps
+    step_bytes = sum(dc.step_bytes[first:]) / steps
+    tok_per_step = sum(dc.accepted[first:]) / steps
     ev = []
     for _ in range(2):
         dc.step(ev)
     torch.cuda.synchronize()
-    res = {"gbs": step_bytes / sec / 1e9, "ms_per_step": sec * 1e3, "bytes_per_step": step_bytes}
+    res = {"gbs": step_bytes / sec / 1e9, "ms_per_step": sec * 1e3, "bytes_per_step": step_bytes,
+           "tok_per_s": tok_per_step / sec}
     for kind, name in ((H.FULL, "full"), (H.SWA, "swa")):
         sel = [(l, e0.elapsed_time(e1) / 1e3) for k, l, e0, e1 in ev if k == kind]
         if sel:
@@ -539,6 +562,33 @@ def wl_mixed_decode(cx, args):
     rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full", "kernels_decode.hip"))
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+    line["full_call_us"] = round(r["full_call_us"], 1)
+    line["swa_call_us"] = round(r["swa_call_us"], 1)
+    return line
+
+
+def wl_mtp_decode(cx, args):
+    """Multi-token decode: one token plus three drafts per sequence per step
+    over one Full and one SWA layer, accepted prefix kept."""
+    import synth
+    wl = synth.MTP
+    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
+    steps, warm = args.decode_steps, 4
+    rows = wl.drafts + 1
+    dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                wl.ring_slots, wl.seed, steps + warm + 8, rows=rows)
+    r = run_decode(cx, dc, "FS", steps, warm)
+    log(f"mtp decode: {r}")
+    config = {"workload": "mtp_decode", "num_seqs": wl.num_seqs,
+              "ctx_range": [wl.ctx_lo, wl.ctx_hi], "rows_per_seq": rows,
+              "accepted_rows": [1, rows], "layers": "1 Full + 1 SWA",
+              "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+              "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
+              "seed": wl.seed}
+    rl = roofline("hbm", r["full_gbs"], None)
+    line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
+    line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+    line["accepted_tok_per_s"] = round(r["tok_per_s"], 1)
     line["full_call_us"] = round(r["full_call_us"], 1)
     line["swa_call_us"] = round(r["swa_call_us"], 1)
     return line
@@ -639,6 +689,7 @@ def wl_swa_single_chunk(cx, args):
 WORKLOADS = {
     "swa_chunked_prefill": wl_swa_chunked_prefill,
     "mixed_decode": wl_mixed_decode,
+    "mtp_decode": wl_mtp_decode,
     "hybrid_stack": wl_hybrid_stack,
     "long_decode": wl_long_decode,
     "swa_single_chunk": wl_swa_single_chunk,

@@ -30,7 +30,8 @@ SWA = HSWA_LAYER_SWA
 __all__ = [
     "HswaError", "NoSpace", "FULL", "SWA", "PAGE_SIZE",
     "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view", "hswa_pool_alloc",
-    "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_read_tables",
+    "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_truncate",
+    "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
     "hswa_last_error", "hswa_version", "kv_cache_shapes", "kv_cache_alloc", "library",
 ]
@@ -206,6 +207,16 @@ def hswa_pool_release(pool: Pool, seq_ids: Sequence[int], stream=None) -> None:
     _check(library().hswa_pool_release(pool.handle, ids.size, _p(ids), _stream(stream)))
 
 
+def hswa_pool_truncate(pool: Pool, seq_ids: Sequence[int], new_len: Sequence[int],
+                       stream=None) -> None:
+    """Cuts each listed sequence back to new_len positions (rejected drafts of
+    a multi-token step); call before the step's evict."""
+    ids, n = _i32(seq_ids), _i32(new_len)
+    if n.size != ids.size:
+        raise ValueError("one new length per sequence")
+    _check(library().hswa_pool_truncate(pool.handle, ids.size, _p(ids), _p(n), _stream(stream)))
+
+
 def hswa_pool_read_tables(pool: Pool) -> dict:
     d = pool.desc
     seq_len = np.empty(d["max_seqs"], np.int32)
@@ -280,20 +291,27 @@ def hswa_prefill_chunk(kind: int, window: int, q, k_new, v_new, seq_ids, cu_q,
 
 
 def hswa_decode_workspace_bytes(kind: int, window: int, num_seqs: int, num_q_heads: int,
-                                num_kv_heads: int, head_dim: int, max_seq_len: int) -> int:
+                                num_kv_heads: int, head_dim: int, max_seq_len: int,
+                                total_q: Optional[int] = None) -> int:
+    """Workspace bytes of a decode call; ``total_q`` is the row count of a
+    multi-row call (None: one row per sequence)."""
     a = _capi.AttnArgs()
     a.kind, a.window, a.num_seqs = kind, window, num_seqs
     a.num_q_heads, a.num_kv_heads, a.head_dim = num_q_heads, num_kv_heads, head_dim
     a.max_seq_len = max_seq_len
+    a.total_q = num_seqs if total_q is None else total_q
     return int(library().hswa_decode_workspace_bytes(C.byref(a)))
 
 
 def hswa_decode(kind: int, window: int, q, k_new, v_new, seq_ids, max_seq_len: int, view,
                 k_cache, v_cache, out, workspace=None, vlen=None, scale: float = 0.0,
-                stream=None) -> None:
-    """One query row per sequence (q [B, Hq, d]) at position seq_len - 1."""
-    a = _args(kind, window, q, k_new, v_new, seq_ids, None, q.shape[0], 1, max_seq_len, view,
-              k_cache, v_cache, out, vlen, scale)
+                stream=None, cu_q=None, max_q_len: int = 1) -> None:
+    """Decode step.  Without ``cu_q``: one query row per sequence (q [B, Hq, d])
+    at position seq_len - 1.  With ``cu_q`` (device int32 [B+1]): 1..4 rows per
+    sequence, its last positions (q [T, Hq, d]); ``max_q_len`` bounds them."""
+    a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0],
+              max_q_len if cu_q is not None else 1, max_seq_len, view, k_cache, v_cache, out,
+              vlen, scale)
     ws = _dptr(workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().hswa_decode(C.byref(a), ws, nbytes, _stream(stream)))

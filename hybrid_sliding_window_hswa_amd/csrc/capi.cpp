@@ -38,8 +38,12 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Shared validation of an attention call.  `decode` selects the one-row-
-// per-sequence form (cu_q ignored).
+// Query rows per sequence a decode call takes: one new token plus up to
+// three drafts of a multi-token verification step.
+constexpr int32_t kMaxDecodeRows = 4;
+
+// Shared validation of an attention call.  `decode` selects the decode form:
+// one row per sequence when cu_q is NULL, else 1..4 rows per sequence.
 int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnParams* p) {
   if (!a) {
     hswa::set_error("args is NULL");
@@ -82,10 +86,24 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
     return HSWA_E_INVAL;
   }
   if (decode) {
-    if (a->total_q != a->num_seqs) {
+    if (!a->cu_q && a->total_q != a->num_seqs) {
       hswa::set_error("decode: total_q (%d) must equal num_seqs (%d)", a->total_q,
                       a->num_seqs);
       return HSWA_E_INVAL;
+    }
+    if (a->cu_q && a->num_seqs > 0) {
+      if (a->max_q_len > kMaxDecodeRows) {
+        hswa::set_error("decode: at most %d rows per sequence (max_q_len %d)", kMaxDecodeRows,
+                        a->max_q_len);
+        return HSWA_E_UNSUPPORTED;
+      }
+      if (a->max_q_len < 1 || a->total_q < 0 ||
+          (int64_t)a->total_q > (int64_t)a->num_seqs * a->max_q_len) {
+        hswa::set_error("decode: need max_q_len >= 1 and 0 <= total_q <= num_seqs * max_q_len "
+                        "(max_q_len %d, total_q %d, num_seqs %d)",
+                        a->max_q_len, a->total_q, a->num_seqs);
+        return HSWA_E_INVAL;
+      }
     }
     if (need_attn && a->max_seq_len < 1 && a->num_seqs > 0) {
       hswa::set_error("decode: max_seq_len must be >= 1");
@@ -139,9 +157,9 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
   p->scale_log2 = scale * 1.4426950408889634f;
   p->num_seqs = a->num_seqs;
   p->seq_ids = a->seq_ids;
-  p->cu_q = decode ? nullptr : a->cu_q;
+  p->cu_q = a->cu_q;
   p->total_q = a->total_q;
-  p->max_q_len = decode ? 1 : a->max_q_len;
+  p->max_q_len = decode && !a->cu_q ? 1 : a->max_q_len;
   p->max_seq_len = a->max_seq_len;
   p->q = (const uint16_t*)a->q;
   p->k_new = (const uint16_t*)a->k_new;
@@ -167,8 +185,8 @@ namespace hswa {
 // into chunks of split_len keys (a multiple of 64) so that the grid has
 // enough workgroups for 256 CUs while the partial results stay small next
 // to the KV bytes; SWA layers read at most W keys and use one split.
-DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d,
-                       int32_t window, int32_t max_seq_len) {
+DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t rows, int32_t hq, int32_t hkv,
+                       int32_t d, int32_t window, int32_t max_seq_len) {
   DecodePlan pl{1, 0, 0};
   if (num_seqs <= 0) return pl;
   if (kind == HSWA_LAYER_SWA) {
@@ -188,7 +206,7 @@ DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t hq, int32_t hkv, 
   n = (max_seq_len + sl - 1) / sl;
   pl.n_splits = (int32_t)n;
   pl.split_len = (int32_t)sl;
-  if (n > 1) pl.ws_bytes = (size_t)num_seqs * hq * n * (d + 2) * sizeof(float);
+  if (n > 1) pl.ws_bytes = (size_t)rows * hq * n * (d + 2) * sizeof(float);
   return pl;
 }
 
@@ -244,7 +262,10 @@ int hswa_prefill_chunk(const hswa_attn_args* a, void* stream) {
 
 size_t hswa_decode_workspace_bytes(const hswa_attn_args* a) {
   if (!a) return 0;
-  return hswa::plan_decode(a->kind, a->num_seqs, a->num_q_heads, a->num_kv_heads,
+  // rows of the call: total_q (one per sequence without cu_q, when a caller
+  // may have left total_q unset)
+  const int32_t rows = a->total_q > a->num_seqs ? a->total_q : a->num_seqs;
+  return hswa::plan_decode(a->kind, a->num_seqs, rows, a->num_q_heads, a->num_kv_heads,
                            a->head_dim, a->window, a->max_seq_len)
       .ws_bytes;
 }
@@ -254,9 +275,9 @@ int hswa_decode(const hswa_attn_args* a, void* ws, size_t ws_bytes, void* stream
   hswa::AttnParams p;
   int rc = validate(a, true, true, &p);
   if (rc) return rc;
-  if (p.num_seqs == 0) return HSWA_OK;
-  hswa::DecodePlan pl = hswa::plan_decode(p.kind, p.num_seqs, p.hq, p.hkv, p.d, p.window,
-                                          p.max_seq_len);
+  if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;
+  hswa::DecodePlan pl = hswa::plan_decode(p.kind, p.num_seqs, p.total_q, p.hq, p.hkv, p.d,
+                                          p.window, p.max_seq_len);
   if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) {
     hswa::set_error("decode workspace: %zu bytes given, %zu needed", ws_bytes, pl.ws_bytes);
     return HSWA_E_INVAL;

@@ -69,7 +69,7 @@ struct AttnParams {
   float scale_log2;      // softmax scale * log2(e)
   int32_t num_seqs;
   const int32_t* seq_ids;
-  const int32_t* cu_q;   // nullptr: one row per sequence
+  const int32_t* cu_q;   // nullptr: one row per sequence (decode)
   int32_t total_q;
   int32_t max_q_len;
   int32_t max_seq_len;
@@ -84,8 +84,8 @@ struct AttnParams {
   // decode split-K
   int32_t n_splits;
   int32_t split_len;
-  float* ws;             // [num_seqs][hq][n_splits][d] partial sums, then
-                         // [num_seqs][hq][n_splits][2] (max, sum)
+  float* ws;             // [total_q][hq][n_splits][d] partial sums, then
+                         // [total_q][hq][n_splits][2] (max, sum)
 };
 
 hipError_t launch_append(const AttnParams& p, hipStream_t stream);
@@ -98,7 +98,8 @@ struct DecodePlan {
   int32_t split_len;
   size_t ws_bytes;
 };
-DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t hq, int32_t hkv,
+// rows = query rows of the call (num_seqs for plain decode).
+DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t rows, int32_t hq, int32_t hkv,
                        int32_t d, int32_t window, int32_t max_seq_len);
 
 }  // namespace hswa

@@ -1,25 +1,37 @@
-// Paged decode attention over the dual pool, one query row per sequence.
+// Paged decode attention over the dual pool: one to four query rows per
+// sequence (one new token, or one token plus the drafts of a multi-token
+// verification step).
 //
 // "MiMo-V2.5 Series Inference Full-Link Optimization" sec. 1.2: decode is
 // bound by the bytes of KV it reads.  A Full layer reads the whole prefix
-// through the Full page table; a SWA layer reads at most W keys from the
-// sequence's ring (sec. 2.1 "KVCache Dual Pool").
+// through the Full page table; a SWA layer reads at most W keys (plus the
+// step's other rows) from the sequence's ring (sec. 2.1 "KVCache Dual
+// Pool").  Sec. 5.2 decodes with three MTP layers, i.e. up to four rows of
+// one sequence are verified at once; they share every K/V byte read here.
 //
 // Design (gfx950):
 //  - One workgroup = 4 wavefronts per (sequence, KV head, split).  Full
 //    layers split the context in split_len-key pieces so the grid fills 256
 //    CUs; pieces are merged by log-sum-exp in decode_combine_kernel.
-//  - The G query heads that share a KV head ride in the N dimension of a
-//    16x16x32 MFMA: S^T[key][head] = K[key][:] . Q[head][:], so every K/V
-//    byte is read from HBM once for all G heads.
+//  - The (row, head) pairs that share a KV head ride in the N dimension of
+//    16x16x32 MFMAs: S^T[key][col] = K[key][:] . Q[col][:], column
+//    col = row * G + head, in 16-column tiles.  Every K/V byte is read from
+//    HBM once for all G heads and all rows of the sequence.  Past 16 columns
+//    (8 heads, more than 2 rows) a wave carries two tiles' state, so two
+//    waves per SIMD fit instead of three; splitting the tiles over wave
+//    pairs measured slower (each pair re-reads the K/V step and has half
+//    the unique bytes in flight), and so did a second V buffer issued one
+//    phase earlier.
 //  - K rows (token-major pages) are the A operand loaded straight from HBM,
 //    16 bytes per lane.  The 32 keys of a step are dealt to the two 16-row
 //    score tiles so that each lane's eight scores are eight consecutive keys
 //    of one page (tile 0 row 4a+r is key 8a+r, tile 1 row 4a+r is key
 //    8a+4+r); with V pages dim-major and in fp16, the PV product
-//    O^T[d][head] = V^T[d][key] . P^T[key][head] then reads each lane's V
+//    O^T[d][col] = V^T[d][key] . P^T[key][col] then reads each lane's V
 //    fragment as 16 contiguous bytes and needs no conversion.  P enters the
 //    PV MFMA as fp16, keeping the weights to 11 significant bits.
+//  - Each column has its own causal (and window) limit: row r of a sequence
+//    with n rows sits at position L - n + r.
 //  - Online softmax in fp32 in the log2 domain (exp2 of prescaled scores).
 //  - Wave w takes 32-key steps w, w+4, ...; the four partial states merge
 //    through LDS in a fixed order, so results depend only on logical key
@@ -37,13 +49,16 @@ namespace {
 
 constexpr int kDecWaves = 4;
 
-template <int D, int KIND, int G>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 4)))
-decode_kernel(AttnParams p) {
-  constexpr int NB = D / 16;  // 16-row d blocks of O^T
-  constexpr int NC = D / 32;  // 32-wide d chunks of the QK reduction
-  __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][G][D];
-  __shared__ float red_ml[kDecWaves][G][2];
+template <int D, int KIND, int G, int QN>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnParams p) {
+  constexpr int NB = D / 16;                  // 16-row d blocks of O^T
+  constexpr int NC = D / 32;                  // 32-wide d chunks of the QK reduction
+  constexpr int NCOL = G * QN;                // (row, head) columns
+  constexpr int NT = (NCOL + 15) / 16;        // 16-column tiles
+  constexpr int CT = NCOL < 16 ? NCOL : 16;   // columns used per tile
+  __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][CT][D];
+  __shared__ float red_ml[kDecWaves][CT][2];
 
   // KV head fastest in the grid: workgroups running at the same time then
   // read all KV heads' slices of the pages, which spreads their traffic over
@@ -54,38 +69,53 @@ decode_kernel(AttnParams p) {
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
   const int L = p.t.seq_len[sid];
+  const int row0 = p.cu_q ? p.cu_q[i] : i;
+  const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;  // rows: positions L-n .. L-1
+  if (n <= 0 || n > L) return;
+  const int nr = min(n, QN);                         // rows computed here
   int klo, khi;  // keys [klo, khi) of this workgroup
   if (KIND == 0) {
     klo = split * p.split_len;
     khi = min(L, klo + p.split_len);
   } else {
-    klo = max(0, L - p.window);
+    klo = max(0, L - n - p.window + 1);  // window start of the first row
     khi = L;
   }
   if (klo >= khi) return;  // whole workgroup idle: no barrier reached
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;  // query head within the group (N index)
+  const int col = lane & 15;  // column within a tile (N index)
   const int q4 = lane >> 4;   // which 8-wide k slice / 4-row group
   const int hq = p.hq;
   const int hkv = p.hkv;
+  const int W = p.window;
 
-  // Q^T fragments: lane holds Q[head col][32c + 8*q4 .. +8]
-  bf16x8 qf[NC];
-  {
-    const bool has = col < G;
-    const uint16_t* qrow = p.q + ((int64_t)i * hq + kvh * G + (has ? col : 0)) * D;
+  // Per column tile t: this lane's column 16t + col is (row, head) =
+  // ((16t + col) / G, (16t + col) % G); its query position and whether it
+  // is a real pair.
+  int cpos[NT];
+  bool con[NT];
+  bf16x8 qf[NT][NC];  // Q^T fragments: lane holds Q[col][32c + 8*q4 .. +8]
+  for (int t = 0; t < NT; ++t) {
+    const int gc = 16 * t + col;
+    const int r = gc / G;
+    con[t] = col < CT && r < nr;
+    cpos[t] = L - n + r;
+    const uint16_t* qrow = p.q + ((int64_t)(row0 + (con[t] ? r : 0)) * hq + kvh * G + gc % G) * D;
     for (int c = 0; c < NC; ++c) {
-      u32x4 w = has ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
-      qf[c] = __builtin_bit_cast(bf16x8, w);
+      u32x4 w = con[t] ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
+      qf[t][c] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
-  f32x4 o[NB];
-  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
-  float lsum = 0.f;
+  f32x4 o[NT][NB];
+  float m[NT], lsum[NT];
+  for (int t = 0; t < NT; ++t) {
+    for (int nb = 0; nb < NB; ++nb) o[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[t] = -INFINITY;
+    lsum[t] = 0.f;
+  }
   const float sl2 = p.scale_log2;
 
   const int s0 = (klo / 32) * 32;
@@ -102,7 +132,7 @@ decode_kernel(AttnParams p) {
     const int idx = KIND == 0 ? pos / kPage : (pos % p.t.ring_slots) / kPage;
     return ptab[__builtin_amdgcn_readfirstlane(idx)];
   };
-  // K: this lane's row `col` of score tile t is key 8*(col/4) + 4t + col%4,
+  // K: this lane's row `col` of score tile kt is key 8*(col/4) + 4kt + col%4,
   // on page col/8.  V: keys 8*q4 .. +8 are page q4/2, offset 8*(q4%2).
   const int kpage = col >> 3;
   const int krow0 = (8 * (col >> 2) + (col & 3)) & 15;
@@ -140,56 +170,67 @@ decode_kernel(AttnParams p) {
     const uint16_t *kbn = kb, *vbn = vb;
     if (more) step_pages(kp0 + 32 * kDecWaves, kbn, vbn);
 
-    // S^T for the two 16-key tiles, then refill K
-    f32x4 s[2];
-    for (int t = 0; t < 2; ++t) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int c = 0; c < NC; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[t][c]), qf[c],
-                                                      acc, 0, 0, 0);
-      s[t] = acc;
-    }
+    // S^T for the two 16-key tiles of every column tile, then refill K
+    f32x4 s[NT][2];
+    for (int t = 0; t < NT; ++t)
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < NC; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kt][c]),
+                                                        qf[t][c], acc, 0, 0, 0);
+        s[t][kt] = acc;
+      }
     if (more)
       for (int c = 0; c < NC; ++c) {
         kr[0][c] = *(const u32x4*)(kbn + 32 * c);
         kr[1][c] = *(const u32x4*)(kbn + 4 * D + 32 * c);
       }
-    // mask: lane value (t, r) is key kp0 + 8*q4 + 4t + r
+    // lane value (kt, r) is key kp0 + 8*q4 + 4kt + r.  Keys outside the
+    // workgroup's range have their V zeroed (their slots may hold stale or
+    // unwritten data); keys inside it but past a column's own position (or
+    // before its window) only get a zero weight.
     unsigned valid = 0;
-    float mx = -INFINITY;
-    float sv[8];
-    for (int t = 0; t < 2; ++t)
-      for (int r = 0; r < 4; ++r) {
-        const int kp = kp0 + 8 * q4 + 4 * t + r;
-        const bool ok = kp >= klo && kp < khi;
-        valid |= (unsigned)ok << (4 * t + r);
-        const float x = ok ? s[t][r] * sl2 : -INFINITY;
-        sv[4 * t + r] = x;
+    for (int j = 0; j < 8; ++j) {
+      const int kp = kp0 + 8 * q4 + j;
+      valid |= (unsigned)(kp >= klo && kp < khi) << j;
+    }
+    f16x8 pf[NT];
+    float alpha[NT];
+    for (int t = 0; t < NT; ++t) {
+      float mx = -INFINITY;
+      float sv[8];
+      for (int j = 0; j < 8; ++j) {
+        const int kp = kp0 + 8 * q4 + j;
+        bool ok = (valid >> j) & 1u;
+        if (QN > 1) ok = ok && kp <= cpos[t] && (KIND == 0 || kp > cpos[t] - W);
+        const float x = ok ? s[t][j >> 2][j & 3] * sl2 : -INFINITY;
+        sv[j] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, xor_lane(mx, 16));
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    f16x8 pf;
-    float ps = 0.f;
-    for (int j = 0; j < 8; ++j) {
-      pf[j] = (_Float16)fast_exp2(sv[j] - m_use);
-      ps += (float)pf[j];  // sum the fp16 weights the PV product uses
+      mx = fmaxf(mx, xor_lane(mx, 16));
+      mx = fmaxf(mx, xor_lane(mx, 32));
+      const float m_new = fmaxf(m[t], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      alpha[t] = fast_exp2(m[t] - m_use);
+      float ps = 0.f;
+      for (int j = 0; j < 8; ++j) {
+        pf[t][j] = (_Float16)fast_exp2(sv[j] - m_use);
+        ps += (float)pf[t][j];  // sum the fp16 weights the PV product uses
+      }
+      lsum[t] = lsum[t] * alpha[t] + ps;
+      m[t] = m_new;
     }
-    lsum = lsum * alpha + ps;
-    m = m_new;
     u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
     if (valid != 0xffu) {
-      // zero V of masked keys: their slots may hold stale or unwritten data
       for (int j = 0; j < 8; ++j)
         if (!((valid >> j) & 1u)) vmask[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
     }
     for (int nb = 0; nb < NB; ++nb) {
       const f16x8 vf = __builtin_bit_cast(f16x8, vr[nb] & vmask);
-      o[nb] *= alpha;
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[nb], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) {
+        o[t][nb] *= alpha[t];
+        o[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[t], o[t][nb], 0, 0, 0);
+      }
     }
     // refill V
     if (more)
@@ -198,60 +239,75 @@ decode_kernel(AttnParams p) {
     vb = vbn;
   }
 
-  // merge the four waves' states (fixed order)
-  lsum += xor_lane(lsum, 16);
-  lsum += xor_lane(lsum, 32);
-  if (col < G) {
-    for (int nb = 0; nb < NB; ++nb)
-      *(f32x4*)(&red_o[wave][col][16 * nb + 4 * q4]) = o[nb];
-    if (q4 == 0) {
-      red_ml[wave][col][0] = m;
-      red_ml[wave][col][1] = lsum;
-    }
-  }
-  __syncthreads();
+  // merge the four waves' states (fixed order), one column tile at a time
   const int hq_base = kvh * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int c = idx / D;
-    const int d = idx % D;
-    float M = -INFINITY;
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_ml[w][c][0]);
-    float num = 0.f, den = 0.f;
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float mw = red_ml[w][c][0];
-      const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-      num += sc * red_o[w][c][d];
-      den += sc * red_ml[w][c][1];
+  for (int t = 0; t < NT; ++t) {
+    float ls = lsum[t];
+    ls += xor_lane(ls, 16);
+    ls += xor_lane(ls, 32);
+    if (t > 0) __syncthreads();  // the previous tile's merge has read LDS
+    if (col < CT) {
+      for (int nb = 0; nb < NB; ++nb)
+        *(f32x4*)(&red_o[wave][col][16 * nb + 4 * q4]) = o[t][nb];
+      if (q4 == 0) {
+        red_ml[wave][col][0] = m[t];
+        red_ml[wave][col][1] = ls;
+      }
     }
-    const int64_t hrow = (int64_t)i * hq + hq_base + c;
-    if (p.n_splits == 1) {
-      p.out[hrow * D + d] = num / den;
-    } else {
-      const int64_t slot = hrow * p.n_splits + split;
-      p.ws[slot * D + d] = num;
-      if (d == 0) {
-        float* ml = p.ws + (int64_t)p.num_seqs * hq * p.n_splits * D;
-        ml[2 * slot] = M;
-        ml[2 * slot + 1] = den;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < CT * D; idx += blockDim.x) {
+      const int c = idx / D;
+      const int d = idx % D;
+      const int g = 16 * t + c;
+      const int r = g / G;
+      if (r >= nr) continue;
+      float M = -INFINITY;
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_ml[w][c][0]);
+      float num = 0.f, den = 0.f;
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float mw = red_ml[w][c][0];
+        const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+        num += sc * red_o[w][c][d];
+        den += sc * red_ml[w][c][1];
+      }
+      const int64_t hrow = (int64_t)(row0 + r) * hq + hq_base + g % G;
+      if (p.n_splits == 1) {
+        p.out[hrow * D + d] = num / den;
+      } else {
+        const int64_t slot = hrow * p.n_splits + split;
+        p.ws[slot * D + d] = num;
+        if (d == 0) {
+          float* ml = p.ws + (int64_t)p.total_q * hq * p.n_splits * D;
+          ml[2 * slot] = M;
+          ml[2 * slot + 1] = den;
+        }
       }
     }
   }
-  if (p.vlen && split == 0 && kvh == 0 && threadIdx.x == 0)
-    p.vlen[i] = KIND == 0 ? L : min(L, p.window);
+  if (p.vlen && split == 0 && kvh == 0 && (int)threadIdx.x < nr) {
+    const int pos = L - n + threadIdx.x;
+    p.vlen[row0 + threadIdx.x] = KIND == 0 ? pos + 1 : min(pos + 1, W);
+  }
 }
 
-// Log-sum-exp merge of the split partial states of one (sequence, head).
+// Log-sum-exp merge of the split partial states of one (query row, head).
+// Block x = (sequence, row within the sequence), y = query head.  A split
+// whose keys all lie past the row's position holds max = -inf and weight 0.
 template <int D>
-__global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p) {
-  const int i = blockIdx.x;
+__global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, int qn) {
+  const int i = blockIdx.x / qn;
+  const int r = blockIdx.x % qn;
   const int h = blockIdx.y;
   const int d = threadIdx.x;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
   const int L = p.t.seq_len[sid];
+  const int row0 = p.cu_q ? p.cu_q[i] : i;
+  const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
+  if (n <= 0 || n > L || r >= n) return;
   const int ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
-  const int64_t hrow = (int64_t)i * p.hq + h;
-  const float* ml = p.ws + (int64_t)p.num_seqs * p.hq * p.n_splits * D;
+  const int64_t hrow = (int64_t)(row0 + r) * p.hq + h;
+  const float* ml = p.ws + (int64_t)p.total_q * p.hq * p.n_splits * D;
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * (hrow * p.n_splits + s)]);
   float num = 0.f, den = 0.f;
@@ -264,20 +320,28 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p) {
   p.out[hrow * D + d] = num / den;
 }
 
-template <int D, int KIND>
-hipError_t launch_decode_g(const AttnParams& p, hipStream_t s) {
+template <int D, int KIND, int QN>
+hipError_t launch_decode_q(const AttnParams& p, hipStream_t s) {
   dim3 grid((unsigned)(p.num_seqs * p.n_splits * p.hkv), 1);
-  const int g = p.hq / p.hkv;
-  switch (g) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, KIND, 1>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, KIND, 2>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, KIND, 4>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, KIND, 8>), grid, dim3(256), 0, s, p); break;
+  switch (p.hq / p.hkv) {
+    case 1: hipLaunchKernelGGL((decode_kernel<D, KIND, 1, QN>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, KIND, 2, QN>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, KIND, 4, QN>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, KIND, 8, QN>), grid, dim3(256), 0, s, p); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.num_seqs, p.hq), dim3(D), 0, s, p);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.num_seqs * QN, p.hq), dim3(D), 0, s, p,
+                     QN);
   return hipGetLastError();
+}
+
+// Rows per sequence: 1 (plain decode), up to 2, up to 4.
+template <int D, int KIND>
+hipError_t launch_decode_g(const AttnParams& p, hipStream_t s) {
+  if (p.max_q_len <= 1) return launch_decode_q<D, KIND, 1>(p, s);
+  if (p.max_q_len == 2) return launch_decode_q<D, KIND, 2>(p, s);
+  return launch_decode_q<D, KIND, 4>(p, s);
 }
 
 }  // namespace

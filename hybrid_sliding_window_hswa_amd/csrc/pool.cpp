@@ -114,6 +114,11 @@ struct hswa_pool {
     freeq[(fhead + fcount) % num_pages] = p;
     ++fcount;
   }
+  void push_page_front(int32_t p) {
+    fhead = (fhead + num_pages - 1) % num_pages;
+    freeq[fhead] = p;
+    ++fcount;
+  }
   int32_t full_slot(int32_t b, int32_t pos) const {
     return fpt[(size_t)b * max_pages + pos / kPage] * kPage + pos % kPage;
   }
@@ -557,6 +562,55 @@ int hswa_pool_release(hswa_pool* p, int32_t n, const int32_t* ids, void* stream)
     p->npages[b] = 0;
     p->len[b] = 0;
     p->res_start[b] = 0;
+  }
+  return flush(p, rb, stream);
+}
+
+int hswa_pool_truncate(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* new_len,
+                       void* stream) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  int rc = check_ids(p, n, ids);
+  if (rc) return rc;
+  if (n > 0 && !new_len) {
+    hswa::set_error("new_len is NULL");
+    return HSWA_E_INVAL;
+  }
+  // every check before any change
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = ids[i];
+    const int32_t k = new_len[i];
+    if (k < 0 || k > p->len[b]) {
+      hswa::set_error("new_len[%d] = %d outside [0, %d] (sequence %d)", i, k, p->len[b], b);
+      return HSWA_E_INVAL;
+    }
+    if (p->res_start[b] > std::max(0, k - p->W + 1)) {
+      hswa::set_error("sequence %d: positions from %d are resident, the window of length %d "
+                      "starts at %d (truncate before evicting)",
+                      b, p->res_start[b], k, std::max(0, k - p->W + 1));
+      return HSWA_E_INVAL;
+    }
+  }
+  RecBuilder rb;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = ids[i];
+    const int32_t k = new_len[i];
+    const int32_t L = p->len[b];
+    if (k == L) continue;
+    int32_t* row = &p->fpt[(size_t)b * p->max_pages];
+    for (int32_t pos = k; pos < L; ++pos) p->map[p->full_slot(b, pos)] = -1;
+    const int32_t keep = (int32_t)ceil_div(k, kPage);
+    // the record copies the page ids of the cleared range before they go
+    if (p->has_dev) rb.add(p, b, k, k, L, 0, 0, keep, p->npages[b], 1, row);
+    for (int32_t lp = p->npages[b] - 1; lp >= keep; --lp) {
+      p->push_page_front(row[lp]);
+      row[lp] = -1;
+    }
+    p->npages[b] = keep;
+    p->len[b] = k;
   }
   return flush(p, rb, stream);
 }

@@ -187,6 +187,20 @@ int hswa_pool_import(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
 int hswa_pool_release(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
                       void* stream);
 
+/* Cuts sequence seq_ids[i] back to new_len[i] positions, e.g. the draft
+ * tokens a multi-token verification step rejected ([MiMo] 5.2 runs three
+ * MTP layers, so a step appends one token plus up to three drafts).
+ * Positions >= new_len lose their SWA entry (map = -1); Full pages that no
+ * longer hold a position go back to the HEAD of the free list, lowest
+ * logical page first, so the next alloc takes them again.  The window of
+ * the new length must still be resident, so call it before the step's
+ * hswa_pool_evict.  HSWA_E_INVAL, with nothing changed, if any new_len is
+ * outside [0, seq_len] or below the resident window
+ * (resident start > max(0, new_len - W + 1)).  Host arrays of n_seqs
+ * entries; device tables updated on `stream`. */
+int hswa_pool_truncate(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
+                       const int32_t* new_len, void* stream);
+
 /* Host copies of the pool's metadata for inspection (each pointer nullable):
  * seq_len [max_seqs], fpt [max_seqs*max_pages_per_seq], map
  * [num_full_pages*16], free_pages [num_full_pages] (free list head first)
@@ -208,11 +222,13 @@ typedef struct hswa_attn_args {
   int32_t num_seqs;         /* sequences in this call                       */
   const int32_t* seq_ids;   /* device [num_seqs], distinct pool sequence ids */
   const int32_t* cu_q;      /* device [num_seqs+1], row offsets of each
-                               sequence's query rows (prefill only)         */
-  int32_t total_q;          /* rows of q / out (prefill: cu_q[num_seqs];
-                               decode: num_seqs)                            */
-  int32_t max_q_len;        /* prefill: max rows of one sequence (host hint
-                               sizing the grid; must be >= the true max)     */
+                               sequence's query rows; required by prefill,
+                               optional for decode (NULL: one row each)     */
+  int32_t total_q;          /* rows of q / out (= cu_q[num_seqs]; decode
+                               without cu_q: num_seqs)                      */
+  int32_t max_q_len;        /* max rows of one sequence (host hint sizing
+                               the grid; must be >= the true max).  Decode
+                               with cu_q: 1..4                               */
   int32_t max_seq_len;      /* decode: >= every listed sequence's length     */
   const void* q;            /* device bf16 [total_q][Hq][head_dim]          */
   const void* k_new;        /* device bf16 [total_q][Hkv][head_dim] or NULL  */
@@ -237,12 +253,21 @@ typedef struct hswa_attn_args {
  * the chunk after evicting the previous one.  Output fp32. */
 int hswa_prefill_chunk(const hswa_attn_args* args, void* stream);
 
-/* Decode step of one layer ([MiMo] 1.2): one query row per listed
- * sequence at position seq_len - 1 (cu_q is ignored).  Appends k_new/v_new
- * when set, then attends; FULL layers split the context across workgroups
- * and merge the parts (log-sum-exp) in a second kernel.  `workspace` is a
- * caller-owned device buffer of at least hswa_decode_workspace_bytes(args)
- * bytes (may be NULL when that is 0); HSWA_E_INVAL if it is smaller. */
+/* Decode step of one layer ([MiMo] 1.2).  Without cu_q: one query row per
+ * listed sequence, at position seq_len - 1.  With cu_q: sequence i has
+ * n_i = cu_q[i+1] - cu_q[i] rows, 1 <= n_i <= max_q_len <= 4, its last n_i
+ * positions (one new token plus the drafts of a multi-token verification
+ * step; [MiMo] 5.2 runs three MTP layers), each row attending causally to
+ * its own keys (SWA: the W keys ending at its position); all rows of a
+ * sequence share every K/V byte read.  A SWA ring must then hold
+ * W - 1 + n_i slots.  max_q_len > 4 is HSWA_E_UNSUPPORTED.  Appends
+ * k_new/v_new when set, then attends; FULL layers split the context across
+ * workgroups and merge the parts (log-sum-exp) in a second kernel.
+ * `workspace` is a caller-owned device buffer of at least
+ * hswa_decode_workspace_bytes(args) bytes (may be NULL when that is 0;
+ * the size depends on kind, window, num_seqs, max(total_q, num_seqs), the
+ * head counts, head_dim and max_seq_len, and no memory is read);
+ * HSWA_E_INVAL if it is smaller. */
 int hswa_decode(const hswa_attn_args* args, void* workspace, size_t ws_bytes,
                 void* stream);
 size_t hswa_decode_workspace_bytes(const hswa_attn_args* args);

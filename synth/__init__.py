@@ -25,6 +25,7 @@ except ImportError:  # pragma: no cover - torch is present in this image
 # a stream.
 ROLE_Q, ROLE_K, ROLE_V = 1, 2, 3
 ROLE_LEN, ROLE_PERM, ROLE_RING = 11, 12, 13
+ROLE_ACCEPT = 14
 
 
 def _mix(*parts: int) -> int:
@@ -81,6 +82,13 @@ def permutation(n: int, *seed_parts: int) -> np.ndarray:
     """A uniform random permutation of 0..n-1 as int32."""
     rng = np.random.default_rng(seed_for(ROLE_PERM, *seed_parts))
     return rng.permutation(n).astype(np.int32)
+
+
+def uniform_ints(n: int, lo: int, hi: int, *seed_parts: int) -> List[int]:
+    """n integers uniform on [lo, hi] from their own stream (e.g. how many
+    draft tokens of a step are accepted)."""
+    rng = np.random.default_rng(seed_for(ROLE_ACCEPT, *seed_parts))
+    return [int(x) for x in rng.integers(lo, hi + 1, size=n)]
 
 
 def sample_indices(n: int, k: int, *seed_parts: int) -> List[int]:
@@ -150,10 +158,24 @@ class LongDecode(Workload):
     ring_slots: int = 128 + 256
 
 
+@dataclasses.dataclass(frozen=True)
+class MtpDecode(Workload):
+    """Multi-token decode: each step verifies one token plus draft tokens
+    (three MTP layers give three drafts) over one Full and one SWA layer,
+    then keeps the accepted prefix."""
+    num_seqs: int = 256
+    ctx_lo: int = 4096
+    ctx_hi: int = 32768
+    drafts: int = 3
+    ring_slots: int = 128 + 16
+
+
 C1 = SwaSingleChunk("swa_single_chunk_1x1024_h8kv2_d64", 8, 2, 64, 128, seed=100)
 C2 = SwaChunkedPrefill("swa_chunked_prefill_8seq_2k-16k_h64kv8_d128", 64, 8, 128, 128, seed=200)
 C3 = MixedDecode("mixed_decode_256seq_4k-32k_full+swa_h64kv8_d128", 64, 8, 128, 128, seed=300)
 C4 = HybridStack("hybrid_stack_70L_64k_chunk4k_h64kv8_d128", 64, 8, 128, 128, seed=400)
 C5 = LongDecode("long_decode_64seq_128k-256k_14L_h64kv8_d128", 64, 8, 128, 128, seed=500)
 
-WORKLOADS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
+MTP = MtpDecode("mtp_decode_256seq_4k-32k_q4_full+swa_h64kv8_d128", 64, 8, 128, 128, seed=600)
+
+WORKLOADS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "MTP": MTP}

@@ -64,8 +64,19 @@ def test_golden_fixtures_through_the_abi():
             elif op["op"] == "evict":
                 ev, cnt = H.hswa_pool_evict(p, op["seq_ids"])
                 assert ev.tolist() == op["evicted"] and cnt.tolist() == op["counts"]
-            else:
+            elif op["op"] == "truncate":
+                if op.get("invalid"):
+                    before = _tables(p)
+                    with pytest.raises(H.HswaError) as e:
+                        H.hswa_pool_truncate(p, op["seq_ids"], op["new_len"])
+                    assert e.value.status == H.HSWA_E_INVAL
+                    assert _tables(p) == before
+                else:
+                    H.hswa_pool_truncate(p, op["seq_ids"], op["new_len"])
+            elif op["op"] == "release":
                 H.hswa_pool_release(p, op["seq_ids"])
+            else:
+                raise AssertionError(f"unknown fixture op {op['op']}")
         seq_len, fpt, mp, free = _tables(p)
         f = sc["final"]
         assert seq_len == f["seq_len"] and fpt == f["fpt"] and free == f["free"]
@@ -108,6 +119,18 @@ def test_random_operations_bit_exact_vs_oracle(seed):
             exp = sim.evict(ids)
             ev, cnt = H.hswa_pool_evict(p, ids)
             assert ev.tolist() == exp[0] and cnt.tolist() == exp[1]
+        elif r < 0.95:
+            lens = [max(0, sim.length[i] - rnd.choice([0, 1, 2, 3, 17, W + 1])) for i in ids]
+            try:
+                sim.truncate(ids, lens)
+            except ValueError:
+                before = _tables(p)
+                with pytest.raises(H.HswaError) as e:
+                    H.hswa_pool_truncate(p, ids, lens)
+                assert e.value.status == H.HSWA_E_INVAL
+                assert _tables(p) == before
+                continue
+            H.hswa_pool_truncate(p, ids, lens)
         else:
             sim.release(ids)
             H.hswa_pool_release(p, ids)
@@ -204,6 +227,46 @@ def test_decode_validation_and_workspace():
     # SWA layers never need one
     a = _args(kind=1, n=4, total_q=4)
     assert lib.hswa_decode_workspace_bytes(C.byref(a)) == 0
+
+
+def test_multi_row_decode_validation_and_workspace():
+    lib = _capi.load()
+    # more than four rows per sequence is outside what is built
+    a = _args(n=2, total_q=10, max_q_len=5)
+    assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_UNSUPPORTED
+    # rows must fit num_seqs * max_q_len; max_q_len >= 1
+    a = _args(n=2, total_q=9, max_q_len=4)
+    assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
+    a = _args(n=2, total_q=2, max_q_len=0)
+    assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
+    # the split-K workspace holds one partial state per (row, head, split)
+    one = _args(kind=0, n=4, total_q=4, hq=64, hkv=8, d=128, max_seq_len=100000)
+    four = _args(kind=0, n=4, total_q=16, max_q_len=4, hq=64, hkv=8, d=128,
+                 max_seq_len=100000)
+    b1 = lib.hswa_decode_workspace_bytes(C.byref(one))
+    b4 = lib.hswa_decode_workspace_bytes(C.byref(four))
+    assert b1 > 0 and b4 == 4 * b1
+    assert H.hswa_decode_workspace_bytes(0, 128, 4, 64, 8, 128, 100000, total_q=16) == b4
+    assert H.hswa_decode_workspace_bytes(0, 128, 4, 64, 8, 128, 100000) == b1
+
+
+def test_truncate_validation():
+    p = _host_pool(8, 32, 2, 4, 8, list(range(8)), [0, 1, 2, 3])
+    H.hswa_pool_alloc(p, [0, 1], [20, 3])
+    H.hswa_pool_evict(p, [0, 1])          # seq 0 keeps positions 13..19
+    before = _tables(p)
+    for ids, lens in (([0], [21]), ([0], [-1]), ([0], [19]), ([0, 1], [20, 4]),
+                      ([0, 0], [20, 20]), ([2], [0])):
+        with pytest.raises(H.HswaError) as e:
+            H.hswa_pool_truncate(p, ids, lens)
+        assert e.value.status == H.HSWA_E_INVAL
+        assert _tables(p) == before
+    page1 = before[1][1][0]                    # sequence 1's only Full page
+    H.hswa_pool_truncate(p, [0, 1], [20, 0])   # 20: no change; 0: page freed
+    seq_len, fpt, mp, free = _tables(p)
+    assert seq_len == [20, 0]
+    assert fpt[1] == [-1] * 4
+    assert free[0] == page1 and len(free) == len(before[3]) + 1
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

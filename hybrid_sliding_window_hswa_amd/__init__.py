@@ -31,7 +31,7 @@ __all__ = [
     "HswaError", "NoSpace", "FULL", "SWA", "PAGE_SIZE",
     "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view", "hswa_pool_alloc",
     "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_truncate",
-    "hswa_pool_read_tables",
+    "hswa_pool_match_len", "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
     "hswa_last_error", "hswa_version", "kv_cache_shapes", "kv_cache_alloc", "library",
 ]
@@ -215,6 +215,19 @@ def hswa_pool_truncate(pool: Pool, seq_ids: Sequence[int], new_len: Sequence[int
     if n.size != ids.size:
         raise ValueError("one new length per sequence")
     _check(library().hswa_pool_truncate(pool.handle, ids.size, _p(ids), _p(n), _stream(stream)))
+
+
+def hswa_pool_match_len(pool: Pool, seq_ids: Sequence[int], want: Sequence[int],
+                        tail: Optional[int] = None) -> np.ndarray:
+    """Window-safe match lengths; ``tail`` defaults to W - 1 (what the next
+    query needs)."""
+    ids, w = _i32(seq_ids), _i32(want)
+    if w.size != ids.size:
+        raise ValueError("one length per sequence")
+    t = pool.desc["window"] - 1 if tail is None else tail
+    out = np.empty(max(ids.size, 1), np.int32)
+    _check(library().hswa_pool_match_len(pool.handle, ids.size, _p(ids), _p(w), t, _p(out)))
+    return out[:ids.size]
 
 
 def hswa_pool_read_tables(pool: Pool) -> dict:

@@ -26,7 +26,7 @@ EXPORTED = (
     "hswa_last_error", "hswa_status_string", "hswa_version",
     "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view",
     "hswa_pool_alloc", "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release",
-    "hswa_pool_truncate", "hswa_pool_read_tables",
+    "hswa_pool_truncate", "hswa_pool_match_len", "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
 )
 
@@ -120,6 +120,8 @@ def load():
                                     C.c_void_p]
     lib.hswa_pool_release.restype = C.c_int
     lib.hswa_pool_release.argtypes = [C.c_void_p, C.c_int32, I32P, C.c_void_p]
+    lib.hswa_pool_match_len.restype = C.c_int
+    lib.hswa_pool_match_len.argtypes = [C.c_void_p, C.c_int32, I32P, I32P, C.c_int32, I32P]
     lib.hswa_pool_truncate.restype = C.c_int
     lib.hswa_pool_truncate.argtypes = [C.c_void_p, C.c_int32, I32P, I32P, C.c_void_p]
     lib.hswa_pool_read_tables.restype = C.c_int

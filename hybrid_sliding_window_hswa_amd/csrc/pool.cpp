@@ -615,6 +615,46 @@ int hswa_pool_truncate(hswa_pool* p, int32_t n, const int32_t* ids, const int32_
   return flush(p, rb, stream);
 }
 
+int hswa_pool_match_len(const hswa_pool* p, int32_t n, const int32_t* ids,
+                        const int32_t* want, int32_t tail, int32_t* out) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  if (n < 0 || (n > 0 && (!ids || !want || !out)) || tail < 0) {
+    hswa::set_error("match_len: bad arguments (n %d, tail %d)", n, tail);
+    return HSWA_E_INVAL;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= p->max_seqs || want[i] < 0) {
+      hswa::set_error("match_len: entry %d: sequence %d / length %d out of range", i, ids[i],
+                      want[i]);
+      return HSWA_E_INVAL;
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = ids[i];
+    int32_t k = std::min(want[i], p->len[b]);
+    // A position without an SWA entry at h rules out every end in
+    // (h, h + tail]; walk back from the match end to the first end whose
+    // tail window has no such position.
+    while (k > 0) {
+      int32_t hole = -1;
+      for (int32_t pos = k - 1; pos >= std::max(0, k - tail); --pos) {
+        if (p->map[p->full_slot(b, pos)] < 0) {
+          hole = pos;
+          break;
+        }
+      }
+      if (hole < 0) break;
+      k = hole;
+    }
+    out[i] = k;
+  }
+  return HSWA_OK;
+}
+
 int hswa_pool_read_tables(const hswa_pool* p, int32_t* seq_len, int32_t* fpt,
                           int32_t* map, int32_t* free_pages, int32_t* n_free) {
   hswa::clear_error();

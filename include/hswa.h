@@ -201,6 +201,17 @@ int hswa_pool_release(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
 int hswa_pool_truncate(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
                        const int32_t* new_len, void* stream);
 
+/* Window-safe prefix-match length ([MiMo] 2.1 "SWA-aware prefix cache
+ * tree", point 1): for each listed sequence, the longest m' <= min(want[i],
+ * seq_len) such that the last min(m', tail) positions before m' all still
+ * hold an SWA entry (map >= 0); the rest of a token match is a miss.  The
+ * query at m' attends to W keys counting itself, so tail = W - 1 is what this
+ * library's attention needs (and what eviction keeps); the page asks for
+ * tail = W.  Host arrays of n_seqs entries; out receives m'.  Reads the host
+ * metadata only.  HSWA_E_INVAL for a bad id, a negative want or tail. */
+int hswa_pool_match_len(const hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
+                        const int32_t* want, int32_t tail, int32_t* out);
+
 /* Host copies of the pool's metadata for inspection (each pointer nullable):
  * seq_len [max_seqs], fpt [max_seqs*max_pages_per_seq], map
  * [num_full_pages*16], free_pages [num_full_pages] (free list head first)

@@ -47,6 +47,13 @@ Readings taken where the pages leave a step open:
   Dropped positions lose their SWA entry; Full pages that no longer hold a
   position go back to the head of the free list, lowest logical page first,
   so the next allocation takes them again.
+* ``window_safe_len`` is the prefix-match rule of "SWA-aware prefix cache
+  tree", point 1: a match of m tokens is usable only as far as the last
+  ``tail`` tokens before its end still hold valid SWA slots (map >= 0); the
+  match is cut back to the longest such length, the rest is a miss.  The
+  page asks for W tail tokens.  The next query at position m' attends to
+  [m' - W + 1, m'], so this library's attention needs W - 1 of them, which
+  is also what eviction keeps; the caller chooses ``tail``.
 * -1 marks "no slot" in every table.
 """
 from __future__ import annotations
@@ -237,6 +244,18 @@ class PoolSim:
             self.pages[b] = self.pages[b][:keep]
             self.free.extendleft(reversed(freed))
             self.length[b] = n
+
+    def window_safe_len(self, b: int, m: int, tail: int) -> int:
+        """Longest m' <= min(m, length) whose last min(m', tail) positions all
+        have an SWA entry (0 if none)."""
+        if not 0 <= b < self.max_seqs:
+            raise ValueError("sequence id out of range")
+        if m < 0 or tail < 0:
+            raise ValueError("negative length")
+        for k in range(min(m, self.length[b]), 0, -1):
+            if all(self.full_slot(b, pos) in self.map for pos in range(max(0, k - tail), k)):
+                return k
+        return 0
 
     # -- table views (what the device tables must hold) ---------------------
     def seq_len_table(self) -> List[int]:

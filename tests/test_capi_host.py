@@ -75,6 +75,9 @@ def test_golden_fixtures_through_the_abi():
                     H.hswa_pool_truncate(p, op["seq_ids"], op["new_len"])
             elif op["op"] == "release":
                 H.hswa_pool_release(p, op["seq_ids"])
+            elif op["op"] == "match":
+                got = H.hswa_pool_match_len(p, [op["seq"]], [op["m"]], op["tail"])
+                assert got.tolist() == [op["expect"]], op
             else:
                 raise AssertionError(f"unknown fixture op {op['op']}")
         seq_len, fpt, mp, free = _tables(p)
@@ -134,6 +137,11 @@ def test_random_operations_bit_exact_vs_oracle(seed):
         else:
             sim.release(ids)
             H.hswa_pool_release(p, ids)
+        mids = list(range(S))
+        want = [rnd.randint(0, sim.length[i] + 5) for i in mids]
+        tail = rnd.choice([0, 1, W - 1, W, 2 * W])
+        assert H.hswa_pool_match_len(p, mids, want, tail).tolist() == \
+            [sim.window_safe_len(i, m, tail) for i, m in zip(mids, want)]
         seq_len, fpt, mp, fr = _tables(p)
         assert seq_len == sim.seq_len_table()
         assert fpt == sim.fpt_table()
@@ -274,3 +282,19 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_capi, "_lib", None)
     with pytest.raises(ImportError):
         _capi.load()
+
+
+def test_match_len_after_eviction_and_validation():
+    W = 128
+    p = _host_pool(W, 256, 2, 64, 128, list(range(128)), list(range(32)))
+    H.hswa_pool_alloc(p, [0, 1], [1000, 50])
+    H.hswa_pool_evict(p, [0, 1])
+    # eviction keeps W - 1 positions: the whole sequence is window safe for the
+    # next query, not under the page's stricter count of W
+    assert H.hswa_pool_match_len(p, [0, 1], [1000, 50]).tolist() == [1000, 50]
+    assert H.hswa_pool_match_len(p, [0, 1], [1000, 50], W).tolist() == [0, 50]
+    assert H.hswa_pool_match_len(p, [0], [999]).tolist() == [0]
+    for ids, want, tail in (([2], [1], 3), ([0], [-1], 3), ([0], [1], -1)):
+        with pytest.raises(H.HswaError) as e:
+            H.hswa_pool_match_len(p, ids, want, tail)
+        assert e.value.status == H.HSWA_E_INVAL

@@ -46,6 +46,8 @@ def _run_fixture(sc):
             assert ev == op["evicted"] and cnt == op["counts"], op
         elif op["op"] == "release":
             p.release(op["seq_ids"])
+        elif op["op"] == "match":
+            assert p.window_safe_len(op["seq"], op["m"], op["tail"]) == op["expect"], op
         elif op["op"] == "truncate":
             if op.get("invalid"):
                 before = _state(p)
@@ -152,6 +154,20 @@ class DictPool:
             self.free = [self.page_of[b].pop(lp) for lp in gone] + self.free
             self.n[b] = n
 
+    def match(self, b, m, tail):
+        # walk back from the end of the match to the first position that lost
+        # its SWA entry; the match may end no later than tail past it
+        k = min(m, self.n[b])
+        hole = -1
+        for p in range(k - 1, -1, -1):
+            if p not in self.alive[b]:
+                hole = p
+                break
+        while k > 0 and max(0, k - tail) <= hole:
+            k -= 1
+            hole = max((p for p in range(k) if p not in self.alive[b]), default=-1)
+        return k
+
     def map_table(self):
         t = [-1] * (self.npages * 16)
         for b in self.alive:
@@ -251,6 +267,9 @@ def test_random_operations_against_second_simulator(seed):
         assert a.map_table() == b.map_table()
         assert a.free_pages() == b.free
         _check_invariants(a, just_evicted)
+        for i in ids:
+            m, tail = rnd.randint(0, a.length[i] + 3), rnd.choice([0, 1, W - 1, W, W + 2])
+            assert a.window_safe_len(i, m, tail) == b.match(i, m, tail)
 
 
 def test_decode_steps_evict_one_token_each():

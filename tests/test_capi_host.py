@@ -287,7 +287,7 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
 def test_match_len_after_eviction_and_validation():
     W = 128
     p = _host_pool(W, 256, 2, 64, 128, list(range(128)), list(range(32)))
-    H.hswa_pool_alloc(p, [0, 1], [1000, 50])
+    H.hswa_pool_import(p, [0, 1], [1000, 50])   # a restored context: the tail resident
     H.hswa_pool_evict(p, [0, 1])
     # eviction keeps W - 1 positions: the whole sequence is window safe for the
     # next query, not under the page's stricter count of W

@@ -25,6 +25,8 @@ Modules:
 * ``pool``      -- the dual-pool slot bookkeeping (Full pages, SWA ring,
   Full-to-SWA map, eviction) as a plain Python simulator.
 * ``closed_forms`` -- scored-pair and resident-KV counts and their ratios.
+* ``transfer``  -- which positions a window-masked tier transfer moves and
+  the packed host image it produces.
 
 Every function in these modules is pinned by ``tests/test_oracle.py`` and
 ``tests/test_oracle_pool.py`` to something other than itself (library
@@ -32,4 +34,4 @@ routines, brute force, closed forms, hand-worked fixtures); the one
 quantity with no pin is listed as "parity unpinned" in ``closed_forms``.
 """
 
-from . import attention, closed_forms, pool  # noqa: F401
+from . import attention, closed_forms, pool, transfer  # noqa: F401

@@ -26,6 +26,17 @@ resident in HBM before the timed region starts):
   long_decode
       64 sequences, contexts uniform in [131072, 262144], 14 layers (6 SWA then
       1 Full, twice), SWA ring of W + 256 slots.  `value` = HBM GB/s.
+  mtp_decode
+      Multi-token decode: the mixed decode's 256 sequences with one token
+      plus three draft tokens per step (rows of a sequence share every K/V
+      byte read); the step keeps a seeded accepted prefix (truncate) before
+      evicting.  `value` = algorithmic HBM GB/s.
+  tier_transfer
+      Window-masked offload and restore of a 14-layer hybrid stack's KV
+      (16 sequences, contexts 4096-32768) through pinned host memory: SWA
+      layers move only their W-1-token windows.  `value` = restore GB/s over
+      PCIe; also offload GB/s and restore + first decode step, serial versus
+      pulled layer by layer on a second stream.
   swa_single_chunk
       One SWA layer, one 1024-token sequence (8 query / 2 KV heads, head_dim
       64) prefilled in one chunk, then 16 decode steps.  `value` = tok/s.
@@ -52,8 +63,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+PCIE_PEAK_GBS = 63.0           # PCIe 5.0 x16, one direction: 32 GT/s * 16 lanes * 128/130 / 8
 MFMA_BF16_PEAK_TFS = 2516.6    # 256 CU * 2.4 GHz * 4096 flop/clk (dense)
-PEAKS = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (MFMA_BF16_PEAK_TFS, "TFLOP/s")}
+PEAKS = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (MFMA_BF16_PEAK_TFS, "TFLOP/s"),
+         "pcie": (PCIE_PEAK_GBS, "GB/s")}
 METRIC = "Hybrid-SWA attn prefill tok/s + decode HBM GB/s (% of MI355X peak)"
 
 CSRC = os.path.join(ROOT, "hybrid_sliding_window_hswa_amd", "csrc")
@@ -268,7 +281,8 @@ class Decode:
     sequence (multi-token decode), then keeps a seeded accepted prefix
     (hswa_pool_truncate) before the eviction."""
 
-    def __init__(self, cx, ctxs, pattern, hq, hkv, d, W, ring, seed, steps_total, rows=1):
+    def __init__(self, cx, ctxs, pattern, hq, hkv, d, W, ring, seed, steps_total, rows=1,
+                 fill=True):
         torch, H = cx.torch, cx.H
         import synth
         self.cx, self.hq, self.hkv, self.d, self.W = cx, hq, hkv, d, W
@@ -294,7 +308,7 @@ class Decode:
             kc, vc = H.kv_cache_alloc(nfull if kind == "F" else B * ring // 16, hkv, d, cx.dev)
             # restore the context: generated per sequence on the device and
             # appended (Full: every position, SWA: the last W-1)
-            for b, c in enumerate(ctxs):
+            for b, c in (enumerate(ctxs) if fill else ()):
                 n = c if kind == "F" else min(c, W - 1)
                 kk = synth.bf16_normal((n, hkv, d), seed, li, b, synth.ROLE_K, device=cx.dev)
                 vv = synth.bf16_normal((n, hkv, d), seed, li, b, synth.ROLE_V, device=cx.dev)
@@ -321,6 +335,7 @@ class Decode:
                            self.view, self.q[li], self.kn[li], self.vn[li], kc, vc, self.out)
             self.args.append(a)
         self.lens = list(ctxs)
+        self.pattern = pattern
         self.nrows = _arr([rows] * B)
         self.step_no = 0
         self.step_bytes = []     # algorithmic bytes of every step run
@@ -594,6 +609,127 @@ def wl_mtp_decode(cx, args):
     return line
 
 
+def wl_tier_transfer(cx, args):
+    """Window-masked offload/restore of a 14-layer hybrid stack through pinned
+    host memory, and restore + first decode step, serial and pulled layer by
+    layer on a second stream."""
+    import synth
+    from hybrid_sliding_window_hswa_amd import _capi
+    torch, H, lib = cx.torch, cx.H, cx.lib
+    wl = synth.TIER
+    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
+    hq, hkv, d, W = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window
+    B, ids = len(ctxs), list(range(len(ctxs)))
+    src = Decode(cx, ctxs, wl.pattern, hq, hkv, d, W, wl.ring_slots, wl.seed, 8)
+    dst = Decode(cx, ctxs, wl.pattern, hq, hkv, d, W, wl.ring_slots, wl.seed + 1, 8, fill=False)
+    plan = {}
+    for kind in (H.FULL, H.SWA):
+        cnt = [int(x) for x in H.hswa_pool_window_counts(src.pool, kind, ids)]
+        plan[kind] = (cnt, cx.i32(np.concatenate([[0], np.cumsum(cnt)])),
+                      cx.i32([L - c for L, c in zip(ctxs, cnt)]))
+    bufs, a_off, a_res = [], [], []
+    for li, (kind, kc, vc) in enumerate(src.layers):
+        cnt, cu, first = plan[kind]
+        T = sum(cnt)
+        bk = torch.empty((T, hkv, d), dtype=torch.bfloat16, pin_memory=True)
+        bv = torch.empty((T, hkv, d), dtype=torch.float16, pin_memory=True)
+        bufs.append((bk, bv))
+        for dc, lst in ((src, a_off), (dst, a_res)):
+            a = _capi.XferArgs()
+            a.kind, a.num_kv_heads, a.head_dim, a.num_seqs = kind, hkv, d, B
+            a.seq_ids, a.cu_tok, a.first_pos = dc.sid.data_ptr(), cu.data_ptr(), first.data_ptr()
+            a.total_tok, a.max_tok = T, max(cnt)
+            a.pool = dc.view
+            a.k_cache, a.v_cache = dc.layers[li][1].data_ptr(), dc.layers[li][2].data_ptr()
+            a.buf_k, a.buf_v = bk.data_ptr(), bv.data_ptr()
+            lst.append(a)
+    kvb = KV_TOKEN_BYTES(hkv, d)
+    masked = sum(sum(plan[kind][0]) for kind, _, _ in src.layers) * kvb
+    unmasked = len(src.layers) * sum(ctxs) * kvb
+    swa_bytes = sum(sum(plan[kind][0]) for kind, _, _ in src.layers if kind == H.SWA) * kvb
+
+    def offload_all():
+        for a in a_off:
+            _check(cx, lib.hswa_kv_offload(C.byref(a), cx.sptr))
+
+    def restore_all(stream=None, events=None):
+        for a in a_res:
+            _check(cx, lib.hswa_kv_restore(C.byref(a), stream or cx.sptr))
+            if events is not None:
+                ev = torch.cuda.Event()
+                ev.record(events[0])
+                events[1].append(ev)
+
+    steps, warm = max(args.steps // 4, 3), 1
+    t_off = timed(cx, offload_all, steps, warm)
+    t_res = timed(cx, restore_all, steps, warm)
+    # one layer's restore, SWA and Full, for the per-kind link rate
+    per_kind = {}
+    for kind in (H.FULL, H.SWA):
+        li = [i for i, (k, _, _) in enumerate(src.layers) if k == kind][0]
+        t = timed(cx, lambda: _check(cx, lib.hswa_kv_restore(C.byref(a_res[li]), cx.sptr)),
+                  steps, warm)
+        per_kind[kind] = (sum(plan[kind][0]) * kvb, t)
+
+    # restore then the first decode step: serial on one stream, or pulled
+    # layer by layer on a second stream while the first computes
+    ids_a, idp = dst.ids
+    ctx_a = _arr(ctxs)
+    copy = torch.cuda.Stream()  # default priority
+    copy_ptr = C.c_void_p(copy.cuda_stream)
+
+    def reset():
+        _check(cx, lib.hswa_pool_release(dst.pool.handle, B, idp, cx.sptr))
+        _check(cx, lib.hswa_pool_import(dst.pool.handle, B, idp, ctx_a[1], None, None, cx.sptr))
+        dst.lens = list(ctxs)
+
+    def serial():
+        reset()
+        restore_all()
+        dst.step()
+
+    def pulled():
+        reset()
+        ready = torch.cuda.Event()
+        ready.record(cx.stream)
+        copy.wait_event(ready)
+        evs = []
+        restore_all(copy_ptr, (copy, evs))
+        h = dst.pool.handle
+        _, onep = dst.nrows
+        _check(cx, lib.hswa_pool_alloc(h, B, idp, onep, None, None, cx.sptr))
+        dst.lens = [x + 1 for x in dst.lens]
+        for a, ev in zip(dst.args, evs):
+            cx.stream.wait_event(ev)
+            _check(cx, lib.hswa_decode(C.byref(a), C.c_void_p(dst.ws.data_ptr()), dst.nbytes_ws,
+                                       cx.sptr))
+        _check(cx, lib.hswa_pool_evict(h, B, idp, None, 0, None, cx.sptr))
+
+    t_ser = timed(cx, serial, steps, warm)
+    t_pull = timed(cx, pulled, steps, warm)
+    torch.cuda.synchronize()
+    res_gbs = masked / t_res / 1e9
+    config = {"workload": "tier_transfer", "num_seqs": B, "ctx_range": [wl.ctx_lo, wl.ctx_hi],
+              "layers": len(wl.pattern), "pattern": "6 SWA then 1 Full, x2",
+              "num_kv_heads": hkv, "head_dim": d, "window": W, "host_buffers": "pinned",
+              "seed": wl.seed}
+    line = base_line(args, round(res_gbs, 2), "GB/s", t_res * 1e3, config,
+                     roofline("pcie", res_gbs, None))
+    line["steps"] = steps
+    line["offload_gbs"] = round(masked / t_off / 1e9, 2)
+    line["offload_ms"] = round(t_off * 1e3, 3)
+    line["restore_full_layer_gbs"] = round(per_kind[H.FULL][0] / per_kind[H.FULL][1] / 1e9, 2)
+    line["restore_swa_layer_gbs"] = round(per_kind[H.SWA][0] / per_kind[H.SWA][1] / 1e9, 2)
+    line["restore_swa_layer_us"] = round(per_kind[H.SWA][1] * 1e6, 1)
+    line["bytes_masked"] = masked
+    line["bytes_unmasked"] = unmasked
+    line["mask_fraction"] = round(masked / unmasked, 5)
+    line["swa_share_of_masked_bytes"] = round(swa_bytes / masked, 5)
+    line["restore_then_step_ms"] = round(t_ser * 1e3, 3)
+    line["pulled_layerwise_ms"] = round(t_pull * 1e3, 3)
+    return line
+
+
 def wl_hybrid_stack(cx, args):
     import synth
     H = cx.H
@@ -690,6 +826,7 @@ WORKLOADS = {
     "swa_chunked_prefill": wl_swa_chunked_prefill,
     "mixed_decode": wl_mixed_decode,
     "mtp_decode": wl_mtp_decode,
+    "tier_transfer": wl_tier_transfer,
     "hybrid_stack": wl_hybrid_stack,
     "long_decode": wl_long_decode,
     "swa_single_chunk": wl_swa_single_chunk,

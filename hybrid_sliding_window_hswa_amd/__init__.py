@@ -33,6 +33,7 @@ __all__ = [
     "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_truncate",
     "hswa_pool_match_len", "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
+    "hswa_pool_window_counts", "hswa_kv_offload", "hswa_kv_restore",
     "hswa_last_error", "hswa_version", "kv_cache_shapes", "kv_cache_alloc", "library",
 ]
 
@@ -337,3 +338,54 @@ def hswa_append_kv(kind: int, k_new, v_new, seq_ids, view, k_cache, v_cache, cu_
               k_cache, v_cache, None, None, 0.0)
     a.num_q_heads = k_new.shape[1]
     _check(library().hswa_append_kv(C.byref(a), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Window-masked tier transfer
+
+
+def hswa_pool_window_counts(pool: Pool, kind: int, seq_ids: Sequence[int]) -> np.ndarray:
+    """Tokens a window-masked transfer moves per sequence (FULL: the length,
+    SWA: min(length, W - 1))."""
+    ids = _i32(seq_ids)
+    out = np.empty(max(ids.size, 1), np.int32)
+    _check(library().hswa_pool_window_counts(pool.handle, kind, ids.size, _p(ids), _p(out)))
+    return out[:ids.size]
+
+
+def _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache, buf_k, buf_v,
+               first_pos):
+    a = _capi.XferArgs()
+    a.kind = kind
+    a.num_kv_heads = k_cache.shape[1]
+    a.head_dim = k_cache.shape[-1]
+    a.num_seqs = seq_ids.shape[0]
+    a.seq_ids = _dptr(seq_ids)
+    a.cu_tok = _dptr(cu_tok)
+    a.first_pos = _dptr(first_pos)
+    a.total_tok = total_tok
+    a.max_tok = max_tok
+    a.pool = view
+    a.k_cache = _dptr(k_cache)
+    a.v_cache = _dptr(v_cache)
+    a.buf_k = _dptr(buf_k)
+    a.buf_v = _dptr(buf_v)
+    return a
+
+
+def hswa_kv_offload(kind: int, seq_ids, cu_tok, total_tok: int, max_tok: int, view, k_cache,
+                    v_cache, buf_k, buf_v, stream=None, first_pos=None) -> None:
+    """Copies n_i = cu_tok[i+1]-cu_tok[i] positions of each listed sequence
+    (from first_pos[i], or its last n_i) from this layer's pages into buf_k
+    (bf16) / buf_v (fp16), [T, Hkv, d], pinned host or device tensors."""
+    a = _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache, buf_k,
+                   buf_v, first_pos)
+    _check(library().hswa_kv_offload(C.byref(a), _stream(stream)))
+
+
+def hswa_kv_restore(kind: int, seq_ids, cu_tok, total_tok: int, max_tok: int, view, k_cache,
+                    v_cache, buf_k, buf_v, stream=None, first_pos=None) -> None:
+    """Writes buf_k/buf_v back into this layer's pages at those positions."""
+    a = _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache, buf_k,
+                   buf_v, first_pos)
+    _check(library().hswa_kv_restore(C.byref(a), _stream(stream)))

@@ -28,6 +28,7 @@ EXPORTED = (
     "hswa_pool_alloc", "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release",
     "hswa_pool_truncate", "hswa_pool_match_len", "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
+    "hswa_pool_window_counts", "hswa_kv_offload", "hswa_kv_restore",
 )
 
 
@@ -86,6 +87,25 @@ class AttnArgs(C.Structure):
     ]
 
 
+class XferArgs(C.Structure):
+    _fields_ = [
+        ("kind", C.c_int32),
+        ("num_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32),
+        ("num_seqs", C.c_int32),
+        ("seq_ids", C.c_void_p),
+        ("cu_tok", C.c_void_p),
+        ("first_pos", C.c_void_p),
+        ("total_tok", C.c_int32),
+        ("max_tok", C.c_int32),
+        ("pool", PoolView),
+        ("k_cache", C.c_void_p),
+        ("v_cache", C.c_void_p),
+        ("buf_k", C.c_void_p),
+        ("buf_v", C.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -132,6 +152,12 @@ def load():
         f.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
     lib.hswa_decode.restype = C.c_int
     lib.hswa_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.hswa_pool_window_counts.restype = C.c_int
+    lib.hswa_pool_window_counts.argtypes = [C.c_void_p, C.c_int32, C.c_int32, I32P, I32P]
+    for name in ("hswa_kv_offload", "hswa_kv_restore"):
+        f = getattr(lib, name)
+        f.restype = C.c_int
+        f.argtypes = [C.POINTER(XferArgs), C.c_void_p]
     lib.hswa_decode_workspace_bytes.restype = C.c_size_t
     lib.hswa_decode_workspace_bytes.argtypes = [C.POINTER(AttnArgs)]
     _lib = lib

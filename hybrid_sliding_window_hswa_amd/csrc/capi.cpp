@@ -300,3 +300,106 @@ int hswa_decode(const hswa_attn_args* a, void* ws, size_t ws_bytes, void* stream
 }
 
 }  // extern "C"
+
+namespace {
+
+// Address the device uses for a transfer buffer: device memory as is, pinned
+// host memory through its device mapping; anything else is refused.
+int device_view(const void* ptr, const char* what, uint16_t** out) {
+  hipPointerAttribute_t at;
+  hipError_t e = hipPointerGetAttributes(&at, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    hswa::set_error("%s is neither device memory nor pinned host memory", what);
+    return HSWA_E_INVAL;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *out = (uint16_t*)ptr;
+    return HSWA_OK;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, const_cast<void*>(ptr), 0);
+    if (e != hipSuccess || !d) {
+      (void)hipGetLastError();
+      hswa::set_error("%s: pinned host memory without a device mapping", what);
+      return HSWA_E_INVAL;
+    }
+    *out = (uint16_t*)d;
+    return HSWA_OK;
+  }
+  hswa::set_error("%s is neither device memory nor pinned host memory", what);
+  return HSWA_E_INVAL;
+}
+
+int xfer(const hswa_xfer_args* a, bool to_host, void* stream) {
+  hswa::clear_error();
+  if (!a) {
+    hswa::set_error("args is NULL");
+    return HSWA_E_INVAL;
+  }
+  if (a->kind != HSWA_LAYER_FULL && a->kind != HSWA_LAYER_SWA) {
+    hswa::set_error("kind must be HSWA_LAYER_FULL or HSWA_LAYER_SWA (got %d)", a->kind);
+    return HSWA_E_INVAL;
+  }
+  if (a->head_dim != 64 && a->head_dim != 128) {
+    hswa::set_error("head_dim must be 64 or 128 (got %d)", a->head_dim);
+    return HSWA_E_INVAL;
+  }
+  if (a->num_kv_heads < 1 || a->num_seqs < 0 || a->total_tok < 0 || a->max_tok < 0 ||
+      (a->total_tok > 0 && a->max_tok < 1)) {
+    hswa::set_error("num_kv_heads >= 1, num_seqs, total_tok, max_tok >= 0 required");
+    return HSWA_E_INVAL;
+  }
+  if (a->num_seqs == 0 || a->total_tok == 0) return HSWA_OK;
+  const hswa_pool_view& v = a->pool;
+  if (!v.seq_len || !v.fpt || !v.rpt || v.ring_slots < 16 || v.ring_slots % 16 ||
+      v.max_pages_per_seq < 1 || v.max_seqs < 1) {
+    hswa::set_error("pool view is invalid");
+    return HSWA_E_INVAL;
+  }
+  if (!a->seq_ids || !a->cu_tok || !a->k_cache || !a->v_cache || !a->buf_k || !a->buf_v) {
+    hswa::set_error("seq_ids, cu_tok, k_cache, v_cache, buf_k and buf_v must be set");
+    return HSWA_E_INVAL;
+  }
+  const void* ptrs[] = {a->k_cache, a->v_cache, a->buf_k, a->buf_v};
+  for (const void* q : ptrs) {
+    if (!aligned16(q)) {
+      hswa::set_error("buffers must be 16-byte aligned");
+      return HSWA_E_INVAL;
+    }
+  }
+  hswa::XferParams p{};
+  p.kind = a->kind;
+  p.hkv = a->num_kv_heads;
+  p.d = a->head_dim;
+  p.num_seqs = a->num_seqs;
+  p.seq_ids = a->seq_ids;
+  p.cu_tok = a->cu_tok;
+  p.first_pos = a->first_pos;
+  p.max_tok = a->max_tok;
+  p.k_cache = (uint16_t*)a->k_cache;
+  p.v_cache = (uint16_t*)a->v_cache;
+  p.t.seq_len = v.seq_len;
+  p.t.fpt = v.fpt;
+  p.t.rpt = v.rpt;
+  p.t.max_pages = v.max_pages_per_seq;
+  p.t.ring_slots = v.ring_slots;
+  p.t.max_seqs = v.max_seqs;
+  int rc = device_view(a->buf_k, "buf_k", &p.buf_k);
+  if (rc) return rc;
+  rc = device_view(a->buf_v, "buf_v", &p.buf_v);
+  if (rc) return rc;
+  hipError_t e = hswa::launch_xfer(p, to_host, (hipStream_t)stream);
+  return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "transfer launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int hswa_kv_offload(const hswa_xfer_args* a, void* stream) { return xfer(a, true, stream); }
+
+int hswa_kv_restore(const hswa_xfer_args* a, void* stream) { return xfer(a, false, stream); }
+
+}  // extern "C"

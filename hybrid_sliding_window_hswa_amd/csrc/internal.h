@@ -88,7 +88,28 @@ struct AttnParams {
                          // [total_q][hq][n_splits][2] (max, sum)
 };
 
+// Window-masked transfer of one layer's KV between the pages and a packed
+// buffer of [token][Hkv][d] 16-bit words (K bf16, V fp16) that the device
+// can address (pinned host memory or device memory).
+struct XferParams {
+  int32_t kind;            // 0 FULL, 1 SWA: which page table maps positions
+  int32_t hkv, d;
+  int32_t num_seqs;
+  const int32_t* seq_ids;
+  const int32_t* cu_tok;   // [num_seqs+1]: sequence i moves
+                           // n_i = cu_tok[i+1]-cu_tok[i] positions from
+  const int32_t* first_pos;  // [num_seqs] first_pos[i] on; nullptr: its last n_i
+  int32_t max_tok;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  Tables t;
+  uint16_t* buf_k;         // device-usable address of the packed buffers
+  uint16_t* buf_v;
+};
+
 hipError_t launch_append(const AttnParams& p, hipStream_t stream);
+// to_host: pages -> buffer (offload); else buffer -> pages (restore)
+hipError_t launch_xfer(const XferParams& p, bool to_host, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);
 hipError_t launch_decode(const AttnParams& p, hipStream_t stream);
 

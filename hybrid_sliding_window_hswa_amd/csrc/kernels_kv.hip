@@ -169,4 +169,137 @@ hipError_t launch_append(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Window-masked transfer ("MiMo-V2.5 Series Inference Full-Link
+// Optimization" sec. 2.1 "KVCache Dual Pool", Data Transfer: tiers exchange
+// only the valid SWA window).  One workgroup per (sequence, 16-position page
+// tile) moves every KV head of the tile.  The packed buffer holds a token's
+// heads contiguously, so each wave moves contiguous runs of it (PCIe-friendly
+// when the buffer is host memory).  K rows copy straight; V goes through LDS
+// between the dim-major fp16 page and token-major rows.  Positions of a tile
+// outside the transferred range are never written (a ring page holds other
+// positions too).
+constexpr int kXferHeads = 8;  // KV heads staged in LDS at a time
+
+template <int D, int KIND, bool TO_HOST>
+__global__ void __launch_bounds__(256) xfer_kernel(XferParams p, int tiles_per_seq) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kPage][kXferHeads][D + 8];
+  const int i = blockIdx.x / tiles_per_seq;
+  const int t = blockIdx.x % tiles_per_seq;
+  const int sid = p.seq_ids[i];
+  if (sid < 0 || sid >= p.t.max_seqs) return;
+  const int tok0 = p.cu_tok[i];
+  const int n = p.cu_tok[i + 1] - tok0;
+  const int L = p.t.seq_len[sid];
+  const int p0 = p.first_pos ? p.first_pos[i] : L - n;  // positions [p0, p0 + n)
+  if (n <= 0 || p0 < 0 || p0 > L - n) return;  // only stored positions move
+  const int tile_pos = (p0 / kPage + t) * kPage;
+  if (tile_pos >= p0 + n) return;
+  const int lo = max(tile_pos, p0);
+  const int hi = min(tile_pos + kPage, p0 + n);
+  const int32_t page = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile_pos, p.t.max_pages,
+                                     p.t.ring_slots);
+  if (page < 0) return;  // position without a page: the caller skipped alloc
+  const int hkv = p.hkv;
+  const int tid = threadIdx.x;
+  // buffer row of position pos, head h
+  auto brow = [&](int pos, int h) { return ((int64_t)(tok0 + pos - p0) * hkv + h) * D; };
+  auto kpage = [&](int h) { return p.k_cache + ((int64_t)page * hkv + h) * kPage * D; };
+  auto vpage = [&](int h) { return p.v_cache + ((int64_t)page * hkv + h) * D * kPage; };
+
+  // K: (token, head, chunk) with the chunk fastest
+  for (int idx = tid; idx < kPage * hkv * CPR; idx += blockDim.x) {
+    const int tok = idx / (hkv * CPR);
+    const int h = (idx / CPR) % hkv;
+    const int c = idx % CPR;
+    const int pos = tile_pos + tok;
+    if (pos < lo || pos >= hi) continue;
+    u32x4* pg = (u32x4*)(kpage(h) + tok * D + c * 8);
+    u32x4* bf = (u32x4*)(p.buf_k + brow(pos, h) + c * 8);
+    if (TO_HOST)
+      *bf = *pg;
+    else
+      *pg = *bf;
+  }
+  // V, kXferHeads heads at a time through LDS
+  for (int h0 = 0; h0 < hkv; h0 += kXferHeads) {
+    const int nh = min(kXferHeads, hkv - h0);
+    if (TO_HOST) {
+      // page (head, dim e, 8-token half) -> LDS [token][head][dim]
+      for (int idx = tid; idx < nh * D * 2; idx += blockDim.x) {
+        const int hh = idx / (2 * D);
+        const int e = (idx / 2) % D;
+        const int half = idx % 2;
+        const u32x4 w = *(const u32x4*)(vpage(h0 + hh) + e * kPage + half * 8);
+        for (int j = 0; j < 8; ++j)
+          vt[half * 8 + j][hh][e] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+      }
+      __syncthreads();
+      for (int idx = tid; idx < kPage * nh * CPR; idx += blockDim.x) {
+        const int tok = idx / (nh * CPR);
+        const int hh = (idx / CPR) % nh;
+        const int c = idx % CPR;
+        const int pos = tile_pos + tok;
+        if (pos >= lo && pos < hi)
+          *(u32x4*)(p.buf_v + brow(pos, h0 + hh) + c * 8) = *(const u32x4*)(&vt[tok][hh][c * 8]);
+      }
+    } else {
+      for (int idx = tid; idx < kPage * nh * CPR; idx += blockDim.x) {
+        const int tok = idx / (nh * CPR);
+        const int hh = (idx / CPR) % nh;
+        const int c = idx % CPR;
+        const int pos = tile_pos + tok;
+        if (pos >= lo && pos < hi)
+          *(u32x4*)(&vt[tok][hh][c * 8]) = *(const u32x4*)(p.buf_v + brow(pos, h0 + hh) + c * 8);
+      }
+      __syncthreads();
+      for (int idx = tid; idx < nh * D * 2; idx += blockDim.x) {
+        const int hh = idx / (2 * D);
+        const int e = (idx / 2) % D;
+        const int half = idx % 2;
+        uint16_t* dst = vpage(h0 + hh) + e * kPage + half * 8;
+        const int pos0 = tile_pos + half * 8;
+        if (pos0 >= lo && pos0 + 8 <= hi) {
+          u32x4 w;
+          for (int j = 0; j < 4; ++j)
+            w[j] = (uint32_t)vt[half * 8 + 2 * j][hh][e] |
+                   ((uint32_t)vt[half * 8 + 2 * j + 1][hh][e] << 16);
+          *(u32x4*)dst = w;
+        } else {
+          for (int j = 0; j < 8; ++j)
+            if (pos0 + j >= lo && pos0 + j < hi) dst[j] = vt[half * 8 + j][hh][e];
+        }
+      }
+    }
+    __syncthreads();  // LDS free for the next head group
+  }
+}
+
+hipError_t launch_xfer(const XferParams& p, bool to_host, hipStream_t s) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  const int tiles = (p.max_tok + 14) / kPage + 1;
+  dim3 grid((unsigned)(p.num_seqs * tiles));
+#define HSWA_XFER(D_, K_)                                                                   \
+  if (to_host)                                                                              \
+    hipLaunchKernelGGL((xfer_kernel<D_, K_, true>), grid, dim3(256), 0, s, p, tiles);       \
+  else                                                                                      \
+    hipLaunchKernelGGL((xfer_kernel<D_, K_, false>), grid, dim3(256), 0, s, p, tiles);
+  if (p.d == 128) {
+    if (p.kind == 0) {
+      HSWA_XFER(128, 0)
+    } else {
+      HSWA_XFER(128, 1)
+    }
+  } else {
+    if (p.kind == 0) {
+      HSWA_XFER(64, 0)
+    } else {
+      HSWA_XFER(64, 1)
+    }
+  }
+#undef HSWA_XFER
+  return hipGetLastError();
+}
+
 }  // namespace hswa

@@ -655,6 +655,31 @@ int hswa_pool_match_len(const hswa_pool* p, int32_t n, const int32_t* ids,
   return HSWA_OK;
 }
 
+int hswa_pool_window_counts(const hswa_pool* p, int32_t kind, int32_t n, const int32_t* ids,
+                            int32_t* counts) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  if ((kind != HSWA_LAYER_FULL && kind != HSWA_LAYER_SWA) || n < 0 ||
+      (n > 0 && (!ids || !counts))) {
+    hswa::set_error("window_counts: bad arguments (kind %d, n %d)", kind, n);
+    return HSWA_E_INVAL;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= p->max_seqs) {
+      hswa::set_error("window_counts: sequence id %d out of range", ids[i]);
+      return HSWA_E_INVAL;
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t L = p->len[ids[i]];
+    counts[i] = kind == HSWA_LAYER_FULL ? L : std::min(L, p->W - 1);
+  }
+  return HSWA_OK;
+}
+
 int hswa_pool_read_tables(const hswa_pool* p, int32_t* seq_len, int32_t* fpt,
                           int32_t* map, int32_t* free_pages, int32_t* n_free) {
   hswa::clear_error();

@@ -288,6 +288,64 @@ size_t hswa_decode_workspace_bytes(const hswa_attn_args* args);
  * NULL: one row per sequence) into k_cache/v_cache.  No attention. */
 int hswa_append_kv(const hswa_attn_args* args, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Window-masked tier transfer ([MiMo] 2.1 "KVCache Dual Pool", Data
+ * Transfer: moves between cache tiers go by the SWA mask, so only the valid
+ * window of a SWA layer crosses the link; "KVCache asynchronous
+ * layer-by-layer pulling": the small SWA pulls hide behind compute, one
+ * layer at a time).
+ *
+ * The mask of a sequence of length L: a SWA layer moves positions
+ * [max(0, L - W + 1), L) -- the window the next query reads, which is what
+ * eviction keeps resident -- and a FULL layer moves [0, L).
+ * -------------------------------------------------------------------- */
+
+/* Tokens the mask moves per listed sequence (host arrays of n_seqs entries,
+ * from the pool's host metadata): FULL seq_len, SWA min(seq_len, W - 1). */
+int hswa_pool_window_counts(const hswa_pool* pool, int32_t kind, int32_t n_seqs,
+                            const int32_t* seq_ids, int32_t* counts_out);
+
+typedef struct hswa_xfer_args {
+  int32_t kind;             /* hswa_layer_kind of the layer whose pages move  */
+  int32_t num_kv_heads;     /* Hkv                                           */
+  int32_t head_dim;         /* 64 or 128                                     */
+  int32_t num_seqs;
+  const int32_t* seq_ids;   /* device [num_seqs], distinct pool sequence ids  */
+  const int32_t* cu_tok;    /* device [num_seqs+1]: sequence i moves
+                               n_i = cu_tok[i+1]-cu_tok[i] positions (the
+                               counts of hswa_pool_window_counts for a masked
+                               move) ...                                     */
+  const int32_t* first_pos; /* ... from device first_pos[i] on, or, when NULL,
+                               its last n_i positions [seq_len - n_i, seq_len).
+                               Explicit positions let a transfer run on one
+                               stream while allocs on another grow seq_len.
+                               A sequence whose range is not below seq_len is
+                               skipped.                                      */
+  int32_t total_tok;        /* cu_tok[num_seqs]                               */
+  int32_t max_tok;          /* host hint >= every per-sequence count          */
+  hswa_pool_view pool;      /* from hswa_pool_get_view                       */
+  void* k_cache;            /* this layer's K pages (layout above)           */
+  void* v_cache;            /* this layer's V pages                          */
+  void* buf_k;              /* [total_tok][Hkv][head_dim] 16-bit words, K as
+                               bf16; pinned host memory (hipHostMalloc, or a
+                               torch pin_memory tensor) or device memory     */
+  void* buf_v;              /* same layout, V as fp16 (the pool's format)    */
+} hswa_xfer_args;
+
+/* Offload: copies the listed positions' K/V from the layer's pages into
+ * buf_k/buf_v (sequences in the order listed, positions ascending).  The
+ * copy is asynchronous on `stream`; read the buffers after it completes.
+ * HSWA_E_INVAL for a bad argument or a buffer that is neither device memory
+ * nor pinned host memory. */
+int hswa_kv_offload(const hswa_xfer_args* args, void* stream);
+
+/* Restore: writes buf_k/buf_v into the pages at the listed positions' slots
+ * (Full slots for FULL layers, ring slots for SWA layers), typically after
+ * hswa_pool_import gave the restored context its slots; other positions of a
+ * page are untouched.  Asynchronous on `stream`; keep the buffers unchanged
+ * until it completes.  Offload then restore gives back the same bits. */
+int hswa_kv_restore(const hswa_xfer_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -176,6 +176,19 @@ C3 = MixedDecode("mixed_decode_256seq_4k-32k_full+swa_h64kv8_d128", 64, 8, 128, 
 C4 = HybridStack("hybrid_stack_70L_64k_chunk4k_h64kv8_d128", 64, 8, 128, 128, seed=400)
 C5 = LongDecode("long_decode_64seq_128k-256k_14L_h64kv8_d128", 64, 8, 128, 128, seed=500)
 
+@dataclasses.dataclass(frozen=True)
+class TierTransfer(Workload):
+    """Window-masked offload and restore of a hybrid stack's KV between HBM
+    and pinned host memory, then the first decode step."""
+    num_seqs: int = 16
+    ctx_lo: int = 4096
+    ctx_hi: int = 32768
+    pattern: str = "SSSSSSF" * 2
+    ring_slots: int = 128
+
+
 MTP = MtpDecode("mtp_decode_256seq_4k-32k_q4_full+swa_h64kv8_d128", 64, 8, 128, 128, seed=600)
 
-WORKLOADS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "MTP": MTP}
+TIER = TierTransfer("tier_transfer_16seq_4k-32k_14L_h64kv8_d128", 64, 8, 128, 128, seed=700)
+
+WORKLOADS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "MTP": MTP, "TIER": TIER}

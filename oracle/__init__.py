@@ -27,6 +27,8 @@ Modules:
 * ``closed_forms`` -- scored-pair and resident-KV counts and their ratios.
 * ``transfer``  -- which positions a window-masked tier transfer moves and
   the packed host image it produces.
+* ``fp8``       -- FP8 (e4m3) KV quantization per token, head and tile with
+  fp32 scales, and its dequantized values.
 
 Every function in these modules is pinned by ``tests/test_oracle.py`` and
 ``tests/test_oracle_pool.py`` to something other than itself (library
@@ -34,4 +36,4 @@ routines, brute force, closed forms, hand-worked fixtures); the one
 quantity with no pin is listed as "parity unpinned" in ``closed_forms``.
 """
 
-from . import attention, closed_forms, pool, transfer  # noqa: F401
+from . import attention, closed_forms, fp8, pool, transfer  # noqa: F401

@@ -26,6 +26,10 @@ resident in HBM before the timed region starts):
   long_decode
       64 sequences, contexts uniform in [131072, 262144], 14 layers (6 SWA then
       1 Full, twice), SWA ring of W + 256 slots.  `value` = HBM GB/s.
+  mixed_decode_fp8
+      The mixed decode over FP8 pages (e4m3 codes with an fp32 scale per
+      token and head, quantized by the append): half the K/V bytes per key.
+      `value` = algorithmic HBM GB/s of the FP8 bytes.
   mtp_decode
       Multi-token decode: the mixed decode's 256 sequences with one token
       plus three draft tokens per step (rows of a sequence share every K/V
@@ -282,13 +286,14 @@ class Decode:
     (hswa_pool_truncate) before the eviction."""
 
     def __init__(self, cx, ctxs, pattern, hq, hkv, d, W, ring, seed, steps_total, rows=1,
-                 fill=True):
+                 fill=True, fp8=False):
         torch, H = cx.torch, cx.H
         import synth
         self.cx, self.hq, self.hkv, self.d, self.W = cx, hq, hkv, d, W
         B = len(ctxs)
         self.B = B
         self.rows = rows
+        self.fp8 = fp8
         self.seed = seed
         self.ctx0 = list(ctxs)
         maxlen = max(ctxs) + steps_total * rows + 1
@@ -304,8 +309,13 @@ class Decode:
         self.sid = cx.i32(ids)
         H.hswa_pool_import(self.pool, ids, ctxs, want_slots=False)
         self.layers = []
+        self.scales = []
         for li, kind in enumerate(pattern):
-            kc, vc = H.kv_cache_alloc(nfull if kind == "F" else B * ring // 16, hkv, d, cx.dev)
+            npg = nfull if kind == "F" else B * ring // 16
+            if fp8:
+                kc, vc, ks, vs = H.kv_cache_alloc_fp8(npg, hkv, d, cx.dev)
+            else:
+                (kc, vc), ks, vs = H.kv_cache_alloc(npg, hkv, d, cx.dev), None, None
             # restore the context: generated per sequence on the device and
             # appended (Full: every position, SWA: the last W-1)
             for b, c in (enumerate(ctxs) if fill else ()):
@@ -313,9 +323,10 @@ class Decode:
                 kk = synth.bf16_normal((n, hkv, d), seed, li, b, synth.ROLE_K, device=cx.dev)
                 vv = synth.bf16_normal((n, hkv, d), seed, li, b, synth.ROLE_V, device=cx.dev)
                 H.hswa_append_kv(H.FULL if kind == "F" else H.SWA, kk, vv, cx.i32([b]), self.view,
-                                 kc, vc, cx.i32([0, n]), n)
+                                 kc, vc, cx.i32([0, n]), n, k_scale=ks, v_scale=vs)
                 del kk, vv
             self.layers.append((H.FULL if kind == "F" else H.SWA, kc, vc))
+            self.scales.append((ks, vs))
         torch.cuda.synchronize()
         # per-step inputs (rows new tokens per sequence per layer)
         T = B * rows
@@ -333,6 +344,10 @@ class Decode:
         for li, (kind, kc, vc) in enumerate(self.layers):
             a = _attn_args(cx, kind, W, hq, hkv, d, self.sid, self.cu, T, rows, maxlen,
                            self.view, self.q[li], self.kn[li], self.vn[li], kc, vc, self.out)
+            if fp8:
+                a.kv_dtype = H.HSWA_KV_FP8
+                a.k_scale = self.scales[li][0].data_ptr()
+                a.v_scale = self.scales[li][1].data_ptr()
             self.args.append(a)
         self.lens = list(ctxs)
         self.pattern = pattern
@@ -379,10 +394,13 @@ class Decode:
         Q read, O written (fp32), and the rows' K/V read and written by the
         append."""
         kvb = KV_TOKEN_BYTES(self.hkv, self.d)
+        # FP8 pages: one byte per K/V element plus an fp32 scale per token,
+        # head and tensor; the append reads bf16 rows and writes FP8 ones
+        kvs = 2 * self.hkv * (self.d + 4) if self.fp8 else kvb
         r = self.rows
         keys = sum(L if kind == self.cx.H.FULL else min(L, self.W - 1 + r) for L in lens)
         T = len(lens) * r
-        return keys * kvb + T * (self.hq * self.d * 2 + self.hq * self.d * 4 + 2 * kvb)
+        return keys * kvs + T * (self.hq * self.d * 2 + self.hq * self.d * 4 + kvb + kvs)
 
 
 # ---------------------------------------------------------------------------
@@ -577,6 +595,33 @@ def wl_mixed_decode(cx, args):
     rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full", "kernels_decode.hip"))
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+    line["full_call_us"] = round(r["full_call_us"], 1)
+    line["swa_call_us"] = round(r["swa_call_us"], 1)
+    return line
+
+
+def wl_mixed_decode_fp8(cx, args):
+    """The mixed decode over FP8 pages (e4m3 codes, fp32 scale per token and
+    head): half the K/V bytes per key."""
+    import synth
+    wl = synth.C3
+    ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
+    steps, warm = args.decode_steps, 4
+    dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
+                wl.ring_slots, wl.seed, steps + warm + 8, fp8=True)
+    r = run_decode(cx, dc, "FS", steps, warm)
+    log(f"decode fp8: {r}")
+    config = {"workload": "mixed_decode_fp8", "num_seqs": wl.num_seqs,
+              "ctx_range": [wl.ctx_lo, wl.ctx_hi], "layers": "1 Full + 1 SWA",
+              "kv_dtype": "fp8 e4m3, fp32 scale per token and head",
+              "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+              "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
+              "seed": wl.seed}
+    rl = roofline("hbm", r["full_gbs"], None)
+    line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
+    line["dtype"] = "fp8 K/V, bf16 MFMA"
+    line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+    line["tok_per_s"] = round(r["tok_per_s"], 1)
     line["full_call_us"] = round(r["full_call_us"], 1)
     line["swa_call_us"] = round(r["swa_call_us"], 1)
     return line
@@ -825,6 +870,7 @@ def wl_swa_single_chunk(cx, args):
 WORKLOADS = {
     "swa_chunked_prefill": wl_swa_chunked_prefill,
     "mixed_decode": wl_mixed_decode,
+    "mixed_decode_fp8": wl_mixed_decode_fp8,
     "mtp_decode": wl_mtp_decode,
     "tier_transfer": wl_tier_transfer,
     "hybrid_stack": wl_hybrid_stack,

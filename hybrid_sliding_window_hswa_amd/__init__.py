@@ -20,8 +20,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _capi
-from ._capi import (HSWA_E_HIP, HSWA_E_INVAL, HSWA_E_NOSPC, HSWA_E_UNSUPPORTED,
-                    HSWA_LAYER_FULL, HSWA_LAYER_SWA, HSWA_OK)
+from ._capi import (HSWA_E_HIP, HSWA_E_INVAL, HSWA_E_NOSPC, HSWA_E_UNSUPPORTED, HSWA_KV_BF16,
+                    HSWA_KV_FP8, HSWA_LAYER_FULL, HSWA_LAYER_SWA, HSWA_OK)
 
 PAGE_SIZE = 16
 FULL = HSWA_LAYER_FULL
@@ -34,7 +34,8 @@ __all__ = [
     "hswa_pool_match_len", "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
     "hswa_pool_window_counts", "hswa_kv_offload", "hswa_kv_restore",
-    "hswa_last_error", "hswa_version", "kv_cache_shapes", "kv_cache_alloc", "library",
+    "hswa_last_error", "hswa_version", "kv_cache_shapes", "kv_cache_alloc",
+    "kv_cache_alloc_fp8", "library",
 ]
 
 
@@ -267,8 +268,28 @@ def kv_cache_alloc(num_pages: int, num_kv_heads: int, head_dim: int, device, fil
             torch.full(vs, fill, dtype=torch.float16, device=device))
 
 
+def kv_cache_alloc_fp8(num_pages: int, num_kv_heads: int, head_dim: int, device, fill=None):
+    """One layer's FP8 pages: K codes [pages, Hkv, 16, d] and V codes
+    [pages, Hkv, d, 16] (uint8, OCP e4m3) with fp32 scales [pages, Hkv, 16]
+    for K and for V.  `fill` (an int code) fills the code buffers and NaN
+    the scales; None leaves them uninitialised."""
+    import torch
+    ks, vs = kv_cache_shapes(num_pages, num_kv_heads, head_dim)
+    sc = (num_pages, num_kv_heads, PAGE_SIZE)
+    if fill is None:
+        return (torch.empty(ks, dtype=torch.uint8, device=device),
+                torch.empty(vs, dtype=torch.uint8, device=device),
+                torch.empty(sc, dtype=torch.float32, device=device),
+                torch.empty(sc, dtype=torch.float32, device=device))
+    return (torch.full(ks, fill, dtype=torch.uint8, device=device),
+            torch.full(vs, fill, dtype=torch.uint8, device=device),
+            torch.full(sc, float("nan"), dtype=torch.float32, device=device),
+            torch.full(sc, float("nan"), dtype=torch.float32, device=device))
+
+
 def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_seq_len,
-          view, k_cache, v_cache, out, vlen, scale) -> _capi.AttnArgs:
+          view, k_cache, v_cache, out, vlen, scale, k_scale=None,
+          v_scale=None) -> _capi.AttnArgs:
     a = _capi.AttnArgs()
     a.kind = kind
     a.window = window
@@ -291,6 +312,9 @@ def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_
     a.v_cache = _dptr(v_cache)
     a.out = _dptr(out)
     a.vlen_out = _dptr(vlen)
+    a.kv_dtype = HSWA_KV_FP8 if k_scale is not None else HSWA_KV_BF16
+    a.k_scale = _dptr(k_scale)
+    a.v_scale = _dptr(v_scale)
     return a
 
 
@@ -319,23 +343,26 @@ def hswa_decode_workspace_bytes(kind: int, window: int, num_seqs: int, num_q_hea
 
 def hswa_decode(kind: int, window: int, q, k_new, v_new, seq_ids, max_seq_len: int, view,
                 k_cache, v_cache, out, workspace=None, vlen=None, scale: float = 0.0,
-                stream=None, cu_q=None, max_q_len: int = 1) -> None:
+                stream=None, cu_q=None, max_q_len: int = 1, k_scale=None,
+                v_scale=None) -> None:
     """Decode step.  Without ``cu_q``: one query row per sequence (q [B, Hq, d])
     at position seq_len - 1.  With ``cu_q`` (device int32 [B+1]): 1..4 rows per
-    sequence, its last positions (q [T, Hq, d]); ``max_q_len`` bounds them."""
+    sequence, its last positions (q [T, Hq, d]); ``max_q_len`` bounds them.
+    With ``k_scale``/``v_scale`` the pages are FP8 (kv_cache_alloc_fp8)."""
     a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0],
               max_q_len if cu_q is not None else 1, max_seq_len, view, k_cache, v_cache, out,
-              vlen, scale)
+              vlen, scale, k_scale, v_scale)
     ws = _dptr(workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().hswa_decode(C.byref(a), ws, nbytes, _stream(stream)))
 
 
 def hswa_append_kv(kind: int, k_new, v_new, seq_ids, view, k_cache, v_cache, cu_q=None,
-                   max_q_len: int = 1, stream=None) -> None:
-    """Writes k_new/v_new rows into this layer's pages (no attention)."""
+                   max_q_len: int = 1, stream=None, k_scale=None, v_scale=None) -> None:
+    """Writes k_new/v_new rows into this layer's pages (no attention); with
+    ``k_scale``/``v_scale`` the pages are FP8 and the rows are quantized."""
     a = _args(kind, 1, None, k_new, v_new, seq_ids, cu_q, k_new.shape[0], max_q_len, 1, view,
-              k_cache, v_cache, None, None, 0.0)
+              k_cache, v_cache, None, None, 0.0, k_scale, v_scale)
     a.num_q_heads = k_new.shape[1]
     _check(library().hswa_append_kv(C.byref(a), _stream(stream)))
 

@@ -16,6 +16,8 @@ HSWA_E_NOSPC = -2
 HSWA_E_HIP = -3
 HSWA_E_UNSUPPORTED = -4
 
+HSWA_KV_BF16 = 0
+HSWA_KV_FP8 = 1
 HSWA_LAYER_FULL = 0
 HSWA_LAYER_SWA = 1
 
@@ -84,6 +86,9 @@ class AttnArgs(C.Structure):
         ("v_cache", C.c_void_p),
         ("out", C.c_void_p),
         ("vlen_out", C.c_void_p),
+        ("kv_dtype", C.c_int32),
+        ("k_scale", C.c_void_p),
+        ("v_scale", C.c_void_p),
     ]
 
 

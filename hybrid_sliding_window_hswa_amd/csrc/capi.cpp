@@ -136,7 +136,16 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
     hswa::set_error("q and out must be set");
     return HSWA_E_INVAL;
   }
-  const void* ptrs[] = {a->q, a->k_new, a->v_new, a->k_cache, a->v_cache, a->out};
+  if (a->kv_dtype != HSWA_KV_BF16 && a->kv_dtype != HSWA_KV_FP8) {
+    hswa::set_error("kv_dtype must be HSWA_KV_BF16 or HSWA_KV_FP8 (got %d)", a->kv_dtype);
+    return HSWA_E_INVAL;
+  }
+  if (a->kv_dtype == HSWA_KV_FP8 && (!a->k_scale || !a->v_scale)) {
+    hswa::set_error("FP8 pages need k_scale and v_scale");
+    return HSWA_E_INVAL;
+  }
+  const void* ptrs[] = {a->q, a->k_new, a->v_new, a->k_cache, a->v_cache, a->out,
+                        a->k_scale, a->v_scale};
   for (const void* q : ptrs) {
     if (q && !aligned16(q)) {
       hswa::set_error("device buffers must be 16-byte aligned");
@@ -174,6 +183,9 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
   p->t.max_seqs = v.max_seqs;
   p->out = a->out;
   p->vlen = a->vlen_out;
+  p->kv_fp8 = a->kv_dtype == HSWA_KV_FP8;
+  p->k_scale = p->kv_fp8 ? (float*)a->k_scale : nullptr;
+  p->v_scale = p->kv_fp8 ? (float*)a->v_scale : nullptr;
   return HSWA_OK;
 }
 
@@ -249,6 +261,10 @@ int hswa_prefill_chunk(const hswa_attn_args* a, void* stream) {
   hswa::AttnParams p;
   int rc = validate(a, false, true, &p);
   if (rc) return rc;
+  if (p.kv_fp8) {
+    hswa::set_error("prefill over FP8 pages is not built (decode and append are)");
+    return HSWA_E_UNSUPPORTED;
+  }
   if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;

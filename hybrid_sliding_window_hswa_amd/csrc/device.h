@@ -50,6 +50,46 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the loop.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// ---------------------------------------------------------------------------
+// FP8 (OCP e4m3: 1 sign, 4 exponent bits with bias 7, 3 fraction bits,
+// subnormals below 2^-6 in steps of 2^-9, largest finite 448, 0x7F NaN).
+
+// e4m3 code of an fp32 value, rounded to nearest with ties to an even
+// fraction, saturated at 448 (every |y| > 448 becomes +-448; no NaN is
+// produced).  Written from the format definition with integer operations.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.0f);
+  if (a < 0.015625f)  // below 2^-6: subnormal step 2^-9 (8 steps = smallest normal)
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  const uint32_t b = __float_as_uint(a);
+  const uint32_t m = b & 0x7fffffu;
+  const uint32_t e = (b >> 23) - 120u;                   // (E - 127) + 7
+  const uint32_t q = (m + 0x7ffffu + ((m >> 20) & 1u)) >> 20;  // 3 bits, ties to even
+  return sign | ((e << 3) + q);                          // q == 8 carries into e
+}
+
+// Four e4m3 codes (one dword, byte j = code j) -> four bf16 (two dwords),
+// exactly: every e4m3 value is a bf16 value.  The hardware conversion to
+// fp32 decodes OCP e4m3 (checked against the definition on all 256 codes).
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return u32x2{(__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u),
+               (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u)};
+}
+
+// The same four codes -> four fp16, exactly (e4m3 values lie in fp16's
+// normal range; the round-toward-zero pack therefore never rounds).
+__device__ __forceinline__ u32x2 e4m3x4_to_f16x4(uint32_t w) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y))};
+}
+
 // Physical page holding the 16-aligned key tile that starts at `pos` for
 // sequence `sid`: Full layers read the Full page table, SWA layers the ring
 // page table (position taken modulo the ring size).

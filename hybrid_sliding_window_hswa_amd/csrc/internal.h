@@ -81,6 +81,11 @@ struct AttnParams {
   Tables t;
   float* out;
   int32_t* vlen;
+  // FP8 pages (kv_fp8 = 1): k_cache/v_cache hold e4m3 codes, one fp32 scale
+  // per (page, KV head, token) in k_scale/v_scale ([page][Hkv][16])
+  int32_t kv_fp8;
+  float* k_scale;
+  float* v_scale;
   // decode split-K
   int32_t n_splits;
   int32_t split_len;

@@ -33,10 +33,16 @@
 //  - Each column has its own causal (and window) limit: row r of a sequence
 //    with n rows sits at position L - n + r.
 //  - Online softmax in fp32 in the log2 domain (exp2 of prescaled scores).
+//  - FP8 pages (e4m3 codes, one fp32 scale per token and head): codes
+//    convert exactly to bf16 (K) and fp16 (V); the K scale multiplies each
+//    score, the V scale (times 2^8) each fp16 weight, so the MFMAs see exact
+//    codes and half the bytes move.
 //  - Wave w takes 32-key steps w, w+4, ...; the four partial states merge
 //    through LDS in a fixed order, so results depend only on logical key
 //    positions, never on where pages sit in memory.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -49,7 +55,7 @@ namespace {
 
 constexpr int kDecWaves = 4;
 
-template <int D, int KIND, int G, int QN>
+template <int D, int KIND, int G, int QN, bool F8>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnParams p) {
   constexpr int NB = D / 16;                  // 16-row d blocks of O^T
@@ -57,6 +63,10 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   constexpr int NCOL = G * QN;                // (row, head) columns
   constexpr int NT = (NCOL + 15) / 16;        // 16-column tiles
   constexpr int CT = NCOL < 16 ? NCOL : 16;   // columns used per tile
+  constexpr int ESZ = F8 ? 1 : 2;             // bytes per stored K/V element
+  // a lane's 8 elements of a K row or V column: 16 bytes (bf16 / fp16) or
+  // 8 bytes (e4m3 codes)
+  typedef typename std::conditional<F8, u32x2, u32x4>::type Raw;
   __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][CT][D];
   __shared__ float red_ml[kDecWaves][CT][2];
 
@@ -120,7 +130,7 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
 
   const int s0 = (klo / 32) * 32;
   const int nsteps = (khi - 1 - s0) / 32 + 1;
-  const int64_t head_stride = (int64_t)kPage * D;  // elements per (page, head) block
+  const int64_t blk = (int64_t)kPage * D * ESZ;  // bytes per (page, head) block
 
   // Page-table row of the sequence, read through the constant address space
   // so the lookups are scalar loads (the tables do not change while the
@@ -133,12 +143,21 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     return ptab[__builtin_amdgcn_readfirstlane(idx)];
   };
   // K: this lane's row `col` of score tile kt is key 8*(col/4) + 4kt + col%4,
-  // on page col/8.  V: keys 8*q4 .. +8 are page q4/2, offset 8*(q4%2).
+  // on page col/8.  V: keys 8*q4 .. +8 are page q4/2, offset 8*(q4%2); the
+  // lane's scores and weights are those same 8 keys, so its FP8 scales are
+  // 8 consecutive floats.
   const int kpage = col >> 3;
   const int krow0 = (8 * (col >> 2) + (col & 3)) & 15;
-  const int k_lane = krow0 * D + 8 * q4;
-  const int v_lane = col * kPage + 8 * (q4 & 1);
-  auto step_pages = [&](int kp0, const uint16_t*& kb, const uint16_t*& vb) {
+  const int k_lane = (krow0 * D + 8 * q4) * ESZ;
+  const int v_lane = (col * kPage + 8 * (q4 & 1)) * ESZ;
+  const uint8_t* kbase = (const uint8_t*)p.k_cache;
+  const uint8_t* vbase = (const uint8_t*)p.v_cache;
+  struct Ptrs {
+    const uint8_t* k;
+    const uint8_t* v;
+    int64_t sc;  // FP8: index of the lane's first key scale
+  };
+  auto step_pages = [&](int kp0) {
     int32_t pg0 = page_at(kp0);
     // a page past the last key: read page 0 again (those keys are masked)
     int32_t pg1 = kp0 + 16 < khi ? page_at(kp0 + 16) : pg0;
@@ -146,29 +165,64 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     // instead of faulting (the result of such a call is undefined)
     pg0 = pg0 < 0 ? 0 : pg0;
     pg1 = pg1 < 0 ? 0 : pg1;
-    kb = p.k_cache + ((int64_t)(kpage ? pg1 : pg0) * hkv + kvh) * head_stride + k_lane;
-    vb = p.v_cache + ((int64_t)((q4 >> 1) ? pg1 : pg0) * hkv + kvh) * head_stride + v_lane;
+    const int64_t vblk = (int64_t)((q4 >> 1) ? pg1 : pg0) * hkv + kvh;
+    return Ptrs{kbase + ((int64_t)(kpage ? pg1 : pg0) * hkv + kvh) * blk + k_lane,
+                vbase + vblk * blk + v_lane, vblk * kPage + 8 * (q4 & 1)};
+  };
+  auto load_k = [&](const Ptrs& pt, Raw (&kr)[2][NC]) {
+    for (int c = 0; c < NC; ++c) {
+      kr[0][c] = *(const Raw*)(pt.k + 32 * c * ESZ);
+      kr[1][c] = *(const Raw*)(pt.k + (4 * D + 32 * c) * ESZ);
+    }
+  };
+  auto load_v = [&](const Ptrs& pt, Raw (&vr)[NB]) {
+    for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const Raw*)(pt.v + 16 * nb * kPage * ESZ);
+  };
+  auto load_scales = [&](const Ptrs& pt, u32x4 (&sc)[4]) {
+    if (F8) {
+      sc[0] = *(const u32x4*)(p.k_scale + pt.sc);
+      sc[1] = *(const u32x4*)(p.k_scale + pt.sc + 4);
+      sc[2] = *(const u32x4*)(p.v_scale + pt.sc);
+      sc[3] = *(const u32x4*)(p.v_scale + pt.sc + 4);
+    }
+  };
+  auto kfrag = [&](const Raw& w) -> bf16x8 {
+    if constexpr (F8) {
+      const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
+      return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+    } else {
+      return __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  auto vfrag = [&](const Raw& w, const Raw& mask) -> f16x8 {
+    if constexpr (F8) {
+      const u32x2 x = w & mask;
+      const u32x2 a = e4m3x4_to_f16x4(x[0]), b = e4m3x4_to_f16x4(x[1]);
+      return __builtin_bit_cast(f16x8, u32x4{a[0], a[1], b[0], b[1]});
+    } else {
+      return __builtin_bit_cast(f16x8, w & mask);
+    }
   };
 
-  // Software pipeline, register-neutral: the K loads of this wave's next
-  // step are issued as soon as the score MFMAs have consumed the current K
-  // fragments, the V loads as soon as the PV MFMAs have consumed V; so each
-  // wave keeps a step's worth of bytes in flight through its math.
-  u32x4 kr[2][NC], vr[NB];
-  const uint16_t *kb, *vb;
+  // Software pipeline, register-neutral: the K loads (and FP8 scales) of
+  // this wave's next step are issued as soon as the score MFMAs have
+  // consumed the current K fragments, the V loads as soon as the PV MFMAs
+  // have consumed V; so each wave keeps a step's worth of bytes in flight
+  // through its math.
+  Raw kr[2][NC], vr[NB];
+  u32x4 sc[4], scn[4];  // FP8 scales of this step and of the next: K 0-1, V 2-3
+  Ptrs pt;
   if (wave < nsteps) {
-    step_pages(s0 + 32 * wave, kb, vb);
-    for (int c = 0; c < NC; ++c) {
-      kr[0][c] = *(const u32x4*)(kb + 32 * c);
-      kr[1][c] = *(const u32x4*)(kb + 4 * D + 32 * c);
-    }
-    for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(vb + 16 * nb * kPage);
+    pt = step_pages(s0 + 32 * wave);
+    load_k(pt, kr);
+    load_v(pt, vr);
+    load_scales(pt, sc);
   }
   for (int st = wave; st < nsteps; st += kDecWaves) {
     const int kp0 = s0 + 32 * st;
     const bool more = st + kDecWaves < nsteps;
-    const uint16_t *kbn = kb, *vbn = vb;
-    if (more) step_pages(kp0 + 32 * kDecWaves, kbn, vbn);
+    Ptrs ptn = pt;
+    if (more) ptn = step_pages(kp0 + 32 * kDecWaves);
 
     // S^T for the two 16-key tiles of every column tile, then refill K
     f32x4 s[NT][2];
@@ -176,15 +230,13 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int c = 0; c < NC; ++c)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kt][c]),
-                                                        qf[t][c], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(kr[kt][c]), qf[t][c], acc, 0, 0, 0);
         s[t][kt] = acc;
       }
-    if (more)
-      for (int c = 0; c < NC; ++c) {
-        kr[0][c] = *(const u32x4*)(kbn + 32 * c);
-        kr[1][c] = *(const u32x4*)(kbn + 4 * D + 32 * c);
-      }
+    if (more) {
+      load_k(ptn, kr);
+      load_scales(ptn, scn);
+    }
     // lane value (kt, r) is key kp0 + 8*q4 + 4kt + r.  Keys outside the
     // workgroup's range have their V zeroed (their slots may hold stale or
     // unwritten data); keys inside it but past a column's own position (or
@@ -193,6 +245,14 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     for (int j = 0; j < 8; ++j) {
       const int kp = kp0 + 8 * q4 + j;
       valid |= (unsigned)(kp >= klo && kp < khi) << j;
+    }
+    // FP8: the K scale multiplies the score; the V scale (times 2^8, undone
+    // at the end) goes into the fp16 weight of the key
+    float kscale[8], vscale[8];
+    for (int j = 0; j < 8; ++j) {
+      kscale[j] = F8 ? __uint_as_float(sc[j >> 2][j & 3]) * sl2 : sl2;
+      vscale[j] = F8 ? ((valid >> j) & 1u ? __uint_as_float(sc[2 + (j >> 2)][j & 3]) * 256.f : 0.f)
+                     : 1.f;
     }
     f16x8 pf[NT];
     float alpha[NT];
@@ -203,7 +263,7 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
         const int kp = kp0 + 8 * q4 + j;
         bool ok = (valid >> j) & 1u;
         if (QN > 1) ok = ok && kp <= cpos[t] && (KIND == 0 || kp > cpos[t] - W);
-        const float x = ok ? s[t][j >> 2][j & 3] * sl2 : -INFINITY;
+        const float x = ok ? s[t][j >> 2][j & 3] * kscale[j] : -INFINITY;
         sv[j] = x;
         mx = fmaxf(mx, x);
       }
@@ -214,30 +274,47 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
       alpha[t] = fast_exp2(m[t] - m_use);
       float ps = 0.f;
       for (int j = 0; j < 8; ++j) {
-        pf[t][j] = (_Float16)fast_exp2(sv[j] - m_use);
-        ps += (float)pf[t][j];  // sum the fp16 weights the PV product uses
+        const float e = fast_exp2(sv[j] - m_use);
+        if (F8) {
+          pf[t][j] = (_Float16)(e * vscale[j]);
+          ps += e;
+        } else {
+          pf[t][j] = (_Float16)e;
+          ps += (float)pf[t][j];  // sum the fp16 weights the PV product uses
+        }
       }
       lsum[t] = lsum[t] * alpha[t] + ps;
       m[t] = m_new;
     }
-    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+    Raw vmask;
+    for (int x = 0; x < (int)(sizeof(Raw) / 4); ++x) vmask[x] = ~0u;
     if (valid != 0xffu) {
       for (int j = 0; j < 8; ++j)
-        if (!((valid >> j) & 1u)) vmask[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
+        if (!((valid >> j) & 1u)) {
+          if (F8)
+            vmask[j >> 2] &= ~(0xffu << (8 * (j & 3)));
+          else
+            vmask[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
     }
     for (int nb = 0; nb < NB; ++nb) {
-      const f16x8 vf = __builtin_bit_cast(f16x8, vr[nb] & vmask);
+      const f16x8 vf = vfrag(vr[nb], vmask);
       for (int t = 0; t < NT; ++t) {
         o[t][nb] *= alpha[t];
         o[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[t], o[t][nb], 0, 0, 0);
       }
     }
     // refill V
-    if (more)
-      for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(vbn + 16 * nb * kPage);
-    kb = kbn;
-    vb = vbn;
+    if (more) {
+      load_v(ptn, vr);
+      if (F8)
+        for (int x = 0; x < 4; ++x) sc[x] = scn[x];
+    }
+    pt = ptn;
   }
+  if (F8)  // the weights carried a factor 2^8
+    for (int t = 0; t < NT; ++t)
+      for (int nb = 0; nb < NB; ++nb) o[t][nb] *= 0.00390625f;
 
   // merge the four waves' states (fixed order), one column tile at a time
   const int hq_base = kvh * G;
@@ -266,9 +343,9 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
       float num = 0.f, den = 0.f;
       for (int w = 0; w < kDecWaves; ++w) {
         const float mw = red_ml[w][c][0];
-        const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-        num += sc * red_o[w][c][d];
-        den += sc * red_ml[w][c][1];
+        const float sc2 = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+        num += sc2 * red_o[w][c][d];
+        den += sc2 * red_ml[w][c][1];
       }
       const int64_t hrow = (int64_t)(row0 + r) * hq + hq_base + g % G;
       if (p.n_splits == 1) {
@@ -320,14 +397,14 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, int qn)
   p.out[hrow * D + d] = num / den;
 }
 
-template <int D, int KIND, int QN>
+template <int D, int KIND, int QN, bool F8>
 hipError_t launch_decode_q(const AttnParams& p, hipStream_t s) {
   dim3 grid((unsigned)(p.num_seqs * p.n_splits * p.hkv), 1);
   switch (p.hq / p.hkv) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, KIND, 1, QN>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, KIND, 2, QN>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, KIND, 4, QN>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, KIND, 8, QN>), grid, dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<D, KIND, 1, QN, F8>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, KIND, 2, QN, F8>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, KIND, 4, QN, F8>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, KIND, 8, QN, F8>), grid, dim3(256), 0, s, p); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
@@ -336,12 +413,18 @@ hipError_t launch_decode_q(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Rows per sequence: 1 (plain decode), up to 2, up to 4.
+// Rows per sequence: 1 (plain decode), up to 2, up to 4; K/V pages in
+// bf16/fp16 or FP8.
+template <int D, int KIND, bool F8>
+hipError_t launch_decode_f(const AttnParams& p, hipStream_t s) {
+  if (p.max_q_len <= 1) return launch_decode_q<D, KIND, 1, F8>(p, s);
+  if (p.max_q_len == 2) return launch_decode_q<D, KIND, 2, F8>(p, s);
+  return launch_decode_q<D, KIND, 4, F8>(p, s);
+}
+
 template <int D, int KIND>
 hipError_t launch_decode_g(const AttnParams& p, hipStream_t s) {
-  if (p.max_q_len <= 1) return launch_decode_q<D, KIND, 1>(p, s);
-  if (p.max_q_len == 2) return launch_decode_q<D, KIND, 2>(p, s);
-  return launch_decode_q<D, KIND, 4>(p, s);
+  return p.kv_fp8 ? launch_decode_f<D, KIND, true>(p, s) : launch_decode_f<D, KIND, false>(p, s);
 }
 
 }  // namespace

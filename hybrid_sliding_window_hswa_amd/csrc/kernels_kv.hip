@@ -151,10 +151,111 @@ __global__ void __launch_bounds__(256) append_kernel(AttnParams p, int tiles_per
   }
 }
 
+// Quantizing KV append for FP8 pages ("Baidu Day0" hybrid-attention
+// article, Layered quantization, point 2: FP8 KV per token, head and
+// 128-element tile).  Same grid as append_kernel.  Each (token, head) row of
+// d <= 128 elements is one tile: amax over the row, scale = amax / 448,
+// codes of x * (448 / amax) in e4m3.  Pages: K [page][Hkv][16][d] codes
+// (token-major), V [page][Hkv][d][16] codes (dim-major, through an LDS
+// transpose), scales [page][Hkv][16] fp32.
+template <int D, int KIND>
+__global__ void __launch_bounds__(256) append_fp8_kernel(AttnParams p, int tiles_per_seq) {
+  constexpr int CPR = D / 8;  // threads per row (8 elements each)
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kPage][D + 16];
+  const int i = blockIdx.x / tiles_per_seq;
+  const int t = blockIdx.x % tiles_per_seq;
+  const int h = blockIdx.y;
+  const int sid = p.seq_ids[i];
+  if (sid < 0 || sid >= p.t.max_seqs) return;
+  const int row0 = p.cu_q ? p.cu_q[i] : i;
+  const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
+  const int L = p.t.seq_len[sid];
+  const int p0 = L - n;
+  const int tile_pos = (p0 / kPage + t) * kPage;
+  if (n <= 0 || n > L || tile_pos >= L) return;
+  const int lo = max(tile_pos, p0);
+  const int hi = min(tile_pos + kPage, L);
+  const int32_t page = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile_pos, p.t.max_pages,
+                                     p.t.ring_slots);
+  if (page < 0) return;
+  const int hkv = p.hkv;
+  const int64_t blk = (int64_t)page * hkv + h;
+  uint8_t* kdst = (uint8_t*)p.k_cache + blk * kPage * D;
+  uint8_t* vdst = (uint8_t*)p.v_cache + blk * D * kPage;
+  const int tid = threadIdx.x;
+  const int tok = tid / CPR;  // rows are groups of CPR consecutive lanes
+  const int c = tid % CPR;
+  const int pos = tile_pos + tok;
+  const bool act = tid < kPage * CPR && pos >= lo && pos < hi;
+  const int64_t row = row0 + (pos - p0);
+  // quantizes this thread's 8 elements of a row (src[0..7] as fp32) with the
+  // row's amax, reduced over the row's CPR lanes
+  auto quant = [&](const uint16_t* src, float* scale_out) -> u32x2 {
+    float x[8];
+    float amax = 0.f;
+    if (act) {
+      const u32x4 w = *(const u32x4*)src;
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf16_lo(w[j]);
+        x[2 * j + 1] = bf16_hi(w[j]);
+      }
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    }
+    for (int m = 1; m < CPR; m <<= 1) amax = fmaxf(amax, xor_lane(amax, m));
+    const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+    *scale_out = __fdiv_rn(amax, 448.0f);
+    u32x2 out = {0u, 0u};
+    if (act)
+      for (int j = 0; j < 8; ++j) out[j >> 2] |= e4m3_encode(x[j] * inv) << (8 * (j & 3));
+    return out;
+  };
+  float ks, vs;
+  const u32x2 kq = quant(p.k_new + (row * hkv + h) * D + c * 8, &ks);
+  const u32x2 vq = quant(p.v_new + (row * hkv + h) * D + c * 8, &vs);
+  if (act) {
+    *(u32x2*)(kdst + tok * D + c * 8) = kq;
+    *(u32x2*)(&vt[tok][c * 8]) = vq;
+    if (c == 0) {
+      p.k_scale[blk * kPage + tok] = ks;
+      p.v_scale[blk * kPage + tok] = vs;
+    }
+  }
+  __syncthreads();
+  // V^T: thread (e, half) owns 8 tokens of dim e
+  if (tid < D * 2) {
+    const int e = tid >> 1;
+    const int half = tid & 1;
+    uint8_t* dst = vdst + e * kPage + half * 8;
+    const int pos0 = tile_pos + half * 8;
+    if (pos0 >= lo && pos0 + 8 <= hi) {
+      u32x2 w = {0u, 0u};
+      for (int j = 0; j < 8; ++j) w[j >> 2] |= (uint32_t)vt[half * 8 + j][e] << (8 * (j & 3));
+      *(u32x2*)dst = w;
+    } else {
+      for (int j = 0; j < 8; ++j)
+        if (pos0 + j >= lo && pos0 + j < hi) dst[j] = vt[half * 8 + j][e];
+    }
+  }
+}
+
 hipError_t launch_append(const AttnParams& p, hipStream_t s) {
   if (p.num_seqs <= 0) return hipSuccess;
   const int tiles = (p.max_q_len + 14) / kPage + 1;
   dim3 grid((unsigned)(p.num_seqs * tiles), (unsigned)p.hkv);
+  if (p.kv_fp8) {
+    if (p.d == 128) {
+      if (p.kind == 0)
+        hipLaunchKernelGGL((append_fp8_kernel<128, 0>), grid, dim3(256), 0, s, p, tiles);
+      else
+        hipLaunchKernelGGL((append_fp8_kernel<128, 1>), grid, dim3(256), 0, s, p, tiles);
+    } else {
+      if (p.kind == 0)
+        hipLaunchKernelGGL((append_fp8_kernel<64, 0>), grid, dim3(256), 0, s, p, tiles);
+      else
+        hipLaunchKernelGGL((append_fp8_kernel<64, 1>), grid, dim3(256), 0, s, p, tiles);
+    }
+    return hipGetLastError();
+  }
   if (p.d == 128) {
     if (p.kind == 0)
       hipLaunchKernelGGL((append_kernel<128, 0>), grid, dim3(256), 0, s, p, tiles);

@@ -73,6 +73,21 @@ typedef enum hswa_layer_kind {
 
 #define HSWA_PAGE_SIZE 16
 
+/* Storage of a layer's K/V pages.  HSWA_KV_FP8 follows the Baidu Day0
+ * hybrid-attention article (Layered quantization, point 2: FP8 KV per
+ * token, head and 128-element tile): OCP e4m3 codes, K [page][Hkv][16][d]
+ * and V [page][Hkv][d][16] bytes, with one fp32 scale per (page, head,
+ * token) for K and for V.  A row x of d <= 128 elements is one tile:
+ * scale = amax/448, codes of x * (448/amax) rounded to nearest (ties to an
+ * even fraction), saturated at 448; the value of a code times the scale is
+ * what attention reads.  Appends quantize and decode reads FP8 pages;
+ * prefill over FP8 pages is HSWA_E_UNSUPPORTED, and the tier transfer moves
+ * BF16 pages only (its buffers hold 16-bit words). */
+typedef enum hswa_kv_dtype {
+  HSWA_KV_BF16 = 0,        /* K bf16, V fp16 (the layout above)             */
+  HSWA_KV_FP8 = 1          /* K/V e4m3 codes plus fp32 scales               */
+} hswa_kv_dtype;
+
 /* Text of the last failure on this thread ("" if none).  Never NULL. */
 const char* hswa_last_error(void);
 /* Static name of a status code. */
@@ -251,6 +266,10 @@ typedef struct hswa_attn_args {
   float* out;               /* device fp32 [total_q][Hq][head_dim]          */
   int32_t* vlen_out;        /* device int32 [total_q] or NULL: number of keys
                                each query row attended to                   */
+  int32_t kv_dtype;         /* hswa_kv_dtype of k_cache/v_cache              */
+  void* k_scale;            /* HSWA_KV_FP8: device fp32 [num_pages][Hkv][16],
+                               one scale per token of each (page, head)      */
+  void* v_scale;            /* HSWA_KV_FP8: the same for V; else NULL        */
 } hswa_attn_args;
 
 /* Chunked prefill of one layer ([MiMo] 1.1 chunked prefill; 2.1 prefix

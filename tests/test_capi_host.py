@@ -298,3 +298,15 @@ def test_match_len_after_eviction_and_validation():
         with pytest.raises(H.HswaError) as e:
             H.hswa_pool_match_len(p, ids, want, tail)
         assert e.value.status == H.HSWA_E_INVAL
+
+
+def test_fp8_argument_validation():
+    lib = _capi.load()
+    a = _args(kv_dtype=2)
+    assert lib.hswa_prefill_chunk(C.byref(a), None) == H.HSWA_E_INVAL
+    a = _args(kv_dtype=H.HSWA_KV_FP8)                     # scales missing
+    assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
+    a = _args(kv_dtype=H.HSWA_KV_FP8, k_scale=1 << 20, v_scale=(1 << 20) + 4)  # misaligned
+    assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
+    a = _args(kv_dtype=H.HSWA_KV_FP8, k_scale=1 << 20, v_scale=1 << 20)
+    assert lib.hswa_prefill_chunk(C.byref(a), None) == H.HSWA_E_UNSUPPORTED

@@ -55,6 +55,68 @@ namespace {
 
 constexpr int kDecWaves = 4;
 
+// Merges the four waves' partial states of a workgroup (fixed order), one
+// column tile at a time, and stores the result (one split) or the partial
+// state for decode_combine_kernel (several splits).  Column 16t + c of tile
+// t is (row, head) = ((16t + c) / G, (16t + c) % G).
+template <int D, int G, int NT, int CT>
+__device__ __forceinline__ void merge_store(const AttnParams& p, float (&red_o)[kDecWaves][CT][D],
+                                            float (&red_ml)[kDecWaves][CT][2],
+                                            const f32x4 (&o)[NT][D / 16], const float (&m)[NT],
+                                            const float (&lsum)[NT], int kvh, int split,
+                                            int row0, int nr) {
+  constexpr int NB = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+  const int hq = p.hq;
+  const int hq_base = kvh * G;
+  for (int t = 0; t < NT; ++t) {
+    float ls = lsum[t];
+    ls += xor_lane(ls, 16);
+    ls += xor_lane(ls, 32);
+    if (t > 0) __syncthreads();  // the previous tile's merge has read LDS
+    if (col < CT) {
+      for (int nb = 0; nb < NB; ++nb)
+        *(f32x4*)(&red_o[wave][col][16 * nb + 4 * q4]) = o[t][nb];
+      if (q4 == 0) {
+        red_ml[wave][col][0] = m[t];
+        red_ml[wave][col][1] = ls;
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < CT * D; idx += blockDim.x) {
+      const int c = idx / D;
+      const int d = idx % D;
+      const int g = 16 * t + c;
+      const int r = g / G;
+      if (r >= nr) continue;
+      float M = -INFINITY;
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_ml[w][c][0]);
+      float num = 0.f, den = 0.f;
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float mw = red_ml[w][c][0];
+        const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+        num += sc * red_o[w][c][d];
+        den += sc * red_ml[w][c][1];
+      }
+      const int64_t hrow = (int64_t)(row0 + r) * hq + hq_base + g % G;
+      if (p.n_splits == 1) {
+        p.out[hrow * D + d] = num / den;
+      } else {
+        const int64_t slot = hrow * p.n_splits + split;
+        p.ws[slot * D + d] = num;
+        if (d == 0) {
+          float* ml = p.ws + (int64_t)p.total_q * hq * p.n_splits * D;
+          ml[2 * slot] = M;
+          ml[2 * slot + 1] = den;
+        }
+      }
+    }
+  }
+}
+
 template <int D, int KIND, int G, int QN, bool F8>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnParams p) {
@@ -316,51 +378,196 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     for (int t = 0; t < NT; ++t)
       for (int nb = 0; nb < NB; ++nb) o[t][nb] *= 0.00390625f;
 
-  // merge the four waves' states (fixed order), one column tile at a time
-  const int hq_base = kvh * G;
-  for (int t = 0; t < NT; ++t) {
-    float ls = lsum[t];
-    ls += xor_lane(ls, 16);
-    ls += xor_lane(ls, 32);
-    if (t > 0) __syncthreads();  // the previous tile's merge has read LDS
-    if (col < CT) {
-      for (int nb = 0; nb < NB; ++nb)
-        *(f32x4*)(&red_o[wave][col][16 * nb + 4 * q4]) = o[t][nb];
-      if (q4 == 0) {
-        red_ml[wave][col][0] = m[t];
-        red_ml[wave][col][1] = ls;
-      }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < CT * D; idx += blockDim.x) {
-      const int c = idx / D;
-      const int d = idx % D;
-      const int g = 16 * t + c;
-      const int r = g / G;
-      if (r >= nr) continue;
-      float M = -INFINITY;
-      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_ml[w][c][0]);
-      float num = 0.f, den = 0.f;
-      for (int w = 0; w < kDecWaves; ++w) {
-        const float mw = red_ml[w][c][0];
-        const float sc2 = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-        num += sc2 * red_o[w][c][d];
-        den += sc2 * red_ml[w][c][1];
-      }
-      const int64_t hrow = (int64_t)(row0 + r) * hq + hq_base + g % G;
-      if (p.n_splits == 1) {
-        p.out[hrow * D + d] = num / den;
-      } else {
-        const int64_t slot = hrow * p.n_splits + split;
-        p.ws[slot * D + d] = num;
-        if (d == 0) {
-          float* ml = p.ws + (int64_t)p.total_q * hq * p.n_splits * D;
-          ml[2 * slot] = M;
-          ml[2 * slot + 1] = den;
-        }
-      }
+  merge_store<D, G, NT, CT>(p, red_o, red_ml, o, m, lsum, kvh, split, row0, nr);
+  if (p.vlen && split == 0 && kvh == 0 && (int)threadIdx.x < nr) {
+    const int pos = L - n + threadIdx.x;
+    p.vlen[row0 + threadIdx.x] = KIND == 0 ? pos + 1 : min(pos + 1, W);
+  }
+}
+
+// FP8 decode with 64-key steps (one column tile: G * QN <= 16).  The step
+// covers four pages; a lane's four score tiles hold all 16 keys of one page
+// (tile kt row 4a + r is key 16a + 4kt + r), so its V fragment for the two
+// PV products of the step is one 16-byte page row (keys 0-7, then 8-15) and
+// its scales are 16 consecutive floats.  Each lane's K fragment is a
+// contiguous quarter of the row (d in [q4 * D/4, (q4 + 1) * D/4)); Q takes
+// the same order of the reduction.  A wave then keeps 16.5 KB in flight per
+// step, as much as the bf16 path, at two waves per SIMD.
+template <int D, int KIND, int G, int QN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4)))
+decode_fp8_kernel(AttnParams p) {
+  constexpr int NB = D / 16;                  // 16-row d blocks of O^T
+  constexpr int NC = D / 32;                  // 32-wide chunks of the QK reduction
+  constexpr int DQ = D / 4;                   // contiguous K bytes of a lane per row
+  constexpr int KV4 = DQ / 16;                // 16-byte loads per row and lane
+  constexpr int NCOL = G * QN;
+  constexpr int CT = NCOL;                    // one tile
+  static_assert(NCOL <= 16, "one column tile");
+  constexpr int SK = 64;                      // keys per step
+  __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][CT][D];
+  __shared__ float red_ml[kDecWaves][CT][2];
+
+  const int kvh = blockIdx.x % p.hkv;
+  const int i = (blockIdx.x / p.hkv) / p.n_splits;
+  const int split = (blockIdx.x / p.hkv) % p.n_splits;
+  const int sid = p.seq_ids[i];
+  if (sid < 0 || sid >= p.t.max_seqs) return;
+  const int L = p.t.seq_len[sid];
+  const int row0 = p.cu_q ? p.cu_q[i] : i;
+  const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
+  if (n <= 0 || n > L) return;
+  const int nr = min(n, QN);
+  int klo, khi;
+  if (KIND == 0) {
+    klo = split * p.split_len;
+    khi = min(L, klo + p.split_len);
+  } else {
+    klo = max(0, L - n - p.window + 1);
+    khi = L;
+  }
+  if (klo >= khi) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+  const int hq = p.hq;
+  const int hkv = p.hkv;
+  const int W = p.window;
+
+  const int crow = col / G;
+  const bool con = col < CT && crow < nr;
+  const int cpos = L - n + crow;
+  bf16x8 qf[1][NC];  // lane holds Q[col][q4 * DQ + 8c .. +8]
+  {
+    const uint16_t* qrow = p.q + ((int64_t)(row0 + (con ? crow : 0)) * hq + kvh * G + col % G) * D;
+    for (int c = 0; c < NC; ++c) {
+      u32x4 w = con ? *(const u32x4*)(qrow + q4 * DQ + 8 * c) : u32x4{0, 0, 0, 0};
+      qf[0][c] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  f32x4 o[1][NB];
+  float m[1] = {-INFINITY}, lsum[1] = {0.f};
+  for (int nb = 0; nb < NB; ++nb) o[0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl2 = p.scale_log2;
+
+  const int s0 = (klo / SK) * SK;
+  const int nsteps = (khi - 1 - s0) / SK + 1;
+  const int64_t blk = (int64_t)kPage * D;  // bytes per (page, head) block
+  typedef const __attribute__((address_space(4))) int32_t* ctab_t;
+  const ctab_t ptab = (ctab_t)(KIND == 0 ? p.t.fpt + (int64_t)sid * p.t.max_pages
+                                         : p.t.rpt + (int64_t)sid * (p.t.ring_slots / kPage));
+  auto page_at = [&](int pos) {
+    const int idx = KIND == 0 ? pos / kPage : (pos % p.t.ring_slots) / kPage;
+    return ptab[__builtin_amdgcn_readfirstlane(idx)];
+  };
+  const uint8_t* kbase = (const uint8_t*)p.k_cache;
+  const uint8_t* vbase = (const uint8_t*)p.v_cache;
+  struct Ptrs {
+    const uint8_t* k;  // this lane's K row (page col/4, row col%4), its d quarter
+    const uint8_t* v;  // page q4, dim col
+    int64_t sc;        // scales of page q4
+  };
+  auto step_pages = [&](int kp0) {
+    int32_t pg[4];
+    for (int x = 0; x < 4; ++x) {
+      // a page past the last key: page 0 of the step again (masked keys);
+      // a missing page (skipped alloc): page 0 of the pool
+      const int32_t v = x == 0 || kp0 + 16 * x < khi ? page_at(kp0 + 16 * x) : pg[0];
+      pg[x] = v < 0 ? 0 : v;
+    }
+    const int32_t pk = pg[col >> 2], pv = pg[q4];
+    return Ptrs{kbase + ((int64_t)pk * hkv + kvh) * blk + (col & 3) * D + q4 * DQ,
+                vbase + ((int64_t)pv * hkv + kvh) * blk + col * kPage,
+                ((int64_t)pv * hkv + kvh) * kPage};
+  };
+  u32x4 kr[4][KV4], vr[NB], sc[8];  // sc: K scales 0-3, V scales 4-7
+  auto load_k = [&](const Ptrs& pt) {
+    for (int kt = 0; kt < 4; ++kt)
+      for (int x = 0; x < KV4; ++x) kr[kt][x] = *(const u32x4*)(pt.k + 4 * kt * D + 16 * x);
+  };
+  auto load_v = [&](const Ptrs& pt) {
+    for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(pt.v + 16 * nb * kPage);
+    for (int x = 0; x < 4; ++x) {
+      sc[x] = *(const u32x4*)(p.k_scale + pt.sc + 4 * x);
+      sc[4 + x] = *(const u32x4*)(p.v_scale + pt.sc + 4 * x);
+    }
+  };
+  Ptrs pt;
+  if (wave < nsteps) {
+    pt = step_pages(s0 + SK * wave);
+    load_k(pt);
+    load_v(pt);
+  }
+  for (int st = wave; st < nsteps; st += kDecWaves) {
+    const int kp0 = s0 + SK * st;
+    const bool more = st + kDecWaves < nsteps;
+    Ptrs ptn = pt;
+    if (more) ptn = step_pages(kp0 + SK * kDecWaves);
+    // S^T of the four 16-key tiles
+    f32x4 s4[4];
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NC; ++c) {
+        const uint32_t* w = (const uint32_t*)&kr[kt][0] + 2 * c;
+        const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]}), qf[0][c], acc, 0, 0, 0);
+      }
+      s4[kt] = acc;
+    }
+    if (more) load_k(ptn);
+    // lane value (kt, r) is key kp0 + 16*q4 + 4kt + r, in-page index 4kt + r
+    unsigned valid = 0;
+    for (int j = 0; j < 16; ++j) {
+      const int kp = kp0 + 16 * q4 + j;
+      valid |= (unsigned)(kp >= klo && kp < khi) << j;
+    }
+    float mx = -INFINITY;
+    float sv[16];
+    for (int j = 0; j < 16; ++j) {
+      const int kp = kp0 + 16 * q4 + j;
+      bool ok = (valid >> j) & 1u;
+      if (QN > 1) ok = ok && kp <= cpos && (KIND == 0 || kp > cpos - W);
+      const float ks = __uint_as_float(sc[j >> 2][j & 3]);
+      const float x = ok ? s4[j >> 2][j & 3] * (ks * sl2) : -INFINITY;
+      sv[j] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float m_new = fmaxf(m[0], mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m[0] - m_use);
+    f16x8 pf[2];
+    float ps = 0.f;
+    for (int j = 0; j < 16; ++j) {
+      const float e = fast_exp2(sv[j] - m_use);
+      // V scale times 2^8 into the fp16 weight; masked keys' scales may be NaN
+      const float vs = (valid >> j) & 1u ? __uint_as_float(sc[4 + (j >> 2)][j & 3]) * 256.f : 0.f;
+      pf[j >> 3][j & 7] = (_Float16)(e * vs);
+      ps += e;
+    }
+    lsum[0] = lsum[0] * alpha + ps;
+    m[0] = m_new;
+    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+    if (valid != 0xffffu)
+      for (int j = 0; j < 16; ++j)
+        if (!((valid >> j) & 1u)) vmask[j >> 2] &= ~(0xffu << (8 * (j & 3)));
+    for (int nb = 0; nb < NB; ++nb) {
+      const u32x4 w = vr[nb] & vmask;
+      o[0][nb] *= alpha;
+      for (int h = 0; h < 2; ++h) {
+        const u32x2 a = e4m3x4_to_f16x4(w[2 * h]), b = e4m3x4_to_f16x4(w[2 * h + 1]);
+        o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(f16x8, u32x4{a[0], a[1], b[0], b[1]}), pf[h], o[0][nb], 0, 0, 0);
+      }
+    }
+    if (more) load_v(ptn);
+    pt = ptn;
+  }
+  for (int nb = 0; nb < NB; ++nb) o[0][nb] *= 0.00390625f;  // the weights carried 2^8
+  merge_store<D, G, 1, CT>(p, red_o, red_ml, o, m, lsum, kvh, split, row0, nr);
   if (p.vlen && split == 0 && kvh == 0 && (int)threadIdx.x < nr) {
     const int pos = L - n + threadIdx.x;
     p.vlen[row0 + threadIdx.x] = KIND == 0 ? pos + 1 : min(pos + 1, W);
@@ -397,14 +604,25 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, int qn)
   p.out[hrow * D + d] = num / den;
 }
 
+// FP8 pages with one column tile take the 64-key kernel; two tiles (8
+// heads, more than two rows) keep the 32-key one, whose registers already
+// hold two tiles' state.
+template <int D, int KIND, int G, int QN, bool F8>
+void launch_decode_one(const AttnParams& p, dim3 grid, hipStream_t s) {
+  if constexpr (F8 && G * QN <= 16)
+    hipLaunchKernelGGL((decode_fp8_kernel<D, KIND, G, QN>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, KIND, G, QN, F8>), grid, dim3(256), 0, s, p);
+}
+
 template <int D, int KIND, int QN, bool F8>
 hipError_t launch_decode_q(const AttnParams& p, hipStream_t s) {
   dim3 grid((unsigned)(p.num_seqs * p.n_splits * p.hkv), 1);
   switch (p.hq / p.hkv) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, KIND, 1, QN, F8>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, KIND, 2, QN, F8>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, KIND, 4, QN, F8>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, KIND, 8, QN, F8>), grid, dim3(256), 0, s, p); break;
+    case 1: launch_decode_one<D, KIND, 1, QN, F8>(p, grid, s); break;
+    case 2: launch_decode_one<D, KIND, 2, QN, F8>(p, grid, s); break;
+    case 4: launch_decode_one<D, KIND, 4, QN, F8>(p, grid, s); break;
+    default: launch_decode_one<D, KIND, 8, QN, F8>(p, grid, s); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;

@@ -617,7 +617,7 @@ def wl_mixed_decode_fp8(cx, args):
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
               "seed": wl.seed}
-    rl = roofline("hbm", r["full_gbs"], None)
+    rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full_fp8", "kernels_decode.hip"))
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
     line["dtype"] = "fp8 K/V, bf16 MFMA"
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)

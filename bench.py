@@ -72,6 +72,7 @@ MFMA_BF16_PEAK_TFS = 2516.6    # 256 CU * 2.4 GHz * 4096 flop/clk (dense)
 PEAKS = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (MFMA_BF16_PEAK_TFS, "TFLOP/s"),
          "pcie": (PCIE_PEAK_GBS, "GB/s")}
 METRIC = "Hybrid-SWA attn prefill tok/s + decode HBM GB/s (% of MI355X peak)"
+ODT = {"f32": "fp32", "f16": "fp16"}
 
 CSRC = os.path.join(ROOT, "hybrid_sliding_window_hswa_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
@@ -145,6 +146,15 @@ def _attn_args(cx, kind, window, hq, hkv, d, seq_ids, cu_q, total_q, max_q_len, 
     a.pool = view
     a.k_cache, a.v_cache = kc.data_ptr(), vc.data_ptr()
     a.out = out.data_ptr() if out is not None else None
+    # the output type must match the buffer: the kernels write 4 or 2 bytes
+    # per element as out_dtype says
+    if out is not None:
+        if out.dtype == cx.torch.float16:
+            a.out_dtype = 1
+        elif out.dtype == cx.torch.float32:
+            a.out_dtype = 0
+        else:
+            raise ValueError(f"output buffer must be float32 or float16, not {out.dtype}")
     a.vlen_out = None
     return a
 
@@ -164,10 +174,12 @@ class ChunkedPrefill:
     the layers ('S' SWA, 'F' Full), each with K/V buffers of its own; all
     layers see the same synthetic Q/K/V (an attention-only stack)."""
 
-    def __init__(self, cx, lens, chunk, hq, hkv, d, W, seed, pattern="S", ring=None):
+    def __init__(self, cx, lens, chunk, hq, hkv, d, W, seed, pattern="S", ring=None,
+                 out="f32"):
         torch, H = cx.torch, cx.H
         import synth
         self.cx = cx
+        self.obytes = 2 if out == "f16" else 4
         self.lens, self.chunk, self.hq, self.hkv, self.d, self.W = lens, chunk, hq, hkv, d, W
         B = len(lens)
         self.B = B
@@ -214,7 +226,8 @@ class ChunkedPrefill:
             self.steps.append(st)
             for b, k in zip(act, n):
                 done[b] += k
-        self.out = torch.empty((max_rows, hq, d), dtype=torch.float32, device=cx.dev)
+        self.out = torch.empty((max_rows, hq, d), device=cx.dev,
+                               dtype=torch.float16 if out == "f16" else torch.float32)
         self.all_ids = _arr(list(range(B)))
         for st in self.steps:
             T = st["q"].shape[0]
@@ -258,7 +271,7 @@ class ChunkedPrefill:
             keys = sum(e for b, a, e in st["rows"])
         else:
             keys = sum((e - a) + min(self.W - 1, a) for b, a, e in st["rows"])
-        return T * self.hq * self.d * (2 + 4) + keys * kvb
+        return T * self.hq * self.d * (2 + self.obytes) + keys * kvb
 
     def attn_flops(self, st, kind):
         """4 * d * Hq flops per scored (query, key) pair."""
@@ -286,7 +299,7 @@ class Decode:
     (hswa_pool_truncate) before the eviction."""
 
     def __init__(self, cx, ctxs, pattern, hq, hkv, d, W, ring, seed, steps_total, rows=1,
-                 fill=True, fp8=False):
+                 fill=True, fp8=False, out="f32"):
         torch, H = cx.torch, cx.H
         import synth
         self.cx, self.hq, self.hkv, self.d, self.W = cx, hq, hkv, d, W
@@ -294,6 +307,7 @@ class Decode:
         self.B = B
         self.rows = rows
         self.fp8 = fp8
+        self.obytes = 2 if out == "f16" else 4
         self.seed = seed
         self.ctx0 = list(ctxs)
         maxlen = max(ctxs) + steps_total * rows + 1
@@ -334,7 +348,8 @@ class Decode:
         self.q = [g((T, hq, d), li, synth.ROLE_Q) for li in range(len(pattern))]
         self.kn = [g((T, hkv, d), li, synth.ROLE_K) for li in range(len(pattern))]
         self.vn = [g((T, hkv, d), li, synth.ROLE_V) for li in range(len(pattern))]
-        self.out = torch.empty((T, hq, d), dtype=torch.float32, device=cx.dev)
+        self.out = torch.empty((T, hq, d), device=cx.dev,
+                               dtype=torch.float16 if out == "f16" else torch.float32)
         self.max_seq_len = maxlen
         self.cu = cx.i32(np.arange(0, T + 1, rows)) if rows > 1 else None
         nb = max(H.hswa_decode_workspace_bytes(H.FULL, W, B, hq, hkv, d, maxlen, total_q=T), 16)
@@ -391,7 +406,7 @@ class Decode:
         (after the step's rows were allocated): the K/V of every key some row
         attends to, read once for all rows of the sequence (Full: L keys; SWA:
         the first row's window through the last row, min(L, W - 1 + rows)),
-        Q read, O written (fp32), and the rows' K/V read and written by the
+        Q read, O written (fp32 or fp16), and the rows' K/V read and written by the
         append."""
         kvb = KV_TOKEN_BYTES(self.hkv, self.d)
         # FP8 pages: one byte per K/V element plus an fp32 scale per token,
@@ -400,7 +415,7 @@ class Decode:
         r = self.rows
         keys = sum(L if kind == self.cx.H.FULL else min(L, self.W - 1 + r) for L in lens)
         T = len(lens) * r
-        return keys * kvs + T * (self.hq * self.d * 2 + self.hq * self.d * 4 + kvb + kvs)
+        return keys * kvs + T * (self.hq * self.d * (2 + self.obytes) + kvb + kvs)
 
 
 # ---------------------------------------------------------------------------
@@ -543,7 +558,7 @@ def wl_swa_chunked_prefill(cx, args):
     wl = synth.C2
     lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
     cp = ChunkedPrefill(cx, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                        wl.window, wl.seed)
+                        wl.window, wl.seed, out=args.out)
     cx.torch.cuda.synchronize()
     log(f"prefill: {cp.tokens} tokens in {len(cp.steps)} chunk steps")
     sec = timed(cx, cp.run, args.steps, args.warmup)
@@ -558,9 +573,10 @@ def wl_swa_chunked_prefill(cx, args):
         "seq_len_range": [wl.len_lo, wl.len_hi], "seq_lens": lens, "chunk": wl.chunk,
         "window": wl.window, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
         "head_dim": wl.head_dim, "page_size": 16, "ring_slots": wl.window + wl.chunk,
-        "output_dtype": "fp32", "seed": wl.seed,
+        "output_dtype": ODT[args.out], "seed": wl.seed,
     }
-    rl = roofline("hbm", ks["gbs"], measured_traffic("prefill_swa", "kernels_prefill.hip"))
+    rl = roofline("hbm", ks["gbs"], measured_traffic("prefill_swa", "kernels_prefill.hip")
+                  if args.out == "f32" else None)
     line = base_line(args, round(cp.tokens / sec, 1), "tok/s", sec * 1e3, config, rl)
     line["kernel"] = {"name": "prefill_kernel<128,SWA>", "avg_us": round(ks["avg_us"], 2),
                       "launches_timed": ks["launches"], "tflops": round(ks["tflops"], 2),
@@ -584,15 +600,16 @@ def wl_mixed_decode(cx, args):
     ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
     steps, warm = args.decode_steps, 4
     dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
-                wl.ring_slots, wl.seed, steps + warm + 8)
+                wl.ring_slots, wl.seed, steps + warm + 8, out=args.out)
     r = run_decode(cx, dc, "FS", steps, warm)
     log(f"decode: {r}")
     config = {"workload": "mixed_decode", "num_seqs": wl.num_seqs,
               "ctx_range": [wl.ctx_lo, wl.ctx_hi], "layers": "1 Full + 1 SWA",
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
-              "seed": wl.seed}
-    rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full", "kernels_decode.hip"))
+              "output_dtype": ODT[args.out], "seed": wl.seed}
+    rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full", "kernels_decode.hip")
+                  if args.out == "f32" else None)
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
     line["full_call_us"] = round(r["full_call_us"], 1)
@@ -608,16 +625,18 @@ def wl_mixed_decode_fp8(cx, args):
     ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
     steps, warm = args.decode_steps, 4
     dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
-                wl.ring_slots, wl.seed, steps + warm + 8, fp8=True)
+                wl.ring_slots, wl.seed, steps + warm + 8, fp8=True, out=args.out)
     r = run_decode(cx, dc, "FS", steps, warm)
     log(f"decode fp8: {r}")
     config = {"workload": "mixed_decode_fp8", "num_seqs": wl.num_seqs,
               "ctx_range": [wl.ctx_lo, wl.ctx_hi], "layers": "1 Full + 1 SWA",
               "kv_dtype": "fp8 e4m3, fp32 scale per token and head",
+              "output_dtype": ODT[args.out],
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
               "seed": wl.seed}
-    rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full_fp8", "kernels_decode.hip"))
+    rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full_fp8", "kernels_decode.hip")
+                  if args.out == "f32" else None)
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
     line["dtype"] = "fp8 K/V, bf16 MFMA"
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
@@ -636,12 +655,13 @@ def wl_mtp_decode(cx, args):
     steps, warm = args.decode_steps, 4
     rows = wl.drafts + 1
     dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
-                wl.ring_slots, wl.seed, steps + warm + 8, rows=rows)
+                wl.ring_slots, wl.seed, steps + warm + 8, rows=rows, out=args.out)
     r = run_decode(cx, dc, "FS", steps, warm)
     log(f"mtp decode: {r}")
     config = {"workload": "mtp_decode", "num_seqs": wl.num_seqs,
               "ctx_range": [wl.ctx_lo, wl.ctx_hi], "rows_per_seq": rows,
               "accepted_rows": [1, rows], "layers": "1 Full + 1 SWA",
+              "output_dtype": ODT[args.out],
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
               "seed": wl.seed}
@@ -889,6 +909,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--out", choices=sorted(ODT), default="f32",
+                    help="attention output type of the prefill and decode workloads "
+                         "(f32 default; f16 halves the bytes written)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first, as the reference for the "
                          "HBM byte counters of a rocprofv3 --pmc run")

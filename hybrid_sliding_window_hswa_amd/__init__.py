@@ -313,6 +313,10 @@ def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_
     a.out = _dptr(out)
     a.vlen_out = _dptr(vlen)
     a.kv_dtype = HSWA_KV_FP8 if k_scale is not None else HSWA_KV_BF16
+    # the output tensor's dtype selects the output type
+    if out is not None and str(out.dtype) not in ("torch.float32", "torch.float16"):
+        raise ValueError(f"out must be float32 or float16, not {out.dtype}")
+    a.out_dtype = 1 if out is not None and str(out.dtype) == "torch.float16" else 0
     a.k_scale = _dptr(k_scale)
     a.v_scale = _dptr(v_scale)
     return a
@@ -322,7 +326,8 @@ def hswa_prefill_chunk(kind: int, window: int, q, k_new, v_new, seq_ids, cu_q,
                        max_q_len: int, view, k_cache, v_cache, out, vlen=None,
                        scale: float = 0.0, stream=None) -> None:
     """q [T, Hq, d] bf16; k_new/v_new [T, Hkv, d] bf16 or None; seq_ids [B] and
-    cu_q [B+1] int32 device tensors; out [T, Hq, d] fp32; vlen [T] int32."""
+    cu_q [B+1] int32 device tensors; out [T, Hq, d] fp32 or fp16; vlen [T]
+    int32."""
     a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0], max_q_len, 0, view,
               k_cache, v_cache, out, vlen, scale)
     _check(library().hswa_prefill_chunk(C.byref(a), _stream(stream)))

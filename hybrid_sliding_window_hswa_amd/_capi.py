@@ -16,6 +16,8 @@ HSWA_E_NOSPC = -2
 HSWA_E_HIP = -3
 HSWA_E_UNSUPPORTED = -4
 
+HSWA_OUT_F32 = 0
+HSWA_OUT_F16 = 1
 HSWA_KV_BF16 = 0
 HSWA_KV_FP8 = 1
 HSWA_LAYER_FULL = 0
@@ -89,6 +91,7 @@ class AttnArgs(C.Structure):
         ("kv_dtype", C.c_int32),
         ("k_scale", C.c_void_p),
         ("v_scale", C.c_void_p),
+        ("out_dtype", C.c_int32),
     ]
 
 

@@ -136,6 +136,10 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
     hswa::set_error("q and out must be set");
     return HSWA_E_INVAL;
   }
+  if (a->out_dtype != HSWA_OUT_F32 && a->out_dtype != HSWA_OUT_F16) {
+    hswa::set_error("out_dtype must be HSWA_OUT_F32 or HSWA_OUT_F16 (got %d)", a->out_dtype);
+    return HSWA_E_INVAL;
+  }
   if (a->kv_dtype != HSWA_KV_BF16 && a->kv_dtype != HSWA_KV_FP8) {
     hswa::set_error("kv_dtype must be HSWA_KV_BF16 or HSWA_KV_FP8 (got %d)", a->kv_dtype);
     return HSWA_E_INVAL;
@@ -182,6 +186,7 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
   p->t.ring_slots = v.ring_slots;
   p->t.max_seqs = v.max_seqs;
   p->out = a->out;
+  p->out_f16 = a->out_dtype == HSWA_OUT_F16;
   p->vlen = a->vlen_out;
   p->kv_fp8 = a->kv_dtype == HSWA_KV_FP8;
   p->k_scale = p->kv_fp8 ? (float*)a->k_scale : nullptr;

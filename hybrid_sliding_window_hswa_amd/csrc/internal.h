@@ -79,7 +79,8 @@ struct AttnParams {
   uint16_t* k_cache;
   uint16_t* v_cache;
   Tables t;
-  float* out;
+  void* out;             // fp32, or fp16 when out_f16
+  int32_t out_f16;
   int32_t* vlen;
   // FP8 pages (kv_fp8 = 1): k_cache/v_cache hold e4m3 codes, one fp32 scale
   // per (page, KV head, token) in k_scale/v_scale ([page][Hkv][16])

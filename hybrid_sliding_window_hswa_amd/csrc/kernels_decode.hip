@@ -55,6 +55,15 @@ namespace {
 
 constexpr int kDecWaves = 4;
 
+// One output element in the caller's output type (fp32, or fp16 rounded to
+// nearest).
+__device__ __forceinline__ void store_out(const AttnParams& p, int64_t idx, float x) {
+  if (p.out_f16)
+    ((_Float16*)p.out)[idx] = (_Float16)x;
+  else
+    ((float*)p.out)[idx] = x;
+}
+
 // Merges the four waves' partial states of a workgroup (fixed order), one
 // column tile at a time, and stores the result (one split) or the partial
 // state for decode_combine_kernel (several splits).  Column 16t + c of tile
@@ -103,7 +112,7 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, float (&red_o)[
       }
       const int64_t hrow = (int64_t)(row0 + r) * hq + hq_base + g % G;
       if (p.n_splits == 1) {
-        p.out[hrow * D + d] = num / den;
+        store_out(p, hrow * D + d, num / den);
       } else {
         const int64_t slot = hrow * p.n_splits + split;
         p.ws[slot * D + d] = num;
@@ -601,7 +610,7 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, int qn)
     num += sc * p.ws[slot * D + d];
     den += sc * ml[2 * slot + 1];
   }
-  p.out[hrow * D + d] = num / den;
+  store_out(p, hrow * D + d, num / den);
 }
 
 // FP8 pages with one column tile take the 64-key kernel; two tiles (8

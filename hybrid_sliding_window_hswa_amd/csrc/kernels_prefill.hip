@@ -33,7 +33,8 @@
 //    is zeroed in LDS before use so that 0 * V stays 0.
 //  - Online softmax in fp32, log2 domain, with lazy rescaling: the two lanes
 //    of a row exchange their maxima only when the running max must move.
-//  - Output fp32, passed through LDS so that stores write whole row pieces.
+//  - Output fp32 (or fp16 on request), passed through LDS so that stores
+//    write whole row pieces.
 #include <hip/hip_runtime.h>
 
 #include "device.h"
@@ -305,15 +306,31 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
         *(f32x4*)(ot + qr * OROW + (32 * mh + 8 * j + 4 * h2) * 4) = v;
       }
     }
-    // lane l stores 16 bytes of row 4k + l / 16 (dims 64 ps + 4 (l % 16) ..);
-    // the output is not read again here, so the stores are non-temporal
-    for (int k = 0; k < 8; ++k) {
-      const int r = 4 * k + (lane >> 4);
-      const f32x4 v = *(const f32x4*)(ot + r * OROW + (lane & 15) * 16);
-      if (r0 + r < nrows) {
-        const int64_t gr = (int64_t)row0 + qb * QB + r0 + r;
-        __builtin_nontemporal_store(v, (f32x4*)(p.out + (gr * hq + head) * D + 64 * ps +
-                                                4 * (lane & 15)));
+    // fp32: lane l stores 16 bytes of row 4k + l / 16 (dims 64 ps + 4 (l % 16)
+    // ..); fp16: 16 bytes of row 8k + l / 8 (dims 64 ps + 8 (l % 8) ..).  The
+    // output is not read again here, so the stores are non-temporal.
+    if (!p.out_f16) {
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + (lane >> 4);
+        const f32x4 v = *(const f32x4*)(ot + r * OROW + (lane & 15) * 16);
+        if (r0 + r < nrows) {
+          const int64_t gr = (int64_t)row0 + qb * QB + r0 + r;
+          __builtin_nontemporal_store(v, (f32x4*)((float*)p.out + (gr * hq + head) * D +
+                                                  64 * ps + 4 * (lane & 15)));
+        }
+      }
+    } else {
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3);
+        const f32x4 a = *(const f32x4*)(ot + r * OROW + (lane & 7) * 32);
+        const f32x4 b = *(const f32x4*)(ot + r * OROW + (lane & 7) * 32 + 16);
+        const u32x4 h = {pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]), pack_f16x2(b[0], b[1]),
+                         pack_f16x2(b[2], b[3])};
+        if (r0 + r < nrows) {
+          const int64_t gr = (int64_t)row0 + qb * QB + r0 + r;
+          __builtin_nontemporal_store(h, (u32x4*)((_Float16*)p.out + (gr * hq + head) * D +
+                                                  64 * ps + 8 * (lane & 7)));
+        }
       }
     }
   }

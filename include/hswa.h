@@ -83,6 +83,15 @@ typedef enum hswa_layer_kind {
  * what attention reads.  Appends quantize and decode reads FP8 pages;
  * prefill over FP8 pages is HSWA_E_UNSUPPORTED, and the tier transfer moves
  * BF16 pages only (its buffers hold 16-bit words). */
+/* Element type of attention outputs.  fp32 keeps the kernels' fp32
+ * accumulation; fp16 halves the bytes written (11 significant bits: within
+ * 2^-11 relative of the fp32 result, e.g. <= 2e-3 absolute for |o| < 8;
+ * outputs are convex combinations of V, so |o| <= max |v|). */
+typedef enum hswa_out_dtype {
+  HSWA_OUT_F32 = 0,
+  HSWA_OUT_F16 = 1
+} hswa_out_dtype;
+
 typedef enum hswa_kv_dtype {
   HSWA_KV_BF16 = 0,        /* K bf16, V fp16 (the layout above)             */
   HSWA_KV_FP8 = 1          /* K/V e4m3 codes plus fp32 scales               */
@@ -263,13 +272,15 @@ typedef struct hswa_attn_args {
   void* k_cache;            /* this layer's K pages: the Full pool for FULL
                                layers, the SWA ring pool for SWA layers     */
   void* v_cache;            /* this layer's V pages (layout above)          */
-  float* out;               /* device fp32 [total_q][Hq][head_dim]          */
+  void* out;                /* device [total_q][Hq][head_dim], fp32 or fp16
+                               as out_dtype says                             */
   int32_t* vlen_out;        /* device int32 [total_q] or NULL: number of keys
                                each query row attended to                   */
   int32_t kv_dtype;         /* hswa_kv_dtype of k_cache/v_cache              */
   void* k_scale;            /* HSWA_KV_FP8: device fp32 [num_pages][Hkv][16],
                                one scale per token of each (page, head)      */
   void* v_scale;            /* HSWA_KV_FP8: the same for V; else NULL        */
+  int32_t out_dtype;        /* hswa_out_dtype of out                         */
 } hswa_attn_args;
 
 /* Chunked prefill of one layer ([MiMo] 1.1 chunked prefill; 2.1 prefix
@@ -280,7 +291,8 @@ typedef struct hswa_attn_args {
  * positions' slots (Full slots for FULL layers, SWA ring slots for SWA
  * layers); then each row attends to its keys through the page tables.
  * Every needed key must be resident, which holds when the caller allocates
- * the chunk after evicting the previous one.  Output fp32. */
+ * the chunk after evicting the previous one.  Output fp32 or fp16
+ * (out_dtype). */
 int hswa_prefill_chunk(const hswa_attn_args* args, void* stream);
 
 /* Decode step of one layer ([MiMo] 1.2).  Without cu_q: one query row per

@@ -76,14 +76,15 @@ class Setup:
 
 
 def chunked_prefill(setup: Setup, seqs: List[SeqData], chunk: int, hq: int,
-                    scale: float = 0.0, seq_ids=None, poison_evicted=True):
+                    scale: float = 0.0, seq_ids=None, poison_evicted=True,
+                    out_dtype=torch.float32):
     """Prefills every sequence in chunks; returns per-sequence fp32 outputs
     [L, Hq, d] (cpu), valid lengths and the host-side slot logs."""
     d = setup.d
     B = len(seqs)
     ids = list(range(B)) if seq_ids is None else list(seq_ids)
     lens = [s.q.shape[0] for s in seqs]
-    outs = [torch.empty((L, hq, d), dtype=torch.float32) for L in lens]
+    outs = [torch.empty((L, hq, d), dtype=out_dtype) for L in lens]
     vlens = [torch.empty(L, dtype=torch.int32) for L in lens]
     log = {"alloc": [], "evict": []}
     done = [0] * B
@@ -100,7 +101,7 @@ def chunked_prefill(setup: Setup, seqs: List[SeqData], chunk: int, hq: int,
         vn = torch.cat([seqs[b].v[a:e] for b, a, e in rows]).to(dev())
         cu = torch.tensor(np.concatenate([[0], np.cumsum(n)]), dtype=torch.int32, device=dev())
         sid = torch.tensor([ids[b] for b in act], dtype=torch.int32, device=dev())
-        out = torch.full((q.shape[0], hq, d), float("nan"), dtype=torch.float32, device=dev())
+        out = torch.full((q.shape[0], hq, d), float("nan"), dtype=out_dtype, device=dev())
         vl = torch.full((q.shape[0],), -7, dtype=torch.int32, device=dev())
         H.hswa_prefill_chunk(setup.kind, setup.W, q, kn, vn, sid, cu, max(n), setup.view,
                              setup.kc, setup.vc, out, vl, scale)

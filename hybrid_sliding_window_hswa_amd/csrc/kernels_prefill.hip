@@ -133,14 +133,8 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   const int hkv = p.hkv;
   const int64_t grow = (int64_t)row0 + qb * QB + (row_ok ? my_row : nrows - 1);
 
-  // Q^T fragments: lane holds Q[row qr][16c + 8*h2 .. +8]
-  bf16x8 qf[NC];
-  {
-    const uint16_t* qrow = p.q + (grow * hq + head) * D;
-    for (int c = 0; c < NC; ++c)
-      qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * c + 8 * h2));
-  }
 
+  bf16x8 qf[NC];  // Q^T fragments, loaded after step 0's transfers are issued
   f32x16 o[NM];
   for (int mb = 0; mb < NM; ++mb)
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
@@ -255,13 +249,28 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
     }
   };
 
-  wait_vm_all();  // Q fragments have arrived: from here on only transfers count
+  // Step 0's transfers, then the Q^T fragments (lane holds Q[row qr][16c +
+  // 8*h2 .. +8]), so that Q's latency overlaps step 0's; the full wait tells
+  // the compiler that Q has arrived (it does not see the transfers), then
+  // step 1's transfers.  Transfers stop at the last step; each wait counts
+  // what was issued after the step it waits for (memory operations complete
+  // in issue order).
   issue(kstart, 0);
-  issue(kstart + 32, 1);
+  {
+    const uint16_t* qrow = p.q + (grow * hq + head) * D;
+    for (int c = 0; c < NC; ++c)
+      qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * c + 8 * h2));
+  }
+  wait_vm_all();
+  if (nsteps > 1) issue(kstart + 32, 1);
   int bc = 0, bn = 2;  // buffers of step s and of step s+2
   for (int s = 0; s < nsteps; ++s) {
     const int kp0 = kstart + 32 * s;
-    wait_vm_at_most<NIW>();  // this wave's part of step s has landed
+    // this wave's part of step s (and, at s = 0, Q) has landed
+    if (s + 1 < nsteps)
+      wait_vm_at_most<NIW>();
+    else
+      wait_vm_at_most<0>();
     __syncthreads();         // every part has; step s-1's buffer is free
     if (!(kp0 >= wg_klo && kp0 + 31 <= wg_khi)) {
       // keys of the step outside the workgroup's range: zero their V
@@ -280,7 +289,7 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
       }
       __syncthreads();
     }
-    issue(kp0 + 64, bn);  // into step s-1's buffer
+    if (s + 2 < nsteps) issue(kp0 + 64, bn);  // into step s-1's buffer
     compute(bc, kp0);
     bc = bc == kBufs - 1 ? 0 : bc + 1;
     bn = bn == kBufs - 1 ? 0 : bn + 1;

@@ -149,8 +149,11 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   // Transfers of one step.  Transfers 0 .. NI/2-1 fill the K region: LDS row
   // r (of 32) holds key swap23(r % 16) of page r / 16, its chunk j at
   // position j ^ (r % CPR).  Transfers NI/2 .. NI-1 copy the two V page
-  // blocks verbatim.  Each transfer reads within one page block, so its
-  // source is a scalar base plus a per-lane offset fixed for the kernel.
+  // blocks verbatim.  Wave w issues transfers w*NIW .. +NIW, which is the K
+  // (w < 2) or V (w >= 2) block of the step's page w & 1: one page id and
+  // one scalar base per wave and step, plus a per-lane offset fixed for the
+  // kernel.
+  static_assert(kPreWaves == 4 && NI == 4 * NIW, "one (tensor, page) block per wave");
   uint32_t voff[NIW];
   for (int ii = 0; ii < NIW; ++ii) {
     const int inst = wave * NIW + ii;
@@ -165,31 +168,24 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
       voff[ii] = ((inst - NI / 2) * 1024 + lane * 16) % VPAGE;
     }
   }
-  const int64_t blk = (int64_t)kPage * D;  // elements per (page, KV head) block
-  // tiles past the range read page 0 (present in every pool); their keys
-  // are masked like any other key outside the range
+  // This wave's page: the table row of the sequence and the page index of
+  // the next step to issue (for SWA a ring page, advanced with wrap-around).
+  const int half = wave & 1;
+  const uint16_t* tens = (wave >= 2 ? p.v_cache : p.k_cache) + (int64_t)kvh * kPage * D;
+  const int64_t pstride = (int64_t)hkv * kPage * D;  // elements per page
+  const int npr = p.t.ring_slots / kPage;             // ring pages of a sequence (SWA)
+  const int32_t* prow = KIND == 0 ? p.t.fpt + (int64_t)sid * p.t.max_pages
+                                  : p.t.rpt + (int64_t)sid * npr;
+  int ipg = KIND == 0 ? kstart / kPage + half : ((kstart + kPage * half) % p.t.ring_slots) / kPage;
+  // a page past the range reads page 0 (present in every pool); its keys are
+  // masked like any other key outside the range
   auto issue = [&](int kp0, int buf) {
-    const int32_t pg0 = kp0 <= wg_khi ? page_of_uniform<KIND>(p.t.fpt, p.t.rpt, sid, kp0,
-                                                              p.t.max_pages, p.t.ring_slots)
-                                      : 0;
-    const int32_t pg1 = kp0 + 16 <= wg_khi
-                            ? page_of_uniform<KIND>(p.t.fpt, p.t.rpt, sid, kp0 + 16,
-                                                    p.t.max_pages, p.t.ring_slots)
-                            : 0;
-    const uint32_t base = lds0 + buf * SBYTES;
-    for (int ii = 0; ii < NIW; ++ii) {
-      const int inst = wave * NIW + ii;  // wave-uniform
-      if (inst < NI / 2) {
-        const int t2 = (inst * 64 / CPR) >> 4;
-        dma16(voff[ii], p.k_cache + ((int64_t)(t2 ? pg1 : pg0) * hkv + kvh) * blk,
-              base + inst * 1024);
-      } else {
-        const int vi = inst - NI / 2;
-        const int t2 = (vi * 1024) / VPAGE;
-        dma16(voff[ii], p.v_cache + ((int64_t)(t2 ? pg1 : pg0) * hkv + kvh) * blk,
-              base + KBYTES + vi * 1024);
-      }
-    }
+    const int32_t pg = kp0 + kPage * half <= wg_khi ? scalar_load_i32(prow, ipg) : 0;
+    ipg += 2;
+    if (KIND != 0 && ipg >= npr) ipg -= npr;
+    const uint16_t* src = tens + pg * pstride;
+    const uint32_t base = lds0 + buf * SBYTES + wave * NIW * 1024;
+    for (int ii = 0; ii < NIW; ++ii) dma16(voff[ii], src, base + ii * 1024);
   };
 
   // One 32-key step of scores, softmax and PV from LDS buffer `buf`.
@@ -229,16 +225,17 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
       m = m_new;
     }
     const float mo = m == -INFINITY ? 0.f : m;
-    float ps = 0.f;
     f16x8 pf0, pf1;
     for (int r = 0; r < 8; ++r) {
-      const float e0 = fast_exp2(__builtin_fmaf(sacc[r], sl2, -mo));
-      const float e1 = fast_exp2(__builtin_fmaf(sacc[r + 8], sl2, -mo));
-      ps += e0 + e1;
-      pf0[r] = (_Float16)e0;
-      pf1[r] = (_Float16)e1;
+      pf0[r] = (_Float16)fast_exp2(__builtin_fmaf(sacc[r], sl2, -mo));
+      pf1[r] = (_Float16)fast_exp2(__builtin_fmaf(sacc[r + 8], sl2, -mo));
     }
-    lsum += ps;
+    // row sum of the fp16 weights the PV product uses, two per dot2
+    const f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
+    for (int r = 0; r < 8; r += 2) {
+      lsum = __builtin_amdgcn_fdot2(f16x2{pf0[r], pf0[r + 1]}, one2, lsum, false);
+      lsum = __builtin_amdgcn_fdot2(f16x2{pf1[r], pf1[r + 1]}, one2, lsum, false);
+    }
     // V fragment: dim 32mb + qr, keys 8*h2 .. +8 of each page
     const uint8_t* v0 = kb + KBYTES + qr * 32 + h2 * 16;
     for (int mb = 0; mb < NM; ++mb) {

@@ -62,6 +62,10 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
                     a->num_q_heads, a->num_kv_heads);
     return HSWA_E_INVAL;
   }
+  if (a->num_kv_heads > hswa::kMaxKvHeads) {
+    hswa::set_error("num_kv_heads (%d) must be <= %d", a->num_kv_heads, hswa::kMaxKvHeads);
+    return HSWA_E_INVAL;
+  }
   int g = a->num_q_heads / a->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) {
     hswa::set_error("query heads per KV head must be 1, 2, 4 or 8 (got %d)", g);
@@ -367,9 +371,10 @@ int xfer(const hswa_xfer_args* a, bool to_host, void* stream) {
     hswa::set_error("head_dim must be 64 or 128 (got %d)", a->head_dim);
     return HSWA_E_INVAL;
   }
-  if (a->num_kv_heads < 1 || a->num_seqs < 0 || a->total_tok < 0 || a->max_tok < 0 ||
-      (a->total_tok > 0 && a->max_tok < 1)) {
-    hswa::set_error("num_kv_heads >= 1, num_seqs, total_tok, max_tok >= 0 required");
+  if (a->num_kv_heads < 1 || a->num_kv_heads > hswa::kMaxKvHeads || a->num_seqs < 0 ||
+      a->total_tok < 0 || a->max_tok < 0 || (a->total_tok > 0 && a->max_tok < 1)) {
+    hswa::set_error("1 <= num_kv_heads <= %d; num_seqs, total_tok, max_tok >= 0 required",
+                    hswa::kMaxKvHeads);
     return HSWA_E_INVAL;
   }
   if (a->num_seqs == 0 || a->total_tok == 0) return HSWA_OK;

@@ -9,6 +9,11 @@
 
 namespace hswa {
 
+// Largest KV head count the entry points accept: the kernels address a
+// page's K or V block of all KV heads (16 tokens x Hkv x d x 2 bytes) with
+// 32-bit byte offsets.
+constexpr int32_t kMaxKvHeads = 1024;
+
 // ---------------------------------------------------------------------------
 // Errors: thread-local text of the last failure (hswa_last_error).
 void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));

@@ -96,7 +96,7 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   if (t >= total_tiles) return;
   const int NY = p.hkv * HG;
   const int yh = t % NY;
-  const int qb = (t / NY) % qblocks;
+  const int qb = qblocks - 1 - (t / NY) % qblocks;  // longest (Full) blocks first
   const int i = (t / NY) / qblocks;
   const int kvh = yh % p.hkv;
   const int hg = yh / p.hkv;
@@ -172,7 +172,7 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   // the next step to issue (for SWA a ring page, advanced with wrap-around).
   const int half = wave & 1;
   const uint16_t* tens = (wave >= 2 ? p.v_cache : p.k_cache) + (int64_t)kvh * kPage * D;
-  const int64_t pstride = (int64_t)hkv * kPage * D;  // elements per page
+  const uint32_t pbytes = (uint32_t)hkv * kPage * D * 2;  // bytes per page (< 2^32)
   const int npr = p.t.ring_slots / kPage;             // ring pages of a sequence (SWA)
   const int32_t* prow = KIND == 0 ? p.t.fpt + (int64_t)sid * p.t.max_pages
                                   : p.t.rpt + (int64_t)sid * npr;
@@ -183,7 +183,8 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
     const int32_t pg = kp0 + kPage * half <= wg_khi ? scalar_load_i32(prow, ipg) : 0;
     ipg += 2;
     if (KIND != 0 && ipg >= npr) ipg -= npr;
-    const uint16_t* src = tens + pg * pstride;
+    const uint16_t* src =
+        (const uint16_t*)((const uint8_t*)tens + (uint64_t)(uint32_t)pg * pbytes);
     const uint32_t base = lds0 + buf * SBYTES + wave * NIW * 1024;
     for (int ii = 0; ii < NIW; ++ii) dma16(voff[ii], src, base + ii * 1024);
   };

@@ -251,7 +251,7 @@ typedef struct hswa_attn_args {
   int32_t kind;             /* hswa_layer_kind                              */
   int32_t window;           /* SWA: 1 <= window <= pool window; FULL: unused */
   int32_t num_q_heads;      /* Hq                                           */
-  int32_t num_kv_heads;     /* Hkv; Hq / Hkv in {1, 2, 4, 8}                 */
+  int32_t num_kv_heads;     /* Hkv in [1, 1024]; Hq / Hkv in {1, 2, 4, 8}    */
   int32_t head_dim;         /* 64 or 128                                    */
   float scale;              /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
   int32_t num_seqs;         /* sequences in this call                       */
@@ -338,7 +338,7 @@ int hswa_pool_window_counts(const hswa_pool* pool, int32_t kind, int32_t n_seqs,
 
 typedef struct hswa_xfer_args {
   int32_t kind;             /* hswa_layer_kind of the layer whose pages move  */
-  int32_t num_kv_heads;     /* Hkv                                           */
+  int32_t num_kv_heads;     /* Hkv in [1, 1024]                              */
   int32_t head_dim;         /* 64 or 128                                     */
   int32_t num_seqs;
   const int32_t* seq_ids;   /* device [num_seqs], distinct pool sequence ids  */

@@ -209,6 +209,7 @@ def _args(**kw):
     (dict(head_dim=96), H.HSWA_E_INVAL),
     (dict(hq=12, hkv=8), H.HSWA_E_INVAL),
     (dict(hq=32, hkv=2), H.HSWA_E_UNSUPPORTED),
+    (dict(hq=2048, hkv=2048), H.HSWA_E_INVAL),  # above the KV head cap
     (dict(kind=5), H.HSWA_E_INVAL),
     (dict(window=32), H.HSWA_E_INVAL),        # above the pool window
     (dict(window=0), H.HSWA_E_INVAL),

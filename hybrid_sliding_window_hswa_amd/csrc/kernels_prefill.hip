@@ -261,8 +261,11 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   }
   wait_vm_all();
   if (nsteps > 1) issue(kstart + 32, 1);
-  int bc = 0, bn = 2;  // buffers of step s and of step s+2
-  for (int s = 0; s < nsteps; ++s) {
+  // One step s over LDS buffer bc (its transfers landed), refilling buffer
+  // bn (step s-1's) with step s+2.  The loop below runs three steps per
+  // iteration so that the buffer indices, hence the LDS offsets, are
+  // compile-time constants.
+  auto step = [&](int s, int bc, int bn) __attribute__((always_inline)) {
     const int kp0 = kstart + 32 * s;
     // this wave's part of step s (and, at s = 0, Q) has landed
     if (s + 1 < nsteps)
@@ -289,8 +292,12 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
     }
     if (s + 2 < nsteps) issue(kp0 + 64, bn);  // into step s-1's buffer
     compute(bc, kp0);
-    bc = bc == kBufs - 1 ? 0 : bc + 1;
-    bn = bn == kBufs - 1 ? 0 : bn + 1;
+  };
+  static_assert(kBufs == 3, "three steps per iteration");
+  for (int s = 0; s < nsteps; s += 3) {
+    step(s, 0, 2);
+    if (s + 1 < nsteps) step(s + 1, 1, 0);
+    if (s + 2 < nsteps) step(s + 2, 2, 1);
   }
   wait_vm_at_most<0>();  // no transfer may land after the workgroup leaves
 

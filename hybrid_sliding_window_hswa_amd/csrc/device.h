@@ -70,24 +70,22 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
 }
 
 // Four e4m3 codes (one dword, byte j = code j) -> four bf16 (two dwords),
-// exactly: every e4m3 value is a bf16 value.  The hardware conversion to
-// fp32 decodes OCP e4m3 (checked against the definition on all 256 codes).
+// exactly: every e4m3 value is a bf16 value.  gfx950's scaled conversion
+// takes two codes (word_sel picks bytes 0-1 or 2-3) straight to a bf16
+// pair; with scale 1 it equals the fp32 decode of OCP e4m3 (itself checked
+// against the definition on all 256 codes) on every non-NaN code pair.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  return u32x2{(__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u),
-               (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u)};
+  return u32x2{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
 }
 
 // The same four codes -> four fp16, exactly (e4m3 values lie in fp16's
-// normal range; the round-toward-zero pack therefore never rounds).
+// normal range).
 __device__ __forceinline__ u32x2 e4m3x4_to_f16x4(uint32_t w) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y))};
+  return u32x2{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
 }
 
 // Physical page holding the 16-aligned key tile that starts at `pos` for

@@ -170,3 +170,36 @@ def test_fp8_decode_d64(gpu):
 
 def test_fp8_multi_row_decode(gpu):
     _fp8_decode_scenario([3000, 40, 129, 9000], 3, 64, 8, 128, 128, 53, max_rows=4)
+
+
+@pytest.mark.parametrize("kind", [H.FULL, H.SWA])
+def test_decode_reads_every_e4m3_code_exactly(gpu, kind):
+    """Every finite e4m3 code, through the decode path, comes back as its
+    exact value.  One stored key's V codes are all 254 finite codes (two KV
+    heads x 128 dims) with V scale 1; its K codes are 448 and Q is all ones,
+    so its score exceeds the new token's (K = 0) by thousands and its weight
+    is 1 while the new token's is 0.  The output is then that key's V, code
+    by code, bit for bit (the fp16 weight 2^8 and the final 2^-8 are exact)."""
+    hkv, d, W = 2, 128, 128
+    P = Fp8Pool([1], hkv, d, W, 61)
+    codes = np.arange(256, dtype=np.uint8).reshape(hkv, d)
+    codes[(codes & 0x7F) == 0x7F] &= 0x80     # the two NaN codes -> +-0
+    kc, vc, ks, vs = P.bufs(kind)
+    s = P.slot(kind, 0, 0)
+    pg, off = s // 16, s % 16
+    kc[pg, :, off, :] = 0x7E
+    vc[pg, :, :, off] = torch.as_tensor(codes, device=dev())
+    ks[pg, :, off] = 1.0
+    vs[pg, :, off] = 1.0
+    H.hswa_pool_alloc(P.pool, [0], [1])
+    q = torch.ones((1, hkv, d), dtype=torch.bfloat16, device=dev())
+    zero = torch.zeros((1, hkv, d), dtype=torch.bfloat16, device=dev())
+    out = torch.full((1, hkv, d), float("nan"), dtype=torch.float32, device=dev())
+    nb = H.hswa_decode_workspace_bytes(kind, W, 1, hkv, hkv, d, 2)
+    ws = torch.empty(max(nb // 4, 1), dtype=torch.float32, device=dev())
+    H.hswa_decode(kind, W, q, zero, zero, P.sid, 2, P.view, kc, vc, out, ws,
+                  k_scale=ks, v_scale=vs)
+    want = F8.E4M3_TABLE[codes].astype(np.float32)
+    got = out.cpu().numpy()[0]
+    assert np.array_equal(got.view(np.uint32) & 0x7FFFFFFF, want.view(np.uint32) & 0x7FFFFFFF) \
+        and np.array_equal(got, want), np.argwhere(got != want)[:5]

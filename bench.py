@@ -887,8 +887,59 @@ def wl_swa_single_chunk(cx, args):
     return line
 
 
+def wl_tp8_share(cx, args):
+    """One GPU's share of an 8-way head split of the default run: the same
+    SWA chunked prefill (lengths, chunk, W) and mixed decode (contexts) with
+    Hq = 8 and Hkv = 1, i.e. what each of eight GPUs holds and computes when
+    KV heads are divided among them (no exchange inside attention)."""
+    import synth
+    H = cx.H
+    wl, wd = synth.C2, synth.C3
+    hq, hkv = wl.num_q_heads // 8, wl.num_kv_heads // 8
+    lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
+    cp = ChunkedPrefill(cx, lens, wl.chunk, hq, hkv, wl.head_dim, wl.window, wl.seed,
+                        out=args.out)
+    cx.torch.cuda.synchronize()
+    sec = timed(cx, cp.run, args.steps, args.warmup)
+    ev = []
+    for _ in range(max(1, min(args.steps, 5))):
+        cp.run(ev)
+    cx.torch.cuda.synchronize()
+    ks = kernel_stats(cp, ev, H.SWA)
+    log(f"tp8 share prefill: {cp.tokens / sec:.4g} tok/s, {sec * 1e3:.3f} ms/step, kernel {ks}")
+    config = {
+        "workload": "tp8_share", "share": "1 of 8 GPUs, KV heads split 8 ways",
+        "num_seqs": wl.num_seqs, "seq_len_range": [wl.len_lo, wl.len_hi], "seq_lens": lens,
+        "chunk": wl.chunk, "window": wl.window, "num_q_heads": hq, "num_kv_heads": hkv,
+        "head_dim": wl.head_dim, "page_size": 16, "ring_slots": wl.window + wl.chunk,
+        "output_dtype": ODT[args.out], "seed": wl.seed,
+    }
+    line = base_line(args, round(cp.tokens / sec, 1), "tok/s", sec * 1e3, config,
+                     roofline("hbm", ks["gbs"], None))
+    line["kernel"] = {"name": "prefill_kernel<128,SWA>", "avg_us": round(ks["avg_us"], 2),
+                      "launches_timed": ks["launches"], "tflops": round(ks["tflops"], 2)}
+    if not args.no_decode:
+        ctxs = synth.uniform_lengths(wd.num_seqs, wd.ctx_lo, wd.ctx_hi, wd.seed)
+        steps, warm = args.decode_steps, 4
+        dc = Decode(cx, ctxs, "FS", hq, hkv, wd.head_dim, wd.window, wd.ring_slots, wd.seed,
+                    steps + warm + 8, out=args.out)
+        r = run_decode(cx, dc, "FS", steps, warm)
+        log(f"tp8 share decode: {r}")
+        line["decode"] = {"num_seqs": wd.num_seqs, "ctx_range": [wd.ctx_lo, wd.ctx_hi],
+                          "layers": "1 Full + 1 SWA", "num_q_heads": hq, "num_kv_heads": hkv,
+                          "value": round(r["gbs"], 1), "unit": "GB/s",
+                          "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                          "ms_per_step": round(r["ms_per_step"], 4),
+                          "roofline": roofline("hbm", r["full_gbs"], None),
+                          "full_call_us": round(r["full_call_us"], 1),
+                          "swa_call_us": round(r["swa_call_us"], 1)}
+    line["cpu_baseline"] = None
+    return line
+
+
 WORKLOADS = {
     "swa_chunked_prefill": wl_swa_chunked_prefill,
+    "tp8_share": wl_tp8_share,
     "mixed_decode": wl_mixed_decode,
     "mixed_decode_fp8": wl_mixed_decode_fp8,
     "mtp_decode": wl_mtp_decode,

@@ -292,3 +292,22 @@ def test_decode_long_context_splits(gpu):
 
 def test_decode_small_heads_d64(gpu):
     _decode_scenario([1500, 90, 700], 3, 8, 2, 64, 128, 81)
+
+
+# ---------------------------------------------------------------------------
+# One GPU's share of an 8-way head split: Hq = 8, Hkv = 1, d = 128
+
+
+@pytest.mark.parametrize("kind", [H.SWA, H.FULL])
+def test_prefill_one_kv_head_share(gpu, kind):
+    hq, hkv, d, W, chunk = 8, 1, 128, 128, 256
+    lens = [900, 37, 513]
+    seqs = make_seqs(lens, hq, hkv, d, 91)
+    maxp = max(lens) // 16 + 2
+    st = Setup(kind, W, W + chunk, len(lens), maxp, len(lens) * maxp + 5, hkv, d, 91)
+    outs, vlens, _ = chunked_prefill(st, seqs, chunk, hq)
+    _check_seq(outs, vlens, seqs, kind, W)
+
+
+def test_decode_one_kv_head_share(gpu):
+    _decode_scenario([20000, 4100, 129, 1], 2, 8, 1, 128, 128, 93, C=128 + 256)

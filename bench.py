@@ -82,9 +82,17 @@ def KV_TOKEN_BYTES(hkv, d):
     return 2 * hkv * d * 2  # K (bf16) and V (fp16) of one token
 
 
+# headers every kernel source includes: a change to them changes the kernels
+KERNEL_HEADERS = ("device.h", "internal.h")
+
+
 def source_sha(fname):
-    with open(os.path.join(CSRC, fname), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over a kernel source followed by the shared device headers."""
+    h = hashlib.sha256()
+    for name in (fname,) + KERNEL_HEADERS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(key, fname):

@@ -11,8 +11,9 @@
 //
 // Design (gfx950):
 //  - One workgroup = 4 wavefronts per (sequence, KV head, split).  Full
-//    layers split the context in split_len-key pieces so the grid fills 256
-//    CUs; pieces are merged by log-sum-exp in decode_combine_kernel.
+//    layers split a context of L keys into ceil(L / split_len) equal pieces
+//    (64-key multiples) so the grid fills 256 CUs without short tail
+//    pieces; pieces are merged by log-sum-exp in decode_combine_kernel.
 //  - The (row, head) pairs that share a KV head ride in the N dimension of
 //    16x16x32 MFMAs: S^T[key][col] = K[key][:] . Q[col][:], column
 //    col = row * G + head, in 16-column tiles.  Every K/V byte is read from
@@ -156,8 +157,12 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   const int nr = min(n, QN);                         // rows computed here
   int klo, khi;  // keys [klo, khi) of this workgroup
   if (KIND == 0) {
-    klo = split * p.split_len;
-    khi = min(L, klo + p.split_len);
+    // the sequence's ceil(L / split_len) splits share its keys evenly, in
+    // 64-key multiples (no short last split); the combine sees the same count
+    const int ns = (L + p.split_len - 1) / p.split_len;
+    const int len = ((L + ns - 1) / ns + 63) / 64 * 64;
+    klo = split * len;
+    khi = min(L, klo + len);
   } else {
     klo = max(0, L - n - p.window + 1);  // window start of the first row
     khi = L;
@@ -428,8 +433,12 @@ decode_fp8_kernel(AttnParams p) {
   const int nr = min(n, QN);
   int klo, khi;
   if (KIND == 0) {
-    klo = split * p.split_len;
-    khi = min(L, klo + p.split_len);
+    // the sequence's ceil(L / split_len) splits share its keys evenly, in
+    // 64-key multiples (no short last split); the combine sees the same count
+    const int ns = (L + p.split_len - 1) / p.split_len;
+    const int len = ((L + ns - 1) / ns + 63) / 64 * 64;
+    klo = split * len;
+    khi = min(L, klo + len);
   } else {
     klo = max(0, L - n - p.window + 1);
     khi = L;

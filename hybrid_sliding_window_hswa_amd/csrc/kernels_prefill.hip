@@ -14,6 +14,8 @@
 //    let three of them share a CU, so one's loads overlap another's math.
 //    The grid runs KV heads fastest: workgroups resident at the same time
 //    then cover all KV heads' slices of the pages (all HBM channels).
+//    Query blocks run last first, so a Full chunk's longest prefixes start
+//    first.
 //  - Scores use the 32x32x16 bf16 MFMA as S^T[key][row] = K . Q^T, with the
 //    Q^T fragments held in registers for the whole key loop and K read from
 //    LDS.  The output uses the 32x32x16 fp16 MFMA as O^T[d][row] = V^T . P^T
@@ -25,14 +27,16 @@
 //  - K/V move global -> LDS by DMA (global_load_lds_dwordx4: each lane's 16
 //    bytes land at the LDS base + 16 * lane), in 32-key steps (two 16-token
 //    pages) through three LDS buffers: the loads of steps s+1 and s+2 are in
-//    flight while step s computes, and no registers hold staged data.  The
-//    K rows' 16-byte chunks are XOR-swizzled by row so that the QK operand
-//    reads are free of bank conflicts without padding.
+//    flight while step s computes, and no registers hold staged data.  Each
+//    wave moves one (K or V, page) block of a step, so it needs one page id
+//    per step.  The K rows' 16-byte chunks are XOR-swizzled by row so that
+//    the QK operand reads are free of bank conflicts without padding.
 //  - Keys outside the workgroup's range (their slots can hold evicted or
 //    unwritten data) get -inf scores through the per-row masks, and their V
 //    is zeroed in LDS before use so that 0 * V stays 0.
 //  - Online softmax in fp32, log2 domain, with lazy rescaling: the two lanes
 //    of a row exchange their maxima only when the running max must move.
+//    The row sum adds the fp16 weights the PV product uses.
 //  - Output fp32 (or fp16 on request), passed through LDS so that stores
 //    write whole row pieces.
 #include <hip/hip_runtime.h>

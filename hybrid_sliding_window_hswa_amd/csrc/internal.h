@@ -30,12 +30,12 @@ struct PoolRec {
   int32_t clr_hi;
   int32_t set_lo;    // positions [set_lo, set_hi) get map = their SWA slot
   int32_t set_hi;
-  int32_t pg_lo;     // logical page of pages[pg_off]
+  int32_t pg_lo;     // logical page of the record's first listed page
   int32_t pg_off;    // offset of this record's pages in the page list
   int32_t fpt_lo;    // fpt entries [fpt_lo, fpt_hi) of the row are written
   int32_t fpt_hi;
   int32_t fpt_clear; // 1: write -1, 0: write the listed physical page
-  int32_t pad;
+  int32_t npg;       // listed pages: logical pages [pg_lo, pg_lo + npg)
 };
 
 struct PoolDev {
@@ -47,13 +47,16 @@ struct PoolDev {
   int32_t ring_slots;
 };
 
-// recs/pages live in pinned host memory readable by the device.  Every
-// block of the launch writes `seq` into done[its index] (pinned host memory)
-// once it has read everything it needs from the staging buffer, so the host
-// knows when the buffer may be reused without recording an event.
-int pool_apply_blocks(int n_recs, int64_t max_range);
+// recs/pages live in pinned host memory readable by the device.  Record x's
+// Full pages sit at pages[x * stride ..] and the ring pages of the same
+// logical pages at pages[(n_recs + x) * stride ..] (stride >= every record's
+// npg), so a block can read its record and its page ids at once.  Every block of the
+// launch writes `seq` into done[its index] (pinned host memory) once it has
+// read everything it needs from the staging buffer, so the host knows when
+// the buffer may be reused without recording an event.
+int pool_apply_blocks(int n_recs, int32_t stride);
 hipError_t launch_pool_apply(const PoolDev& dev, const PoolRec* recs, int n_recs,
-                             const int32_t* pages, int64_t max_range, int32_t* done,
+                             const int32_t* pages, int32_t stride, int32_t* done,
                              int32_t seq, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

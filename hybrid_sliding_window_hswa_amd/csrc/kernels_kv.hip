@@ -21,45 +21,38 @@ using namespace dev;
 
 // ---------------------------------------------------------------------------
 // Applies one pool operation's records to the device tables.  Block x is a
-// record (one sequence); blocks along y and threads stride over its ranges.
-// Records and page lists sit in pinned host memory, read over the bus: the
-// record is read once per block, and each listed page id once per thread
-// that needs it (map entries are written a whole page at a time).
+// record (one sequence); blocks along y and threads stride over its listed
+// pages (thread j handles logical page pg_lo + j: its fpt entry and its 16
+// map entries).  Records and page lists sit in pinned host memory, read over
+// the bus.  Record x's Full pages start at pages[x * stride] and the ring
+// pages of the same logical pages at pages[(n_recs + x) * stride] (a logical
+// page's 16 positions share one ring page, as the ring holds whole pages), so
+// a thread issues the reads of its page ids together with the read of the
+// record and the block pays one bus round trip.
 __global__ void __launch_bounds__(256) pool_apply_kernel(PoolDev d, const PoolRec* recs,
-                                                         const int32_t* pages, int32_t* done,
-                                                         int32_t seq) {
-  __shared__ PoolRec rs;
-  if (threadIdx.x == 0) rs = recs[blockIdx.x];
-  __syncthreads();
-  const PoolRec r = rs;
-  const int tid = blockIdx.y * blockDim.x + threadIdx.x;
-  const int stride = gridDim.y * blockDim.x;
-  if (tid == 0) d.seq_len[r.seq] = r.new_len;
+                                                         const int32_t* pages, int32_t stride,
+                                                         int32_t* done, int32_t seq) {
+  const int j0 = blockIdx.y * blockDim.x + threadIdx.x;
+  const int jstep = gridDim.y * blockDim.x;
+  const int32_t* pg = pages + (int64_t)blockIdx.x * stride;
+  const int32_t* rg = pages + (int64_t)(gridDim.x + blockIdx.x) * stride;
+  const int32_t first = j0 < stride ? pg[j0] : 0;  // before the record arrives
+  const int32_t rfirst = j0 < stride ? rg[j0] : 0;
+  const PoolRec r = recs[blockIdx.x];
+  if (j0 == 0) d.seq_len[r.seq] = r.new_len;
   int32_t* row = d.fpt + (int64_t)r.seq * d.max_pages;
-  const int32_t* pg = pages + r.pg_off;
-  for (int lp = r.fpt_lo + tid; lp < r.fpt_hi; lp += stride)
-    row[lp] = r.fpt_clear ? -1 : pg[lp - r.pg_lo];
-  if (r.clr_hi > r.clr_lo) {
-    for (int lp = r.clr_lo / kPage + tid; lp <= (r.clr_hi - 1) / kPage; lp += stride) {
-      int32_t* m = d.map + pg[lp - r.pg_lo] * kPage;
-      for (int x = 0; x < kPage; ++x) {
-        const int pos = lp * kPage + x;
-        if (pos >= r.clr_lo && pos < r.clr_hi) m[x] = -1;
-      }
-    }
-  }
-  if (r.set_hi > r.set_lo) {
-    const int rp = d.ring_slots / kPage;
-    const int32_t* rring = d.rpt + (int64_t)r.seq * rp;
-    for (int lp = r.set_lo / kPage + tid; lp <= (r.set_hi - 1) / kPage; lp += stride) {
-      int32_t* m = d.map + pg[lp - r.pg_lo] * kPage;
-      for (int x = 0; x < kPage; ++x) {
-        const int pos = lp * kPage + x;
-        if (pos >= r.set_lo && pos < r.set_hi) {
-          const int32_t q = pos % d.ring_slots;
-          m[x] = rring[q / kPage] * kPage + q % kPage;
-        }
-      }
+  if (r.fpt_clear)  // cleared entries need no page id
+    for (int lp = r.fpt_lo + j0; lp < r.fpt_hi; lp += jstep) row[lp] = -1;
+  for (int j = j0; j < r.npg; j += jstep) {
+    const int32_t page = j == j0 ? first : pg[j];
+    const int32_t rpage = j == j0 ? rfirst : rg[j];
+    const int lp = r.pg_lo + j;
+    if (!r.fpt_clear && lp >= r.fpt_lo && lp < r.fpt_hi) row[lp] = page;
+    int32_t* m = d.map + (int64_t)page * kPage;
+    for (int x = 0; x < kPage; ++x) {
+      const int pos = lp * kPage + x;
+      if (pos >= r.clr_lo && pos < r.clr_hi) m[x] = -1;
+      if (pos >= r.set_lo && pos < r.set_hi) m[x] = rpage * kPage + x;
     }
   }
   // every read of the staging buffer by this block is complete
@@ -69,20 +62,20 @@ __global__ void __launch_bounds__(256) pool_apply_kernel(PoolDev d, const PoolRe
                        __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-int pool_apply_blocks(int n_recs, int64_t max_range) {
-  int64_t y = (max_range / kPage + 255) / 256;  // one page per thread
+int pool_apply_blocks(int n_recs, int32_t stride) {
+  int64_t y = ((int64_t)stride + 255) / 256;  // one listed page per thread
   if (y < 1) y = 1;
   if (y > 64) y = 64;
   return n_recs * (int)y;
 }
 
 hipError_t launch_pool_apply(const PoolDev& d, const PoolRec* recs, int n_recs,
-                             const int32_t* pages, int64_t max_range, int32_t* done,
+                             const int32_t* pages, int32_t stride, int32_t* done,
                              int32_t seq, hipStream_t s) {
   if (n_recs <= 0) return hipSuccess;
-  const int y = pool_apply_blocks(n_recs, max_range) / n_recs;
+  const int y = pool_apply_blocks(n_recs, stride) / n_recs;
   hipLaunchKernelGGL(pool_apply_kernel, dim3(n_recs, (unsigned)y), dim3(256), 0, s, d, recs,
-                     pages, done, seq);
+                     pages, stride, done, seq);
   return hipGetLastError();
 }
 

@@ -163,8 +163,9 @@ int check_ids(hswa_pool* p, int32_t n, const int32_t* ids) {
 // record's page list spans every logical page any of them touches.
 struct RecBuilder {
   std::vector<PoolRec> recs;
-  std::vector<int32_t> pages;
-  int64_t max_range = 0;
+  std::vector<int32_t> pages;  // records' page lists, back to back (at pg_off)
+  std::vector<int32_t> rpages; // ring page of each listed logical page
+  int32_t max_npg = 0;
 
   void add(const hswa_pool* p, int32_t b, int32_t new_len, int32_t clr_lo,
            int32_t clr_hi, int32_t set_lo, int32_t set_hi, int32_t fpt_lo,
@@ -198,23 +199,28 @@ struct RecBuilder {
     }
     r.pg_lo = (int32_t)lo;
     r.pg_off = (int32_t)pages.size();
-    for (int64_t lp = lo; lp < hi; ++lp) pages.push_back(page_src[lp]);
+    r.npg = (int32_t)(hi - lo);
+    const int32_t* ring = &p->rpt[(size_t)b * p->ring_pages_per_seq];
+    for (int64_t lp = lo; lp < hi; ++lp) {
+      pages.push_back(page_src[lp]);
+      rpages.push_back(ring[(lp * kPage) % p->C / kPage]);
+    }
     recs.push_back(r);
-    max_range = std::max<int64_t>(max_range, r.clr_hi - r.clr_lo);
-    max_range = std::max<int64_t>(max_range, r.set_hi - r.set_lo);
-    max_range = std::max<int64_t>(max_range, r.fpt_hi - r.fpt_lo);
+    max_npg = std::max(max_npg, r.npg);
   }
 };
 
 // Copies the records into a staging buffer and enqueues the apply kernel.
-// Buffer layout: records, page list, then one completion word per block.
+// Buffer layout: records, Full page lists (record x's at x * stride), ring
+// page lists (at (n_recs + x) * stride), then one completion word per block.
 int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
   if (!p->has_dev || rb.recs.empty()) return HSWA_OK;
   hipStream_t s = (hipStream_t)stream;
   const int n_recs = (int)rb.recs.size();
-  const int nblk = hswa::pool_apply_blocks(n_recs, rb.max_range);
+  const int32_t stride = std::max<int32_t>(1, rb.max_npg);
+  const int nblk = hswa::pool_apply_blocks(n_recs, stride);
   size_t rec_bytes = rb.recs.size() * sizeof(PoolRec);
-  size_t done_off = (rec_bytes + rb.pages.size() * sizeof(int32_t) + 63) / 64 * 64;
+  size_t done_off = (rec_bytes + 2 * (size_t)n_recs * stride * sizeof(int32_t) + 63) / 64 * 64;
   size_t bytes = done_off + (size_t)nblk * sizeof(int32_t);
   Stage& st = p->stage[p->next_stage];
   p->next_stage = (p->next_stage + 1) % kStages;
@@ -232,8 +238,15 @@ int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
     st.cap = cap;
   }
   memcpy(st.buf, rb.recs.data(), rec_bytes);
-  if (!rb.pages.empty())
-    memcpy((char*)st.buf + rec_bytes, rb.pages.data(), rb.pages.size() * sizeof(int32_t));
+  int32_t* lists = (int32_t*)((char*)st.buf + rec_bytes);
+  for (int x = 0; x < n_recs; ++x) {
+    const PoolRec& r = rb.recs[x];
+    if (r.npg > 0) {
+      memcpy(lists + (size_t)x * stride, rb.pages.data() + r.pg_off, r.npg * sizeof(int32_t));
+      memcpy(lists + (size_t)(n_recs + x) * stride, rb.rpages.data() + r.pg_off,
+             r.npg * sizeof(int32_t));
+    }
+  }
   void* dptr = nullptr;
   hipError_t e = hipHostGetDevicePointer(&dptr, st.buf, 0);
   if (e != hipSuccess) return hswa::hip_fail(e, "hipHostGetDevicePointer");
@@ -243,7 +256,7 @@ int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
   st.done = (volatile int32_t*)((char*)st.buf + done_off);
   for (int i = 0; i < nblk; ++i) st.done[i] = 0;
   e = hswa::launch_pool_apply(p->dev, (const PoolRec*)dptr, n_recs,
-                              (const int32_t*)((char*)dptr + rec_bytes), rb.max_range,
+                              (const int32_t*)((char*)dptr + rec_bytes), stride,
                               (int32_t*)((char*)dptr + done_off), st.seq, s);
   if (e != hipSuccess) return hswa::hip_fail(e, "pool table update launch");
   st.pending = true;

@@ -88,9 +88,11 @@ hipError_t launch_pool_apply(const PoolDev& d, const PoolRec* recs, int n_recs,
 template <int D, int KIND>
 __global__ void __launch_bounds__(256) append_kernel(AttnParams p, int tiles_per_seq) {
   __shared__ uint16_t vt[kPage][D + 8];
-  const int i = blockIdx.x / tiles_per_seq;
-  const int t = blockIdx.x % tiles_per_seq;
-  const int h = blockIdx.y;
+  // KV heads run fastest: the workgroups of one tile, resident together,
+  // read whole token rows [Hkv][d] of the input between them
+  const int h = blockIdx.x % p.hkv;
+  const int i = (blockIdx.x / p.hkv) / tiles_per_seq;
+  const int t = (blockIdx.x / p.hkv) % tiles_per_seq;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;  // invalid id: nothing to write
   const int row0 = p.cu_q ? p.cu_q[i] : i;
@@ -155,9 +157,9 @@ template <int D, int KIND>
 __global__ void __launch_bounds__(256) append_fp8_kernel(AttnParams p, int tiles_per_seq) {
   constexpr int CPR = D / 8;  // threads per row (8 elements each)
   __shared__ __attribute__((aligned(16))) uint8_t vt[kPage][D + 16];
-  const int i = blockIdx.x / tiles_per_seq;
-  const int t = blockIdx.x % tiles_per_seq;
-  const int h = blockIdx.y;
+  const int h = blockIdx.x % p.hkv;  // KV heads fastest, as in append_kernel
+  const int i = (blockIdx.x / p.hkv) / tiles_per_seq;
+  const int t = (blockIdx.x / p.hkv) % tiles_per_seq;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
   const int row0 = p.cu_q ? p.cu_q[i] : i;
@@ -234,7 +236,9 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(AttnParams p, int tiles
 hipError_t launch_append(const AttnParams& p, hipStream_t s) {
   if (p.num_seqs <= 0) return hipSuccess;
   const int tiles = (p.max_q_len + 14) / kPage + 1;
-  dim3 grid((unsigned)(p.num_seqs * tiles), (unsigned)p.hkv);
+  const int64_t blocks = (int64_t)p.num_seqs * tiles * p.hkv;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks);
   if (p.kv_fp8) {
     if (p.d == 128) {
       if (p.kind == 0)

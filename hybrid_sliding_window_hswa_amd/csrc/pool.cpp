@@ -165,7 +165,6 @@ struct RecBuilder {
   std::vector<PoolRec> recs;
   std::vector<int32_t> pages;  // records' page lists, back to back (at pg_off)
   std::vector<int32_t> rpages; // ring page of each listed logical page
-  int32_t max_npg = 0;
 
   void add(const hswa_pool* p, int32_t b, int32_t new_len, int32_t clr_lo,
            int32_t clr_hi, int32_t set_lo, int32_t set_hi, int32_t fpt_lo,
@@ -206,20 +205,17 @@ struct RecBuilder {
       rpages.push_back(ring[(lp * kPage) % p->C / kPage]);
     }
     recs.push_back(r);
-    max_npg = std::max(max_npg, r.npg);
   }
 };
 
-// Copies the records into a staging buffer and enqueues the apply kernel.
-// Buffer layout: records, Full page lists (record x's at x * stride), ring
-// page lists (at (n_recs + x) * stride), then one completion word per block.
-int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
-  if (!p->has_dev || rb.recs.empty()) return HSWA_OK;
-  hipStream_t s = (hipStream_t)stream;
-  const int n_recs = (int)rb.recs.size();
-  const int32_t stride = std::max<int32_t>(1, rb.max_npg);
+// Copies a group of records (rb.recs[idx[0..n_recs)]) into a staging buffer
+// and enqueues the apply kernel.  Buffer layout: records, Full page lists
+// (record x's at x * stride), ring page lists (at (n_recs + x) * stride),
+// then one completion word per block.
+int flush_group(hswa_pool* p, const RecBuilder& rb, const int* idx, int n_recs,
+                int32_t stride, hipStream_t s) {
   const int nblk = hswa::pool_apply_blocks(n_recs, stride);
-  size_t rec_bytes = rb.recs.size() * sizeof(PoolRec);
+  size_t rec_bytes = (size_t)n_recs * sizeof(PoolRec);
   size_t done_off = (rec_bytes + 2 * (size_t)n_recs * stride * sizeof(int32_t) + 63) / 64 * 64;
   size_t bytes = done_off + (size_t)nblk * sizeof(int32_t);
   Stage& st = p->stage[p->next_stage];
@@ -237,10 +233,11 @@ int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
     }
     st.cap = cap;
   }
-  memcpy(st.buf, rb.recs.data(), rec_bytes);
+  PoolRec* recs = (PoolRec*)st.buf;
   int32_t* lists = (int32_t*)((char*)st.buf + rec_bytes);
   for (int x = 0; x < n_recs; ++x) {
-    const PoolRec& r = rb.recs[x];
+    const PoolRec& r = rb.recs[idx[x]];
+    recs[x] = r;
     if (r.npg > 0) {
       memcpy(lists + (size_t)x * stride, rb.pages.data() + r.pg_off, r.npg * sizeof(int32_t));
       memcpy(lists + (size_t)(n_recs + x) * stride, rb.rpages.data() + r.pg_off,
@@ -260,6 +257,37 @@ int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
                               (int32_t*)((char*)dptr + done_off), st.seq, s);
   if (e != hipSuccess) return hswa::hip_fail(e, "pool table update launch");
   st.pending = true;
+  return HSWA_OK;
+}
+
+// Enqueues the records' device-table updates.  Each record is one sequence,
+// so they apply in any order.  Their page lists are padded to a common
+// length per launch: records go out longest list first, in groups whose
+// padded lists stay within twice their own size (plus 256 entries), which
+// is one group when the lists are alike (the usual case) and a few when one
+// list dwarfs the others.
+int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
+  if (!p->has_dev || rb.recs.empty()) return HSWA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int n = (int)rb.recs.size();
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return rb.recs[a].npg > rb.recs[b].npg; });
+  int i = 0;
+  while (i < n) {
+    const int32_t stride = std::max<int32_t>(1, rb.recs[order[i]].npg);
+    int64_t sum = 0;
+    int j = i;
+    for (; j < n; ++j) {
+      const int64_t npg = rb.recs[order[j]].npg;
+      if (j > i && (int64_t)(j - i + 1) * stride > 2 * (sum + npg) + 256) break;
+      sum += npg;
+    }
+    int rc = flush_group(p, rb, order.data() + i, j - i, stride, s);
+    if (rc) return rc;
+    i = j;
+  }
   return HSWA_OK;
 }
 

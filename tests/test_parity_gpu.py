@@ -87,6 +87,34 @@ def test_pool_device_tables_match_oracle(gpu, seed):
         assert t["rpt"].cpu().view(S, C // 16).tolist() == sim.rpt_table()
 
 
+def test_pool_tables_with_lopsided_page_lists(gpu):
+    """One sequence with thousands of pages next to many with one: the
+    table updates go out in several launches (page lists are padded per
+    launch), and every table still matches the oracle simulator."""
+    W, C, S = 64, 128, 48
+    maxp, npages = 400, 600
+    free = synth.permutation(npages, 9, 1)
+    ring = synth.permutation(S * C // 16, 9, 2)
+    pool = H.hswa_pool_create(W, C, S, maxp, npages, free, ring, device=dev())
+    sim = PoolSim(W, C, S, maxp, npages, free, ring)
+    t = pool.tables
+    ids = list(range(S))
+    n = [6000] + [1] * (S - 2) + [200]
+    assert [list(x) for x in H.hswa_pool_import(pool, ids, n)] == \
+        [list(x) for x in sim.import_context(ids, n)]
+    for step in range(3):
+        k = [3] * S
+        k[0] = 60
+        assert [list(x) for x in H.hswa_pool_alloc(pool, ids, k)] == \
+            [list(x) for x in sim.alloc(ids, k)]
+        assert [list(x) for x in H.hswa_pool_evict(pool, ids)] == \
+            [list(x) for x in sim.evict(ids)]
+    torch.cuda.synchronize()
+    assert t["seq_len"].cpu().tolist() == sim.seq_len_table()
+    assert t["fpt"].cpu().view(S, maxp).tolist() == sim.fpt_table()
+    assert t["map"].cpu().tolist() == sim.map_table()
+
+
 # ---------------------------------------------------------------------------
 # SWA single-chunk prefill then decode steps (one sequence, d = 64, g = 4)
 

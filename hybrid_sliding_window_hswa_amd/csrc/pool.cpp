@@ -10,12 +10,13 @@
 // sec. 3.
 //
 // The host keeps the authoritative metadata.  Each operation computes its
-// effect on the host, then enqueues one small kernel that applies the same
-// effect to the caller's device tables.  The kernel reads a compact record
-// list (position ranges and page ids, not per-slot values) straight from a
-// pinned, device-readable staging buffer; a ring of staging buffers with
-// one event each keeps the host from overwriting a buffer the device has
-// not read yet.
+// effect on the host, then enqueues one small kernel (a few, for very
+// uneven page lists) that applies the same effect to the caller's device
+// tables.  The kernel reads a compact record list (position ranges and page
+// ids, not per-slot values) straight from a pinned, device-readable staging
+// buffer; a ring of staging buffers, each with completion words that the
+// kernel's blocks write when done reading, keeps the host from overwriting
+// a buffer the device has not read yet.
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <string.h>

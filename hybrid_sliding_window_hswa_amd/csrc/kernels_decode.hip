@@ -127,6 +127,9 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, float (&red_o)[
   }
 }
 
+// Lazy rescaling of the bf16/fp16 decode (scores are in the log2 domain).
+constexpr float kDecLazy = 8.0f;
+
 template <int D, int KIND, int G, int QN, bool F8>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnParams p) {
@@ -332,6 +335,7 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     }
     f16x8 pf[NT];
     float alpha[NT];
+    bool resc[NT];  // wave-uniform: this tile's O is rescaled in this step
     for (int t = 0; t < NT; ++t) {
       float mx = -INFINITY;
       float sv[8];
@@ -345,9 +349,19 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
       }
       mx = fmaxf(mx, xor_lane(mx, 16));
       mx = fmaxf(mx, xor_lane(mx, 32));
-      const float m_new = fmaxf(m[t], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[t] = fast_exp2(m[t] - m_use);
+      // bf16/fp16 pages: the running max moves (and O is rescaled) only when
+      // a score exceeds it by more than 2^kDecLazy, so the fp16 weights stay
+      // <= 2^kDecLazy.  FP8 weights carry the V scale and move every step.
+      resc[t] = F8 || __builtin_amdgcn_ballot_w64(mx > m[t] + kDecLazy) != 0;
+      if (resc[t]) {
+        const float m_new = fmaxf(m[t], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        alpha[t] = fast_exp2(m[t] - m_use);
+        m[t] = m_new;
+      } else {
+        alpha[t] = 1.f;
+      }
+      const float m_use = m[t] == -INFINITY ? 0.f : m[t];
       float ps = 0.f;
       for (int j = 0; j < 8; ++j) {
         const float e = fast_exp2(sv[j] - m_use);
@@ -360,7 +374,6 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
         }
       }
       lsum[t] = lsum[t] * alpha[t] + ps;
-      m[t] = m_new;
     }
     Raw vmask;
     for (int x = 0; x < (int)(sizeof(Raw) / 4); ++x) vmask[x] = ~0u;
@@ -376,7 +389,7 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     for (int nb = 0; nb < NB; ++nb) {
       const f16x8 vf = vfrag(vr[nb], vmask);
       for (int t = 0; t < NT; ++t) {
-        o[t][nb] *= alpha[t];
+        if (resc[t]) o[t][nb] *= alpha[t];
         o[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[t], o[t][nb], 0, 0, 0);
       }
     }

@@ -62,7 +62,11 @@ constexpr float kLazy = 8.0f;
 
 // 16 bytes per lane from sbase + voff (the lane's byte offset) into LDS at
 // lds_base + 16 * lane.  The transfer counts on the vector-memory counter;
-// the kernel waits for it explicitly (the compiler does not see it).
+// the kernel waits for it explicitly (the compiler does not see it).  M0
+// (the LDS address of the transfer) is written inside the statement; the
+// compiler warns that it cannot preserve a clobbered M0, and nothing else
+// in these kernels uses M0 (no LDS-size or relative-addressing forms on
+// gfx950), so no value of its is live across the statement.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
                "s"(sbase)

@@ -30,9 +30,10 @@ Modules:
 * ``fp8``       -- FP8 (e4m3) KV quantization per token, head and tile with
   fp32 scales, and its dequantized values.
 
-Every function in these modules is pinned by ``tests/test_oracle.py`` and
-``tests/test_oracle_pool.py`` to something other than itself (library
-routines, brute force, closed forms, hand-worked fixtures); the one
+Every function in these modules is pinned by ``tests/test_oracle*.py`` to
+something other than itself (library routines, brute force, closed forms,
+hand-worked fixtures); ``tests/test_oracle_mutants.py`` plants mistakes in
+copies of these modules and checks that the pins catch them.  The one
 quantity with no pin is listed as "parity unpinned" in ``closed_forms``.
 """
 

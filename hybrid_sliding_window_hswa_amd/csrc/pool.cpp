@@ -248,8 +248,9 @@ int flush_group(hswa_pool* p, const RecBuilder& rb, const int* idx, int n_recs,
   void* dptr = nullptr;
   hipError_t e = hipHostGetDevicePointer(&dptr, st.buf, 0);
   if (e != hipSuccess) return hswa::hip_fail(e, "hipHostGetDevicePointer");
-  st.seq = ++p->flush_seq;
-  if (st.seq <= 0) st.seq = p->flush_seq = 1;  // positive, never a stale value
+  // positive and never a stale value; wraps to 1 before int32 overflow
+  p->flush_seq = p->flush_seq == INT32_MAX ? 1 : p->flush_seq + 1;
+  st.seq = p->flush_seq;
   st.nblk = nblk;
   st.done = (volatile int32_t*)((char*)st.buf + done_off);
   for (int i = 0; i < nblk; ++i) st.done[i] = 0;

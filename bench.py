@@ -556,6 +556,31 @@ def copy_calibration(cx):
     torch.cuda.empty_cache()
 
 
+def copy_ceiling(cx):
+    """Practical HBM ceiling measured in the same run: a plain 1 GiB
+    device-to-device copy (torch's copy kernel), timed with events on the
+    launch stream over 10 copies after 2 untimed ones.  GB/s counts the bytes
+    read plus the bytes written.  A copy is half writes; the decode kernels
+    only read, so they can exceed it."""
+    torch = cx.torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=cx.dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cx.stream)
+    for _ in range(10):
+        b.copy_(a)
+    e1.record(cx.stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / 10
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * n / sec / 1e9, 1)
+
+
 # ---------------------------------------------------------------------------
 # Workloads
 
@@ -594,7 +619,7 @@ def wl_swa_chunked_prefill(cx, args):
         line["decode"] = {**d["config"], "value": d["value"], "unit": d["unit"],
                           "frac": d["step_frac_of_hbm_peak"], "ms_per_step": d["ms_per_step"],
                           "roofline": d["roofline"], "full_call_us": d["full_call_us"],
-                          "swa_call_us": d["swa_call_us"]}
+                          "swa_call_us": d["swa_call_us"], "copy_ceiling": d["copy_ceiling"]}
     line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(cx, cp, args.cpu_seconds)
@@ -622,6 +647,8 @@ def wl_mixed_decode(cx, args):
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
     line["full_call_us"] = round(r["full_call_us"], 1)
     line["swa_call_us"] = round(r["swa_call_us"], 1)
+    cc = copy_ceiling(cx)
+    line["copy_ceiling"] = {"gbs": cc, "full_call_frac": round(r["full_gbs"] / cc, 4)}
     return line
 
 
@@ -867,6 +894,8 @@ def wl_long_decode(cx, args):
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
     line["full_call_us"] = round(r["full_call_us"], 1)
     line["swa_call_us"] = round(r["swa_call_us"], 1)
+    cc = copy_ceiling(cx)
+    line["copy_ceiling"] = {"gbs": cc, "full_call_frac": round(r["full_gbs"] / cc, 4)}
     return line
 
 

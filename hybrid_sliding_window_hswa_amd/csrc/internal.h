@@ -25,7 +25,7 @@ int hip_fail(hipError_t e, const char* what);
 // a pool operation; the kernel applies all records of one operation.
 struct PoolRec {
   int32_t seq;       // sequence id
-  int32_t new_len;   // seq_len after the operation
+  int32_t new_len;   // seq_len after the operation; < 0 leaves it unwritten
   int32_t clr_lo;    // positions [clr_lo, clr_hi) lose their SWA entry
   int32_t clr_hi;
   int32_t set_lo;    // positions [set_lo, set_hi) get map = their SWA slot

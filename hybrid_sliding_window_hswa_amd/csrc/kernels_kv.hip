@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(256) pool_apply_kernel(PoolDev d, const PoolRe
   const int32_t first = j0 < stride ? pg[j0] : 0;  // before the record arrives
   const int32_t rfirst = j0 < stride ? rg[j0] : 0;
   const PoolRec r = recs[blockIdx.x];
-  if (j0 == 0) d.seq_len[r.seq] = r.new_len;
+  if (j0 == 0 && r.new_len >= 0) d.seq_len[r.seq] = r.new_len;
   int32_t* row = d.fpt + (int64_t)r.seq * d.max_pages;
   if (r.fpt_clear)  // cleared entries need no page id
     for (int lp = r.fpt_lo + j0; lp < r.fpt_hi; lp += jstep) row[lp] = -1;

@@ -576,9 +576,9 @@ int hswa_pool_evict(hswa_pool* p, int32_t n, const int32_t* ids, int32_t* evicte
     }
     if (counts_out) counts_out[i] = cnt;
     p->res_start[b] = std::max(lo, keep_from);
+    // the device effect is map entries only (length and fpt unwritten)
     if (p->has_dev && cnt > 0)
-      rb.add(p, b, p->len[b], lo, lo + cnt, 0, 0, 0, 0, 0,
-             &p->fpt[(size_t)b * p->max_pages]);
+      rb.add(p, b, -1, lo, lo + cnt, 0, 0, 0, 0, 0, &p->fpt[(size_t)b * p->max_pages]);
   }
   return flush(p, rb, stream);
 }

@@ -189,7 +189,13 @@ int hswa_pool_alloc(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
  * nullable, capacity evicted_cap entries) receives the Full slots released,
  * ascending position per sequence, sequences in the order listed;
  * counts_out (host, nullable, n_seqs entries) the number per sequence.
- * HSWA_E_INVAL, with nothing changed, if evicted_cap is too small. */
+ * HSWA_E_INVAL, with nothing changed, if evicted_cap is too small.
+ * On the device the call writes only the map entries of the released
+ * positions: seq_len, fpt and rpt are left alone, and no attention kernel
+ * reads the map.  `stream` may therefore be a second stream on which the
+ * eviction overlaps attention over the same pool, provided it is ordered
+ * after the alloc that set those entries and before the next alloc,
+ * import, release or truncate of the pool (which may reuse their pages). */
 int hswa_pool_evict(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
                     int32_t* evicted_out, int64_t evicted_cap,
                     int32_t* counts_out, void* stream);

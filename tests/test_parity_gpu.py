@@ -339,3 +339,84 @@ def test_prefill_one_kv_head_share(gpu, kind):
 
 def test_decode_one_kv_head_share(gpu):
     _decode_scenario([20000, 4100, 129, 1], 2, 8, 1, 128, 128, 93, C=128 + 256)
+
+
+# ---------------------------------------------------------------------------
+# Evictions on a second stream, overlapping the append and attention
+
+
+def test_evictions_on_a_second_stream(gpu):
+    """Each chunk step's eviction runs on another stream right after the
+    step's alloc, beside its append and attention, with no host wait inside
+    the loop; the next alloc and the final table read wait for it.  The
+    outputs equal the same chunked prefill with evictions on the launch
+    stream bitwise, and the device tables equal the oracle simulator's."""
+    W, C, hq, hkv, d, chunk = 32, 32 + 128, 8, 2, 64, 128
+    lens = [300, 517, 90, 128]
+    B = len(lens)
+    seqs = make_seqs(lens, hq, hkv, d, seed=41)
+    maxp, npages = max(lens) // 16 + 2, B * (max(lens) // 16 + 2)
+
+    def run(side):
+        st = Setup(H.SWA, W, C, B, maxp, npages, hkv, d, seed=41)
+        main = torch.cuda.current_stream()
+        sim = PoolSim(W, C, B, maxp, npages, synth.permutation(npages, 41, 1),
+                      synth.permutation(B * C // 16, 41, 2))
+        outs = [torch.empty((L, hq, d), dtype=torch.float32, device=dev()) for L in lens]
+        vls = [torch.empty(L, dtype=torch.int32, device=dev()) for L in lens]
+        done, evicted = [0] * B, None
+        while True:
+            act = [b for b in range(B) if done[b] < lens[b]]
+            if not act:
+                break
+            n = [min(chunk, lens[b] - done[b]) for b in act]
+            if evicted is not None:
+                main.wait_event(evicted)
+            got = H.hswa_pool_alloc(st.pool, act, n)
+            exp = sim.alloc(act, n)
+            assert list(got[0]) == exp[0] and list(got[1]) == exp[1]
+            if side is not None:
+                allocated = torch.cuda.Event()
+                allocated.record(main)
+                side.wait_event(allocated)
+                got = H.hswa_pool_evict(st.pool, act, stream=side)
+                evicted = torch.cuda.Event()
+                evicted.record(side)
+            rows = [(b, done[b], done[b] + k) for b, k in zip(act, n)]
+            q = torch.cat([seqs[b].q[a:e] for b, a, e in rows]).to(dev())
+            kn = torch.cat([seqs[b].k[a:e] for b, a, e in rows]).to(dev())
+            vn = torch.cat([seqs[b].v[a:e] for b, a, e in rows]).to(dev())
+            cu = torch.tensor(np.concatenate([[0], np.cumsum(n)]), dtype=torch.int32,
+                              device=dev())
+            sid = torch.tensor(act, dtype=torch.int32, device=dev())
+            out = torch.empty((q.shape[0], hq, d), dtype=torch.float32, device=dev())
+            vl = torch.empty(q.shape[0], dtype=torch.int32, device=dev())
+            H.hswa_prefill_chunk(H.SWA, W, q, kn, vn, sid, cu, max(n), st.view, st.kc, st.vc,
+                                 out, vl)
+            if side is None:
+                got = H.hswa_pool_evict(st.pool, act)
+            exp = sim.evict(act)
+            assert list(got[0]) == exp[0] and list(got[1]) == exp[1]
+            o = 0
+            for b, a, e in rows:
+                outs[b][a:e].copy_(out[o:o + e - a])
+                vls[b][a:e].copy_(vl[o:o + e - a])
+                o += e - a
+            for b, k in zip(act, n):
+                done[b] += k
+        if evicted is not None:
+            main.wait_event(evicted)
+        torch.cuda.synchronize()
+        t = st.pool.tables
+        assert t["seq_len"].cpu().tolist() == sim.seq_len_table()
+        assert t["fpt"].cpu().view(B, maxp).tolist() == sim.fpt_table()
+        assert t["map"].cpu().tolist() == sim.map_table()
+        return [x.cpu() for x in outs], [x.cpu() for x in vls]
+
+    base, base_vl = run(None)
+    side = torch.cuda.Stream()   # default priority
+    overlapped, overlapped_vl = run(side)
+    for b in range(B):
+        assert torch.equal(base[b], overlapped[b]), f"sequence {b} differs"
+        assert torch.equal(base_vl[b], overlapped_vl[b])
+    _check_seq(overlapped, overlapped_vl, seqs, H.SWA, W)

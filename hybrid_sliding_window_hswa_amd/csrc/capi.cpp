@@ -404,6 +404,7 @@ int xfer(const hswa_xfer_args* a, bool to_host, void* stream) {
   p.cu_tok = a->cu_tok;
   p.first_pos = a->first_pos;
   p.max_tok = a->max_tok;
+  p.total_tok = a->total_tok;
   p.k_cache = (uint16_t*)a->k_cache;
   p.v_cache = (uint16_t*)a->v_cache;
   p.t.seq_len = v.seq_len;

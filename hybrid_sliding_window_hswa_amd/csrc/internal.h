@@ -114,6 +114,7 @@ struct XferParams {
                            // n_i = cu_tok[i+1]-cu_tok[i] positions from
   const int32_t* first_pos;  // [num_seqs] first_pos[i] on; nullptr: its last n_i
   int32_t max_tok;
+  int32_t total_tok;       // tokens the packed buffers hold
   uint16_t* k_cache;
   uint16_t* v_cache;
   Tables t;

@@ -156,7 +156,7 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   const int L = p.t.seq_len[sid];
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;  // rows: positions L-n .. L-1
-  if (n <= 0 || n > L) return;
+  if (n <= 0 || n > L || row0 < 0 || row0 + n > p.total_q) return;
   const int nr = min(n, QN);                         // rows computed here
   int klo, khi;  // keys [klo, khi) of this workgroup
   if (KIND == 0) {
@@ -442,7 +442,7 @@ decode_fp8_kernel(AttnParams p) {
   const int L = p.t.seq_len[sid];
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
-  if (n <= 0 || n > L) return;
+  if (n <= 0 || n > L || row0 < 0 || row0 + n > p.total_q) return;
   const int nr = min(n, QN);
   int klo, khi;
   if (KIND == 0) {
@@ -619,7 +619,7 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, int qn)
   const int L = p.t.seq_len[sid];
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
-  if (n <= 0 || n > L || r >= n) return;
+  if (n <= 0 || n > L || r >= n || row0 < 0 || row0 + n > p.total_q) return;
   const int ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
   const int64_t hrow = (int64_t)(row0 + r) * p.hq + h;
   const float* ml = p.ws + (int64_t)p.total_q * p.hq * p.n_splits * D;

@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(256) append_kernel(AttnParams p, int tiles_per
   const int L = p.t.seq_len[sid];
   const int p0 = L - n;
   const int tile_pos = (p0 / kPage + t) * kPage;
-  if (n <= 0 || n > L || tile_pos >= L) return;
+  if (n <= 0 || n > L || tile_pos >= L || row0 < 0 || row0 + n > p.total_q) return;
   const int lo = max(tile_pos, p0);
   const int hi = min(tile_pos + kPage, L);
   const bool whole = (lo == tile_pos) && (hi == tile_pos + kPage);
@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(AttnParams p, int tiles
   const int L = p.t.seq_len[sid];
   const int p0 = L - n;
   const int tile_pos = (p0 / kPage + t) * kPage;
-  if (n <= 0 || n > L || tile_pos >= L) return;
+  if (n <= 0 || n > L || tile_pos >= L || row0 < 0 || row0 + n > p.total_q) return;
   const int lo = max(tile_pos, p0);
   const int hi = min(tile_pos + kPage, L);
   const int32_t page = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile_pos, p.t.max_pages,
@@ -292,6 +292,7 @@ __global__ void __launch_bounds__(256) xfer_kernel(XferParams p, int tiles_per_s
   const int L = p.t.seq_len[sid];
   const int p0 = p.first_pos ? p.first_pos[i] : L - n;  // positions [p0, p0 + n)
   if (n <= 0 || p0 < 0 || p0 > L - n) return;  // only stored positions move
+  if (tok0 < 0 || tok0 + n > p.total_tok) return;  // tokens outside the buffers
   const int tile_pos = (p0 / kPage + t) * kPage;
   if (tile_pos >= p0 + n) return;
   const int lo = max(tile_pos, p0);

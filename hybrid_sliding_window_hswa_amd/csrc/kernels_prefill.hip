@@ -116,6 +116,7 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   if (sid < 0 || sid >= p.t.max_seqs) return;
   const int L = p.t.seq_len[sid];
   if (n > L) return;         // rows without allocated positions
+  if (row0 < 0 || row0 + n > p.total_q) return;  // rows outside q / out
   const int W = p.window;
   const int P0 = L - n + qb * QB;        // position of the workgroup's row 0
   const int nrows = min(QB, n - qb * QB);

@@ -266,7 +266,9 @@ typedef struct hswa_attn_args {
                                sequence's query rows; required by prefill,
                                optional for decode (NULL: one row each)     */
   int32_t total_q;          /* rows of q / out (= cu_q[num_seqs]; decode
-                               without cu_q: num_seqs)                      */
+                               without cu_q: num_seqs).  A sequence whose
+                               rows [cu_q[i], cu_q[i+1]) leave [0, total_q)
+                               is skipped: nothing of it is read or written */
   int32_t max_q_len;        /* max rows of one sequence (host hint sizing
                                the grid; must be >= the true max).  Decode
                                with cu_q: 1..4                               */
@@ -358,7 +360,9 @@ typedef struct hswa_xfer_args {
                                stream while allocs on another grow seq_len.
                                A sequence whose range is not below seq_len is
                                skipped.                                      */
-  int32_t total_tok;        /* cu_tok[num_seqs]                               */
+  int32_t total_tok;        /* cu_tok[num_seqs]; a sequence whose tokens
+                               [cu_tok[i], cu_tok[i+1]) leave [0, total_tok)
+                               is skipped                                    */
   int32_t max_tok;          /* host hint >= every per-sequence count          */
   hswa_pool_view pool;      /* from hswa_pool_get_view                       */
   void* k_cache;            /* this layer's K pages (layout above)           */

@@ -420,3 +420,52 @@ def test_evictions_on_a_second_stream(gpu):
         assert torch.equal(base[b], overlapped[b]), f"sequence {b} differs"
         assert torch.equal(base_vl[b], overlapped_vl[b])
     _check_seq(overlapped, overlapped_vl, seqs, H.SWA, W)
+
+
+# ---------------------------------------------------------------------------
+# Row offsets that leave the row buffers: the sequence is skipped
+
+
+def test_rows_beyond_total_q_are_skipped(gpu):
+    """cu_q gives sequence 1 more rows than q / out hold: its append and
+    attention are skipped (nothing read or written for it), while sequence
+    0 is computed as usual.  Prefill, then a two-row decode."""
+    hq, hkv, d, W, C = 8, 2, 64, 4, 32
+    seqs = make_seqs([7, 12], hq, hkv, d, 53)
+    st = Setup(H.SWA, W, C, 2, 4, 8, hkv, d, 53)
+    s0, s1 = seqs
+    sid = torch.tensor([0, 1], dtype=torch.int32, device=dev())
+
+    # prefill: sequence 0 has rows [0, 5), sequence 1 claims [5, 12) of 10
+    H.hswa_pool_alloc(st.pool, [0, 1], [5, 7])
+    q = torch.cat([s0.q[:5], s1.q[:5]]).to(dev())
+    kn = torch.cat([s0.k[:5], s1.k[:5]]).to(dev())
+    vn = torch.cat([s0.v[:5], s1.v[:5]]).to(dev())
+    cu = torch.tensor([0, 5, 12], dtype=torch.int32, device=dev())
+    out = torch.full((10, hq, d), 7.0, dtype=torch.float32, device=dev())
+    vl = torch.full((10,), -5, dtype=torch.int32, device=dev())
+    H.hswa_prefill_chunk(H.SWA, W, q, kn, vn, sid, cu, 7, st.view, st.kc, st.vc, out, vl)
+    torch.cuda.synchronize()
+    o = out.cpu().double().numpy()
+    assert np.all(o[5:] == 7.0) and np.all(vl.cpu().numpy()[5:] == -5)
+    assert float(np.max(np.abs(o[:5] - oracle_rows(s0, list(range(5)), OA.SWA, W)))) < TOL
+    assert vl.cpu().tolist()[:5] == [OA.valid_length(p, OA.SWA, W) for p in range(5)]
+    # sequence 1's ring slots were never written: still the NaN fill
+    assert torch.isnan(st.kc[torch.as_tensor(st.ring_pages[1].astype(np.int64))]).all()
+
+    # decode: sequence 0 has rows [0, 2), sequence 1 claims [2, 5) of 4
+    H.hswa_pool_evict(st.pool, [0, 1])
+    H.hswa_pool_alloc(st.pool, [0, 1], [2, 3])
+    q = torch.cat([s0.q[5:7], s1.q[7:9]]).to(dev())
+    kn = torch.cat([s0.k[5:7], s1.k[7:9]]).to(dev())
+    vn = torch.cat([s0.v[5:7], s1.v[7:9]]).to(dev())
+    cu = torch.tensor([0, 2, 5], dtype=torch.int32, device=dev())
+    out = torch.full((4, hq, d), 7.0, dtype=torch.float32, device=dev())
+    vl = torch.full((4,), -5, dtype=torch.int32, device=dev())
+    H.hswa_decode(H.SWA, W, q, kn, vn, sid, 10, st.view, st.kc, st.vc, out, None, vl,
+                  cu_q=cu, max_q_len=3)
+    torch.cuda.synchronize()
+    o = out.cpu().double().numpy()
+    assert np.all(o[2:] == 7.0) and np.all(vl.cpu().numpy()[2:] == -5)
+    assert float(np.max(np.abs(o[:2] - oracle_rows(s0, [5, 6], OA.SWA, W)))) < TOL
+    assert vl.cpu().tolist()[:2] == [W, W]

@@ -287,9 +287,48 @@ def kv_cache_alloc_fp8(num_pages: int, num_kv_heads: int, head_dim: int, device,
             torch.full(sc, float("nan"), dtype=torch.float32, device=device))
 
 
+def _expect(name, t, dtypes, shape=None, min_rows=None, device=True):
+    """Checks a tensor argument before its address reaches a kernel: the
+    dtype, the shape (None entries are free), a lower bound on the leading
+    dimension, and that it lives in device memory (a host address handed to
+    a kernel would fault)."""
+    if t is None:
+        return
+    if str(t.dtype) not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(dtypes)}, not {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != w
+                                         for g, w in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if min_rows is not None and t.shape[0] < min_rows:
+        raise ValueError(f"{name} has {t.shape[0]} rows, the call needs {min_rows}")
+
+
+_BF16, _F16, _F32, _I32, _U8 = ("torch.bfloat16",), ("torch.float16",), ("torch.float32",), \
+    ("torch.int32",), ("torch.uint8",)
+
+
 def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_seq_len,
           view, k_cache, v_cache, out, vlen, scale, k_scale=None,
           v_scale=None) -> _capi.AttnArgs:
+    fp8 = k_scale is not None
+    _expect("k_cache", k_cache, _U8 if fp8 else _BF16, (None, None, PAGE_SIZE, None))
+    hkv, d = k_cache.shape[1], k_cache.shape[3]
+    _expect("v_cache", v_cache, _U8 if fp8 else _F16, (k_cache.shape[0], hkv, d, PAGE_SIZE))
+    _expect("k_scale", k_scale, _F32, (k_cache.shape[0], hkv, PAGE_SIZE))
+    _expect("v_scale", v_scale, _F32, (k_cache.shape[0], hkv, PAGE_SIZE))
+    if fp8 and v_scale is None:
+        raise ValueError("FP8 pages need both k_scale and v_scale")
+    _expect("q", q, _BF16, (None, None, d), total_q)
+    _expect("k_new", k_new, _BF16, (None, hkv, d), total_q)
+    _expect("v_new", v_new, _BF16, (None, hkv, d), total_q)
+    _expect("seq_ids", seq_ids, _I32, (None,))
+    _expect("cu_q", cu_q, _I32, (seq_ids.shape[0] + 1,))
+    hq_ = q.shape[1] if q is not None else None
+    _expect("out", out, _F32 + _F16, (None, hq_, d), total_q)
+    _expect("vlen", vlen, _I32, (None,), total_q)
     a = _capi.AttnArgs()
     a.kind = kind
     a.window = window
@@ -387,6 +426,17 @@ def hswa_pool_window_counts(pool: Pool, kind: int, seq_ids: Sequence[int]) -> np
 
 def _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache, buf_k, buf_v,
                first_pos):
+    _expect("k_cache", k_cache, _BF16, (None, None, PAGE_SIZE, None))
+    hkv, d = k_cache.shape[1], k_cache.shape[3]
+    _expect("v_cache", v_cache, _F16, (k_cache.shape[0], hkv, d, PAGE_SIZE))
+    _expect("seq_ids", seq_ids, _I32, (None,))
+    _expect("cu_tok", cu_tok, _I32, (seq_ids.shape[0] + 1,))
+    _expect("first_pos", first_pos, _I32, (seq_ids.shape[0],))
+    # the packed buffers may be pinned host memory; the library checks that
+    _expect("buf_k", buf_k, _BF16 + _F16 + ("torch.int16",), (None, hkv, d), total_tok,
+            device=False)
+    _expect("buf_v", buf_v, _BF16 + _F16 + ("torch.int16",), (None, hkv, d), total_tok,
+            device=False)
     a = _capi.XferArgs()
     a.kind = kind
     a.num_kv_heads = k_cache.shape[1]

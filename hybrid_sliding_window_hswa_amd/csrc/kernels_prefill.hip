@@ -191,7 +191,10 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   auto issue = [&](int kp0, int buf) {
     const int32_t pg = kp0 + kPage * half <= wg_khi ? scalar_load_i32(prow, ipg) : 0;
     ipg += 2;
-    if (KIND != 0 && ipg >= npr) ipg -= npr;
+    if (KIND != 0) {  // two wraps: a ring of one page (npr = 1) steps past it twice
+      if (ipg >= npr) ipg -= npr;
+      if (ipg >= npr) ipg -= npr;
+    }
     const uint16_t* src =
         (const uint16_t*)((const uint8_t*)tens + (uint64_t)(uint32_t)pg * pbytes);
     const uint32_t base = lds0 + buf * SBYTES + wave * NIW * 1024;

@@ -469,3 +469,19 @@ def test_rows_beyond_total_q_are_skipped(gpu):
     assert np.all(o[2:] == 7.0) and np.all(vl.cpu().numpy()[2:] == -5)
     assert float(np.max(np.abs(o[:2] - oracle_rows(s0, [5, 6], OA.SWA, W)))) < TOL
     assert vl.cpu().tolist()[:2] == [W, W]
+
+
+# ---------------------------------------------------------------------------
+# A SWA ring of a single page (C = 16): the ring page index wraps twice per
+# 32-key step, so every step must come back to that page
+
+
+@pytest.mark.parametrize("W,chunk", [(5, 7), (9, 8), (1, 16)])
+def test_swa_ring_of_one_page(gpu, W, chunk):
+    hq, hkv, d = 4, 2, 64
+    lens = [258, 3, 40]
+    seqs = make_seqs(lens, hq, hkv, d, 97)
+    maxp = max(lens) // 16 + 2
+    st = Setup(H.SWA, W, 16, len(lens), maxp, len(lens) * maxp, hkv, d, 97)
+    outs, vlens, _ = chunked_prefill(st, seqs, chunk, hq)
+    _check_seq(outs, vlens, seqs, H.SWA, W)

@@ -203,3 +203,18 @@ def test_decode_reads_every_e4m3_code_exactly(gpu, kind):
     got = out.cpu().numpy()[0]
     assert np.array_equal(got.view(np.uint32) & 0x7FFFFFFF, want.view(np.uint32) & 0x7FFFFFFF) \
         and np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_fp8_decode_random_configuration(gpu, case):
+    """Seeded random shapes: contexts 1-3,000 tokens, GQA group, KV heads
+    1-3, d, window 1-200 (rings down to one page), 1-4 rows per sequence."""
+    import random
+    rnd = random.Random(9100 + case)
+    g, hkv = rnd.choice([1, 2, 4, 8]), rnd.choice([1, 2, 3])
+    d, W = rnd.choice([64, 128]), rnd.choice([1, 2, 5, 33, 128, 200])
+    ctxs = [rnd.randint(1, 3000) for _ in range(rnd.randint(1, 5))]
+    steps, rows = rnd.randint(1, 3), rnd.choice([1, 2, 3, 4])
+    print(f"case {case}: g {g} hkv {hkv} d {d} W {W} ctxs {ctxs} steps {steps} rows {rows}",
+          flush=True)
+    _fp8_decode_scenario(ctxs, steps, g * hkv, hkv, d, W, 300 + case, max_rows=rows)

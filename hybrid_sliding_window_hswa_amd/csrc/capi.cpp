@@ -256,11 +256,11 @@ int hswa_append_kv(const hswa_attn_args* a, void* stream) {
   bool decode = a && a->cu_q == nullptr;
   int rc = validate(a, decode, false, &p);
   if (rc) return rc;
+  if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;  // nothing to write
   if (!a->k_new) {
     hswa::set_error("append: k_new and v_new are required");
     return HSWA_E_INVAL;
   }
-  if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;
   hipError_t e = hswa::launch_append(p, (hipStream_t)stream);
   return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "append launch");
 }

@@ -322,9 +322,10 @@ int hswa_decode(const hswa_attn_args* args, void* workspace, size_t ws_bytes,
                 void* stream);
 size_t hswa_decode_workspace_bytes(const hswa_attn_args* args);
 
-/* KV append alone: writes k_new/v_new (both required) of the query rows
- * described as for hswa_prefill_chunk (cu_q given) or hswa_decode (cu_q
- * NULL: one row per sequence) into k_cache/v_cache.  No attention. */
+/* KV append alone: writes k_new/v_new (both required when there are rows)
+ * of the query rows described as for hswa_prefill_chunk (cu_q given) or
+ * hswa_decode (cu_q NULL: one row per sequence) into k_cache/v_cache.  No
+ * attention.  A call with no rows (num_seqs or total_q 0) does nothing. */
 int hswa_append_kv(const hswa_attn_args* args, void* stream);
 
 /* ------------------------------------------------------------------------

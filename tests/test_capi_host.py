@@ -311,3 +311,15 @@ def test_fp8_argument_validation():
     assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
     a = _args(kv_dtype=H.HSWA_KV_FP8, k_scale=1 << 20, v_scale=1 << 20)
     assert lib.hswa_prefill_chunk(C.byref(a), None) == H.HSWA_E_UNSUPPORTED
+
+
+def test_append_without_rows_is_a_noop():
+    """An append with no rows returns OK without needing k_new / v_new (no
+    kernel is launched); with rows, missing k_new / v_new is E_INVAL."""
+    lib = _capi.load()
+    a = _args(total_q=0, n=1, k_new=None, v_new=None)
+    assert lib.hswa_append_kv(C.byref(a), None) == H.HSWA_OK
+    a = _args(total_q=0, n=0, k_new=None, v_new=None)
+    assert lib.hswa_append_kv(C.byref(a), None) == H.HSWA_OK
+    a = _args(total_q=3, n=2, max_q_len=2, k_new=None, v_new=None)
+    assert lib.hswa_append_kv(C.byref(a), None) == H.HSWA_E_INVAL

@@ -167,3 +167,19 @@ def test_mtp_decode_two_rows_and_small_window(gpu):
 
 def test_mtp_decode_one_row_matches_plain_decode(gpu):
     _mtp_scenario([900, 33, 4100], 3, 64, 8, 128, 128, 641, max_rows=1, check_plain=True)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_mtp_decode_random_configuration(gpu, case):
+    """Seeded random shapes for multi-token verification with rejected
+    drafts: contexts 0-3,000 tokens, GQA group, KV heads 1-3, d, window
+    1-200 (rings down to one page), up to 2-4 rows per step."""
+    import random
+    rnd = random.Random(9300 + case)
+    g, hkv = rnd.choice([1, 2, 4, 8]), rnd.choice([1, 2, 3])
+    d, W = rnd.choice([64, 128]), rnd.choice([1, 2, 5, 33, 128, 200])
+    ctxs = [rnd.randint(0, 3000) for _ in range(rnd.randint(1, 5))]
+    steps, rows = rnd.randint(1, 4), rnd.choice([2, 3, 4])
+    print(f"case {case}: g {g} hkv {hkv} d {d} W {W} ctxs {ctxs} steps {steps} rows {rows}",
+          flush=True)
+    _mtp_scenario(ctxs, steps, g * hkv, hkv, d, W, 700 + case, max_rows=rows)

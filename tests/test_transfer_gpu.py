@@ -215,3 +215,27 @@ def test_explicit_positions_ignore_later_growth(gpu):
     torch.cuda.synchronize()
     assert torch.equal(bk[:T].view(torch.int16), bk0[:T].view(torch.int16))
     assert torch.equal(bv[:T].view(torch.int16), bv0[:T].view(torch.int16))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_offload_random_configuration(gpu, case):
+    """Seeded random shapes: KV heads 1-12, d, window 1-200 (rings down to
+    one page), 1-6 sequences of 0-3,000 tokens, pinned or device buffers;
+    the packed image of both layer kinds equals the oracle's bit for bit."""
+    import random
+    rnd = random.Random(9500 + case)
+    hkv, d = rnd.choice([1, 2, 3, 8, 12]), rnd.choice([64, 128])
+    W = rnd.choice([1, 2, 5, 33, 128, 200])
+    lens = [rnd.randint(0, 3000) for _ in range(rnd.randint(1, 6))]
+    pinned = rnd.random() < 0.5
+    print(f"case {case}: hkv {hkv} d {d} W {W} lens {lens} pinned {pinned}", flush=True)
+    k, v = _contexts(lens, hkv, d, 800 + case)
+    src = Layers(lens, hkv, d, W, 800 + case, 4)
+    src.fill(k, v)
+    for kind in (H.FULL, H.SWA):
+        (bk, bv), cnt = src.move(kind, True, pinned=pinned)
+        assert cnt == OT.transfer_counts(kind, lens, W)
+        ek, ev = OT.host_image(kind, W, [(_bits(k[b]), _bits(v[b])) for b in src.ids])
+        T = sum(cnt)
+        assert np.array_equal(_bits(bk)[:T].reshape(-1), ek.reshape(-1)), kind
+        assert np.array_equal(_bits(bv)[:T].reshape(-1), ev.reshape(-1)), kind

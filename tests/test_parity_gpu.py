@@ -485,3 +485,19 @@ def test_swa_ring_of_one_page(gpu, W, chunk):
     st = Setup(H.SWA, W, 16, len(lens), maxp, len(lens) * maxp, hkv, d, 97)
     outs, vlens, _ = chunked_prefill(st, seqs, chunk, hq)
     _check_seq(outs, vlens, seqs, H.SWA, W)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_decode_random_configuration(gpu, case):
+    """Seeded random single-row decode over a Full and a SWA layer: contexts
+    1-20,000 tokens (several splits), GQA group, KV heads 1-3, d, window
+    1-200 (ring slack drawn too)."""
+    rnd = random.Random(9700 + case)
+    g, hkv = rnd.choice([1, 2, 4, 8]), rnd.choice([1, 2, 3])
+    d, W = rnd.choice([64, 128]), rnd.choice([1, 2, 5, 33, 128, 200])
+    ctxs = [rnd.randint(1, 20000) for _ in range(rnd.randint(1, 6))]
+    C = 16 * (-(-W // 16)) + rnd.choice([0, 16, 64])
+    steps = rnd.randint(1, 3)
+    print(f"case {case}: g {g} hkv {hkv} d {d} W {W} C {C} ctxs {ctxs} steps {steps}",
+          flush=True)
+    _decode_scenario(ctxs, steps, g * hkv, hkv, d, W, 900 + case, C=C)

@@ -105,3 +105,36 @@ def test_random_configuration(gpu, case):
             L = cur[b] + n[b]
             st.poison_ring_positions(b, list(range(L - W + 1 - cnt[b], L - W + 1)))
             cur[b] = L
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_large_configuration(gpu, case):
+    """Longer random prefills (up to 6,000 tokens, chunks up to 2,048, up to
+    64 query heads) checked on sampled rows: every chunk's first and last
+    rows, the window edges, and 200 random rows per sequence."""
+    rnd = random.Random(7500 + case)
+    kind = rnd.choice([H.SWA, H.FULL])
+    d, g, hkv = rnd.choice([64, 128]), rnd.choice([1, 2, 4, 8]), rnd.choice([1, 2, 8])
+    W = rnd.choice([16, 100, 128, 129, 256])
+    chunk = rnd.choice([256, 1000, 2048])
+    lens = [rnd.randint(1, 6000) for _ in range(rnd.randint(1, 3))]
+    hq = g * hkv
+    print(f"case {case}: kind {kind} d {d} g {g} hkv {hkv} W {W} chunk {chunk} lens {lens}",
+          flush=True)
+    seqs = make_seqs(lens, hq, hkv, d, 500 + case)
+    C = -(-(W - 1 + chunk) // 16) * 16
+    maxp = max(lens) // 16 + 2
+    st = Setup(kind, W, C, len(lens), maxp, len(lens) * maxp + 3, hkv, d, 500 + case)
+    outs, vlens, _ = chunked_prefill(st, seqs, chunk, hq)
+    for b, s in enumerate(seqs):
+        L = lens[b]
+        pick = {0, L - 1, min(L - 1, W - 1), min(L - 1, W)}
+        for a in range(0, L, chunk):
+            pick |= {a, min(L - 1, a + chunk - 1)}
+        pick |= set(rnd.randrange(L) for _ in range(200))
+        pos = sorted(pick)
+        got = outs[b][pos].double().numpy()
+        assert np.all(np.isfinite(got)), f"non-finite output in sequence {b}"
+        err = float(np.max(np.abs(got - oracle_rows(s, pos, kind, W))))
+        assert err < TOL, f"sequence {b}: max-abs error {err:.3e}"
+        assert vlens[b][pos].tolist() == [OA.valid_length(p, kind, W) for p in pos]

@@ -501,3 +501,66 @@ def test_decode_random_configuration(gpu, case):
     print(f"case {case}: g {g} hkv {hkv} d {d} W {W} C {C} ctxs {ctxs} steps {steps}",
           flush=True)
     _decode_scenario(ctxs, steps, g * hkv, hkv, d, W, 900 + case, C=C)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_pool_device_tables_random_with_truncate(gpu, seed):
+    """Random alloc / evict / import / truncate / release sequences on random
+    geometries (windows 1-200, rings from one page): host results and all
+    four device tables bit-exact against the oracle simulator after every
+    operation, refused operations included."""
+    rnd = random.Random(4000 + seed)
+    W = rnd.choice([1, 2, 5, 16, 33, 128, 200])
+    C = 16 * (-(-W // 16) + rnd.choice([0, 0, 1, 3]))
+    S, maxp = rnd.randint(1, 6), rnd.randint(2, 30)
+    npages = rnd.randint(4, S * maxp)
+    free = synth.permutation(npages, 40 + seed, 1)
+    ring = synth.permutation(S * C // 16, 40 + seed, 2)
+    pool = H.hswa_pool_create(W, C, S, maxp, npages, free, ring, device=dev())
+    sim = PoolSim(W, C, S, maxp, npages, free, ring)
+    t = pool.tables
+    for step in range(100):
+        ids = rnd.sample(range(S), rnd.randint(1, S))
+        r = rnd.random()
+        if r < 0.4:
+            n = [rnd.choice([0, 1, 2, 4, 16, rnd.randint(0, C)]) for _ in ids]
+            try:
+                exp = sim.alloc(ids, n)
+            except NoSpace:
+                with pytest.raises(H.NoSpace):
+                    H.hswa_pool_alloc(pool, ids, n)
+                continue
+            got = H.hswa_pool_alloc(pool, ids, n)
+            assert list(got[0]) == exp[0] and list(got[1]) == exp[1]
+        elif r < 0.55:
+            # cut back up to 4 drafts, or far below the window (refused)
+            lens = [max(0, sim.length[i] - rnd.choice([0, 1, 3, 4, W + 5])) for i in ids]
+            try:
+                sim.truncate(ids, lens)
+            except ValueError:
+                with pytest.raises(H.HswaError):
+                    H.hswa_pool_truncate(pool, ids, lens)
+                continue
+            H.hswa_pool_truncate(pool, ids, lens)
+        elif r < 0.85:
+            exp = sim.evict(ids)
+            got = H.hswa_pool_evict(pool, ids)
+            assert list(got[0]) == exp[0] and list(got[1]) == exp[1]
+        elif r < 0.95:
+            n = [rnd.randint(0, 3 * W + 20) for _ in ids]
+            try:
+                exp = sim.import_context(ids, n)
+            except NoSpace:
+                with pytest.raises(H.NoSpace):
+                    H.hswa_pool_import(pool, ids, n)
+                continue
+            got = H.hswa_pool_import(pool, ids, n)
+            assert list(got[0]) == exp[0] and list(got[1]) == exp[1]
+        else:
+            sim.release(ids)
+            H.hswa_pool_release(pool, ids)
+        torch.cuda.synchronize()
+        assert t["seq_len"].cpu().tolist() == sim.seq_len_table()
+        assert t["fpt"].cpu().view(S, maxp).tolist() == sim.fpt_table()
+        assert t["map"].cpu().tolist() == sim.map_table()
+        assert t["rpt"].cpu().view(S, C // 16).tolist() == sim.rpt_table()

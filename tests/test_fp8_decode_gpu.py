@@ -87,7 +87,28 @@ def test_quantizing_append_matches_oracle(gpu, d, hkv):
     # a few rows scaled far down and one all-zero row: subnormal codes, zero scale
     k[0][3] *= 1e-4
     v[2][5] = 0
-    P = Fp8Pool(lens, hkv, d, W, 5)
+    _check_quantizing_append(lens, hkv, d, W, 5, k, v)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_quantizing_append_random_configuration(gpu, case):
+    """Seeded random shapes: KV heads 1-12, d, window 1-200 (rings down to
+    one page), 1-6 sequences of 1-1,500 tokens (partial page tiles)."""
+    import random
+    rnd = random.Random(9900 + case)
+    hkv, d = rnd.choice([1, 2, 3, 8, 12]), rnd.choice([64, 128])
+    W = rnd.choice([1, 2, 5, 33, 128, 200])
+    lens = [rnd.randint(1, 1500) for _ in range(rnd.randint(1, 6))]
+    print(f"case {case}: hkv {hkv} d {d} W {W} lens {lens}", flush=True)
+    k = [synth.bf16_normal((L, hkv, d), 60 + case, 0, b, synth.ROLE_K) for b, L in enumerate(lens)]
+    v = [synth.bf16_normal((L, hkv, d), 60 + case, 0, b, synth.ROLE_V) for b, L in enumerate(lens)]
+    _check_quantizing_append(lens, hkv, d, W, 60 + case, k, v)
+
+
+def _check_quantizing_append(lens, hkv, d, W, seed, k, v):
+    """Codes and scales of every stored position equal the oracle
+    quantizer's, bit for bit, in both the Full pages and the SWA ring."""
+    P = Fp8Pool(lens, hkv, d, W, seed)
     P.append_context(k, v, lens)
     torch.cuda.synchronize()
     for kind in (H.FULL, H.SWA):

@@ -17,7 +17,7 @@ from harness import TOL, SeqData, Setup, chunked_prefill, dev, make_seqs, oracle
 
 pytestmark = pytest.mark.gpu
 
-CASES = 64
+CASES = 128
 
 
 def _draw(case):

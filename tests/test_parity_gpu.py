@@ -513,7 +513,7 @@ def test_pool_device_tables_random_with_truncate(gpu, seed):
     W = rnd.choice([1, 2, 5, 16, 33, 128, 200])
     C = 16 * (-(-W // 16) + rnd.choice([0, 0, 1, 3]))
     S, maxp = rnd.randint(1, 6), rnd.randint(2, 30)
-    npages = rnd.randint(4, S * maxp)
+    npages = rnd.randint(2, max(4, S * maxp))
     free = synth.permutation(npages, 40 + seed, 1)
     ring = synth.permutation(S * C // 16, 40 + seed, 2)
     pool = H.hswa_pool_create(W, C, S, maxp, npages, free, ring, device=dev())

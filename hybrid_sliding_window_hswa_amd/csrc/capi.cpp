@@ -384,6 +384,11 @@ int xfer(const hswa_xfer_args* a, bool to_host, void* stream) {
     hswa::set_error("pool view is invalid");
     return HSWA_E_INVAL;
   }
+  if (a->kind == HSWA_LAYER_SWA && a->max_tok > v.ring_slots) {
+    hswa::set_error("SWA transfer of %d positions per sequence: the ring holds %d", a->max_tok,
+                    v.ring_slots);
+    return HSWA_E_INVAL;
+  }
   if (!a->seq_ids || !a->cu_tok || !a->k_cache || !a->v_cache || !a->buf_k || !a->buf_v) {
     hswa::set_error("seq_ids, cu_tok, k_cache, v_cache, buf_k and buf_v must be set");
     return HSWA_E_INVAL;

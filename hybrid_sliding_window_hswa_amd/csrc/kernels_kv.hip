@@ -295,8 +295,12 @@ __global__ void __launch_bounds__(256) xfer_kernel(XferParams p, int tiles_per_s
   if (tok0 < 0 || tok0 + n > p.total_tok) return;  // tokens outside the buffers
   const int tile_pos = (p0 / kPage + t) * kPage;
   if (tile_pos >= p0 + n) return;
-  const int lo = max(tile_pos, p0);
+  // A SWA ring of C slots holds at most positions [L - C, L): an older
+  // position's slot belongs to a newer one, so it is neither read (offload)
+  // nor written (restore, which would overwrite live K/V).
+  const int lo = max(max(tile_pos, p0), KIND == 0 ? 0 : L - p.t.ring_slots);
   const int hi = min(tile_pos + kPage, p0 + n);
+  if (lo >= hi) return;
   const int32_t page = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile_pos, p.t.max_pages,
                                      p.t.ring_slots);
   if (page < 0) return;  // position without a page: the caller skipped alloc

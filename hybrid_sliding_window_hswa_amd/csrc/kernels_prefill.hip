@@ -185,7 +185,8 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   const int npr = p.t.ring_slots / kPage;             // ring pages of a sequence (SWA)
   const int32_t* prow = KIND == 0 ? p.t.fpt + (int64_t)sid * p.t.max_pages
                                   : p.t.rpt + (int64_t)sid * npr;
-  int ipg = KIND == 0 ? kstart / kPage + half : ((kstart + kPage * half) % p.t.ring_slots) / kPage;
+  int ipg = KIND == 0 ? kstart / kPage + half
+                      : ((kstart + kPage * half) % p.t.ring_slots) / kPage;
   // a page past the range reads page 0 (present in every pool); its keys are
   // masked like any other key outside the range
   auto issue = [&](int kp0, int buf) {
@@ -362,6 +363,24 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   }
   if (row_ok && p.vlen && kvh == 0 && hl == 0 && h2 == 0)
     p.vlen[grow] = KIND == 0 ? my_pos + 1 : min(my_pos + 1, W);
+
+  // The grid holds qblocks query blocks per sequence, sized by the caller's
+  // max_q_len.  Rows past them (a hint below the true row count) are not
+  // computed; the last block's workgroups fill them with NaN (vlen -1) so
+  // the violation shows instead of leaving stale output.
+  if (qb == qblocks - 1 && n > qblocks * QB) {
+    const int64_t rlo = (int64_t)row0 + qblocks * QB, rhi = (int64_t)row0 + n;
+    for (int64_t e = tid; e < (rhi - rlo) * HPW * D; e += kPreThreads) {
+      const int64_t r = rlo + e / (HPW * D);
+      const int hh = kvh * G + hg * HPW + (int)((e / D) % HPW);
+      const int64_t idx = (r * hq + hh) * D + e % D;
+      if (p.out_f16)
+        ((_Float16*)p.out)[idx] = (_Float16)__builtin_nanf("");
+      else
+        ((float*)p.out)[idx] = __builtin_nanf("");
+      if (p.vlen && kvh == 0 && hg == 0 && e % (HPW * D) == 0) p.vlen[r] = -1;
+    }
+  }
 }
 
 template <int D, int KIND, int G>

@@ -270,9 +270,15 @@ typedef struct hswa_attn_args {
                                rows [cu_q[i], cu_q[i+1]) leave [0, total_q)
                                is skipped: nothing of it is read or written */
   int32_t max_q_len;        /* max rows of one sequence (host hint sizing
-                               the grid; must be >= the true max).  Decode
-                               with cu_q: 1..4                               */
-  int32_t max_seq_len;      /* decode: >= every listed sequence's length     */
+                               the grid; must be >= the true max).  Prefill
+                               rows past a smaller hint are not computed:
+                               they are written as NaN, with vlen_out -1.
+                               Decode with cu_q: 1..4                        */
+  int32_t max_seq_len;      /* decode: the longest listed sequence's length
+                               (host hint sizing the split-K plan and the
+                               workspace).  A smaller hint costs speed, not
+                               correctness: a longer sequence is cut into
+                               the planned number of (longer) splits        */
   const void* q;            /* device bf16 [total_q][Hq][head_dim]          */
   const void* k_new;        /* device bf16 [total_q][Hkv][head_dim] or NULL  */
   const void* v_new;        /* device bf16 [total_q][Hkv][head_dim] or NULL  */
@@ -364,7 +370,12 @@ typedef struct hswa_xfer_args {
   int32_t total_tok;        /* cu_tok[num_seqs]; a sequence whose tokens
                                [cu_tok[i], cu_tok[i+1]) leave [0, total_tok)
                                is skipped                                    */
-  int32_t max_tok;          /* host hint >= every per-sequence count          */
+  int32_t max_tok;          /* host hint >= every per-sequence count; SWA:
+                               at most ring_slots (HSWA_E_INVAL otherwise).
+                               SWA positions below seq_len - ring_slots are
+                               no longer in the ring (their slots hold newer
+                               positions): offload leaves their buffer rows
+                               unwritten and restore does not write them    */
   hswa_pool_view pool;      /* from hswa_pool_get_view                       */
   void* k_cache;            /* this layer's K pages (layout above)           */
   void* v_cache;            /* this layer's V pages                          */

@@ -20,10 +20,12 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _capi
-from ._capi import (HSWA_E_HIP, HSWA_E_INVAL, HSWA_E_NOSPC, HSWA_E_UNSUPPORTED, HSWA_KV_BF16,
-                    HSWA_KV_FP8, HSWA_LAYER_FULL, HSWA_LAYER_SWA, HSWA_OK)
+from ._capi import (HSWA_DECODE_SCRATCH_BYTES, HSWA_E_HIP, HSWA_E_INVAL, HSWA_E_NOSPC,
+                    HSWA_E_UNSUPPORTED, HSWA_KV_BF16, HSWA_KV_FP8, HSWA_LAYER_FULL,
+                    HSWA_LAYER_SWA, HSWA_OK)
 
 PAGE_SIZE = 16
+DECODE_SCRATCH_BYTES = HSWA_DECODE_SCRATCH_BYTES
 FULL = HSWA_LAYER_FULL
 SWA = HSWA_LAYER_SWA
 
@@ -33,6 +35,7 @@ __all__ = [
     "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_truncate",
     "hswa_pool_match_len", "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
+    "hswa_decode_noalloc", "DECODE_SCRATCH_BYTES",
     "hswa_pool_window_counts", "hswa_kv_offload", "hswa_kv_restore",
     "hswa_last_error", "hswa_version", "kv_cache_shapes", "kv_cache_alloc",
     "kv_cache_alloc_fp8", "library",
@@ -399,6 +402,19 @@ def hswa_decode(kind: int, window: int, q, k_new, v_new, seq_ids, max_seq_len: i
     ws = _dptr(workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().hswa_decode(C.byref(a), ws, nbytes, _stream(stream)))
+
+
+def hswa_decode_noalloc(kind: int, window: int, q, k_new, v_new, seq_ids, max_seq_len: int,
+                        view, k_cache, v_cache, out, vlen=None, scale: float = 0.0,
+                        stream=None, cu_q=None, max_q_len: int = 1, k_scale=None,
+                        v_scale=None) -> None:
+    """hswa_decode without a workspace: the split-K state goes to the
+    library's device scratch (no allocation).  Calls on one GPU share it, so
+    keep them on one stream."""
+    a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0],
+              max_q_len if cu_q is not None else 1, max_seq_len, view, k_cache, v_cache, out,
+              vlen, scale, k_scale, v_scale)
+    _check(library().hswa_decode_noalloc(C.byref(a), _stream(stream)))
 
 
 def hswa_append_kv(kind: int, k_new, v_new, seq_ids, view, k_cache, v_cache, cu_q=None,

@@ -22,6 +22,7 @@ HSWA_KV_BF16 = 0
 HSWA_KV_FP8 = 1
 HSWA_LAYER_FULL = 0
 HSWA_LAYER_SWA = 1
+HSWA_DECODE_SCRATCH_BYTES = 128 << 20
 
 I32P = C.POINTER(C.c_int32)
 
@@ -32,6 +33,7 @@ EXPORTED = (
     "hswa_pool_alloc", "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release",
     "hswa_pool_truncate", "hswa_pool_match_len", "hswa_pool_read_tables",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
+    "hswa_decode_noalloc",
     "hswa_pool_window_counts", "hswa_kv_offload", "hswa_kv_restore",
 )
 
@@ -160,6 +162,8 @@ def load():
         f.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
     lib.hswa_decode.restype = C.c_int
     lib.hswa_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.hswa_decode_noalloc.restype = C.c_int
+    lib.hswa_decode_noalloc.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
     lib.hswa_pool_window_counts.restype = C.c_int
     lib.hswa_pool_window_counts.argtypes = [C.c_void_p, C.c_int32, C.c_int32, I32P, I32P]
     for name in ("hswa_kv_offload", "hswa_kv_restore"):

@@ -198,7 +198,60 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
   return HSWA_OK;
 }
 
+// Body of hswa_decode and hswa_decode_noalloc.  With `noalloc` the split-K
+// partial states go to the library's device scratch (refused when the plan
+// needs more than it holds) instead of the caller's workspace; both use the
+// same plan, hence the same kernels and bitwise the same results.
+int decode_call(const hswa_attn_args* a, void* ws, size_t ws_bytes, bool noalloc,
+                void* stream) {
+  hswa::clear_error();
+  hswa::AttnParams p;
+  int rc = validate(a, true, true, &p);
+  if (rc) return rc;
+  if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;
+  hswa::DecodePlan pl = hswa::plan_decode(p.kind, p.num_seqs, p.total_q, p.hq, p.hkv, p.d,
+                                          p.window, p.max_seq_len);
+  if (noalloc) {
+    if (pl.ws_bytes > hswa::kDecodeScratchBytes) {
+      hswa::set_error("decode_noalloc: the split-K state needs %zu bytes, the device scratch "
+                      "holds %zu; use hswa_decode with a workspace",
+                      pl.ws_bytes, hswa::kDecodeScratchBytes);
+      return HSWA_E_INVAL;
+    }
+    ws = nullptr;
+    if (pl.ws_bytes > 0) {
+      float* s = nullptr;
+      hipError_t e = hswa::decode_scratch(&s);
+      if (e != hipSuccess) return hswa::hip_fail(e, "device scratch address");
+      ws = s;
+    }
+  } else {
+    if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) {
+      hswa::set_error("decode workspace: %zu bytes given, %zu needed", ws_bytes, pl.ws_bytes);
+      return HSWA_E_INVAL;
+    }
+    if (ws && !aligned16(ws)) {
+      hswa::set_error("workspace must be 16-byte aligned");
+      return HSWA_E_INVAL;
+    }
+  }
+  p.n_splits = pl.n_splits;
+  p.split_len = pl.split_len;
+  p.ws = (float*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (p.k_new) {
+    e = hswa::launch_append(p, s);
+    if (e != hipSuccess) return hswa::hip_fail(e, "append launch");
+  }
+  e = hswa::launch_decode(p, s);
+  return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "decode launch");
+}
+
 }  // namespace
+
+static_assert(HSWA_DECODE_SCRATCH_BYTES == hswa::kDecodeScratchBytes,
+              "header and library agree on the decode scratch size");
 
 namespace hswa {
 
@@ -296,32 +349,11 @@ size_t hswa_decode_workspace_bytes(const hswa_attn_args* a) {
 }
 
 int hswa_decode(const hswa_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
-  hswa::clear_error();
-  hswa::AttnParams p;
-  int rc = validate(a, true, true, &p);
-  if (rc) return rc;
-  if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;
-  hswa::DecodePlan pl = hswa::plan_decode(p.kind, p.num_seqs, p.total_q, p.hq, p.hkv, p.d,
-                                          p.window, p.max_seq_len);
-  if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) {
-    hswa::set_error("decode workspace: %zu bytes given, %zu needed", ws_bytes, pl.ws_bytes);
-    return HSWA_E_INVAL;
-  }
-  if (ws && !aligned16(ws)) {
-    hswa::set_error("workspace must be 16-byte aligned");
-    return HSWA_E_INVAL;
-  }
-  p.n_splits = pl.n_splits;
-  p.split_len = pl.split_len;
-  p.ws = (float*)ws;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  if (p.k_new) {
-    e = hswa::launch_append(p, s);
-    if (e != hipSuccess) return hswa::hip_fail(e, "append launch");
-  }
-  e = hswa::launch_decode(p, s);
-  return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "decode launch");
+  return decode_call(a, ws, ws_bytes, false, stream);
+}
+
+int hswa_decode_noalloc(const hswa_attn_args* a, void* stream) {
+  return decode_call(a, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

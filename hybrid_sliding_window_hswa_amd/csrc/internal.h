@@ -128,6 +128,14 @@ hipError_t launch_xfer(const XferParams& p, bool to_host, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);
 hipError_t launch_decode(const AttnParams& p, hipStream_t stream);
 
+// Device scratch of the allocation-free decode (hswa_decode_noalloc): the
+// split-K partial states of one call live in a file-scope device array of
+// this many bytes instead of a caller's workspace.
+constexpr size_t kDecodeScratchBytes = (size_t)128 << 20;
+// Device address of this GPU's copy of that array (the current device's),
+// looked up once per device.
+hipError_t decode_scratch(float** out);
+
 // Split-K plan for decode: shared by the workspace query and the launch.
 struct DecodePlan {
   int32_t n_splits;

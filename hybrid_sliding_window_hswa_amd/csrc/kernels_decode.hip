@@ -43,6 +43,8 @@
 //    positions, never on where pages sit in memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -683,6 +685,42 @@ hipError_t launch_decode_g(const AttnParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Split-K partial states of the allocation-free decode entry point.  Each
+// GPU the library runs on holds its own copy of this array (allocated with
+// the code object, kept until the process ends).  In host code its name
+// stands for a host-side shadow, not a device address: kernels receive the
+// address that hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!a) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    a = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!a) {
+      void* ptr = nullptr;  // this device is current
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!ptr) return hipErrorInvalidSymbol;
+      a = (float*)ptr;
+      g_scratch_addr[dev].store(a, std::memory_order_release);
+    }
+  }
+  *out = a;
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const AttnParams& p, hipStream_t s) {
   if (p.num_seqs <= 0) return hipSuccess;

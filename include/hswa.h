@@ -328,6 +328,24 @@ int hswa_decode(const hswa_attn_args* args, void* workspace, size_t ws_bytes,
                 void* stream);
 size_t hswa_decode_workspace_bytes(const hswa_attn_args* args);
 
+/* Decode without allocation, for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, plan, kernels and
+ * results (bitwise) as hswa_decode with a workspace of
+ * hswa_decode_workspace_bytes(args) bytes; the split-K partial states go
+ * instead to a device array of HSWA_DECODE_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends (its address is
+ * looked up on the first call on a device).  No memory is allocated and
+ * nothing in the array needs clearing between calls.  HSWA_E_INVAL, with
+ * nothing launched, when the call needs more than the array holds
+ * (hswa_decode_workspace_bytes(args) > HSWA_DECODE_SCRATCH_BYTES, e.g.
+ * 1,024 rows of 64 heads at d = 128 over 8 splits).  Every call on one GPU
+ * shares the array: calls whose device work overlaps (other streams, other
+ * host threads) race and give undefined results, so issue them in order on
+ * one stream. */
+#define HSWA_DECODE_SCRATCH_BYTES ((size_t)128 << 20)
+int hswa_decode_noalloc(const hswa_attn_args* args, void* stream);
+
 /* KV append alone: writes k_new/v_new (both required when there are rows)
  * of the query rows described as for hswa_prefill_chunk (cu_q given) or
  * hswa_decode (cu_q NULL: one row per sequence) into k_cache/v_cache.  No

@@ -12,8 +12,12 @@ resident in HBM before the timed region starts):
       seeded random permutation.  One step = the whole chunked prefill of the
       batch: for every chunk, pool alloc (joint capacity check + device table
       update), KV append, SWA attention, out-of-window eviction; then release.
-      `value` = prefill tokens/s.  The same run times the mixed decode below
-      and reports it under "decode".
+      `value` = prefill tokens/s.  The same run measures the other four
+      configurations and embeds each, with its own roofline and oracle
+      baseline: the mixed decode under "decode", the single-chunk run under
+      "single_chunk", the 70-layer stack under "hybrid_stack" and the
+      long-context decode under "long_decode" (--headline-only skips the
+      last three).
   mixed_decode
       256 sequences, contexts uniform in [4096, 32768], one Full layer (paged
       Full pool, 16-token pages in random order) and one SWA layer (ring of
@@ -50,6 +54,11 @@ stream it is launched on; `roofline.achieved` = algorithmic bytes (or flops)
 per launch / that duration.  `roofline.traffic` is the measured HBM bytes
 per launch from rocprofv3 counters (profiles/traffic.json), given only when
 they were taken on the current kernel source, else null.
+
+`cpu_baseline` is the oracle (fp64 NumPy, untuned, one thread) timed on a
+bounded sample of the same workload, with the host's core count and NumPy's
+default BLAS thread count recorded beside it.  `dtype` names the MFMA input
+types; `precision` spells out the type of every stage.
 """
 from __future__ import annotations
 
@@ -349,6 +358,9 @@ class Decode:
                 del kk, vv
             self.layers.append((H.FULL if kind == "F" else H.SWA, kc, vc))
             self.scales.append((ks, vs))
+            if fill and sum(ctxs) > (1 << 22):
+                torch.cuda.synchronize()
+                log(f"decode setup: layer {li + 1} of {len(pattern)} restored")
         torch.cuda.synchronize()
         # per-step inputs (rows new tokens per sequence per layer)
         T = B * rows
@@ -430,6 +442,35 @@ class Decode:
 # CPU baseline (the oracle, untuned)
 
 
+def host_info():
+    """Host cores this process may use and the BLAS thread count NumPy would
+    use by default (the oracle is timed on one thread)."""
+    info = {"host_cores": len(os.sched_getaffinity(0)), "blas_threads_default": None}
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+        info["blas_threads_default"] = max(n) if n else None
+    except Exception:
+        pass
+    return info
+
+
+def _one_thread():
+    """Context that holds NumPy's BLAS to one thread (a no-op without
+    threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(1)
+    except Exception:
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def _baseline(value, unit, sample, dt):
+    return {"value": round(value, 2), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{sample}; fp64 NumPy on 1 thread, {dt:.1f} s", **host_info()}
+
+
 def cpu_baseline_prefill(cx, cp: ChunkedPrefill, budget_s: float, seed=7):
     """The oracle (fp64 NumPy, one thread) on a bounded sample of the same
     prefill: query rows drawn uniformly from the batch, each with all heads
@@ -437,11 +478,6 @@ def cpu_baseline_prefill(cx, cp: ChunkedPrefill, budget_s: float, seed=7):
     the oracle is timed."""
     import synth
     from oracle import attention as OA
-    try:
-        from threadpoolctl import threadpool_limits
-        threadpool_limits(1)
-    except Exception:
-        pass
     rng = np.random.default_rng(seed)
     W = cp.W
 
@@ -461,14 +497,120 @@ def cpu_baseline_prefill(cx, cp: ChunkedPrefill, budget_s: float, seed=7):
             OA.attend(q, [rel], k, v, OA.SWA, W)
         return time.perf_counter() - t0
 
-    per_row = run(draw(32)) / 32
-    n = max(64, int(budget_s / max(per_row, 1e-6)))
-    sample = draw(n)
-    dt = run(sample)
-    return {"value": round(n / dt, 2), "unit": "tok/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} query rows (each with all {cp.hq} heads and its {W}-key window) "
-                      f"drawn uniformly from the {cp.B} sequences; fp64 NumPy on 1 thread, "
-                      f"{dt:.1f} s"}
+    with _one_thread():
+        per_row = run(draw(32)) / 32
+        n = max(64, int(budget_s / max(per_row, 1e-6)))
+        sample = draw(n)
+        dt = run(sample)
+    return _baseline(n / dt, "tok/s", f"{n} query rows (each with all {cp.hq} heads and its "
+                     f"{W}-key window) drawn uniformly from the {cp.B} sequences", dt)
+
+
+def cpu_baseline_single_chunk(cx, cp: ChunkedPrefill, dc_ctx, budget_s: float):
+    """The oracle on the whole single-chunk workload: every prefill row of the
+    sequence, then one row per decode step over its restored window, repeated
+    until about budget_s of CPU time; tok/s over prefill plus decode rows."""
+    import synth
+    from oracle import attention as OA
+    W, L = cp.W, cp.lens[0]
+    q, k, v = (synth.to_f64(t) for t in (cp.q[0], cp.k[0], cp.v[0]))
+    dq, dk, dv = dc_ctx  # decode rows [n, Hq, d] and their windows [n, W, Hkv, d]
+    passes, dt = 0, 0.0
+    with _one_thread():
+        while passes < 1 or dt < budget_s:
+            t0 = time.perf_counter()
+            OA.attend(q, range(L), k, v, OA.SWA, W)
+            for i in range(dq.shape[0]):
+                OA.attend(dq[i:i + 1], [dk.shape[1] - 1], dk[i], dv[i], OA.SWA, W)
+            dt += time.perf_counter() - t0
+            passes += 1
+    rows = L + dq.shape[0]
+    return _baseline(rows * passes / dt, "tok/s",
+                     f"the whole workload ({L} prefill rows + {dq.shape[0]} decode rows, all "
+                     f"heads) x {passes} passes", dt)
+
+
+def cpu_baseline_decode(cx, dc, sample_seqs, sample_layers, budget_s: float):
+    """The oracle on sampled (sequence, layer) decode calls of the same
+    workload: the first step's query row of each sampled sequence against its
+    restored context plus the step's new key.  GB/s-equivalent = the calls'
+    algorithmic bytes (as the GPU line counts them) / oracle time; every
+    sampled sequence runs all sampled layers, in order, until the budget is
+    spent (at least one sequence)."""
+    import synth
+    from oracle import attention as OA
+    torch, H = cx.torch, cx.H
+    W, hkv, d = dc.W, dc.hkv, dc.d
+    done_bytes, dt, nseq, ncall = 0, 0.0, 0, 0
+    for b in sample_seqs:
+        ctx = dc.ctx0[b]
+        for li in sample_layers:
+            kind = dc.layers[li][0]
+            n = ctx if kind == H.FULL else min(ctx, W - 1)
+            kk = synth.bf16_normal((n, hkv, d), dc.seed, li, b, synth.ROLE_K, device=cx.dev)
+            vv = synth.bf16_normal((n, hkv, d), dc.seed, li, b, synth.ROLE_V, device=cx.dev)
+            k = synth.to_f64(torch.cat([kk, dc.kn[li][b:b + 1]]))
+            v = synth.to_f64(torch.cat([vv, dc.vn[li][b:b + 1]]))
+            q = synth.to_f64(dc.q[li][b:b + 1])
+            del kk, vv
+            with _one_thread():
+                t0 = time.perf_counter()
+                OA.attend(q, [n], k, v, kind, W)
+                dt += time.perf_counter() - t0
+            del k, v
+            done_bytes += dc.layer_bytes(kind, [ctx + 1])
+            ncall += 1
+        nseq += 1
+        if dt >= budget_s:
+            break
+    kinds = "".join("F" if dc.layers[li][0] == H.FULL else "S" for li in sample_layers)
+    return _baseline(done_bytes / dt / 1e9, "GB/s",
+                     f"{nseq} sequences (the shortest and longest context first, then seeded "
+                     f"ones) x layers {kinds}: {ncall} calls of one query row with all heads",
+                     dt)
+
+
+def cpu_baseline_stack(cx, cp: ChunkedPrefill, pattern: str, budget_s: float, seed=13):
+    """The oracle on sampled query rows of the 70-layer stack (every layer
+    sees the same Q/K/V): Full rows at the chunk edges and seeded positions,
+    SWA rows at seeded positions.  Time per scored pair is measured for each
+    kind and scaled by the stack's pair counts, giving tok/s-equivalent of
+    the hybrid stack and of the all-Full variant."""
+    import synth
+    from oracle import attention as OA
+    N, W, chunk = cp.lens[0], cp.W, cp.chunk
+    k, v = synth.to_f64(cp.k[0]), synth.to_f64(cp.v[0])
+    rng = np.random.default_rng(seed)
+    edges = [p for a in range(0, N, chunk) for p in (a, a + chunk - 1)]
+    full_pos = [edges[0], edges[-1]] + [int(x) for x in rng.integers(0, N, 64)] + edges[1:-1]
+    swa_pos = [int(x) for x in rng.integers(W, N, 4096)]
+    res = {}
+    with _one_thread():
+        for kind, plist in ((OA.FULL, full_pos), (OA.SWA, swa_pos)):
+            t, keys, rows = 0.0, 0, 0
+            for pos in plist:
+                q = synth.to_f64(cp.q[0][pos:pos + 1])
+                t0 = time.perf_counter()
+                OA.attend(q, [pos], k, v, kind, W)
+                t += time.perf_counter() - t0
+                keys += OA.valid_length(pos, kind, W)
+                rows += 1
+                if t >= budget_s / 2 and rows >= 4:
+                    break
+            res[kind] = (t, keys, rows)
+    s_full = N * (N + 1) // 2
+    s_swa = _pairs_swa(N, W)
+    t_full = res[OA.FULL][0] / res[OA.FULL][1] * s_full    # one Full layer, all rows
+    t_swa = res[OA.SWA][0] / res[OA.SWA][1] * s_swa
+    nf, ns = pattern.count("F"), pattern.count("S")
+    stack = nf * t_full + ns * t_swa
+    out = _baseline(N / stack, "tok/s",
+                    f"{res[OA.FULL][2]} Full rows (chunk edges and seeded positions) and "
+                    f"{res[OA.SWA][2]} SWA rows, all heads; time per scored pair scaled by the "
+                    f"stack's pair counts ({nf} Full + {ns} SWA layers)",
+                    res[OA.FULL][0] + res[OA.SWA][0])
+    out["all_full_value"] = round(N / (len(pattern) * t_full), 4)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -535,11 +677,34 @@ def run_decode(cx, dc, pattern, steps, warm):
     return res
 
 
+# What the bf16-page path computes in: bf16 inputs and K pages, V pages in
+# fp16 (converted exactly from bf16 by the append), the QK product on the
+# bf16 MFMA, the PV product on the fp16 MFMA with fp16 weights, softmax and
+# accumulation in fp32, fp32 output (fp16 with --out f16).
+PRECISION = {"inputs": "bf16", "k_pages": "bf16", "v_pages": "fp16",
+             "qk_mfma": "bf16 x bf16 -> fp32", "pv_mfma": "fp16 x fp16 -> fp32",
+             "softmax": "fp32", "output": "fp32"}
+
+
 def base_line(args, value, unit, ms, config, rl):
+    prec = dict(PRECISION, output=ODT[getattr(args, "out", "f32")])
     return {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": config, "roofline": rl}
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16/fp16",
+            "precision": prec, "data": "synthetic", "config": config, "roofline": rl}
+
+
+# keys of the output contract that a config embedded in the default line
+# does not repeat
+_CONTRACT = ("metric", "n_gpus", "warmup", "higher_is_better", "scaling", "vs_baseline", "data",
+             "precision")
+
+
+def embed(line):
+    """A workload's line as a sub-object of the default line: its config
+    keys, then its measurements (value, unit, roofline, cpu_baseline ...)."""
+    cfg = line.pop("config")
+    return {**cfg, **{k: v for k, v in line.items() if k not in _CONTRACT}}
 
 
 def copy_calibration(cx):
@@ -614,16 +779,26 @@ def wl_swa_chunked_prefill(cx, args):
     line["kernel"] = {"name": "prefill_kernel<128,SWA>", "avg_us": round(ks["avg_us"], 2),
                       "launches_timed": ks["launches"], "tflops": round(ks["tflops"], 2),
                       "mfma_frac": round(ks["tflops"] / MFMA_BF16_PEAK_TFS, 4)}
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(cx, cp, args.cpu_seconds)
+        log(f"cpu baseline: {line['cpu_baseline']}")
+    del cp
+    cx.torch.cuda.empty_cache()
     if not args.no_decode:
         d = wl_mixed_decode(cx, args)
         line["decode"] = {**d["config"], "value": d["value"], "unit": d["unit"],
                           "frac": d["step_frac_of_hbm_peak"], "ms_per_step": d["ms_per_step"],
                           "roofline": d["roofline"], "full_call_us": d["full_call_us"],
-                          "swa_call_us": d["swa_call_us"], "copy_ceiling": d["copy_ceiling"]}
-    line["cpu_baseline"] = None
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_prefill(cx, cp, args.cpu_seconds)
-        log(f"cpu baseline: {line['cpu_baseline']}")
+                          "swa_call_us": d["swa_call_us"], "copy_ceiling": d["copy_ceiling"],
+                          "cpu_baseline": d["cpu_baseline"]}
+    if not args.headline_only:
+        # the other configurations of the workload statement, each with its
+        # own roofline and oracle baseline
+        for key, fn in (("single_chunk", wl_swa_single_chunk), ("hybrid_stack", wl_hybrid_stack),
+                        ("long_decode", wl_long_decode)):
+            line[key] = embed(fn(cx, args))
+            cx.torch.cuda.empty_cache()
     return line
 
 
@@ -649,7 +824,20 @@ def wl_mixed_decode(cx, args):
     line["swa_call_us"] = round(r["swa_call_us"], 1)
     cc = copy_ceiling(cx)
     line["copy_ceiling"] = {"gbs": cc, "full_call_frac": round(r["full_gbs"] / cc, 4)}
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        seqs = _sample_seqs(ctxs, 16, wl.seed)
+        line["cpu_baseline"] = cpu_baseline_decode(cx, dc, seqs, [0, 1], args.cpu_seconds)
+        log(f"decode cpu baseline: {line['cpu_baseline']}")
     return line
+
+
+def _sample_seqs(ctxs, n, seed):
+    """The shortest- and longest-context sequences, then seeded others."""
+    lo, hi = int(np.argmin(ctxs)), int(np.argmax(ctxs))
+    rest = [int(b) for b in np.random.default_rng(seed + 17).permutation(len(ctxs))
+            if b not in (lo, hi)]
+    return ([lo, hi] + rest)[:n]
 
 
 def wl_mixed_decode_fp8(cx, args):
@@ -846,9 +1034,14 @@ def wl_hybrid_stack(cx, args):
         cp.run(ev)
         cx.torch.cuda.synchronize()
         res[variant] = {"sec": sec, "full": kernel_stats(cp, ev, H.FULL),
-                        "swa": kernel_stats(cp, ev, H.SWA)}
+                        "swa": kernel_stats(cp, ev, H.SWA),
+                        "flops": sum(cp.attn_flops(st, kind) for st in cp.steps
+                                     for kind, _, _ in cp.layers)}
         log(f"stack {variant}: {wl.seq_len / sec:.4g} tok/s, {sec:.3f} s/step, "
             f"full {res[variant]['full']}, swa {res[variant]['swa']}")
+        if variant == "hybrid" and not args.no_cpu_baseline:
+            res["cpu"] = cpu_baseline_stack(cx, cp, wl.pattern, args.cpu_seconds)
+            log(f"stack cpu baseline: {res['cpu']}")
         del cp, ev
         cx.torch.cuda.empty_cache()
     hy, af = res["hybrid"], res["all_full"]
@@ -869,6 +1062,8 @@ def wl_hybrid_stack(cx, args):
                         "ms_per_step": round(af["sec"] * 1e3, 3),
                         "full_kernel_tflops": round(af["full"]["tflops"], 1)}
     line["time_ratio_hybrid_over_all_full"] = round(hy["sec"] / af["sec"], 5)
+    line["flop_ratio_hybrid_over_all_full"] = round(hy["flops"] / af["flops"], 6)
+    line["cpu_baseline"] = res.get("cpu")
     return line
 
 
@@ -896,6 +1091,14 @@ def wl_long_decode(cx, args):
     line["swa_call_us"] = round(r["swa_call_us"], 1)
     cc = copy_ceiling(cx)
     line["copy_ceiling"] = {"gbs": cc, "full_call_frac": round(r["full_gbs"] / cc, 4)}
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        full = [i for i, k in enumerate(wl.pattern) if k == "F"][:2]
+        swa = [i for i, k in enumerate(wl.pattern) if k == "S"][:1] + \
+              [i for i, k in enumerate(wl.pattern) if k == "S" and i > full[0]][:1]
+        seqs = _sample_seqs(ctxs, 4, wl.seed)
+        line["cpu_baseline"] = cpu_baseline_decode(cx, dc, seqs, full + swa, args.cpu_seconds)
+        log(f"long decode cpu baseline: {line['cpu_baseline']}")
     return line
 
 
@@ -921,6 +1124,22 @@ def wl_swa_single_chunk(cx, args):
                 wl.window + 16, wl.seed, wl.decode_steps + 8)
     r = run_decode(cx, dc, "S", wl.decode_steps, 2)
     line["decode_step_us"] = round(r["ms_per_step"] * 1e3, 2)
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        import synth
+        W, n = wl.window, wl.decode_steps
+        tail = [synth.bf16_normal((W - 1, wl.num_kv_heads, wl.head_dim), wl.seed, 0, 0, role,
+                                  device=cx.dev) for role in (synth.ROLE_K, synth.ROLE_V)]
+        # keys of decode step t (position L + t): the restored tail, then the
+        # step's new key once per earlier step (every step appends the same row)
+        ks, vs = (synth.to_f64(cx.torch.cat([t] + [new[0:1]] * n)) for t, new in
+                  zip(tail, (dc.kn[0], dc.vn[0])))
+        dk = np.stack([ks[t:t + W] for t in range(n)])
+        dv = np.stack([vs[t:t + W] for t in range(n)])
+        dq = np.repeat(synth.to_f64(dc.q[0][0:1]), n, axis=0)
+        line["cpu_baseline"] = cpu_baseline_single_chunk(cx, cp, (dq, dk, dv),
+                                                         min(args.cpu_seconds, 2.0))
+        log(f"single chunk cpu baseline: {line['cpu_baseline']}")
     return line
 
 
@@ -997,6 +1216,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="default workload: measure the chunked prefill and the mixed decode "
+                         "only, not the single-chunk, 70-layer stack and long-context decode "
+                         "configurations")
     ap.add_argument("--out", choices=sorted(ODT), default="f32",
                     help="attention output type of the prefill and decode workloads "
                          "(f32 default; f16 halves the bytes written)")

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "index.h"
+
 namespace hswa {
 namespace dev {
 
@@ -95,9 +97,8 @@ template <int KIND>
 __device__ __forceinline__ int32_t page_of(const int32_t* __restrict__ fpt,
                                            const int32_t* __restrict__ rpt, int32_t sid,
                                            int32_t pos, int32_t max_pages, int32_t ring) {
-  if (KIND == 0) return fpt[(int64_t)sid * max_pages + pos / kPage];
-  int32_t r = pos % ring;
-  return rpt[(int64_t)sid * (ring / kPage) + r / kPage];
+  const int32_t e = idx::table_entry(KIND, pos, ring);
+  return KIND == 0 ? fpt[(int64_t)sid * max_pages + e] : rpt[(int64_t)sid * (ring / kPage) + e];
 }
 
 // The same lookup for a wave-uniform (sid, pos), as a scalar load: the
@@ -116,8 +117,9 @@ __device__ __forceinline__ int32_t page_of_uniform(const int32_t* __restrict__ f
                                                    const int32_t* __restrict__ rpt, int32_t sid,
                                                    int32_t pos, int32_t max_pages,
                                                    int32_t ring) {
-  return KIND == 0 ? scalar_load_i32(fpt, sid * max_pages + pos / kPage)
-                   : scalar_load_i32(rpt, sid * (ring / kPage) + (pos % ring) / kPage);
+  const int32_t e = idx::table_entry(KIND, pos, ring);
+  return KIND == 0 ? scalar_load_i32(fpt, sid * max_pages + e)
+                   : scalar_load_i32(rpt, sid * (ring / kPage) + e);
 }
 
 }  // namespace dev

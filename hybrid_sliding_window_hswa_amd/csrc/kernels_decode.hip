@@ -58,17 +58,6 @@ namespace {
 
 constexpr int kDecWaves = 4;
 
-// Keys per split of a Full-layer sequence of L keys.  Its
-// min(n_splits, ceil(L / split_len)) splits share the keys evenly, in 64-key
-// multiples (no short last split), so the splits cover every key even when
-// a caller's max_seq_len hint (which sized n_splits) is below L; split s
-// holds keys [s * len, min(L, (s + 1) * len)), and ceil(L / len) splits are
-// non-empty.  The decode kernels and the combine compute the same value.
-__device__ __forceinline__ int split_keys(int L, int n_splits, int split_len) {
-  const int ns = min(n_splits, (L + split_len - 1) / split_len);
-  return ((L + ns - 1) / ns + 63) / 64 * 64;
-}
-
 // One output element in the caller's output type (fp32, or fp16 rounded to
 // nearest).
 __device__ __forceinline__ void store_out(const AttnParams& p, int64_t idx, float x) {
@@ -173,7 +162,7 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   const int nr = min(n, QN);                         // rows computed here
   int klo, khi;  // keys [klo, khi) of this workgroup
   if (KIND == 0) {
-    const int len = split_keys(L, p.n_splits, p.split_len);
+    const int len = idx::split_keys(L, p.n_splits, p.split_len);
     klo = split * len;
     khi = min(L, klo + len);
   } else {
@@ -228,8 +217,7 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   const ctab_t ptab = (ctab_t)(KIND == 0 ? p.t.fpt + (int64_t)sid * p.t.max_pages
                                          : p.t.rpt + (int64_t)sid * (p.t.ring_slots / kPage));
   auto page_at = [&](int pos) {
-    const int idx = KIND == 0 ? pos / kPage : (pos % p.t.ring_slots) / kPage;
-    return ptab[__builtin_amdgcn_readfirstlane(idx)];
+    return ptab[__builtin_amdgcn_readfirstlane(idx::table_entry(KIND, pos, p.t.ring_slots))];
   };
   // K: this lane's row `col` of score tile kt is key 8*(col/4) + 4kt + col%4,
   // on page col/8.  V: keys 8*q4 .. +8 are page q4/2, offset 8*(q4%2); the
@@ -456,7 +444,7 @@ decode_fp8_kernel(AttnParams p) {
   const int nr = min(n, QN);
   int klo, khi;
   if (KIND == 0) {
-    const int len = split_keys(L, p.n_splits, p.split_len);
+    const int len = idx::split_keys(L, p.n_splits, p.split_len);
     klo = split * len;
     khi = min(L, klo + len);
   } else {
@@ -496,8 +484,7 @@ decode_fp8_kernel(AttnParams p) {
   const ctab_t ptab = (ctab_t)(KIND == 0 ? p.t.fpt + (int64_t)sid * p.t.max_pages
                                          : p.t.rpt + (int64_t)sid * (p.t.ring_slots / kPage));
   auto page_at = [&](int pos) {
-    const int idx = KIND == 0 ? pos / kPage : (pos % p.t.ring_slots) / kPage;
-    return ptab[__builtin_amdgcn_readfirstlane(idx)];
+    return ptab[__builtin_amdgcn_readfirstlane(idx::table_entry(KIND, pos, p.t.ring_slots))];
   };
   const uint8_t* kbase = (const uint8_t*)p.k_cache;
   const uint8_t* vbase = (const uint8_t*)p.v_cache;
@@ -627,7 +614,7 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, int qn)
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
   if (n <= 0 || n > L || r >= n || row0 < 0 || row0 + n > p.total_q) return;
-  const int len = split_keys(L, p.n_splits, p.split_len);
+  const int len = idx::split_keys(L, p.n_splits, p.split_len);
   const int ns = (L + len - 1) / len;  // the splits that hold keys
   const int64_t hrow = (int64_t)(row0 + r) * p.hq + h;
   const float* ml = p.ws + (int64_t)p.total_q * p.hq * p.n_splits * D;

@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(256) append_kernel(AttnParams p, int tiles_per
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
   const int L = p.t.seq_len[sid];
   const int p0 = L - n;
-  const int tile_pos = (p0 / kPage + t) * kPage;
+  const int tile_pos = idx::tile_pos(p0, t);
   if (n <= 0 || n > L || tile_pos >= L || row0 < 0 || row0 + n > p.total_q) return;
   const int lo = max(tile_pos, p0);
   const int hi = min(tile_pos + kPage, L);
@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(AttnParams p, int tiles
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
   const int L = p.t.seq_len[sid];
   const int p0 = L - n;
-  const int tile_pos = (p0 / kPage + t) * kPage;
+  const int tile_pos = idx::tile_pos(p0, t);
   if (n <= 0 || n > L || tile_pos >= L || row0 < 0 || row0 + n > p.total_q) return;
   const int lo = max(tile_pos, p0);
   const int hi = min(tile_pos + kPage, L);
@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(AttnParams p, int tiles
 
 hipError_t launch_append(const AttnParams& p, hipStream_t s) {
   if (p.num_seqs <= 0) return hipSuccess;
-  const int tiles = (p.max_q_len + 14) / kPage + 1;
+  const int tiles = idx::tiles_for(p.max_q_len);
   const int64_t blocks = (int64_t)p.num_seqs * tiles * p.hkv;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks);
@@ -293,12 +293,12 @@ __global__ void __launch_bounds__(256) xfer_kernel(XferParams p, int tiles_per_s
   const int p0 = p.first_pos ? p.first_pos[i] : L - n;  // positions [p0, p0 + n)
   if (n <= 0 || p0 < 0 || p0 > L - n) return;  // only stored positions move
   if (tok0 < 0 || tok0 + n > p.total_tok) return;  // tokens outside the buffers
-  const int tile_pos = (p0 / kPage + t) * kPage;
+  const int tile_pos = idx::tile_pos(p0, t);
   if (tile_pos >= p0 + n) return;
   // A SWA ring of C slots holds at most positions [L - C, L): an older
   // position's slot belongs to a newer one, so it is neither read (offload)
   // nor written (restore, which would overwrite live K/V).
-  const int lo = max(max(tile_pos, p0), KIND == 0 ? 0 : L - p.t.ring_slots);
+  const int lo = max(max(tile_pos, p0), KIND == 0 ? 0 : idx::ring_oldest(L, p.t.ring_slots));
   const int hi = min(tile_pos + kPage, p0 + n);
   if (lo >= hi) return;
   const int32_t page = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile_pos, p.t.max_pages,
@@ -381,7 +381,7 @@ __global__ void __launch_bounds__(256) xfer_kernel(XferParams p, int tiles_per_s
 
 hipError_t launch_xfer(const XferParams& p, bool to_host, hipStream_t s) {
   if (p.num_seqs <= 0) return hipSuccess;
-  const int tiles = (p.max_tok + 14) / kPage + 1;
+  const int tiles = idx::tiles_for(p.max_tok);
   dim3 grid((unsigned)(p.num_seqs * tiles));
 #define HSWA_XFER(D_, K_)                                                                   \
   if (to_host)                                                                              \

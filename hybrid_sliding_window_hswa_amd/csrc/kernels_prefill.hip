@@ -185,17 +185,12 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   const int npr = p.t.ring_slots / kPage;             // ring pages of a sequence (SWA)
   const int32_t* prow = KIND == 0 ? p.t.fpt + (int64_t)sid * p.t.max_pages
                                   : p.t.rpt + (int64_t)sid * npr;
-  int ipg = KIND == 0 ? kstart / kPage + half
-                      : ((kstart + kPage * half) % p.t.ring_slots) / kPage;
+  int ipg = idx::prefill_first_entry(KIND, kstart, half, p.t.ring_slots);
   // a page past the range reads page 0 (present in every pool); its keys are
   // masked like any other key outside the range
   auto issue = [&](int kp0, int buf) {
     const int32_t pg = kp0 + kPage * half <= wg_khi ? scalar_load_i32(prow, ipg) : 0;
-    ipg += 2;
-    if (KIND != 0) {  // two wraps: a ring of one page (npr = 1) steps past it twice
-      if (ipg >= npr) ipg -= npr;
-      if (ipg >= npr) ipg -= npr;
-    }
+    ipg = idx::prefill_next_entry(KIND, ipg, npr);
     const uint16_t* src =
         (const uint16_t*)((const uint8_t*)tens + (uint64_t)(uint32_t)pg * pbytes);
     const uint32_t base = lds0 + buf * SBYTES + wave * NIW * 1024;

@@ -504,9 +504,9 @@ void hswa_pool_destroy(hswa_pool* p) {
   if (!p) return;
   for (auto& st : p->stage) {
     wait_stage(st);
-    if (st.buf) hipHostFree(st.buf);
+    if (st.buf) (void)hipHostFree(st.buf);
   }
-  for (void* b : p->retired) hipHostFree(b);
+  for (void* b : p->retired) (void)hipHostFree(b);
   delete p;
 }
 

@@ -26,7 +26,8 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Two bf16 (packed in one dword) -> two fp16 (packed).  Exact for
-// |x| < 65504 and |x| >= 2^-14; smaller magnitudes round to fp16 subnormals.
+// 2^-14 <= |x| <= 65280 (the largest bf16 below fp16's limit); smaller
+// magnitudes round to fp16 subnormals, |x| >= 65536 rounds to +-inf.
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   f16x2 h = {(_Float16)bf16_lo(w), (_Float16)bf16_hi(w)};
   return __builtin_bit_cast(uint32_t, h);

@@ -248,12 +248,14 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   };
   auto load_k = [&](const Ptrs& pt, Raw (&kr)[2][NC]) {
     for (int c = 0; c < NC; ++c) {
-      kr[0][c] = *(const Raw*)(pt.k + 32 * c * ESZ);
-      kr[1][c] = *(const Raw*)(pt.k + (4 * D + 32 * c) * ESZ);
+      kr[0][c] = __builtin_nontemporal_load((const Raw*)(pt.k + 32 * c * ESZ));
+      kr[1][c] =
+          __builtin_nontemporal_load((const Raw*)(pt.k + (4 * D + 32 * c) * ESZ));
     }
   };
   auto load_v = [&](const Ptrs& pt, Raw (&vr)[NB]) {
-    for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const Raw*)(pt.v + 16 * nb * kPage * ESZ);
+    for (int nb = 0; nb < NB; ++nb)
+      vr[nb] = __builtin_nontemporal_load((const Raw*)(pt.v + 16 * nb * kPage * ESZ));
   };
   auto load_scales = [&](const Ptrs& pt, u32x4 (&sc)[4]) {
     if (F8) {
@@ -281,6 +283,8 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     }
   };
 
+  // K/V bytes are read once, so their loads are non-temporal (a long-context
+  // Full call measured 2.3% faster; the mixed decode unchanged).
   // Software pipeline, register-neutral: the K loads (and FP8 scales) of
   // this wave's next step are issued as soon as the score MFMAs have
   // consumed the current K fragments, the V loads as soon as the PV MFMAs
@@ -509,10 +513,12 @@ decode_fp8_kernel(AttnParams p) {
   u32x4 kr[4][KV4], vr[NB], sc[8];  // sc: K scales 0-3, V scales 4-7
   auto load_k = [&](const Ptrs& pt) {
     for (int kt = 0; kt < 4; ++kt)
-      for (int x = 0; x < KV4; ++x) kr[kt][x] = *(const u32x4*)(pt.k + 4 * kt * D + 16 * x);
+      for (int x = 0; x < KV4; ++x)
+        kr[kt][x] = __builtin_nontemporal_load((const u32x4*)(pt.k + 4 * kt * D + 16 * x));
   };
   auto load_v = [&](const Ptrs& pt) {
-    for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(pt.v + 16 * nb * kPage);
+    for (int nb = 0; nb < NB; ++nb)
+      vr[nb] = __builtin_nontemporal_load((const u32x4*)(pt.v + 16 * nb * kPage));
     for (int x = 0; x < 4; ++x) {
       sc[x] = *(const u32x4*)(p.k_scale + pt.sc + 4 * x);
       sc[4 + x] = *(const u32x4*)(p.v_scale + pt.sc + 4 * x);

@@ -9,7 +9,8 @@
 //                           product (keys are its reduction dim).  V is
 //                           stored in fp16 because that product runs on the
 //                           fp16 MFMA; bf16 -> fp16 is exact for
-//                           2^-14 <= |v| < 65504.
+//                           2^-14 <= |v| <= 65280 (every bf16 value
+//                           there), |v| >= 65536 becomes +-inf.
 #include <hip/hip_runtime.h>
 
 #include "device.h"

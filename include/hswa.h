@@ -41,9 +41,13 @@
  *  A token's slot is page * 16 + offset.  One (page, head) block is
  *  16 * head_dim * 2 bytes contiguous for K and for V.  V is kept in fp16
  *  because the PV product runs on the fp16 MFMA: the append converts the
- *  bf16 input, exactly for 2^-14 <= |v| < 65504 (smaller magnitudes round to
- *  fp16 subnormals, error < 2^-25); V values must be finite with
- *  |v| < 65504.  Callers that write pages themselves write V in fp16.
+ *  bf16 input with round to nearest even, which is exact for every bf16
+ *  value with 2^-14 <= |v| <= 65280 (65280 is the largest bf16 value below
+ *  fp16's limit 65504), rounds smaller magnitudes to fp16 subnormals (error
+ *  <= 2^-25) and turns |v| >= 65536 (the next bf16 value) into +-inf, which
+ *  makes the attention outputs of that dimension non-finite for every query
+ *  whose window holds the key.  The supported V domain is |v| <= 65280.
+ *  Callers that write pages themselves write V in fp16.
  */
 #ifndef HSWA_H
 #define HSWA_H

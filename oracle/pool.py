@@ -53,7 +53,25 @@ Readings taken where the pages leave a step open:
   match is cut back to the longest such length, the rest is a miss.  The
   page asks for W tail tokens.  The next query at position m' attends to
   [m' - W + 1, m'], so this library's attention needs W - 1 of them, which
-  is also what eviction keeps; the caller chooses ``tail``.
+  is also what eviction keeps; the caller chooses ``tail``.  A position of
+  a sequence holds an SWA entry of that sequence only from its first
+  resident position on (a page shared with another sequence may carry the
+  other one's entries).
+* ``fork`` reuses a matched prefix for another request (point 3 of the same
+  part: a prefix node keeps a Full segment index and an SWA segment map, so
+  the Full part stays shareable whatever happens to the SWA part).  An
+  empty sequence dst takes the first m positions of src, m window-safe for
+  src with tail W - 1.  The Full pages wholly below dst's window start
+  max(0, m - W + 1) are shared (a reference count per page); the pages from
+  the one holding that start to the one holding m - 1 are fresh (taken from
+  the free-list head, logical order), and the window positions get dst's
+  ring slots.  Every map entry so keeps one owner: shared positions are
+  outside dst's window for good, and its window sits on its own pages.  The
+  caller copies the K/V of [16 * first fresh page, m) (Full layers) and of
+  the window (SWA layers) from src to dst.  Not enough free pages: NoSpace,
+  nothing changed.  A sequence's pages are freed when the last sequence
+  holding them releases them; truncating into a shared page (which a later
+  append would overwrite under the other holder) is refused.
 * -1 marks "no slot" in every table.
 """
 from __future__ import annotations
@@ -98,6 +116,7 @@ class PoolSim:
         self.res_start = [0] * max_seqs   # first position still in the SWA pool
         self.pages: List[List[int]] = [[] for _ in range(max_seqs)]
         self.map: Dict[int, int] = {}     # Full slot -> SWA slot, resident only
+        self.refs: Dict[int, int] = {}    # Full page -> sequences holding it
 
     # -- slot formulas --------------------------------------------------
     def full_slot(self, b: int, pos: int) -> int:
@@ -152,7 +171,7 @@ class PoolSim:
             L = self.length[b]
             for pos in range(L, L + n):
                 if pos % PAGE == 0:
-                    self.pages[b].append(self.free.popleft())
+                    self._take_page(b)
                 fs, ss = self.full_slot(b, pos), self.swa_slot(b, pos)
                 self.map[fs] = ss
                 full_out.append(fs)
@@ -202,7 +221,7 @@ class PoolSim:
             self.res_start[b] = max(self.res_start[b], keep_from)
             for pos in range(L, new_len):
                 if pos % PAGE == 0:
-                    self.pages[b].append(self.free.popleft())
+                    self._take_page(b)
                 fs = self.full_slot(b, pos)
                 full_out.append(fs)
                 if pos >= keep_from:
@@ -214,13 +233,35 @@ class PoolSim:
             self.length[b] = new_len
         return full_out, swa_out
 
+    def _take_page(self, b: int) -> None:
+        pg = self.free.popleft()
+        self.refs[pg] = 1
+        self.pages[b].append(pg)
+
+    def _drop_page(self, pg: int) -> bool:
+        """One holder lets go of a page; True when it is free again."""
+        self.refs[pg] -= 1
+        if self.refs[pg] == 0:
+            del self.refs[pg]
+            return True
+        return False
+
+    def shared_pages(self, b: int) -> int:
+        """Leading pages of b that another sequence also holds."""
+        n = 0
+        while n < len(self.pages[b]) and self.refs[self.pages[b][n]] > 1:
+            n += 1
+        return n
+
     def release(self, seq_ids) -> None:
-        """End the listed requests: free their Full pages and SWA entries."""
+        """End the listed requests: drop their SWA entries and their hold on
+        their Full pages; pages no other sequence holds go back to the tail
+        of the free list in logical-page order."""
         ids = self._check_ids(seq_ids)
         for b in ids:
             for pos in range(self.res_start[b], self.length[b]):
                 del self.map[self.full_slot(b, pos)]
-            self.free.extend(self.pages[b])
+            self.free.extend(pg for pg in self.pages[b] if self._drop_page(pg))
             self.pages[b] = []
             self.length[b] = 0
             self.res_start[b] = 0
@@ -236,14 +277,62 @@ class PoolSim:
                 raise ValueError("new length outside [0, current length]")
             if self.res_start[b] > max(0, n - self.W + 1):
                 raise ValueError("the window of the new length was already evicted")
+            if n < self.length[b] and n < PAGE * self.shared_pages(b):
+                raise ValueError("the cut reaches a page another sequence holds")
         for b, n in zip(ids, lens):
             for pos in range(n, self.length[b]):
                 del self.map[self.full_slot(b, pos)]
             keep = self._pages_for(n)
             freed = self.pages[b][keep:]
+            for pg in freed:
+                self._drop_page(pg)
             self.pages[b] = self.pages[b][:keep]
             self.free.extendleft(reversed(freed))
             self.length[b] = n
+
+    def fork(self, src_ids, dst_ids, lens) -> Tuple[List[int], List[int]]:
+        """Give each empty dst_ids[i] the first lens[i] positions of
+        src_ids[i] (see the module docstring).  Returns, per fork, the first
+        position whose Full-layer K/V the caller copies and the first
+        position whose SWA-layer K/V it copies (both up to lens[i])."""
+        dsts = self._check_ids(dst_ids, lens)
+        srcs = [int(b) for b in src_ids]
+        ms = [int(m) for m in lens]
+        if len(srcs) != len(dsts):
+            raise ValueError("one source per fork")
+        for a, b, m in zip(srcs, dsts, ms):
+            if not 0 <= a < self.max_seqs or a in dsts:
+                raise ValueError("source out of range or also a destination")
+            if self.length[b] != 0:
+                raise ValueError("a fork's destination must be empty")
+            if m > self.length[a]:
+                raise ValueError("fork longer than its source")
+            if self.window_safe_len(a, m, self.W - 1) != m:
+                raise ValueError("fork length is not window-safe for its source")
+        need = 0
+        for a, b, m in zip(srcs, dsts, ms):
+            own = max(0, m - self.W + 1) // PAGE
+            if self._pages_for(m) > self.max_pages:
+                raise NoSpace("fork would exceed its page-table row")
+            need += self._pages_for(m) - own
+        if need > len(self.free):
+            raise NoSpace("Full pool exhausted")
+        full_from, swa_from = [], []
+        for a, b, m in zip(srcs, dsts, ms):
+            start = max(0, m - self.W + 1)
+            own = start // PAGE
+            for pg in self.pages[a][:own]:
+                self.refs[pg] += 1
+                self.pages[b].append(pg)
+            for _ in range(own, self._pages_for(m)):
+                self._take_page(b)
+            for pos in range(start, m):
+                self.map[self.full_slot(b, pos)] = self.swa_slot(b, pos)
+            self.length[b] = m
+            self.res_start[b] = start
+            full_from.append(PAGE * own)
+            swa_from.append(start)
+        return full_from, swa_from
 
     def window_safe_len(self, b: int, m: int, tail: int) -> int:
         """Longest m' <= min(m, length) whose last min(m', tail) positions all
@@ -253,7 +342,8 @@ class PoolSim:
         if m < 0 or tail < 0:
             raise ValueError("negative length")
         for k in range(min(m, self.length[b]), 0, -1):
-            if all(self.full_slot(b, pos) in self.map for pos in range(max(0, k - tail), k)):
+            if all(pos >= self.res_start[b] and self.full_slot(b, pos) in self.map
+                   for pos in range(max(0, k - tail), k)):
                 return k
         return 0
 

@@ -43,6 +43,7 @@ SDPA_GQA = ("test_matches_torch_sdpa_fp64", dict(kind=1, window=5, hq=8, hkv=2, 
 SDPA_FULL = ("test_matches_torch_sdpa_fp64", dict(kind=0, window=0, hq=6, hkv=1, d=32))
 FSUM = ("test_brute_force_fsum", dict(window=5))
 POOL_RANDOM = [("test_random_operations_against_second_simulator", dict(seed=s)) for s in range(12)]
+FORK_RANDOM = ("test_random_forks_against_second_simulator", {})
 
 # (name, binding, old text, new text, pins that must each fail; a list
 # inside the list means "at least one of these")
@@ -112,8 +113,32 @@ CASES = [
      "+ n > self.C:", "+ n >= self.C:",
      [POOL_RANDOM]),
     ("released_pages_to_head", "test_oracle_pool",
-     "self.free.extend(self.pages[b])", "self.free.extendleft(self.pages[b])",
+     "self.free.extend(pg for pg in self.pages[b] if self._drop_page(pg))",
+     "self.free.extendleft(pg for pg in self.pages[b] if self._drop_page(pg))",
      [("test_hand_worked_fixtures", {}), POOL_RANDOM]),
+    # -- prefix reuse (fork) -------------------------------------------------------
+    ("fork_shares_the_window_page", "test_oracle_pool",
+     "            own = start // PAGE\n", "            own = -(-start // PAGE)\n",
+     [("test_hand_worked_fixtures", {}), FORK_RANDOM]),
+    ("fork_takes_no_reference", "test_oracle_pool",
+     "                self.refs[pg] += 1\n", "                self.refs[pg] += 0\n",
+     [("test_hand_worked_fixtures", {}), FORK_RANDOM]),
+    ("fork_window_one_position_short", "test_oracle_pool",
+     "            for pos in range(start, m):", "            for pos in range(start + 1, m):",
+     [("test_hand_worked_fixtures", {}), FORK_RANDOM]),
+    ("match_reads_another_holders_entries", "test_oracle_pool",
+     "if all(pos >= self.res_start[b] and self.full_slot(b, pos) in self.map",
+     "if all(self.full_slot(b, pos) in self.map",
+     [("test_hand_worked_fixtures", {}), FORK_RANDOM]),
+    ("cut_into_shared_page_allowed", "test_oracle_pool",
+     "            if n < self.length[b] and n < PAGE * self.shared_pages(b):",
+     "            if False:",
+     [("test_hand_worked_fixtures", {}),
+      [("test_cut_into_shared_page_refused", dict(seed=s)) for s in range(8)]]),
+    ("fork_not_window_safe_accepted", "test_oracle_pool",
+     "            if self.window_safe_len(a, m, self.W - 1) != m:",
+     "            if self.window_safe_len(a, m, 0) != m:",
+     [FORK_RANDOM]),
     ("truncated_pages_to_tail", "test_oracle_pool",
      "self.free.extendleft(reversed(freed))", "self.free.extend(freed)",
      [("test_hand_worked_fixtures", {}), POOL_RANDOM]),

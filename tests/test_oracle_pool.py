@@ -46,6 +46,9 @@ def _run_fixture(sc):
             assert ev == op["evicted"] and cnt == op["counts"], op
         elif op["op"] == "release":
             p.release(op["seq_ids"])
+        elif op["op"] == "fork":
+            full_from, swa_from = p.fork(op["src"], op["dst"], op["m"])
+            assert full_from == op["full_from"] and swa_from == op["swa_from"], op
         elif op["op"] == "match":
             assert p.window_safe_len(op["seq"], op["m"], op["tail"]) == op["expect"], op
         elif op["op"] == "truncate":
@@ -84,6 +87,7 @@ class DictPool:
         self.alive = {b: set() for b in range(max_seqs)}  # resident positions
         self.n = {b: 0 for b in range(max_seqs)}
         self.npages = npages
+        self.holders = {}                                 # physical page -> sequences
 
     def fslot(self, b, pos):
         return self.page_of[b][pos // 16] * 16 + pos % 16
@@ -118,6 +122,7 @@ class DictPool:
             for pos in range(self.n[b], end):
                 if pos // 16 not in self.page_of[b]:
                     self.page_of[b][pos // 16] = self.free.pop(0)
+                    self.holders[self.page_of[b][pos // 16]] = {b}
                 fo.append(self.fslot(b, pos))
                 if importing and pos <= end - self.W:
                     so.append(-1)
@@ -136,9 +141,14 @@ class DictPool:
             self.alive[b] -= set(gone)
         return out, cnt
 
+    def _let_go(self, b, pg):
+        self.holders[pg].discard(b)
+        return not self.holders[pg]
+
     def release(self, ids):
         for b in ids:
-            self.free += [self.page_of[b][i] for i in sorted(self.page_of[b])]
+            self.free += [self.page_of[b][i] for i in sorted(self.page_of[b])
+                          if self._let_go(b, self.page_of[b][i])]
             self.page_of[b] = {}
             self.alive[b] = set()
             self.n[b] = 0
@@ -148,11 +158,48 @@ class DictPool:
             lo = min(self.alive[b]) if self.alive[b] else self.n[b]
             if n < 0 or n > self.n[b] or lo > max(0, n - self.W + 1):
                 raise ValueError()
+            # no page another sequence holds may lose or change positions
+            if n < self.n[b] and any(len(self.holders[pg]) > 1 and (lp + 1) * 16 > n
+                                     for lp, pg in self.page_of[b].items()):
+                raise ValueError()
         for b, n in zip(ids, lens):
             self.alive[b] = {p for p in self.alive[b] if p < n}
             gone = sorted(lp for lp in self.page_of[b] if lp * 16 >= n)
+            for lp in gone:
+                self._let_go(b, self.page_of[b][lp])
             self.free = [self.page_of[b].pop(lp) for lp in gone] + self.free
             self.n[b] = n
+
+    def fork(self, srcs, dsts, ms):
+        if len(set(dsts)) != len(dsts) or set(srcs) & set(dsts):
+            raise ValueError()
+        fresh = 0
+        for a, b, m in zip(srcs, dsts, ms):
+            if self.n[b] != 0 or m > self.n[a] or self.match(a, m, self.W - 1) != m:
+                raise ValueError()
+            first_own = max(0, m - self.W + 1) // 16
+            last = (m + 15) // 16
+            if last > self.maxp:
+                raise NoSpace()
+            fresh += last - first_own
+        if fresh > len(self.free):
+            raise NoSpace()
+        out = ([], [])
+        for a, b, m in zip(srcs, dsts, ms):
+            win = max(0, m - self.W + 1)
+            for lp in range((m + 15) // 16):
+                if (lp + 1) * 16 <= win:          # wholly below the window: shared
+                    pg = self.page_of[a][lp]
+                    self.holders[pg].add(b)
+                else:
+                    pg = self.free.pop(0)
+                    self.holders[pg] = {b}
+                self.page_of[b][lp] = pg
+            self.alive[b] = set(range(win, m))
+            self.n[b] = m
+            out[0].append(16 * (win // 16))
+            out[1].append(win)
+        return out
 
     def match(self, b, m, tail):
         # walk back from the end of the match to the first position that lost
@@ -190,21 +237,33 @@ def _check_invariants(p: PoolSim, just_evicted):
             if pos in res:
                 assert m[fs] == p.swa_slot(b, pos)
                 res_slots.append(m[fs])
-            else:
-                assert m[fs] == -1
+            elif p.refs[p.pages[b][pos // 16]] == 1:
+                assert m[fs] == -1   # (a shared page may carry another holder's entries)
         if b in just_evicted and L > 0:
             # every position the next query can see (its W-1 predecessors) is resident
             for pos in range(max(0, L - p.W + 1), L):
                 assert m[p.full_slot(b, pos)] >= 0
     # map injective on resident tokens
     assert len(res_slots) == len(set(res_slots))
-    # Full pages are conserved
-    used = sum(len(x) for x in p.pages)
-    assert used + len(p.free) == p.num_full_pages
-    assert len(set(p.free) | {q for x in p.pages for q in x}) == p.num_full_pages
+    # Full pages are conserved; a page's count is the number of sequences holding it
+    used = {q for x in p.pages for q in x}
+    assert len(used) + len(p.free) == p.num_full_pages
+    assert len(used | set(p.free)) == p.num_full_pages
+    holders = {}
+    for x in p.pages:
+        for q in x:
+            holders[q] = holders.get(q, 0) + 1
+    assert holders == p.refs
+    # on a shared page at most one holder has resident positions, so every
+    # map entry has one owner
+    for q, n in p.refs.items():
+        if n > 1:
+            owners = [b for b in range(p.max_seqs) if q in p.pages[b] and any(
+                p.pages[b][pos // 16] == q for pos in p.resident(b))]
+            assert len(owners) <= 1
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_operations_against_second_simulator(seed):
     rnd = random.Random(seed)
     W = rnd.choice([1, 2, 5, 16, 33, 128])
@@ -261,6 +320,27 @@ def test_random_operations_against_second_simulator(seed):
                 continue
             assert a.import_context(ids, ns) == exp
             just_evicted = {i for i, n in zip(ids, ns) if n > 0}
+        elif r < 0.98:
+            # fork a window-safe prefix of one sequence into an empty one
+            empty = [i for i in range(S) if a.length[i] == 0]
+            src = rnd.randrange(S)
+            dsts = [i for i in empty if i != src]
+            if not dsts or a.length[src] == 0:
+                continue
+            dst = rnd.choice(dsts)
+            want = rnd.randint(1, a.length[src])
+            m = rnd.choice([a.window_safe_len(src, want, W - 1), want])
+            if m == 0:
+                continue
+            try:
+                exp = b.fork([src], [dst], [m])
+            except (ValueError, NoSpace) as e:
+                before = _state(a)
+                with pytest.raises(type(e)):
+                    a.fork([src], [dst], [m])
+                assert _state(a) == before
+                continue
+            assert a.fork([src], [dst], [m]) == exp
         else:
             a.release(ids)
             b.release(ids)
@@ -270,6 +350,138 @@ def test_random_operations_against_second_simulator(seed):
         for i in ids:
             m, tail = rnd.randint(0, a.length[i] + 3), rnd.choice([0, 1, W - 1, W, W + 2])
             assert a.window_safe_len(i, m, tail) == b.match(i, m, tail)
+
+
+def _fork_sequence(seed, stats):
+    """Seeded operations with forks about a quarter of the time: short
+    windows and roomy page budgets, so forks share pages and forks of forks
+    share further."""
+    rnd = random.Random(1000 + seed)
+    W = rnd.choice([1, 2, 5, 16, 20, 33])
+    C = 16 * rnd.randint(max(1, -(-W // 16)), max(1, -(-W // 16)) + 2)
+    S = rnd.randint(3, 6)
+    maxp = rnd.randint(6, 16)
+    npages = rnd.randint(S * maxp // 2, S * maxp)
+    free_order = list(range(npages))
+    rnd.shuffle(free_order)
+    ring = list(range(S * C // 16))
+    rnd.shuffle(ring)
+    a = PoolSim(W, C, S, maxp, npages, free_order, ring)
+    b = DictPool(W, C, S, maxp, npages, free_order, ring)
+    for step in range(150):
+        r = rnd.random()
+        just_evicted = set()
+        if r < 0.25:
+            src = rnd.randrange(S)
+            empty = [i for i in range(S) if a.length[i] == 0 and i != src]
+            if not empty or a.length[src] == 0:
+                continue
+            dst = rnd.choice(empty)
+            want = rnd.randint(1, a.length[src])
+            m = rnd.choice([a.window_safe_len(src, want, W - 1)] * 3 + [want])
+            if m == 0:
+                continue
+            try:
+                exp = b.fork([src], [dst], [m])
+            except (ValueError, NoSpace) as e:
+                before = _state(a)
+                with pytest.raises(type(e)):
+                    a.fork([src], [dst], [m])
+                assert _state(a) == before
+                continue
+            was_shared = a.refs.get(a.pages[src][0], 0) > 1 if a.pages[src] else False
+            assert a.fork([src], [dst], [m]) == exp
+            stats["forks"] += 1
+            stats["shared"] += exp[0][0] > 0
+            stats["chained"] += was_shared and exp[0][0] > 0
+        elif r < 0.5:
+            ids = rnd.sample(range(S), rnd.randint(1, S))
+            ns = [rnd.choice([0, 1, 3, 16, 30]) for _ in ids]
+            try:
+                exp = b.alloc(ids, ns)
+            except NoSpace:
+                with pytest.raises(NoSpace):
+                    a.alloc(ids, ns)
+                continue
+            assert a.alloc(ids, ns) == exp
+        elif r < 0.7:
+            ids = rnd.sample(range(S), rnd.randint(1, S))
+            assert a.evict(ids) == b.evict(ids)
+            just_evicted = set(ids)
+        elif r < 0.8:
+            ids = rnd.sample(range(S), rnd.randint(1, S))
+            ns = [rnd.randint(0, 2 * W + 40) for _ in ids]
+            try:
+                exp = b.alloc(ids, ns, importing=True)
+            except NoSpace:
+                with pytest.raises(NoSpace):
+                    a.import_context(ids, ns)
+                continue
+            assert a.import_context(ids, ns) == exp
+            just_evicted = {i for i, n in zip(ids, ns) if n > 0}
+        elif r < 0.9:
+            ids = rnd.sample(range(S), 1)
+            lens = [max(0, a.length[ids[0]] - rnd.choice([1, 2, 17, 40, 100]))]
+            try:
+                b.truncate(ids, lens)
+            except ValueError:
+                before = _state(a)
+                with pytest.raises(ValueError):
+                    a.truncate(ids, lens)
+                assert _state(a) == before
+                continue
+            a.truncate(ids, lens)
+        else:
+            ids = rnd.sample(range(S), rnd.randint(1, 2))
+            a.release(ids)
+            b.release(ids)
+        assert a.map_table() == b.map_table()
+        assert a.free_pages() == b.free
+        _check_invariants(a, just_evicted)
+        for i in range(S):
+            m, tail = rnd.randint(0, a.length[i] + 3), rnd.choice([0, 1, W - 1, W])
+            assert a.window_safe_len(i, m, tail) == b.match(i, m, tail)
+
+
+def test_random_forks_against_second_simulator():
+    stats = {"forks": 0, "shared": 0, "chained": 0}
+    for seed in range(24):
+        _fork_sequence(seed, stats)
+    # the sequences exercised what they are for
+    assert stats["forks"] >= 100 and stats["shared"] >= 30 and stats["chained"] >= 3, stats
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cut_into_shared_page_refused(seed):
+    """A source that was never evicted is forked; cutting it to a length the
+    window rule allows but that reaches a shared page is refused (a later
+    append would overwrite the fork's K/V), in both simulators, with nothing
+    changed; a cut that keeps the shared pages whole is allowed."""
+    rnd = random.Random(2000 + seed)
+    W = rnd.choice([1, 2, 3, 5, 9])
+    C = 16 * rnd.randint(3, 5)
+    free_order = list(range(24))
+    rnd.shuffle(free_order)
+    a = PoolSim(W, C, 2, 8, 24, free_order, list(range(2 * C // 16)))
+    b = DictPool(W, C, 2, 8, 24, free_order, list(range(2 * C // 16)))
+    L = rnd.randint(W + 16, C)
+    assert a.alloc([0], [L]) == b.alloc([0], [L])
+    m = rnd.randint(W + 15, L)
+    assert a.fork([0], [1], [m]) == b.fork([0], [1], [m])
+    sh = a.shared_pages(0)
+    assert sh == (m - W + 1) // 16 >= 1
+    n = rnd.randrange(W - 1, 16 * sh)
+    before = _state(a)
+    with pytest.raises(ValueError):
+        b.truncate([0], [n])
+    with pytest.raises(ValueError):
+        a.truncate([0], [n])
+    assert _state(a) == before
+    n = rnd.randint(16 * sh, L)
+    a.truncate([0], [n])
+    b.truncate([0], [n])
+    assert a.map_table() == b.map_table() and a.free_pages() == b.free
+    _check_invariants(a, set())
 
 
 def test_decode_steps_evict_one_token_each():

@@ -33,7 +33,7 @@ __all__ = [
     "HswaError", "NoSpace", "FULL", "SWA", "PAGE_SIZE",
     "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view", "hswa_pool_alloc",
     "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_truncate",
-    "hswa_pool_match_len", "hswa_pool_read_tables",
+    "hswa_pool_match_len", "hswa_pool_read_tables", "hswa_pool_fork", "hswa_kv_copy",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
     "hswa_decode_noalloc", "DECODE_SCRATCH_BYTES",
     "hswa_pool_window_counts", "hswa_kv_offload", "hswa_kv_restore",
@@ -233,6 +233,22 @@ def hswa_pool_match_len(pool: Pool, seq_ids: Sequence[int], want: Sequence[int],
     out = np.empty(max(ids.size, 1), np.int32)
     _check(library().hswa_pool_match_len(pool.handle, ids.size, _p(ids), _p(w), t, _p(out)))
     return out[:ids.size]
+
+
+def hswa_pool_fork(pool: Pool, src_ids: Sequence[int], dst_ids: Sequence[int],
+                   lens: Sequence[int], stream=None):
+    """Empty sequences dst_ids[i] take the first lens[i] (window-safe)
+    positions of src_ids[i].  Returns (full_from, swa_from): per fork, the
+    first position whose K/V hswa_kv_copy must copy for FULL and for SWA
+    layers."""
+    src, dst, n = _i32(src_ids), _i32(dst_ids), _i32(lens)
+    if not (src.size == dst.size == n.size):
+        raise ValueError("one source, destination and length per fork")
+    ff = np.empty(max(dst.size, 1), np.int32)
+    sf = np.empty(max(dst.size, 1), np.int32)
+    _check(library().hswa_pool_fork(pool.handle, dst.size, _p(src), _p(dst), _p(n), _p(ff),
+                                     _p(sf), _stream(stream)))
+    return ff[:dst.size], sf[:dst.size]
 
 
 def hswa_pool_read_tables(pool: Pool) -> dict:
@@ -487,3 +503,25 @@ def hswa_kv_restore(kind: int, seq_ids, cu_tok, total_tok: int, max_tok: int, vi
     a = _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache, buf_k,
                    buf_v, first_pos)
     _check(library().hswa_kv_restore(C.byref(a), _stream(stream)))
+
+
+def hswa_kv_copy(kind: int, src_ids, dst_ids, first_pos, end_pos, max_tok: int, view, k_cache,
+                 v_cache, stream=None) -> None:
+    """Copies this layer's K/V of positions [first_pos[i], end_pos[i]) from
+    sequence src_ids[i] to dst_ids[i] (device int32 tensors), page to page,
+    e.g. after hswa_pool_fork."""
+    _expect("k_cache", k_cache, _BF16, (None, None, PAGE_SIZE, None))
+    hkv, d = k_cache.shape[1], k_cache.shape[3]
+    _expect("v_cache", v_cache, _F16, (k_cache.shape[0], hkv, d, PAGE_SIZE))
+    for name, t in (("src_ids", src_ids), ("dst_ids", dst_ids), ("first_pos", first_pos),
+                    ("end_pos", end_pos)):
+        _expect(name, t, _I32, (src_ids.shape[0],))
+    a = _capi.KvCopyArgs()
+    a.kind, a.num_kv_heads, a.head_dim = kind, hkv, d
+    a.num_seqs = src_ids.shape[0]
+    a.src_ids, a.dst_ids = _dptr(src_ids), _dptr(dst_ids)
+    a.first_pos, a.end_pos = _dptr(first_pos), _dptr(end_pos)
+    a.max_tok = max_tok
+    a.pool = view
+    a.k_cache, a.v_cache = _dptr(k_cache), _dptr(v_cache)
+    _check(library().hswa_kv_copy(C.byref(a), _stream(stream)))

@@ -31,10 +31,10 @@ EXPORTED = (
     "hswa_last_error", "hswa_status_string", "hswa_version",
     "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view",
     "hswa_pool_alloc", "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release",
-    "hswa_pool_truncate", "hswa_pool_match_len", "hswa_pool_read_tables",
+    "hswa_pool_truncate", "hswa_pool_match_len", "hswa_pool_read_tables", "hswa_pool_fork",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
     "hswa_decode_noalloc",
-    "hswa_pool_window_counts", "hswa_kv_offload", "hswa_kv_restore",
+    "hswa_pool_window_counts", "hswa_kv_offload", "hswa_kv_restore", "hswa_kv_copy",
 )
 
 
@@ -116,6 +116,23 @@ class XferArgs(C.Structure):
     ]
 
 
+class KvCopyArgs(C.Structure):
+    _fields_ = [
+        ("kind", C.c_int32),
+        ("num_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32),
+        ("num_seqs", C.c_int32),
+        ("src_ids", C.c_void_p),
+        ("dst_ids", C.c_void_p),
+        ("first_pos", C.c_void_p),
+        ("end_pos", C.c_void_p),
+        ("max_tok", C.c_int32),
+        ("pool", PoolView),
+        ("k_cache", C.c_void_p),
+        ("v_cache", C.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -154,6 +171,9 @@ def load():
     lib.hswa_pool_match_len.argtypes = [C.c_void_p, C.c_int32, I32P, I32P, C.c_int32, I32P]
     lib.hswa_pool_truncate.restype = C.c_int
     lib.hswa_pool_truncate.argtypes = [C.c_void_p, C.c_int32, I32P, I32P, C.c_void_p]
+    lib.hswa_pool_fork.restype = C.c_int
+    lib.hswa_pool_fork.argtypes = [C.c_void_p, C.c_int32, I32P, I32P, I32P, I32P, I32P,
+                                   C.c_void_p]
     lib.hswa_pool_read_tables.restype = C.c_int
     lib.hswa_pool_read_tables.argtypes = [C.c_void_p, I32P, I32P, I32P, I32P, I32P]
     for name in ("hswa_prefill_chunk", "hswa_append_kv"):
@@ -170,6 +190,8 @@ def load():
         f = getattr(lib, name)
         f.restype = C.c_int
         f.argtypes = [C.POINTER(XferArgs), C.c_void_p]
+    lib.hswa_kv_copy.restype = C.c_int
+    lib.hswa_kv_copy.argtypes = [C.POINTER(KvCopyArgs), C.c_void_p]
     lib.hswa_decode_workspace_bytes.restype = C.c_size_t
     lib.hswa_decode_workspace_bytes.argtypes = [C.POINTER(AttnArgs)]
     _lib = lib

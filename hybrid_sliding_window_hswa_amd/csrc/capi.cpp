@@ -462,6 +462,69 @@ int xfer(const hswa_xfer_args* a, bool to_host, void* stream) {
 
 extern "C" {
 
+int hswa_kv_copy(const hswa_kv_copy_args* a, void* stream) {
+  hswa::clear_error();
+  if (!a) {
+    hswa::set_error("args is NULL");
+    return HSWA_E_INVAL;
+  }
+  if (a->kind != HSWA_LAYER_FULL && a->kind != HSWA_LAYER_SWA) {
+    hswa::set_error("kind must be HSWA_LAYER_FULL or HSWA_LAYER_SWA (got %d)", a->kind);
+    return HSWA_E_INVAL;
+  }
+  if (a->head_dim != 64 && a->head_dim != 128) {
+    hswa::set_error("head_dim must be 64 or 128 (got %d)", a->head_dim);
+    return HSWA_E_INVAL;
+  }
+  if (a->num_kv_heads < 1 || a->num_kv_heads > hswa::kMaxKvHeads || a->num_seqs < 0 ||
+      a->max_tok < 0) {
+    hswa::set_error("1 <= num_kv_heads <= %d; num_seqs, max_tok >= 0 required",
+                    hswa::kMaxKvHeads);
+    return HSWA_E_INVAL;
+  }
+  if (a->num_seqs == 0 || a->max_tok == 0) return HSWA_OK;
+  const hswa_pool_view& v = a->pool;
+  if (!v.seq_len || !v.fpt || !v.rpt || v.ring_slots < 16 || v.ring_slots % 16 ||
+      v.max_pages_per_seq < 1 || v.max_seqs < 1) {
+    hswa::set_error("pool view is invalid");
+    return HSWA_E_INVAL;
+  }
+  if (a->kind == HSWA_LAYER_SWA && a->max_tok > v.ring_slots) {
+    hswa::set_error("SWA copy of %d positions per sequence: the ring holds %d", a->max_tok,
+                    v.ring_slots);
+    return HSWA_E_INVAL;
+  }
+  if (!a->src_ids || !a->dst_ids || !a->first_pos || !a->end_pos || !a->k_cache ||
+      !a->v_cache) {
+    hswa::set_error("src_ids, dst_ids, first_pos, end_pos, k_cache and v_cache must be set");
+    return HSWA_E_INVAL;
+  }
+  if (!aligned16(a->k_cache) || !aligned16(a->v_cache)) {
+    hswa::set_error("k_cache and v_cache must be 16-byte aligned");
+    return HSWA_E_INVAL;
+  }
+  hswa::CopyParams p{};
+  p.kind = a->kind;
+  p.hkv = a->num_kv_heads;
+  p.d = a->head_dim;
+  p.num_seqs = a->num_seqs;
+  p.src_ids = a->src_ids;
+  p.dst_ids = a->dst_ids;
+  p.first_pos = a->first_pos;
+  p.end_pos = a->end_pos;
+  p.max_tok = a->max_tok;
+  p.k_cache = (uint16_t*)a->k_cache;
+  p.v_cache = (uint16_t*)a->v_cache;
+  p.t.seq_len = v.seq_len;
+  p.t.fpt = v.fpt;
+  p.t.rpt = v.rpt;
+  p.t.max_pages = v.max_pages_per_seq;
+  p.t.ring_slots = v.ring_slots;
+  p.t.max_seqs = v.max_seqs;
+  hipError_t e = hswa::launch_copy(p, (hipStream_t)stream);
+  return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "copy launch");
+}
+
 int hswa_kv_offload(const hswa_xfer_args* a, void* stream) { return xfer(a, true, stream); }
 
 int hswa_kv_restore(const hswa_xfer_args* a, void* stream) { return xfer(a, false, stream); }

@@ -122,7 +122,23 @@ struct XferParams {
   uint16_t* buf_v;
 };
 
+// Copy of one layer's K/V between two sequences of a pool, page to page.
+struct CopyParams {
+  int32_t kind;
+  int32_t hkv, d;
+  int32_t num_seqs;
+  const int32_t* src_ids;
+  const int32_t* dst_ids;
+  const int32_t* first_pos;
+  const int32_t* end_pos;
+  int32_t max_tok;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  Tables t;
+};
+
 hipError_t launch_append(const AttnParams& p, hipStream_t stream);
+hipError_t launch_copy(const CopyParams& p, hipStream_t stream);
 // to_host: pages -> buffer (offload); else buffer -> pages (restore)
 hipError_t launch_xfer(const XferParams& p, bool to_host, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);

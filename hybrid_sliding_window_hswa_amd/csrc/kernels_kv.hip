@@ -269,6 +269,87 @@ hipError_t launch_append(const AttnParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// K/V copy between two sequences of one pool, for prefix reuse ("MiMo-V2.5
+// Series Inference Full-Link Optimization" sec. 2.1, "SWA-aware prefix cache
+// tree", point 3).  One workgroup per (pair, 16-position page tile) copies
+// every KV head of the tile.  A position sits at the same in-page offset in
+// both sequences (pos % 16 for Full pages; (pos mod C) % 16 = pos % 16 in a
+// ring of C slots), so the copy moves K rows and V columns between the two
+// pages at that offset: whole 16-byte pieces when the tile is whole,
+// element by element otherwise.
+template <int D, int KIND>
+__global__ void __launch_bounds__(256) copy_kernel(CopyParams p, int tiles_per_pair) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per K row
+  const int i = blockIdx.x / tiles_per_pair;
+  const int t = blockIdx.x % tiles_per_pair;
+  const int a = p.src_ids[i], b = p.dst_ids[i];
+  if (a < 0 || a >= p.t.max_seqs || b < 0 || b >= p.t.max_seqs || a == b) return;
+  const int La = p.t.seq_len[a], Lb = p.t.seq_len[b];
+  int p0 = p.first_pos[i];
+  int p1 = min(p.end_pos[i], min(La, Lb));     // stored in both sequences
+  if (KIND != 0)                               // still held by both rings
+    p0 = max(p0, max(idx::ring_oldest(La, p.t.ring_slots), idx::ring_oldest(Lb, p.t.ring_slots)));
+  p0 = max(p0, 0);
+  if (p1 - p0 > p.max_tok) p1 = p0 + p.max_tok;  // the grid covers max_tok positions
+  const int tile_pos = idx::tile_pos(p0, t);
+  if (p0 >= p1 || tile_pos >= p1) return;
+  const int lo = max(tile_pos, p0), hi = min(tile_pos + kPage, p1);
+  const int32_t pa = page_of<KIND>(p.t.fpt, p.t.rpt, a, tile_pos, p.t.max_pages, p.t.ring_slots);
+  const int32_t pb = page_of<KIND>(p.t.fpt, p.t.rpt, b, tile_pos, p.t.max_pages, p.t.ring_slots);
+  if (pa < 0 || pb < 0) return;  // a position without a page: the caller skipped alloc
+  const int hkv = p.hkv;
+  const int tid = threadIdx.x;
+  const bool whole = lo == tile_pos && hi == tile_pos + kPage;
+  // K rows: (head, token, chunk), chunks fastest
+  for (int e = tid; e < hkv * kPage * CPR; e += blockDim.x) {
+    const int h = e / (kPage * CPR);
+    const int tok = (e / CPR) % kPage;
+    const int c = e % CPR;
+    if (tile_pos + tok < lo || tile_pos + tok >= hi) continue;
+    const int64_t off = (int64_t)h * kPage * D + tok * D + c * 8;
+    *(u32x4*)(p.k_cache + (int64_t)pb * hkv * kPage * D + off) =
+        *(const u32x4*)(p.k_cache + (int64_t)pa * hkv * kPage * D + off);
+  }
+  // V columns: (head, dim, 8-token half)
+  for (int e = tid; e < hkv * D * 2; e += blockDim.x) {
+    const int h = e / (2 * D);
+    const int dim = (e / 2) % D;
+    const int half = e % 2;
+    const int64_t off = (int64_t)h * D * kPage + dim * kPage + half * 8;
+    const uint16_t* src = p.v_cache + (int64_t)pa * hkv * D * kPage + off;
+    uint16_t* dst = p.v_cache + (int64_t)pb * hkv * D * kPage + off;
+    if (whole) {
+      *(u32x4*)dst = *(const u32x4*)src;
+    } else {
+      for (int j = 0; j < 8; ++j) {
+        const int pos = tile_pos + half * 8 + j;
+        if (pos >= lo && pos < hi) dst[j] = src[j];
+      }
+    }
+  }
+}
+
+hipError_t launch_copy(const CopyParams& p, hipStream_t s) {
+  if (p.num_seqs <= 0 || p.max_tok <= 0) return hipSuccess;
+  const int tiles = idx::tiles_for(p.max_tok);
+  const int64_t blocks = (int64_t)p.num_seqs * tiles;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks);
+  if (p.d == 128) {
+    if (p.kind == 0)
+      hipLaunchKernelGGL((copy_kernel<128, 0>), grid, dim3(256), 0, s, p, tiles);
+    else
+      hipLaunchKernelGGL((copy_kernel<128, 1>), grid, dim3(256), 0, s, p, tiles);
+  } else {
+    if (p.kind == 0)
+      hipLaunchKernelGGL((copy_kernel<64, 0>), grid, dim3(256), 0, s, p, tiles);
+    else
+      hipLaunchKernelGGL((copy_kernel<64, 1>), grid, dim3(256), 0, s, p, tiles);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Window-masked transfer ("MiMo-V2.5 Series Inference Full-Link
 // Optimization" sec. 2.1 "KVCache Dual Pool", Data Transfer: tiers exchange
 // only the valid SWA window).  One workgroup per (sequence, 16-position page

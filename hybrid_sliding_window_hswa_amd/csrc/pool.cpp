@@ -95,6 +95,7 @@ struct hswa_pool {
   std::vector<int32_t> map;        // [num_pages*16]
   std::vector<int32_t> freeq;      // FIFO ring of free pages
   int64_t fhead = 0, fcount = 0;
+  std::vector<int32_t> refs;       // per Full page: sequences holding it
   std::vector<uint32_t> mark;      // per-sequence epoch for duplicate checks
   uint32_t epoch = 0;
   // device mirror
@@ -109,7 +110,18 @@ struct hswa_pool {
     int32_t p = freeq[fhead];
     fhead = (fhead + 1) % num_pages;
     --fcount;
+    refs[p] = 1;
     return p;
+  }
+  // one holder lets go of a page; true when no sequence holds it any more
+  bool drop_page(int32_t p) { return --refs[p] == 0; }
+  // leading pages of sequence b that another sequence also holds (a fork
+  // shares a prefix of its source's pages, so shared pages form a prefix)
+  int32_t shared_pages(int32_t b) const {
+    int32_t n = 0;
+    const int32_t* row = &fpt[(size_t)b * max_pages];
+    while (n < npages[b] && refs[row[n]] > 1) ++n;
+    return n;
   }
   void push_page(int32_t p) {
     freeq[(fhead + fcount) % num_pages] = p;
@@ -462,6 +474,7 @@ int hswa_pool_create(const hswa_pool_desc* d, hswa_pool** out) {
     p->rpt.assign(d->ring_pages, d->ring_pages + nring);
     p->map.assign((size_t)p->num_pages * kPage, -1);
     p->freeq.assign(d->full_free_order, d->full_free_order + p->num_pages);
+    p->refs.assign(p->num_pages, 0);
     p->fhead = 0;
     p->fcount = p->num_pages;
   } catch (const std::bad_alloc&) {
@@ -599,7 +612,7 @@ int hswa_pool_release(hswa_pool* p, int32_t n, const int32_t* ids, void* stream)
     for (int32_t pos = lo; pos < hi; ++pos) p->map[p->full_slot(b, pos)] = -1;
     if (p->has_dev) rb.add(p, b, 0, lo, hi, 0, 0, 0, p->npages[b], 1, row);
     for (int32_t lp = 0; lp < p->npages[b]; ++lp) {
-      p->push_page(row[lp]);
+      if (p->drop_page(row[lp])) p->push_page(row[lp]);  // last holder
       row[lp] = -1;
     }
     p->npages[b] = 0;
@@ -636,6 +649,14 @@ int hswa_pool_truncate(hswa_pool* p, int32_t n, const int32_t* ids, const int32_
                       b, p->res_start[b], k, std::max(0, k - p->W + 1));
       return HSWA_E_INVAL;
     }
+    // a page another sequence holds may neither be freed nor take new
+    // positions (a later append would overwrite the other holder's K/V)
+    const int32_t sh = p->shared_pages(b);
+    if (k < p->len[b] && (int64_t)k < (int64_t)kPage * sh) {
+      hswa::set_error("sequence %d: length %d cuts into its first %d pages, which another "
+                      "sequence also holds", b, k, sh);
+      return HSWA_E_INVAL;
+    }
   }
   RecBuilder rb;
   for (int32_t i = 0; i < n; ++i) {
@@ -649,6 +670,7 @@ int hswa_pool_truncate(hswa_pool* p, int32_t n, const int32_t* ids, const int32_
     // the record copies the page ids of the cleared range before they go
     if (p->has_dev) rb.add(p, b, k, k, L, 0, 0, keep, p->npages[b], 1, row);
     for (int32_t lp = p->npages[b] - 1; lp >= keep; --lp) {
+      p->drop_page(row[lp]);  // held by b alone (checked above)
       p->push_page_front(row[lp]);
       row[lp] = -1;
     }
@@ -681,11 +703,13 @@ int hswa_pool_match_len(const hswa_pool* p, int32_t n, const int32_t* ids,
     int32_t k = std::min(want[i], p->len[b]);
     // A position without an SWA entry at h rules out every end in
     // (h, h + tail]; walk back from the match end to the first end whose
-    // tail window has no such position.
+    // tail window has no such position.  Positions before the sequence's
+    // first resident one have none of its entries (a page it shares with
+    // another sequence may carry that one's).
     while (k > 0) {
       int32_t hole = -1;
       for (int32_t pos = k - 1; pos >= std::max(0, k - tail); --pos) {
-        if (p->map[p->full_slot(b, pos)] < 0) {
+        if (pos < p->res_start[b] || p->map[p->full_slot(b, pos)] < 0) {
           hole = pos;
           break;
         }
@@ -696,6 +720,85 @@ int hswa_pool_match_len(const hswa_pool* p, int32_t n, const int32_t* ids,
     out[i] = k;
   }
   return HSWA_OK;
+}
+
+int hswa_pool_fork(hswa_pool* p, int32_t n, const int32_t* src_ids, const int32_t* dst_ids,
+                   const int32_t* lens, int32_t* full_from, int32_t* swa_from, void* stream) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  int rc = check_ids(p, n, dst_ids);  // destinations distinct and in range
+  if (rc) return rc;
+  if (n > 0 && (!src_ids || !lens)) {
+    hswa::set_error("fork: src_ids and lens are required");
+    return HSWA_E_INVAL;
+  }
+  // every check before any change: sources in range and not destinations,
+  // destinations empty, lengths window-safe for their sources, then the
+  // Full pages of all forks together
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t a = src_ids[i], b = dst_ids[i], m = lens[i];
+    if (a < 0 || a >= p->max_seqs || p->mark[a] == p->epoch) {
+      hswa::set_error("fork %d: source %d out of range or also a destination", i, a);
+      return HSWA_E_INVAL;
+    }
+    if (p->len[b] != 0) {
+      hswa::set_error("fork %d: destination %d holds %d positions (must be empty)", i, b,
+                      p->len[b]);
+      return HSWA_E_INVAL;
+    }
+    if (m < 0 || m > p->len[a]) {
+      hswa::set_error("fork %d: length %d outside [0, %d]", i, m, p->len[a]);
+      return HSWA_E_INVAL;
+    }
+    for (int32_t pos = std::max(0, m - (p->W - 1)); pos < m; ++pos) {
+      if (pos < p->res_start[a] || p->map[p->full_slot(a, pos)] < 0) {
+        hswa::set_error("fork %d: position %d of source %d has left the SWA pool, so %d "
+                        "positions are not window-safe (see hswa_pool_match_len)", i, pos, a, m);
+        return HSWA_E_INVAL;
+      }
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t m = lens[i];
+    const int64_t pages = ceil_div(m, kPage);
+    if (pages > p->max_pages) {
+      hswa::set_error("fork %d: %lld pages, a table row holds %d", i, (long long)pages,
+                      p->max_pages);
+      return HSWA_E_NOSPC;
+    }
+    need += pages - std::max(0, m - p->W + 1) / kPage;
+  }
+  if (need > p->fcount) {
+    hswa::set_error("Full pool: %lld pages needed, %lld free", (long long)need,
+                    (long long)p->fcount);
+    return HSWA_E_NOSPC;
+  }
+  RecBuilder rb;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t a = src_ids[i], b = dst_ids[i], m = lens[i];
+    const int32_t start = std::max(0, m - p->W + 1);   // dst's window start
+    const int32_t own = start / kPage;                 // pages shared below it
+    const int32_t pages = (int32_t)ceil_div(m, kPage);
+    const int32_t* srow = &p->fpt[(size_t)a * p->max_pages];
+    int32_t* row = &p->fpt[(size_t)b * p->max_pages];
+    for (int32_t lp = 0; lp < own; ++lp) {
+      row[lp] = srow[lp];
+      ++p->refs[row[lp]];
+    }
+    for (int32_t lp = own; lp < pages; ++lp) row[lp] = p->pop_page();
+    for (int32_t pos = start; pos < m; ++pos) p->map[p->full_slot(b, pos)] = p->swa_slot(b, pos);
+    p->npages[b] = pages;
+    p->len[b] = m;
+    p->res_start[b] = start;
+    if (full_from) full_from[i] = kPage * own;
+    if (swa_from) swa_from[i] = start;
+    if (p->has_dev) rb.add(p, b, m, 0, 0, start, m, 0, pages, 0, row);
+  }
+  return flush(p, rb, stream);
 }
 
 int hswa_pool_window_counts(const hswa_pool* p, int32_t kind, int32_t n, const int32_t* ids,

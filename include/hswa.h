@@ -238,13 +238,41 @@ int hswa_pool_truncate(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
 /* Window-safe prefix-match length ([MiMo] 2.1 "SWA-aware prefix cache
  * tree", point 1): for each listed sequence, the longest m' <= min(want[i],
  * seq_len) such that the last min(m', tail) positions before m' all still
- * hold an SWA entry (map >= 0); the rest of a token match is a miss.  The
+ * hold an SWA entry of that sequence (map >= 0, at or after its first
+ * resident position); the rest of a token match is a miss.  The
  * query at m' attends to W keys counting itself, so tail = W - 1 is what this
  * library's attention needs (and what eviction keeps); the page asks for
  * tail = W.  Host arrays of n_seqs entries; out receives m'.  Reads the host
  * metadata only.  HSWA_E_INVAL for a bad id, a negative want or tail. */
 int hswa_pool_match_len(const hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
                         const int32_t* want, int32_t tail, int32_t* out);
+
+/* Prefix reuse across requests ([MiMo] 2.1 "SWA-aware prefix cache tree",
+ * points 1 and 3: a matched prefix keeps its Full part shareable and its SWA
+ * part usable as far as the window-safe match reaches).  Empty sequence
+ * dst_ids[i] takes the first lens[i] positions of src_ids[i]; lens[i] must be
+ * window-safe for the source with tail W - 1 (hswa_pool_match_len), i.e. the
+ * source still holds SWA entries for the W - 1 positions before it.
+ *   - The Full pages wholly below the destination's window start
+ *     s = max(0, lens[i] - W + 1) are shared with the source (each page
+ *     counts the sequences holding it; release frees it when the last one
+ *     lets go).
+ *   - The pages from the one holding s up to the one holding lens[i] - 1 are
+ *     fresh (free-list head, logical order), and positions [s, lens[i]) get
+ *     the destination's ring slots and map entries.  Every map entry so has
+ *     one owner: shared positions stay outside the destination's window.
+ *   - full_from[i] / swa_from[i] (host, nullable) receive the first position
+ *     whose K/V the caller copies from source to destination with
+ *     hswa_kv_copy, up to lens[i]: 16 * (s / 16) for FULL layers (the fresh
+ *     pages), s for SWA layers (the window).
+ * Checks come first and nothing changes on failure: HSWA_E_INVAL for a bad
+ * id, a destination that is not empty or is also a source, a length outside
+ * [0, source length] or not window-safe; HSWA_E_NOSPC when the Full pool
+ * lacks the fresh pages of all forks together or a row is too short.  A
+ * sequence may not be cut (hswa_pool_truncate) into a page another sequence
+ * holds: HSWA_E_INVAL.  Device tables are updated on `stream`. */
+int hswa_pool_fork(hswa_pool* pool, int32_t n, const int32_t* src_ids, const int32_t* dst_ids,
+                   const int32_t* lens, int32_t* full_from, int32_t* swa_from, void* stream);
 
 /* Host copies of the pool's metadata for inspection (each pointer nullable):
  * seq_len [max_seqs], fpt [max_seqs*max_pages_per_seq], map
@@ -420,6 +448,40 @@ int hswa_kv_offload(const hswa_xfer_args* args, void* stream);
  * page are untouched.  Asynchronous on `stream`; keep the buffers unchanged
  * until it completes.  Offload then restore gives back the same bits. */
 int hswa_kv_restore(const hswa_xfer_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * K/V copy between sequences of one pool, for prefix reuse ([MiMo] 2.1
+ * "SWA-aware prefix cache tree", point 3): after hswa_pool_fork, a FULL
+ * layer copies positions [full_from, len) of each fork and a SWA layer
+ * [swa_from, len) from the source's pages to the destination's.
+ * -------------------------------------------------------------------- */
+typedef struct hswa_kv_copy_args {
+  int32_t kind;             /* hswa_layer_kind of the layer whose pages copy */
+  int32_t num_kv_heads;     /* Hkv in [1, 1024]                               */
+  int32_t head_dim;         /* 64 or 128                                      */
+  int32_t num_seqs;         /* copies in this call                           */
+  const int32_t* src_ids;   /* device [num_seqs]: source sequence ids        */
+  const int32_t* dst_ids;   /* device [num_seqs]: destination sequence ids   */
+  const int32_t* first_pos; /* device [num_seqs]: copy i moves positions     */
+  const int32_t* end_pos;   /* [first_pos[i], end_pos[i]) (device) ...        */
+  int32_t max_tok;          /* ... host hint >= every end_pos - first_pos;
+                               SWA: at most ring_slots                        */
+  hswa_pool_view pool;      /* from hswa_pool_get_view                        */
+  void* k_cache;            /* this layer's K pages (bf16, layout above)      */
+  void* v_cache;            /* this layer's V pages (fp16)                    */
+} hswa_kv_copy_args;
+
+/* Copies, for every listed pair, the K and V of positions [first_pos,
+ * end_pos) from the source's slots to the destination's slots of the same
+ * positions (Full slots for FULL layers, ring slots for SWA layers); the
+ * bits are copied verbatim and other positions of a page are untouched.
+ * Positions at or beyond either sequence's length are not copied, nor, for
+ * SWA layers, positions older than length - ring_slots of either sequence
+ * (their slots hold newer positions); a pair with equal ids copies nothing.
+ * Asynchronous on `stream`, ordered after the hswa_pool_fork that gave the
+ * destination its slots.  HSWA_E_INVAL for a bad argument or an SWA max_tok
+ * above ring_slots; BF16 pages only. */
+int hswa_kv_copy(const hswa_kv_copy_args* args, void* stream);
 
 #ifdef __cplusplus
 }

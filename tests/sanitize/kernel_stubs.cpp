@@ -15,6 +15,7 @@ hipError_t launch_pool_apply(const PoolDev&, const PoolRec*, int, const int32_t*
 }
 hipError_t launch_append(const AttnParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_xfer(const XferParams&, bool, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_copy(const CopyParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_prefill(const AttnParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode(const AttnParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t decode_scratch(float**) { return hipErrorNoDevice; }

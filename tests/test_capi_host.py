@@ -75,6 +75,9 @@ def test_golden_fixtures_through_the_abi():
                     H.hswa_pool_truncate(p, op["seq_ids"], op["new_len"])
             elif op["op"] == "release":
                 H.hswa_pool_release(p, op["seq_ids"])
+            elif op["op"] == "fork":
+                ff, sf = H.hswa_pool_fork(p, op["src"], op["dst"], op["m"])
+                assert ff.tolist() == op["full_from"] and sf.tolist() == op["swa_from"], op
             elif op["op"] == "match":
                 got = H.hswa_pool_match_len(p, [op["seq"]], [op["m"]], op["tail"])
                 assert got.tolist() == [op["expect"]], op
@@ -86,7 +89,7 @@ def test_golden_fixtures_through_the_abi():
         assert {str(i): s for i, s in enumerate(mp) if s >= 0} == f["map_nonneg"]
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_random_operations_bit_exact_vs_oracle(seed):
     rnd = random.Random(1000 + seed)
     W = rnd.choice([1, 3, 16, 64, 128])
@@ -122,7 +125,30 @@ def test_random_operations_bit_exact_vs_oracle(seed):
             exp = sim.evict(ids)
             ev, cnt = H.hswa_pool_evict(p, ids)
             assert ev.tolist() == exp[0] and cnt.tolist() == exp[1]
-        elif r < 0.95:
+        elif r < 0.93:
+            # fork a (mostly window-safe) prefix into empty sequences
+            empty = [i for i in range(S) if sim.length[i] == 0]
+            full_seqs = [i for i in range(S) if sim.length[i] > 0]
+            if not empty or not full_seqs:
+                continue
+            dst = rnd.sample(empty, rnd.randint(1, len(empty)))
+            src = [rnd.choice(full_seqs) for _ in dst]
+            want = [rnd.randint(0, sim.length[a]) for a in src]
+            m = [rnd.choice([sim.window_safe_len(a, w, W - 1)] * 3 + [w])
+                 for a, w in zip(src, want)]
+            try:
+                exp = sim.fork(src, dst, m)
+            except (ValueError, NoSpace) as err:
+                before = _tables(p)
+                with pytest.raises(H.NoSpace if isinstance(err, NoSpace) else H.HswaError) as e:
+                    H.hswa_pool_fork(p, src, dst, m)
+                if not isinstance(err, NoSpace):
+                    assert e.value.status == H.HSWA_E_INVAL
+                assert _tables(p) == before
+                continue
+            ff, sf = H.hswa_pool_fork(p, src, dst, m)
+            assert ff.tolist() == exp[0] and sf.tolist() == exp[1]
+        elif r < 0.96:
             lens = [max(0, sim.length[i] - rnd.choice([0, 1, 2, 3, 17, W + 1])) for i in ids]
             try:
                 sim.truncate(ids, lens)
@@ -323,3 +349,56 @@ def test_append_without_rows_is_a_noop():
     assert lib.hswa_append_kv(C.byref(a), None) == H.HSWA_OK
     a = _args(total_q=3, n=2, max_q_len=2, k_new=None, v_new=None)
     assert lib.hswa_append_kv(C.byref(a), None) == H.HSWA_E_INVAL
+
+
+def test_fork_validation():
+    """Forks are checked before anything changes: a destination that is not
+    empty or is also a source, a length past the source or not window-safe
+    (E_INVAL); too few free pages for all forks together (E_NOSPC)."""
+    W, C_ = 8, 32
+    p = _host_pool(W, C_, 5, 8, 12, list(range(12)), list(range(10)))
+    H.hswa_pool_alloc(p, [0, 1], [30, 5])          # pages: 2 + 1, free 9
+    H.hswa_pool_evict(p, [0, 1])                   # sequence 0 keeps 23..29
+    before = _tables(p)
+    bad = [([0], [1], [10]),        # destination not empty
+           ([0], [0], [10]),        # destination is its own source
+           ([0, 2], [2, 3], [5, 1]),  # a destination is also a source
+           ([0], [2], [31]),        # longer than the source
+           ([0], [2], [20]),        # position 13 left the SWA pool: not window-safe
+           ([5], [2], [1])]         # source out of range
+    for src, dst, m in bad:
+        with pytest.raises(H.HswaError) as e:
+            H.hswa_pool_fork(p, src, dst, m)
+        assert e.value.status == H.HSWA_E_INVAL, (src, dst, m)
+        assert _tables(p) == before
+    # a 30-position fork shares page 0 and needs one fresh page (positions
+    # 16-31 hold its window 23..29); two need two, and one is free
+    H.hswa_pool_import(p, [4], [128])              # 8 pages: free 1
+    before = _tables(p)
+    with pytest.raises(H.NoSpace):
+        H.hswa_pool_fork(p, [0, 0], [2, 3], [30, 30])
+    assert _tables(p) == before
+    H.hswa_pool_release(p, [4])
+    ff, sf = H.hswa_pool_fork(p, [0, 0], [2, 3], [30, 30])
+    assert ff.tolist() == [16, 16] and sf.tolist() == [23, 23]
+    t = H.hswa_pool_read_tables(p)
+    assert t["fpt"][2][0] == t["fpt"][3][0] == t["fpt"][0][0]
+    assert len({t["fpt"][b][1] for b in (0, 2, 3)}) == 3
+    # the shared page outlives its first holder
+    H.hswa_pool_release(p, [0, 2])
+    assert t["fpt"][0][0] not in H.hswa_pool_read_tables(p)["free"].tolist()
+    H.hswa_pool_release(p, [3])
+    assert t["fpt"][0][0] in H.hswa_pool_read_tables(p)["free"].tolist()
+
+
+def test_kv_copy_validation():
+    from hybrid_sliding_window_hswa_amd import _capi
+    lib = _capi.load()
+    a = _capi.KvCopyArgs()
+    a.kind, a.num_kv_heads, a.head_dim, a.num_seqs, a.max_tok = 1, 2, 128, 1, 16
+    assert lib.hswa_kv_copy(C.byref(a), None) == H.HSWA_E_INVAL   # no pool view
+    a.head_dim = 96
+    assert lib.hswa_kv_copy(C.byref(a), None) == H.HSWA_E_INVAL
+    a.head_dim, a.num_seqs = 128, 0
+    assert lib.hswa_kv_copy(C.byref(a), None) == H.HSWA_OK         # nothing to copy
+    assert lib.hswa_kv_copy(None, None) == H.HSWA_E_INVAL

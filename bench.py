@@ -192,7 +192,7 @@ class ChunkedPrefill:
     layers see the same synthetic Q/K/V (an attention-only stack)."""
 
     def __init__(self, cx, lens, chunk, hq, hkv, d, W, seed, pattern="S", ring=None,
-                 out="f32"):
+                 out="f32", one_stream=False):
         torch, H = cx.torch, cx.H
         import synth
         self.cx = cx
@@ -234,6 +234,7 @@ class ChunkedPrefill:
                 "ids": _arr(act), "n": _arr(n), "nseq": len(act), "max_n": max(n),
                 "sid": cx.i32(act),
                 "cu": cx.i32(np.concatenate([[0], np.cumsum(n)])),
+                "qpos": cx.i32([done[b] for b in act]),
                 "q": cat([self.q[b][a:e] for b, a, e in rows]),
                 "k": cat([self.k[b][a:e] for b, a, e in rows]),
                 "v": cat([self.v[b][a:e] for b, a, e in rows]),
@@ -246,6 +247,16 @@ class ChunkedPrefill:
         self.out = torch.empty((max_rows, hq, d), device=cx.dev,
                                dtype=torch.float16 if out == "f16" else torch.float32)
         self.all_ids = _arr(list(range(B)))
+        # An all-SWA stack passes each sequence's first row position (q_pos):
+        # its appends and attention then read no pool table that alloc,
+        # evict or release write, and those pool calls go to a second stream
+        # (default priority) beside the attention, with no waits between the
+        # streams.  Full layers read the Full page table that alloc writes,
+        # so a stack with Full layers keeps one stream.
+        self.side = None
+        if "F" not in pattern and not one_stream:
+            self.side_stream = torch.cuda.Stream()
+            self.side = C.c_void_p(self.side_stream.cuda_stream)
         for st in self.steps:
             T = st["q"].shape[0]
             st["args"] = []
@@ -254,16 +265,19 @@ class ChunkedPrefill:
                                  0, self.view, None, st["k"], st["v"], kc, vc, None)
                 att = _attn_args(cx, kind, W, hq, hkv, d, st["sid"], st["cu"], T, st["max_n"],
                                  0, self.view, st["q"], None, None, kc, vc, self.out)
+                if "F" not in pattern:
+                    app.q_pos = att.q_pos = st["qpos"].data_ptr()
                 st["args"].append((app, att))
         self.tokens = sum(lens)
 
     def run(self, events=None):
         lib, cx = self.cx.lib, self.cx
         h = self.pool.handle
+        ps = self.side or cx.sptr  # stream of the pool calls
         for st in self.steps:
             ids, idp = st["ids"]
             n, np_ = st["n"]
-            _check(cx, lib.hswa_pool_alloc(h, st["nseq"], idp, np_, None, None, cx.sptr))
+            _check(cx, lib.hswa_pool_alloc(h, st["nseq"], idp, np_, None, None, ps))
             for app, att in st["args"]:
                 _check(cx, lib.hswa_append_kv(C.byref(app), cx.sptr))
                 if events is not None:
@@ -274,9 +288,9 @@ class ChunkedPrefill:
                 if events is not None:
                     e1.record(cx.stream)
                     events.append((att.kind, st, e0, e1))
-            _check(cx, lib.hswa_pool_evict(h, st["nseq"], idp, None, 0, None, cx.sptr))
+            _check(cx, lib.hswa_pool_evict(h, st["nseq"], idp, None, 0, None, ps))
         ids, idp = self.all_ids
-        _check(cx, lib.hswa_pool_release(h, self.B, idp, cx.sptr))
+        _check(cx, lib.hswa_pool_release(h, self.B, idp, ps))
 
     def attn_bytes(self, st, kind):
         """Algorithmic HBM bytes of one attention launch: Q read (bf16), O
@@ -756,7 +770,7 @@ def wl_swa_chunked_prefill(cx, args):
     wl = synth.C2
     lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
     cp = ChunkedPrefill(cx, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                        wl.window, wl.seed, out=args.out)
+                        wl.window, wl.seed, out=args.out, one_stream=args.single_stream)
     cx.torch.cuda.synchronize()
     log(f"prefill: {cp.tokens} tokens in {len(cp.steps)} chunk steps")
     sec = timed(cx, cp.run, args.steps, args.warmup)
@@ -772,6 +786,8 @@ def wl_swa_chunked_prefill(cx, args):
         "window": wl.window, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
         "head_dim": wl.head_dim, "page_size": 16, "ring_slots": wl.window + wl.chunk,
         "output_dtype": ODT[args.out], "seed": wl.seed,
+        "pool_calls": ("launch stream" if args.single_stream else
+                       "second stream, beside appends and attention (q_pos given)"),
     }
     rl = roofline("hbm", ks["gbs"], measured_traffic("prefill_swa", "kernels_prefill.hip")
                   if args.out == "f32" else None)
@@ -1216,6 +1232,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="chunked prefill: issue the pool calls on the launch stream, after "
+                         "the attention they follow, instead of on a second stream")
     ap.add_argument("--headline-only", action="store_true",
                     help="default workload: measure the chunked prefill and the mixed decode "
                          "only, not the single-chunk, 70-layer stack and long-context decode "

@@ -331,7 +331,7 @@ _BF16, _F16, _F32, _I32, _U8 = ("torch.bfloat16",), ("torch.float16",), ("torch.
 
 def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_seq_len,
           view, k_cache, v_cache, out, vlen, scale, k_scale=None,
-          v_scale=None) -> _capi.AttnArgs:
+          v_scale=None, q_pos=None) -> _capi.AttnArgs:
     fp8 = k_scale is not None
     _expect("k_cache", k_cache, _U8 if fp8 else _BF16, (None, None, PAGE_SIZE, None))
     hkv, d = k_cache.shape[1], k_cache.shape[3]
@@ -345,6 +345,7 @@ def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_
     _expect("v_new", v_new, _BF16, (None, hkv, d), total_q)
     _expect("seq_ids", seq_ids, _I32, (None,))
     _expect("cu_q", cu_q, _I32, (seq_ids.shape[0] + 1,))
+    _expect("q_pos", q_pos, _I32, (seq_ids.shape[0],))
     hq_ = q.shape[1] if q is not None else None
     _expect("out", out, _F32 + _F16, (None, hq_, d), total_q)
     _expect("vlen", vlen, _I32, (None,), total_q)
@@ -377,17 +378,18 @@ def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_
     a.out_dtype = 1 if out is not None and str(out.dtype) == "torch.float16" else 0
     a.k_scale = _dptr(k_scale)
     a.v_scale = _dptr(v_scale)
+    a.q_pos = _dptr(q_pos)
     return a
 
 
 def hswa_prefill_chunk(kind: int, window: int, q, k_new, v_new, seq_ids, cu_q,
                        max_q_len: int, view, k_cache, v_cache, out, vlen=None,
-                       scale: float = 0.0, stream=None) -> None:
+                       scale: float = 0.0, stream=None, q_pos=None) -> None:
     """q [T, Hq, d] bf16; k_new/v_new [T, Hkv, d] bf16 or None; seq_ids [B] and
     cu_q [B+1] int32 device tensors; out [T, Hq, d] fp32 or fp16; vlen [T]
-    int32."""
+    int32; q_pos [B] int32 (optional): each sequence's first row position."""
     a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0], max_q_len, 0, view,
-              k_cache, v_cache, out, vlen, scale)
+              k_cache, v_cache, out, vlen, scale, q_pos=q_pos)
     _check(library().hswa_prefill_chunk(C.byref(a), _stream(stream)))
 
 
@@ -407,14 +409,14 @@ def hswa_decode_workspace_bytes(kind: int, window: int, num_seqs: int, num_q_hea
 def hswa_decode(kind: int, window: int, q, k_new, v_new, seq_ids, max_seq_len: int, view,
                 k_cache, v_cache, out, workspace=None, vlen=None, scale: float = 0.0,
                 stream=None, cu_q=None, max_q_len: int = 1, k_scale=None,
-                v_scale=None) -> None:
+                v_scale=None, q_pos=None) -> None:
     """Decode step.  Without ``cu_q``: one query row per sequence (q [B, Hq, d])
     at position seq_len - 1.  With ``cu_q`` (device int32 [B+1]): 1..4 rows per
     sequence, its last positions (q [T, Hq, d]); ``max_q_len`` bounds them.
     With ``k_scale``/``v_scale`` the pages are FP8 (kv_cache_alloc_fp8)."""
     a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0],
               max_q_len if cu_q is not None else 1, max_seq_len, view, k_cache, v_cache, out,
-              vlen, scale, k_scale, v_scale)
+              vlen, scale, k_scale, v_scale, q_pos)
     ws = _dptr(workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().hswa_decode(C.byref(a), ws, nbytes, _stream(stream)))
@@ -423,22 +425,23 @@ def hswa_decode(kind: int, window: int, q, k_new, v_new, seq_ids, max_seq_len: i
 def hswa_decode_noalloc(kind: int, window: int, q, k_new, v_new, seq_ids, max_seq_len: int,
                         view, k_cache, v_cache, out, vlen=None, scale: float = 0.0,
                         stream=None, cu_q=None, max_q_len: int = 1, k_scale=None,
-                        v_scale=None) -> None:
+                        v_scale=None, q_pos=None) -> None:
     """hswa_decode without a workspace: the split-K state goes to the
     library's device scratch (no allocation).  Calls on one GPU share it, so
     keep them on one stream."""
     a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0],
               max_q_len if cu_q is not None else 1, max_seq_len, view, k_cache, v_cache, out,
-              vlen, scale, k_scale, v_scale)
+              vlen, scale, k_scale, v_scale, q_pos)
     _check(library().hswa_decode_noalloc(C.byref(a), _stream(stream)))
 
 
 def hswa_append_kv(kind: int, k_new, v_new, seq_ids, view, k_cache, v_cache, cu_q=None,
-                   max_q_len: int = 1, stream=None, k_scale=None, v_scale=None) -> None:
+                   max_q_len: int = 1, stream=None, k_scale=None, v_scale=None,
+                   q_pos=None) -> None:
     """Writes k_new/v_new rows into this layer's pages (no attention); with
     ``k_scale``/``v_scale`` the pages are FP8 and the rows are quantized."""
     a = _args(kind, 1, None, k_new, v_new, seq_ids, cu_q, k_new.shape[0], max_q_len, 1, view,
-              k_cache, v_cache, None, None, 0.0, k_scale, v_scale)
+              k_cache, v_cache, None, None, 0.0, k_scale, v_scale, q_pos)
     a.num_q_heads = k_new.shape[1]
     _check(library().hswa_append_kv(C.byref(a), _stream(stream)))
 

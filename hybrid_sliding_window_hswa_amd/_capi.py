@@ -94,6 +94,7 @@ class AttnArgs(C.Structure):
         ("k_scale", C.c_void_p),
         ("v_scale", C.c_void_p),
         ("out_dtype", C.c_int32),
+        ("q_pos", C.c_void_p),
     ]
 
 

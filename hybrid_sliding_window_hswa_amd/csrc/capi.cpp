@@ -175,6 +175,7 @@ int validate(const hswa_attn_args* a, bool decode, bool need_attn, hswa::AttnPar
   p->num_seqs = a->num_seqs;
   p->seq_ids = a->seq_ids;
   p->cu_q = a->cu_q;
+  p->q_pos = a->q_pos;
   p->total_q = a->total_q;
   p->max_q_len = decode && !a->cu_q ? 1 : a->max_q_len;
   p->max_seq_len = a->max_seq_len;

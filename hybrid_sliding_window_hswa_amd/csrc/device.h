@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "index.h"
+#include "internal.h"
 
 namespace hswa {
 namespace dev {
@@ -121,6 +122,14 @@ __device__ __forceinline__ int32_t page_of_uniform(const int32_t* __restrict__ f
   const int32_t e = idx::table_entry(KIND, pos, ring);
   return KIND == 0 ? scalar_load_i32(fpt, sid * max_pages + e)
                    : scalar_load_i32(rpt, sid * (ring / kPage) + e);
+}
+
+// Length of sequence i of an attention or append call whose n rows are its
+// last positions: the caller's q_pos (first row's position) plus n when
+// given, else the pool's seq_len.  With q_pos the kernels read no pool table
+// that an alloc writes (for SWA layers; Full layers still read fpt).
+__device__ __forceinline__ int call_len(const AttnParams& p, int i, int sid, int n) {
+  return p.q_pos ? p.q_pos[i] + n : p.t.seq_len[sid];
 }
 
 }  // namespace dev

@@ -78,6 +78,7 @@ struct AttnParams {
   int32_t num_seqs;
   const int32_t* seq_ids;
   const int32_t* cu_q;   // nullptr: one row per sequence (decode)
+  const int32_t* q_pos;  // nullptr: rows end at seq_len; else first row's position
   int32_t total_q;
   int32_t max_q_len;
   int32_t max_seq_len;

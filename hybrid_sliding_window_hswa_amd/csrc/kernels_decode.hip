@@ -155,9 +155,9 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   const int split = (blockIdx.x / p.hkv) % p.n_splits;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
-  const int L = p.t.seq_len[sid];
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;  // rows: positions L-n .. L-1
+  const int L = call_len(p, i, sid, n);
   if (n <= 0 || n > L || row0 < 0 || row0 + n > p.total_q) return;
   const int nr = min(n, QN);                         // rows computed here
   int klo, khi;  // keys [klo, khi) of this workgroup
@@ -441,9 +441,9 @@ decode_fp8_kernel(AttnParams p) {
   const int split = (blockIdx.x / p.hkv) % p.n_splits;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
-  const int L = p.t.seq_len[sid];
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
+  const int L = call_len(p, i, sid, n);
   if (n <= 0 || n > L || row0 < 0 || row0 + n > p.total_q) return;
   const int nr = min(n, QN);
   int klo, khi;
@@ -616,9 +616,9 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, int qn)
   const int d = threadIdx.x;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
-  const int L = p.t.seq_len[sid];
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
+  const int L = call_len(p, i, sid, n);
   if (n <= 0 || n > L || r >= n || row0 < 0 || row0 + n > p.total_q) return;
   const int len = idx::split_keys(L, p.n_splits, p.split_len);
   const int ns = (L + len - 1) / len;  // the splits that hold keys

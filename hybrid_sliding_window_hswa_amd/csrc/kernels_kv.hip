@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(256) append_kernel(AttnParams p, int tiles_per
   if (sid < 0 || sid >= p.t.max_seqs) return;  // invalid id: nothing to write
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
-  const int L = p.t.seq_len[sid];
+  const int L = call_len(p, i, sid, n);
   const int p0 = L - n;
   const int tile_pos = idx::tile_pos(p0, t);
   if (n <= 0 || n > L || tile_pos >= L || row0 < 0 || row0 + n > p.total_q) return;
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(AttnParams p, int tiles
   if (sid < 0 || sid >= p.t.max_seqs) return;
   const int row0 = p.cu_q ? p.cu_q[i] : i;
   const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
-  const int L = p.t.seq_len[sid];
+  const int L = call_len(p, i, sid, n);
   const int p0 = L - n;
   const int tile_pos = idx::tile_pos(p0, t);
   if (n <= 0 || n > L || tile_pos >= L || row0 < 0 || row0 + n > p.total_q) return;

@@ -114,7 +114,7 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   if (qb * QB >= n) return;  // whole workgroup idle: no barrier reached
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
-  const int L = p.t.seq_len[sid];
+  const int L = call_len(p, i, sid, n);
   if (n > L) return;         // rows without allocated positions
   if (row0 < 0 || row0 + n > p.total_q) return;  // rows outside q / out
   const int W = p.window;

@@ -327,6 +327,17 @@ typedef struct hswa_attn_args {
                                one scale per token of each (page, head)      */
   void* v_scale;            /* HSWA_KV_FP8: the same for V; else NULL        */
   int32_t out_dtype;        /* hswa_out_dtype of out                         */
+  const int32_t* q_pos;     /* device [num_seqs] or NULL: position of each
+                               sequence's first query row.  NULL: the rows
+                               are the last positions, [seq_len - n, seq_len)
+                               read from the pool's seq_len table.  Given:
+                               [q_pos[i], q_pos[i] + n) (they must have
+                               slots), and SWA attention and appends then
+                               read no table that an alloc, evict or import
+                               writes (only the fixed ring table), so those
+                               pool calls may run on another stream beside
+                               them.  Full layers still read fpt, so their
+                               alloc must precede them.                      */
 } hswa_attn_args;
 
 /* Chunked prefill of one layer ([MiMo] 1.1 chunked prefill; 2.1 prefix

@@ -53,6 +53,37 @@ constexpr int32_t split_keys(int32_t L, int32_t n_splits, int32_t split_len) {
   return ((L + ns - 1) / ns + 63) / 64 * 64;
 }
 
+// Decode: the first position of the page that a workgroup reads as page x
+// (0-based, 16 keys each) of the step starting at kp0, over its key range
+// [klo, khi).  A page holding a key of the range is itself; a page with none
+// (before klo in the first step, at or past khi in the last) is replaced by
+// the step's first page that holds one, so the lanes that would read it load
+// lines the step reads anyway and a call reads no page outside its range.
+constexpr int32_t decode_page_pos(int32_t kp0, int32_t x, int32_t klo, int32_t khi) {
+  const int32_t first = kp0 + kPage * x;
+  if (first + kPage > klo && first < khi) return first;
+  return (klo > kp0 ? klo : kp0) / kPage * kPage;
+}
+
+// FP8 decode grid: the scales of a page live in [Hkv][16] fp32 rows of 64
+// bytes, so KV heads 2j and 2j + 1 share a 128-byte line.  Workgroups go to
+// the 8 XCDs (each with its own L2) round-robin by block index, so blocks b
+// and b + 8 share an XCD.  With an even head count, pair p = (unit, heads
+// 2j and 2j + 1), unit = (sequence, split), takes blocks 16 (p / 8) + p % 8
+// and that + 8: both heads of a line on one XCD, each line fetched once.
+// Returns false for the padding blocks of the last 16-block group.
+constexpr bool fp8_block(int32_t b, int32_t hkv, int32_t units, int32_t* unit, int32_t* head) {
+  const int32_t group = b / 16, r = b % 16;
+  const int32_t pair = 8 * group + r % 8;
+  *unit = pair / (hkv / 2);
+  *head = 2 * (pair % (hkv / 2)) + r / 8;
+  return *unit < units;
+}
+// Blocks of that grid: units * hkv rounded up to whole 16-block groups.
+constexpr int32_t fp8_blocks(int32_t hkv, int32_t units) {
+  return (units * (hkv / 2) + 7) / 8 * 16;
+}
+
 // Append and transfer grids: page tiles per sequence for up to max_rows
 // positions (a range of max_rows positions starting anywhere in a page
 // touches at most this many pages), and the first position of tile t of a

@@ -58,6 +58,21 @@ namespace {
 
 constexpr int kDecWaves = 4;
 
+// K/V page loads, non-temporal or plain.  A Full layer's keys are read once
+// per call; on bf16 pages non-temporal loads measured 7% faster on 128K-256K
+// contexts, on FP8 pages 6% slower (same box, alternating runs), so only
+// bf16 Full layers use them.  A SWA window's first and last keys can share
+// one ring page (a ring of W slots), which two steps of a wave then read:
+// plain loads let the second read hit L2, where non-temporal ones went to
+// HBM again (10% more bytes per call).
+template <bool NT, typename T>
+__device__ __forceinline__ T ld_kv(const T* a) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(a);
+  else
+    return *a;
+}
+
 // One output element in the caller's output type (fp32, or fp16 rounded to
 // nearest).
 __device__ __forceinline__ void store_out(const AttnParams& p, int64_t idx, float x) {
@@ -129,6 +144,20 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, float (&red_o)[
   }
 }
 
+// Block -> ((sequence, split) unit, KV head).  KV heads run fastest, so
+// workgroups running at the same time read all heads' slices of the pages,
+// which spreads their traffic over all HBM channels.  FP8 pages with an even
+// head count pair heads 2j and 2j + 1 on one XCD, whose scale rows share a
+// 128-byte line (idx::fp8_block).  False for padding blocks.
+template <bool F8>
+__device__ __forceinline__ bool decode_block(const AttnParams& p, int* unit, int* kvh) {
+  if (F8 && (p.hkv & 1) == 0)
+    return idx::fp8_block(blockIdx.x, p.hkv, p.num_seqs * p.n_splits, unit, kvh);
+  *kvh = blockIdx.x % p.hkv;
+  *unit = blockIdx.x / p.hkv;
+  return true;
+}
+
 // Lazy rescaling of the bf16/fp16 decode (scores are in the log2 domain).
 constexpr float kDecLazy = 8.0f;
 
@@ -147,12 +176,10 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][CT][D];
   __shared__ float red_ml[kDecWaves][CT][2];
 
-  // KV head fastest in the grid: workgroups running at the same time then
-  // read all KV heads' slices of the pages, which spreads their traffic over
-  // all HBM channels (one head's 4 KB slices alone concentrate on a few).
-  const int kvh = blockIdx.x % p.hkv;
-  const int i = (blockIdx.x / p.hkv) / p.n_splits;
-  const int split = (blockIdx.x / p.hkv) % p.n_splits;
+  int unit, kvh;  // unit = (sequence, split)
+  if (!decode_block<F8>(p, &unit, &kvh)) return;
+  const int i = unit / p.n_splits;
+  const int split = unit % p.n_splits;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
   const int row0 = p.cu_q ? p.cu_q[i] : i;
@@ -235,9 +262,10 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     int64_t sc;  // FP8: index of the lane's first key scale
   };
   auto step_pages = [&](int kp0) {
-    int32_t pg0 = page_at(kp0);
-    // a page past the last key: read page 0 again (those keys are masked)
-    int32_t pg1 = kp0 + 16 < khi ? page_at(kp0 + 16) : pg0;
+    // a page with no key of [klo, khi) reads the step's other page (those
+    // keys are masked)
+    int32_t pg0 = page_at(idx::decode_page_pos(kp0, 0, klo, khi));
+    int32_t pg1 = page_at(idx::decode_page_pos(kp0, 1, klo, khi));
     // a missing page means the caller skipped alloc: read page 0 of the pool
     // instead of faulting (the result of such a call is undefined)
     pg0 = pg0 < 0 ? 0 : pg0;
@@ -248,14 +276,14 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   };
   auto load_k = [&](const Ptrs& pt, Raw (&kr)[2][NC]) {
     for (int c = 0; c < NC; ++c) {
-      kr[0][c] = __builtin_nontemporal_load((const Raw*)(pt.k + 32 * c * ESZ));
+      kr[0][c] = ld_kv<KIND == 0 && !F8>((const Raw*)(pt.k + 32 * c * ESZ));
       kr[1][c] =
-          __builtin_nontemporal_load((const Raw*)(pt.k + (4 * D + 32 * c) * ESZ));
+          ld_kv<KIND == 0 && !F8>((const Raw*)(pt.k + (4 * D + 32 * c) * ESZ));
     }
   };
   auto load_v = [&](const Ptrs& pt, Raw (&vr)[NB]) {
     for (int nb = 0; nb < NB; ++nb)
-      vr[nb] = __builtin_nontemporal_load((const Raw*)(pt.v + 16 * nb * kPage * ESZ));
+      vr[nb] = ld_kv<KIND == 0 && !F8>((const Raw*)(pt.v + 16 * nb * kPage * ESZ));
   };
   auto load_scales = [&](const Ptrs& pt, u32x4 (&sc)[4]) {
     if (F8) {
@@ -283,8 +311,6 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
     }
   };
 
-  // K/V bytes are read once, so their loads are non-temporal (a long-context
-  // Full call measured 2.3% faster; the mixed decode unchanged).
   // Software pipeline, register-neutral: the K loads (and FP8 scales) of
   // this wave's next step are issued as soon as the score MFMAs have
   // consumed the current K fragments, the V loads as soon as the PV MFMAs
@@ -436,9 +462,10 @@ decode_fp8_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][CT][D];
   __shared__ float red_ml[kDecWaves][CT][2];
 
-  const int kvh = blockIdx.x % p.hkv;
-  const int i = (blockIdx.x / p.hkv) / p.n_splits;
-  const int split = (blockIdx.x / p.hkv) % p.n_splits;
+  int unit, kvh;  // unit = (sequence, split)
+  if (!decode_block<true>(p, &unit, &kvh)) return;
+  const int i = unit / p.n_splits;
+  const int split = unit % p.n_splits;
   const int sid = p.seq_ids[i];
   if (sid < 0 || sid >= p.t.max_seqs) return;
   const int row0 = p.cu_q ? p.cu_q[i] : i;
@@ -500,9 +527,9 @@ decode_fp8_kernel(AttnParams p) {
   auto step_pages = [&](int kp0) {
     int32_t pg[4];
     for (int x = 0; x < 4; ++x) {
-      // a page past the last key: page 0 of the step again (masked keys);
-      // a missing page (skipped alloc): page 0 of the pool
-      const int32_t v = x == 0 || kp0 + 16 * x < khi ? page_at(kp0 + 16 * x) : pg[0];
+      // a page with no key of [klo, khi): a page of the step that has one
+      // (masked keys); a missing page (skipped alloc): page 0 of the pool
+      const int32_t v = page_at(idx::decode_page_pos(kp0, x, klo, khi));
       pg[x] = v < 0 ? 0 : v;
     }
     const int32_t pk = pg[col >> 2], pv = pg[q4];
@@ -514,11 +541,11 @@ decode_fp8_kernel(AttnParams p) {
   auto load_k = [&](const Ptrs& pt) {
     for (int kt = 0; kt < 4; ++kt)
       for (int x = 0; x < KV4; ++x)
-        kr[kt][x] = __builtin_nontemporal_load((const u32x4*)(pt.k + 4 * kt * D + 16 * x));
+        kr[kt][x] = ld_kv<false>((const u32x4*)(pt.k + 4 * kt * D + 16 * x));
   };
   auto load_v = [&](const Ptrs& pt) {
     for (int nb = 0; nb < NB; ++nb)
-      vr[nb] = __builtin_nontemporal_load((const u32x4*)(pt.v + 16 * nb * kPage));
+      vr[nb] = ld_kv<false>((const u32x4*)(pt.v + 16 * nb * kPage));
     for (int x = 0; x < 4; ++x) {
       sc[x] = *(const u32x4*)(p.k_scale + pt.sc + 4 * x);
       sc[4 + x] = *(const u32x4*)(p.v_scale + pt.sc + 4 * x);
@@ -649,7 +676,8 @@ void launch_decode_one(const AttnParams& p, dim3 grid, hipStream_t s) {
 
 template <int D, int KIND, int QN, bool F8>
 hipError_t launch_decode_q(const AttnParams& p, hipStream_t s) {
-  dim3 grid((unsigned)(p.num_seqs * p.n_splits * p.hkv), 1);
+  const int units = p.num_seqs * p.n_splits;
+  dim3 grid((unsigned)(F8 && p.hkv % 2 == 0 ? idx::fp8_blocks(p.hkv, units) : units * p.hkv), 1);
   switch (p.hq / p.hkv) {
     case 1: launch_decode_one<D, KIND, 1, QN, F8>(p, grid, s); break;
     case 2: launch_decode_one<D, KIND, 2, QN, F8>(p, grid, s); break;

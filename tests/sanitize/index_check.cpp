@@ -104,8 +104,15 @@ static void decode_walk(int kind, int32_t L, int32_t n, int32_t W, int32_t C, in
     for (int32_t st = 0; st < nsteps; ++st) {
       const int32_t kp0 = s0 + step_keys * st;
       for (int32_t x = 0; x < step_keys / kPage; ++x) {
-        if (x > 0 && kp0 + kPage * x >= khi) continue;  // the kernel reuses page 0 of the step
-        const int32_t e = table_entry(kind, kp0 + kPage * x, C);
+        const int32_t own = kp0 + kPage * x;
+        const int32_t pos = decode_page_pos(kp0, x, klo, khi);
+        // the page read holds a key of the range and lies in the step; a
+        // page that holds one is read itself
+        CHECK(pos % kPage == 0 && pos + kPage > klo && pos < khi && pos >= kp0 &&
+              pos < kp0 + step_keys && (pos == own || own + kPage <= klo || own >= khi),
+              "decode: step %d page %d reads position %d (klo %d khi %d)", kp0, x, pos, klo,
+              khi);
+        const int32_t e = table_entry(kind, pos, C);
         CHECK(e >= 0 && e < rl, "decode: entry %d outside row of %d (kind %d L %d n %d W %d C %d "
               "splits %d/%d split %d step %d)", e, rl, kind, L, n, W, C, n_splits, split_len,
               split, st);
@@ -201,6 +208,29 @@ int main() {
         decode_walk(kFull, L, 1, 0, 16, ns, sl, 32);
         decode_walk(kFull, L, 1, 0, 16, ns, sl, 64);
       }
+  // FP8 decode grid: a bijection onto (unit, head), heads 2j and 2j + 1 of a
+  // unit on blocks of the same XCD (block index mod 8)
+  for (int32_t hkv = 2; hkv <= 16; hkv += 2)
+    for (int32_t units = 1; units <= 300; units += (units < 40 ? 1 : 37)) {
+      const int32_t nb = fp8_blocks(hkv, units);
+      CHECK(nb % 16 == 0 && nb >= units * hkv && nb < units * hkv + 16,
+            "fp8 grid: %d blocks for %d x %d", nb, units, hkv);
+      std::vector<int32_t> block_of(units * hkv, -1);
+      for (int32_t b = 0; b < nb; ++b) {
+        int32_t u = -1, h = -1;
+        if (!fp8_block(b, hkv, units, &u, &h)) continue;
+        CHECK(u >= 0 && u < units && h >= 0 && h < hkv, "fp8 block %d -> (%d, %d)", b, u, h);
+        CHECK(block_of[u * hkv + h] < 0, "fp8 blocks %d and %d -> (%d, %d)",
+              block_of[u * hkv + h], b, u, h);
+        block_of[u * hkv + h] = b;
+      }
+      for (int32_t u = 0; u < units; ++u)
+        for (int32_t h = 0; h < hkv; h += 2) {
+          const int32_t b0 = block_of[u * hkv + h], b1 = block_of[u * hkv + h + 1];
+          CHECK(b0 >= 0 && b1 >= 0 && b0 % 8 == b1 % 8, "fp8 heads %d, %d of unit %d on "
+                "blocks %d, %d", h, h + 1, u, b0, b1);
+        }
+    }
   printf("index checks passed: %ld\n", g_checks);
   return 0;
 }

@@ -92,7 +92,7 @@ def KV_TOKEN_BYTES(hkv, d):
 
 
 # headers every kernel source includes: a change to them changes the kernels
-KERNEL_HEADERS = ("device.h", "internal.h")
+KERNEL_HEADERS = ("device.h", "internal.h", "index.h")
 
 
 def source_sha(fname):
@@ -115,6 +115,20 @@ def measured_traffic(key, fname):
     if t.get("source_sha256") != source_sha(fname):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def measured_mfma_ops(key, fname):
+    """MFMA ops (units of 512 flops, bf16 plus fp16) per launch from the
+    committed counter summary, if it was taken on the current source of the
+    kernel; else None."""
+    try:
+        with open(TRAFFIC) as f:
+            t = json.load(f)["mfma_ops"][key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha(fname):
+        return None
+    return t.get("mops_per_launch")
 
 
 def log(*a):
@@ -795,6 +809,10 @@ def wl_swa_chunked_prefill(cx, args):
     line["kernel"] = {"name": "prefill_kernel<128,SWA>", "avg_us": round(ks["avg_us"], 2),
                       "launches_timed": ks["launches"], "tflops": round(ks["tflops"], 2),
                       "mfma_frac": round(ks["tflops"] / MFMA_BF16_PEAK_TFS, 4)}
+    # the kernel writes more than it reads (fp32 O): a copy, half writes, is
+    # the practical ceiling next to which its GB/s is read
+    cc = copy_ceiling(cx)
+    line["copy_ceiling"] = {"gbs": cc, "kernel_frac": round(ks["gbs"] / cc, 4)}
     line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(cx, cp, args.cpu_seconds)
@@ -904,7 +922,8 @@ def wl_mtp_decode(cx, args):
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
               "seed": wl.seed}
-    rl = roofline("hbm", r["full_gbs"], None)
+    rl = roofline("hbm", r["full_gbs"],
+                  measured_traffic("decode_full_mtp", "kernels_decode.hip"))
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
     line["accepted_tok_per_s"] = round(r["tok_per_s"], 1)
@@ -1079,6 +1098,14 @@ def wl_hybrid_stack(cx, args):
                         "full_kernel_tflops": round(af["full"]["tflops"], 1)}
     line["time_ratio_hybrid_over_all_full"] = round(hy["sec"] / af["sec"], 5)
     line["flop_ratio_hybrid_over_all_full"] = round(hy["flops"] / af["flops"], 6)
+    # the same ratio from the MFMA op counters (rocprofv3), which include the
+    # masked parts of the tiles the kernels compute
+    mf = measured_mfma_ops("prefill_full", "kernels_prefill.hip")
+    ms = measured_mfma_ops("prefill_swa_stack", "kernels_prefill.hip")
+    nf = wl.pattern.count("F")
+    line["mfma_op_ratio_hybrid_over_all_full"] = (
+        round((nf * mf + (len(wl.pattern) - nf) * ms) / (len(wl.pattern) * mf), 6)
+        if mf and ms else None)
     line["cpu_baseline"] = res.get("cpu")
     return line
 
@@ -1099,7 +1126,8 @@ def wl_long_decode(cx, args):
               "pattern": "6 SWA then 1 Full, x2", "ring_slots": wl.ring_slots,
               "window": wl.window, "num_q_heads": wl.num_q_heads,
               "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "seed": wl.seed}
-    rl = roofline("hbm", r["full_gbs"], None)
+    rl = roofline("hbm", r["full_gbs"],
+                  measured_traffic("decode_full_long", "kernels_decode.hip"))
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
     line["steps"] = steps
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
@@ -1134,7 +1162,8 @@ def wl_swa_single_chunk(cx, args):
               "window": wl.window, "num_q_heads": wl.num_q_heads,
               "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "seed": wl.seed}
     line = base_line(args, round(L / sec, 1), "tok/s", sec * 1e3, config,
-                     roofline("hbm", ks["gbs"], None))
+                     roofline("hbm", ks["gbs"],
+                              measured_traffic("prefill_swa_d64", "kernels_prefill.hip")))
     line["kernel"] = {"name": "prefill_kernel<64,SWA>", "avg_us": round(ks["avg_us"], 2)}
     dc = Decode(cx, [L], "S", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
                 wl.window + 16, wl.seed, wl.decode_steps + 8)

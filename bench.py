@@ -206,10 +206,11 @@ class ChunkedPrefill:
     layers see the same synthetic Q/K/V (an attention-only stack)."""
 
     def __init__(self, cx, lens, chunk, hq, hkv, d, W, seed, pattern="S", ring=None,
-                 out="f32", one_stream=False):
+                 out="f32", one_stream=False, combine_pool_ops=True):
         torch, H = cx.torch, cx.H
         import synth
         self.cx = cx
+        self.combine_pool_ops = combine_pool_ops
         self.obytes = 2 if out == "f16" else 4
         self.lens, self.chunk, self.hq, self.hkv, self.d, self.W = lens, chunk, hq, hkv, d, W
         B = len(lens)
@@ -288,10 +289,20 @@ class ChunkedPrefill:
         lib, cx = self.cx.lib, self.cx
         h = self.pool.handle
         ps = self.side or cx.sptr  # stream of the pool calls
+        prev = None  # the previous chunk step's sequences, evicted at this step's start
         for st in self.steps:
             ids, idp = st["ids"]
             n, np_ = st["n"]
-            _check(cx, lib.hswa_pool_alloc(h, st["nseq"], idp, np_, None, None, ps))
+            if prev is None:
+                _check(cx, lib.hswa_pool_alloc(h, st["nseq"], idp, np_, None, None, ps))
+            elif self.combine_pool_ops:
+                # the previous step's eviction and this step's alloc: one
+                # table-update launch
+                _check(cx, lib.hswa_pool_evict_alloc(h, prev[0], prev[1], None, 0, None,
+                                                     st["nseq"], idp, np_, None, None, ps))
+            else:
+                _check(cx, lib.hswa_pool_evict(h, prev[0], prev[1], None, 0, None, ps))
+                _check(cx, lib.hswa_pool_alloc(h, st["nseq"], idp, np_, None, None, ps))
             for app, att in st["args"]:
                 _check(cx, lib.hswa_append_kv(C.byref(app), cx.sptr))
                 if events is not None:
@@ -302,7 +313,9 @@ class ChunkedPrefill:
                 if events is not None:
                     e1.record(cx.stream)
                     events.append((att.kind, st, e0, e1))
-            _check(cx, lib.hswa_pool_evict(h, st["nseq"], idp, None, 0, None, ps))
+            prev = (st["nseq"], idp)
+        if prev is not None:
+            _check(cx, lib.hswa_pool_evict(h, prev[0], prev[1], None, 0, None, ps))
         ids, idp = self.all_ids
         _check(cx, lib.hswa_pool_release(h, self.B, idp, ps))
 
@@ -784,7 +797,8 @@ def wl_swa_chunked_prefill(cx, args):
     wl = synth.C2
     lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
     cp = ChunkedPrefill(cx, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                        wl.window, wl.seed, out=args.out, one_stream=args.single_stream)
+                        wl.window, wl.seed, out=args.out, one_stream=args.single_stream,
+                        combine_pool_ops=not args.separate_pool_ops)
     cx.torch.cuda.synchronize()
     log(f"prefill: {cp.tokens} tokens in {len(cp.steps)} chunk steps")
     sec = timed(cx, cp.run, args.steps, args.warmup)
@@ -801,7 +815,9 @@ def wl_swa_chunked_prefill(cx, args):
         "head_dim": wl.head_dim, "page_size": 16, "ring_slots": wl.window + wl.chunk,
         "output_dtype": ODT[args.out], "seed": wl.seed,
         "pool_calls": ("launch stream" if args.single_stream else
-                       "second stream, beside appends and attention (q_pos given)"),
+                       "second stream, beside appends and attention (q_pos given)") +
+                      ("; evict and alloc separate" if args.separate_pool_ops else
+                       "; each step's evict joined to the next step's alloc"),
     }
     rl = roofline("hbm", ks["gbs"], measured_traffic("prefill_swa", "kernels_prefill.hip")
                   if args.out == "f32" else None)
@@ -1264,6 +1280,9 @@ def main():
     ap.add_argument("--single-stream", action="store_true",
                     help="chunked prefill: issue the pool calls on the launch stream, after "
                          "the attention they follow, instead of on a second stream")
+    ap.add_argument("--separate-pool-ops", action="store_true",
+                    help="chunked prefill: evict each step and alloc the next as two pool "
+                         "calls instead of one hswa_pool_evict_alloc")
     ap.add_argument("--headline-only", action="store_true",
                     help="default workload: measure the chunked prefill and the mixed decode "
                          "only, not the single-chunk, 70-layer stack and long-context decode "

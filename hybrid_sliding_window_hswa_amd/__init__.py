@@ -32,7 +32,7 @@ SWA = HSWA_LAYER_SWA
 __all__ = [
     "HswaError", "NoSpace", "FULL", "SWA", "PAGE_SIZE",
     "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view", "hswa_pool_alloc",
-    "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release", "hswa_pool_truncate",
+    "hswa_pool_evict", "hswa_pool_evict_alloc", "hswa_pool_import", "hswa_pool_release", "hswa_pool_truncate",
     "hswa_pool_match_len", "hswa_pool_read_tables", "hswa_pool_fork", "hswa_kv_copy",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
     "hswa_decode_noalloc", "DECODE_SCRATCH_BYTES",
@@ -205,6 +205,30 @@ def hswa_pool_evict(pool: Pool, seq_ids: Sequence[int], want_slots: bool = True,
     if ev is not None:
         ev = ev[:int(cnt.sum())]
     return ev, cnt
+
+
+def hswa_pool_evict_alloc(pool: Pool, ev_ids: Sequence[int], al_ids: Sequence[int],
+                          n_new: Sequence[int], want_slots: bool = True,
+                          capacity: Optional[int] = None, stream=None):
+    """hswa_pool_evict(ev_ids) then hswa_pool_alloc(al_ids, n_new) as one
+    operation (one device-table update).  Returns (evicted_full_slots,
+    counts, full_slots, swa_slots); the slot arrays are None if not wanted."""
+    ev_i, al_i, n = _i32(ev_ids), _i32(al_ids), _i32(n_new)
+    if n.size != al_i.size:
+        raise ValueError("one n_new per allocated sequence")
+    cap = capacity if capacity is not None else ev_i.size * pool.desc["ring_slots"]
+    ev = np.empty(max(cap, 1), np.int32) if want_slots else None
+    cnt = np.empty(max(ev_i.size, 1), np.int32)
+    tot = int(np.clip(n, 0, None).sum()) if n.size else 0
+    full = np.empty(tot, np.int32) if want_slots else None
+    swa = np.empty(tot, np.int32) if want_slots else None
+    _check(library().hswa_pool_evict_alloc(pool.handle, ev_i.size, _p(ev_i), _p(ev), cap,
+                                           _p(cnt), al_i.size, _p(al_i), _p(n), _p(full),
+                                           _p(swa), _stream(stream)))
+    cnt = cnt[:ev_i.size]
+    if ev is not None:
+        ev = ev[:int(cnt.sum())]
+    return ev, cnt, full, swa
 
 
 def hswa_pool_release(pool: Pool, seq_ids: Sequence[int], stream=None) -> None:

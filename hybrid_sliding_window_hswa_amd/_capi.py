@@ -30,7 +30,8 @@ I32P = C.POINTER(C.c_int32)
 EXPORTED = (
     "hswa_last_error", "hswa_status_string", "hswa_version",
     "hswa_pool_create", "hswa_pool_destroy", "hswa_pool_get_view",
-    "hswa_pool_alloc", "hswa_pool_evict", "hswa_pool_import", "hswa_pool_release",
+    "hswa_pool_alloc", "hswa_pool_evict", "hswa_pool_evict_alloc", "hswa_pool_import",
+    "hswa_pool_release",
     "hswa_pool_truncate", "hswa_pool_match_len", "hswa_pool_read_tables", "hswa_pool_fork",
     "hswa_prefill_chunk", "hswa_decode", "hswa_decode_workspace_bytes", "hswa_append_kv",
     "hswa_decode_noalloc",
@@ -166,6 +167,9 @@ def load():
     lib.hswa_pool_evict.restype = C.c_int
     lib.hswa_pool_evict.argtypes = [C.c_void_p, C.c_int32, I32P, I32P, C.c_int64, I32P,
                                     C.c_void_p]
+    lib.hswa_pool_evict_alloc.restype = C.c_int
+    lib.hswa_pool_evict_alloc.argtypes = [C.c_void_p, C.c_int32, I32P, I32P, C.c_int64, I32P,
+                                          C.c_int32, I32P, I32P, I32P, I32P, C.c_void_p]
     lib.hswa_pool_release.restype = C.c_int
     lib.hswa_pool_release.argtypes = [C.c_void_p, C.c_int32, I32P, C.c_void_p]
     lib.hswa_pool_match_len.restype = C.c_int

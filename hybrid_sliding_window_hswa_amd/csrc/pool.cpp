@@ -305,15 +305,72 @@ int flush(hswa_pool* p, const RecBuilder& rb, void* stream) {
   return HSWA_OK;
 }
 
-// Shared body of alloc (ring checked) and import (ring not checked; only
-// in-window positions get SWA slots).
-int alloc_impl(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new,
-               int32_t* full_out, int32_t* swa_out, void* stream, bool importing) {
-  hswa::clear_error();
-  if (!p) {
-    hswa::set_error("pool is NULL");
+// The device effect of an eviction or an alloc on one sequence: the new
+// length (-1: unchanged), map entries cleared [clr_lo, clr_hi) and set
+// [set_lo, set_hi) by position, and fpt entries [fpt_lo, fpt_hi) written
+// from the sequence's row.  An eviction and an alloc of one sequence touch
+// disjoint positions and pages, so their effects merge into one record.
+struct Eff {
+  int32_t b, new_len, clr_lo, clr_hi, set_lo, set_hi, fpt_lo, fpt_hi;
+};
+
+// Records of the effects (built after the host change, which keeps every
+// page id the records list), then one flush.
+int flush_effs(hswa_pool* p, const std::vector<Eff>& effs, void* stream) {
+  if (!p->has_dev) return HSWA_OK;
+  RecBuilder rb;
+  for (const Eff& e : effs)
+    rb.add(p, e.b, e.new_len, e.clr_lo, e.clr_hi, e.set_lo, e.set_hi, e.fpt_lo, e.fpt_hi, 0,
+           &p->fpt[(size_t)e.b * p->max_pages]);
+  return flush(p, rb, stream);
+}
+
+// Checks of an eviction: ids and the capacity of evicted_out.
+int evict_check(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* evicted_out,
+                int64_t evicted_cap) {
+  int rc = check_ids(p, n, ids);
+  if (rc) return rc;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = ids[i];
+    int32_t keep_from = std::max(0, p->len[b] - p->W + 1);
+    total += std::max(0, keep_from - p->res_start[b]);
+  }
+  if (evicted_out && total > evicted_cap) {
+    hswa::set_error("evicted_out holds %lld entries, %lld needed", (long long)evicted_cap,
+                    (long long)total);
     return HSWA_E_INVAL;
   }
+  return HSWA_OK;
+}
+
+// The eviction's host change; its device effect goes to effs.
+void evict_host(hswa_pool* p, int32_t n, const int32_t* ids, int32_t* evicted_out,
+                int32_t* counts_out, std::vector<Eff>& effs) {
+  int64_t o = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = ids[i];
+    int32_t keep_from = std::max(0, p->len[b] - p->W + 1);
+    int32_t lo = p->res_start[b];
+    int32_t cnt = std::max(0, keep_from - lo);
+    for (int32_t pos = lo; pos < lo + cnt; ++pos) {
+      int32_t fs = p->full_slot(b, pos);
+      p->map[fs] = -1;
+      if (evicted_out) evicted_out[o] = fs;
+      ++o;
+    }
+    if (counts_out) counts_out[i] = cnt;
+    p->res_start[b] = std::max(lo, keep_from);
+    // the device effect is map entries only (length and fpt unwritten)
+    if (cnt > 0) effs.push_back(Eff{b, -1, lo, lo + cnt, 0, 0, 0, 0});
+  }
+}
+
+// Checks of an alloc (ring checked) or import (ring not checked).  res_at,
+// if given, is each sequence's first resident position at the time of the
+// alloc (an eviction in the same operation comes first).
+int alloc_check(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new,
+                bool importing, const std::vector<int32_t>* res_at) {
   int rc = check_ids(p, n, ids);
   if (rc) return rc;
   if (n > 0 && !n_new) {
@@ -343,9 +400,10 @@ int alloc_impl(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new
       return HSWA_E_NOSPC;
     }
     need_pages += pages - p->npages[b];
-    if (!importing && (int64_t)(p->len[b] - p->res_start[b]) + k > p->C) {
+    const int32_t res = res_at ? (*res_at)[b] : p->res_start[b];
+    if (!importing && (int64_t)(p->len[b] - res) + k > p->C) {
       hswa::set_error("SWA ring of sequence %d: %d resident + %lld new > %d slots", b,
-                      p->len[b] - p->res_start[b], (long long)k, p->C);
+                      p->len[b] - res, (long long)k, p->C);
       return HSWA_E_NOSPC;
     }
   }
@@ -354,7 +412,12 @@ int alloc_impl(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new
                     (long long)p->fcount);
     return HSWA_E_NOSPC;
   }
-  RecBuilder rb;
+  return HSWA_OK;
+}
+
+// The alloc's (or import's) host change; its device effect goes to effs.
+void alloc_host(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new,
+                int32_t* full_out, int32_t* swa_out, bool importing, std::vector<Eff>& effs) {
   size_t o = 0;
   for (int32_t i = 0; i < n; ++i) {
     int32_t b = ids[i];
@@ -384,11 +447,25 @@ int alloc_impl(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new
     }
     p->npages[b] = (int32_t)ceil_div(new_len, kPage);
     p->len[b] = new_len;
-    if (p->has_dev)
-      rb.add(p, b, new_len, clr_lo, clr_hi, std::max(L, keep_from), new_len, old_pages,
-             p->npages[b], 0, row);
+    effs.push_back(
+        Eff{b, new_len, clr_lo, clr_hi, std::max(L, keep_from), new_len, old_pages, p->npages[b]});
   }
-  return flush(p, rb, stream);
+}
+
+// Shared body of alloc (ring checked) and import (ring not checked; only
+// in-window positions get SWA slots).
+int alloc_impl(hswa_pool* p, int32_t n, const int32_t* ids, const int32_t* n_new,
+               int32_t* full_out, int32_t* swa_out, void* stream, bool importing) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
+    return HSWA_E_INVAL;
+  }
+  int rc = alloc_check(p, n, ids, n_new, importing, nullptr);
+  if (rc) return rc;
+  std::vector<Eff> effs;
+  alloc_host(p, n, ids, n_new, full_out, swa_out, importing, effs);
+  return flush_effs(p, effs, stream);
 }
 
 }  // namespace
@@ -561,39 +638,56 @@ int hswa_pool_evict(hswa_pool* p, int32_t n, const int32_t* ids, int32_t* evicte
     hswa::set_error("pool is NULL");
     return HSWA_E_INVAL;
   }
-  int rc = check_ids(p, n, ids);
+  int rc = evict_check(p, n, ids, evicted_out, evicted_cap);
   if (rc) return rc;
-  int64_t total = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    int32_t b = ids[i];
-    int32_t keep_from = std::max(0, p->len[b] - p->W + 1);
-    total += std::max(0, keep_from - p->res_start[b]);
-  }
-  if (evicted_out && total > evicted_cap) {
-    hswa::set_error("evicted_out holds %lld entries, %lld needed", (long long)evicted_cap,
-                    (long long)total);
+  std::vector<Eff> effs;
+  evict_host(p, n, ids, evicted_out, counts_out, effs);
+  return flush_effs(p, effs, stream);
+}
+
+int hswa_pool_evict_alloc(hswa_pool* p, int32_t n_ev, const int32_t* ev_ids,
+                          int32_t* evicted_out, int64_t evicted_cap, int32_t* counts_out,
+                          int32_t n_al, const int32_t* al_ids, const int32_t* n_new,
+                          int32_t* full_out, int32_t* swa_out, void* stream) {
+  hswa::clear_error();
+  if (!p) {
+    hswa::set_error("pool is NULL");
     return HSWA_E_INVAL;
   }
-  RecBuilder rb;
-  int64_t o = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    int32_t b = ids[i];
-    int32_t keep_from = std::max(0, p->len[b] - p->W + 1);
-    int32_t lo = p->res_start[b];
-    int32_t cnt = std::max(0, keep_from - lo);
-    for (int32_t pos = lo; pos < lo + cnt; ++pos) {
-      int32_t fs = p->full_slot(b, pos);
-      p->map[fs] = -1;
-      if (evicted_out) evicted_out[o] = fs;
-      ++o;
-    }
-    if (counts_out) counts_out[i] = cnt;
-    p->res_start[b] = std::max(lo, keep_from);
-    // the device effect is map entries only (length and fpt unwritten)
-    if (p->has_dev && cnt > 0)
-      rb.add(p, b, -1, lo, lo + cnt, 0, 0, 0, 0, 0, &p->fpt[(size_t)b * p->max_pages]);
+  // every check of both before any change; the alloc sees the rings as the
+  // eviction leaves them
+  int rc = evict_check(p, n_ev, ev_ids, evicted_out, evicted_cap);
+  if (rc) return rc;
+  std::vector<int32_t> res_at(p->res_start);
+  for (int32_t i = 0; i < n_ev; ++i) {
+    const int32_t b = ev_ids[i];
+    res_at[b] = std::max(res_at[b], std::max(0, p->len[b] - p->W + 1));
   }
-  return flush(p, rb, stream);
+  rc = alloc_check(p, n_al, al_ids, n_new, false, &res_at);
+  if (rc) return rc;
+  std::vector<Eff> effs;
+  evict_host(p, n_ev, ev_ids, evicted_out, counts_out, effs);
+  const size_t n_evict_effs = effs.size();
+  alloc_host(p, n_al, al_ids, n_new, full_out, swa_out, false, effs);
+  // one record per sequence: a sequence's eviction joins its alloc
+  std::vector<int32_t> ev_of(p->max_seqs, -1);
+  for (size_t x = 0; x < n_evict_effs; ++x) ev_of[effs[x].b] = (int32_t)x;
+  std::vector<bool> merged(n_evict_effs, false);
+  std::vector<Eff> out;
+  out.reserve(effs.size());
+  for (size_t x = n_evict_effs; x < effs.size(); ++x) {
+    Eff e = effs[x];
+    const int32_t v = ev_of[e.b];
+    if (v >= 0) {  // an alloc clears nothing, so the eviction's range fits
+      e.clr_lo = effs[v].clr_lo;
+      e.clr_hi = effs[v].clr_hi;
+      merged[v] = true;
+    }
+    out.push_back(e);
+  }
+  for (size_t x = 0; x < n_evict_effs; ++x)
+    if (!merged[x]) out.push_back(effs[x]);
+  return flush_effs(p, out, stream);
 }
 
 int hswa_pool_release(hswa_pool* p, int32_t n, const int32_t* ids, void* stream) {

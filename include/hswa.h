@@ -204,6 +204,20 @@ int hswa_pool_evict(hswa_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
                     int32_t* evicted_out, int64_t evicted_cap,
                     int32_t* counts_out, void* stream);
 
+/* One chunk step's end and the next one's start ([MiMo] 2.1 prefix tree,
+ * point 2, and Dual Pool; Scheduling Constraints): hswa_pool_evict of
+ * ev_ids followed by hswa_pool_alloc of al_ids, with the same arguments and
+ * outputs as those two calls, as one operation.  Every check of both runs
+ * first, the alloc's ring check counting the eviction, and nothing changes
+ * if one fails.  A sequence may be listed in both (each list without
+ * repeats).  The device tables receive both effects in one table-update
+ * launch on `stream` instead of two; the eviction's second-stream rule does
+ * not apply, since the alloc's effects ride along. */
+int hswa_pool_evict_alloc(hswa_pool* pool, int32_t n_ev, const int32_t* ev_ids,
+                          int32_t* evicted_out, int64_t evicted_cap, int32_t* counts_out,
+                          int32_t n_al, const int32_t* al_ids, const int32_t* n_new,
+                          int32_t* full_slots_out, int32_t* swa_slots_out, void* stream);
+
 /* Appends n_new[i] positions whose K/V the caller stores directly, e.g. a
  * context restored from another cache tier where only the in-window SWA KV
  * moves ([MiMo] 2.1 Dual Pool, "Data Transfer").  Every new position gets a

@@ -1,6 +1,7 @@
 """C ABI checks that need no GPU: the library loads and exports every
 declared symbol; the host pool bookkeeping is bit-exact against the oracle
 simulator; argument validation rejects bad calls before any launch."""
+import copy
 import ctypes as C
 import json
 import os
@@ -106,7 +107,26 @@ def test_random_operations_bit_exact_vs_oracle(seed):
     for _ in range(150):
         ids = rnd.sample(range(S), rnd.randint(1, S))
         r = rnd.random()
-        if r < 0.45 or r >= 0.8 and r < 0.9:
+        if rnd.random() < 0.15:
+            # a chunk-step boundary: evict one set, then alloc another, as
+            # one operation; on failure neither part may change anything
+            ev_ids = rnd.sample(range(S), rnd.randint(0, S))
+            n = [rnd.choice([0, 1, 2, 7, 16, rnd.randint(0, 2 * C_)]) for _ in ids]
+            snap = copy.deepcopy(sim)
+            try:
+                e_ev = sim.evict(ev_ids)
+                e_al = sim.alloc(ids, n)
+            except NoSpace:
+                sim = snap
+                before = _tables(p)
+                with pytest.raises(H.NoSpace):
+                    H.hswa_pool_evict_alloc(p, ev_ids, ids, n)
+                assert _tables(p) == before
+                continue
+            ev, cnt, full, swa = H.hswa_pool_evict_alloc(p, ev_ids, ids, n)
+            assert ev.tolist() == e_ev[0] and cnt.tolist() == e_ev[1]
+            assert full.tolist() == e_al[0] and swa.tolist() == e_al[1]
+        elif r < 0.45 or r >= 0.8 and r < 0.9:
             imp = r >= 0.8
             n = [rnd.choice([0, 1, 2, 7, 16, rnd.randint(0, 2 * C_)]) for _ in ids]
             fn_sim = sim.import_context if imp else sim.alloc
@@ -173,6 +193,42 @@ def test_random_operations_bit_exact_vs_oracle(seed):
         assert fpt == sim.fpt_table()
         assert mp == sim.map_table()
         assert fr == sim.free_pages()
+
+
+def test_evict_alloc_validation():
+    """The alloc's ring check counts the eviction that comes first; a failed
+    check changes nothing (not even the eviction); each list rejects repeats
+    but a sequence may be in both."""
+    p = _host_pool(8, 16, 2, 8, 16, list(range(16)), [0, 1])
+    sim = PoolSim(8, 16, 2, 8, 16, list(range(16)), [0, 1])
+    H.hswa_pool_alloc(p, [0, 1], [16, 5])
+    sim.alloc([0, 1], [16, 5])
+    # alone, 9 more positions overflow sequence 0's ring (16 resident + 9 > 16)
+    before = _tables(p)
+    with pytest.raises(H.NoSpace):
+        H.hswa_pool_alloc(p, [0], [9])
+    # after the eviction 7 stay resident: 7 + 10 > 16 still fails, and the
+    # eviction is not applied either
+    with pytest.raises(H.NoSpace):
+        H.hswa_pool_evict_alloc(p, [0, 1], [0], [10])
+    assert _tables(p) == before
+    for bad in (([0, 0], [1], [1]), ([0], [1, 1], [1, 1]), ([2], [0], [1]), ([0], [0], [-1])):
+        with pytest.raises(H.HswaError) as e:
+            H.hswa_pool_evict_alloc(p, *bad)
+        assert e.value.status == H.HSWA_E_INVAL
+        assert _tables(p) == before
+    with pytest.raises(H.HswaError):
+        H.hswa_pool_evict_alloc(p, [0], [0], [9], capacity=3)   # evicted_out too small
+    assert _tables(p) == before
+    # 7 + 9 = 16 fits once the eviction comes first
+    ev, cnt, full, swa = H.hswa_pool_evict_alloc(p, [0, 1], [0], [9])
+    e_ev = sim.evict([0, 1])
+    e_al = sim.alloc([0], [9])
+    assert ev.tolist() == e_ev[0] and cnt.tolist() == e_ev[1] == [9, 0]
+    assert full.tolist() == e_al[0] and swa.tolist() == e_al[1]
+    seq_len, fpt, mp, fr = _tables(p)
+    assert (seq_len, fpt, mp, fr) == (sim.seq_len_table(), sim.fpt_table(), sim.map_table(),
+                                      sim.free_pages())
 
 
 def test_pool_create_rejects_bad_descriptions():

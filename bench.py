@@ -1271,7 +1271,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # after the setup's idle time the GPU takes about 15 chunked-prefill
+    # steps (~18 ms) to reach its steady clock; 30 warm-up steps cover it
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="swa_chunked_prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--decode-steps", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -911,7 +911,14 @@ def wl_mixed_decode_fp8(cx, args):
     rl = roofline("hbm", r["full_gbs"], measured_traffic("decode_full_fp8", "kernels_decode.hip")
                   if args.out == "f32" else None)
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
-    line["dtype"] = "fp8 K/V, bf16 MFMA"
+    line["dtype"] = "fp8 K/V, bf16/fp16 MFMA"
+    # FP8 pages: codes turn exactly into bf16 (K) and fp16 (V) operands; the
+    # K scale multiplies each score, the V scale rides in the fp16 weight
+    line["precision"] = dict(line["precision"], k_pages="e4m3 + fp32 scale per token and head",
+                             v_pages="e4m3 + fp32 scale per token and head",
+                             qk_mfma="bf16 (exact e4m3 codes) x bf16 -> fp32, times the K scale",
+                             pv_mfma="fp16 (exact e4m3 codes) x fp16 (weight x V scale x 2^8) "
+                                     "-> fp32")
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
     line["tok_per_s"] = round(r["tok_per_s"], 1)
     line["full_call_us"] = round(r["full_call_us"], 1)

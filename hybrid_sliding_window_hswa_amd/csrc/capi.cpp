@@ -10,6 +10,7 @@
 #include <string>
 
 #include "../../include/hswa.h"
+#include "index.h"
 #include "internal.h"
 
 namespace hswa {
@@ -239,6 +240,7 @@ int decode_call(const hswa_attn_args* a, void* ws, size_t ws_bytes, bool noalloc
   p.n_splits = pl.n_splits;
   p.split_len = pl.split_len;
   p.ws = (float*)ws;
+  p.queue = pl.n_splits > 1 ? (int32_t*)((char*)ws + pl.queue_off) : nullptr;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (p.k_new) {
@@ -281,7 +283,13 @@ DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t rows, int32_t hq,
   n = (max_seq_len + sl - 1) / sl;
   pl.n_splits = (int32_t)n;
   pl.split_len = (int32_t)sl;
-  if (n > 1) pl.ws_bytes = (size_t)rows * hq * n * (d + 2) * sizeof(float);
+  if (n > 1) {
+    // partial states, then (256-byte aligned) the work-queue state: counters,
+    // unit count and the list of up to num_seqs * n units
+    const size_t partial = (size_t)rows * hq * n * (d + 2) * sizeof(float);
+    pl.queue_off = (partial + 255) / 256 * 256;
+    pl.ws_bytes = pl.queue_off + ((size_t)idx::kQueueList + (size_t)num_seqs * n) * 4;
+  }
   return pl;
 }
 

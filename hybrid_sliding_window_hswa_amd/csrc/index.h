@@ -84,6 +84,44 @@ constexpr int32_t fp8_blocks(int32_t hkv, int32_t units) {
   return (units * (hkv / 2) + 7) / 8 * 16;
 }
 
+// Decode work queues (split-K calls).  A pre-pass lists the (sequence,
+// split) units that hold keys; a grid of resident workgroups then takes
+// (unit, KV head) items from a queue by an atomic counter, so no workgroup
+// slot is spent on an empty split.  bf16/fp16 pages use one queue for the
+// whole grid.  FP8 pages (paired heads) use 8 queues, queue q = block index
+// mod 8 (one per XCD: blocks go to the XCDs round-robin), so that heads 2j
+// and 2j + 1 of a unit, whose scales share 128-byte lines, run on one XCD.
+// Queue state: the counters at kQueueStride * q, the unit count at
+// kQueueCount, the unit list from kQueueList (int32 words).
+constexpr int32_t kQueues = 8;
+constexpr int32_t kQueueStride = 32;  // one 128-byte line per counter
+constexpr int32_t kQueueCount = kQueues * kQueueStride;
+constexpr int32_t kQueueList = kQueueCount + kQueueStride;
+
+// The queue that block b takes its items from.
+constexpr int32_t queue_of_block(int32_t b, bool paired) { return paired ? b % kQueues : 0; }
+
+// Item k of queue q over `units` listed units and hkv heads.  Unpaired (one
+// queue): item k is (unit, head) = (k / hkv, k % hkv), unit-major.  Paired
+// (hkv even, 8 queues): heads 2j and 2j + 1 of a unit are items 2m and
+// 2m + 1 of queue q, for head pairs P = 8m + q of the unit-major (unit,
+// pair) order.  False once the queue is exhausted.
+constexpr bool queue_item(int32_t k, int32_t q, int32_t units, int32_t hkv, bool paired,
+                          int32_t* unit, int32_t* head) {
+  if (paired) {
+    const int32_t hp = hkv / 2;
+    const int64_t P = (int64_t)kQueues * (k / 2) + q;
+    if (P >= (int64_t)units * hp) return false;
+    *unit = (int32_t)(P / hp);
+    *head = 2 * (int32_t)(P % hp) + k % 2;
+    return true;
+  }
+  if (q != 0 || (int64_t)k >= (int64_t)units * hkv) return false;
+  *unit = k / hkv;
+  *head = k % hkv;
+  return true;
+}
+
 // Append and transfer grids: page tiles per sequence for up to max_rows
 // positions (a range of max_rows positions starting anywhere in a page
 // touches at most this many pages), and the first position of tile t of a

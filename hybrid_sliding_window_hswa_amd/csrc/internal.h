@@ -101,6 +101,9 @@ struct AttnParams {
   int32_t split_len;
   float* ws;             // [total_q][hq][n_splits][d] partial sums, then
                          // [total_q][hq][n_splits][2] (max, sum)
+  int32_t* queue;        // split-K calls: work-queue state after the partial
+                         // states (idx::kQueue*); nullptr: one workgroup per
+                         // (sequence, split, KV head)
 };
 
 // Window-masked transfer of one layer's KV between the pages and a packed
@@ -158,6 +161,7 @@ struct DecodePlan {
   int32_t n_splits;
   int32_t split_len;
   size_t ws_bytes;
+  size_t queue_off;  // byte offset of the work-queue state in the workspace
 };
 // rows = query rows of the call (num_seqs for plain decode).
 DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t rows, int32_t hq, int32_t hkv,

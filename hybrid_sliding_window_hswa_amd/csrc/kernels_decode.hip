@@ -43,6 +43,8 @@
 //    positions, never on where pages sit in memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -161,9 +163,41 @@ __device__ __forceinline__ bool decode_block(const AttnParams& p, int* unit, int
 // Lazy rescaling of the bf16/fp16 decode (scores are in the log2 domain).
 constexpr float kDecLazy = 8.0f;
 
+// Split-K calls: the workgroup takes (unit, KV head) items from its queue
+// (idx::queue_item) until the queue is exhausted and runs body(unit, head)
+// on each; the pre-pass (decode_units_kernel) has listed the units that
+// hold keys and zeroed the counters.  Other calls: one item, from the block
+// index.  Every workgroup ends once its queue's counter passes the item
+// count, which no other workgroup waits on.
+// (SWA layers read one split and take the block-index path only.)
+template <int KIND, bool PAIRED, typename F>
+__device__ __forceinline__ void for_each_item(const AttnParams& p, F&& body) {
+  const bool queued = KIND == 0 && p.queue;  // uniform
+  const bool paired = PAIRED && (p.hkv & 1) == 0;
+  __shared__ int s_k;
+  const int q = idx::queue_of_block(blockIdx.x, paired);
+  for (int it = 0;; ++it) {
+    int unit, kvh;
+    if (!queued) {
+      if (it > 0 || !decode_block<PAIRED>(p, &unit, &kvh)) return;
+    } else {
+      if (threadIdx.x == 0)
+        s_k = __hip_atomic_fetch_add(p.queue + idx::kQueueStride * q, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const int k = s_k;
+      __syncthreads();  // every wave has read s_k before it is written again
+      const int units = min(p.queue[idx::kQueueCount], p.num_seqs * p.n_splits);
+      int a;
+      if (!idx::queue_item(k, q, units, p.hkv, paired, &a, &kvh)) return;
+      unit = p.queue[idx::kQueueList + a];
+    }
+    body(unit, kvh);
+  }
+}
+
 template <int D, int KIND, int G, int QN, bool F8>
-__global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnParams p) {
+__device__ __forceinline__ void decode_unit(const AttnParams& p, const int unit, const int kvh) {
   constexpr int NB = D / 16;                  // 16-row d blocks of O^T
   constexpr int NC = D / 32;                  // 32-wide d chunks of the QK reduction
   constexpr int NCOL = G * QN;                // (row, head) columns
@@ -176,8 +210,7 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][CT][D];
   __shared__ float red_ml[kDecWaves][CT][2];
 
-  int unit, kvh;  // unit = (sequence, split)
-  if (!decode_block<F8>(p, &unit, &kvh)) return;
+  // unit = (sequence, split)
   const int i = unit / p.n_splits;
   const int split = unit % p.n_splits;
   const int sid = p.seq_ids[i];
@@ -440,6 +473,13 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
   }
 }
 
+
+template <int D, int KIND, int G, int QN, bool F8>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnParams p) {
+  for_each_item<KIND, F8>(p, [&](int unit, int kvh) { decode_unit<D, KIND, G, QN, F8>(p, unit, kvh); });
+}
+
 // FP8 decode with 64-key steps (one column tile: G * QN <= 16).  The step
 // covers four pages; a lane's four score tiles hold all 16 keys of one page
 // (tile kt row 4a + r is key 16a + 4kt + r), so its V fragment for the two
@@ -449,8 +489,8 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
 // the same order of the reduction.  A wave then keeps 16.5 KB in flight per
 // step, as much as the bf16 path, at two waves per SIMD.
 template <int D, int KIND, int G, int QN>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4)))
-decode_fp8_kernel(AttnParams p) {
+__device__ __forceinline__ void decode_fp8_unit(const AttnParams& p, const int unit,
+                                                const int kvh) {
   constexpr int NB = D / 16;                  // 16-row d blocks of O^T
   constexpr int NC = D / 32;                  // 32-wide chunks of the QK reduction
   constexpr int DQ = D / 4;                   // contiguous K bytes of a lane per row
@@ -462,8 +502,7 @@ decode_fp8_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][CT][D];
   __shared__ float red_ml[kDecWaves][CT][2];
 
-  int unit, kvh;  // unit = (sequence, split)
-  if (!decode_block<true>(p, &unit, &kvh)) return;
+  // unit = (sequence, split)
   const int i = unit / p.n_splits;
   const int split = unit % p.n_splits;
   const int sid = p.seq_ids[i];
@@ -632,6 +671,13 @@ decode_fp8_kernel(AttnParams p) {
   }
 }
 
+
+template <int D, int KIND, int G, int QN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4)))
+decode_fp8_kernel(AttnParams p) {
+  for_each_item<KIND, true>(p, [&](int unit, int kvh) { decode_fp8_unit<D, KIND, G, QN>(p, unit, kvh); });
+}
+
 // Log-sum-exp merge of the split partial states of one (query row, head).
 // Block x = (sequence, row within the sequence), y = query head.  A split
 // whose keys all lie past the row's position holds max = -inf and weight 0.
@@ -663,28 +709,116 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, int qn)
   store_out(p, hrow * D + d, num / den);
 }
 
+// Pre-pass of a split-K call: lists the (sequence, split) units that hold
+// keys (a sequence of L keys has ceil(L / len) of its n_splits pieces of
+// len keys), longest pieces first, with their count, and zeroes the queue
+// counters.  Longest first keeps the grid's tail short: the last items
+// taken are the shortest.  Pieces are sorted by length in kLenBuckets
+// classes (counting sort through LDS counters, so the order within a class
+// varies; every item writes its own partial state, so results do not).
+// Sequences the decode kernels skip (bad id, no rows, rows past the
+// length) get no units.  One workgroup, 256 sequences at a time.
+constexpr int kLenBuckets = 64;
+
+__device__ __forceinline__ int units_of(const AttnParams& p, int i, int* bucket) {
+  const int sid = p.seq_ids[i];
+  if (sid < 0 || sid >= p.t.max_seqs) return 0;
+  const int row0 = p.cu_q ? p.cu_q[i] : i;
+  const int n = p.cu_q ? p.cu_q[i + 1] - row0 : 1;
+  const int L = call_len(p, i, sid, n);
+  if (n <= 0 || n > L || row0 < 0 || row0 + n > p.total_q) return 0;
+  const int len = idx::split_keys(L, p.n_splits, p.split_len);
+  const int64_t b = (int64_t)(len - 1) * kLenBuckets / max(p.split_len, 64);
+  *bucket = (int)min<int64_t>(b, kLenBuckets - 1);
+  return (L + len - 1) / len;
+}
+
+__global__ void __launch_bounds__(256) decode_units_kernel(AttnParams p) {
+  __shared__ int hist[kLenBuckets];
+  const int tid = threadIdx.x;
+  if (tid < kLenBuckets) hist[tid] = 0;
+  if (tid < idx::kQueues) p.queue[idx::kQueueStride * tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < p.num_seqs; i += 256) {
+    int b = 0;
+    const int ns = units_of(p, i, &b);
+    if (ns > 0) atomicAdd(&hist[b], ns);
+  }
+  __syncthreads();
+  if (tid == 0) {  // start of each class, longest class first
+    int run = 0;
+    for (int b = kLenBuckets - 1; b >= 0; --b) {
+      const int c = hist[b];
+      hist[b] = run;
+      run += c;
+    }
+    p.queue[idx::kQueueCount] = run;
+  }
+  __syncthreads();
+  for (int i = tid; i < p.num_seqs; i += 256) {
+    int b = 0;
+    const int ns = units_of(p, i, &b);
+    if (ns <= 0) continue;
+    const int at = atomicAdd(&hist[b], ns);
+    for (int sp = 0; sp < ns; ++sp) p.queue[idx::kQueueList + at + sp] = i * p.n_splits + sp;
+  }
+}
+
+// Workgroups of a queue grid: as many as the device holds at once (a
+// multiple of the 8 queues), at most one per item.
+template <typename K>
+hipError_t queue_grid(K kernel, int64_t items, unsigned* grid) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+  if (e != hipSuccess) return e;
+  const int64_t q = idx::kQueues;
+  int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1) / q * q;
+  g = std::min<int64_t>(std::max<int64_t>(g, q), (items + q - 1) / q * q);
+  *grid = (unsigned)g;
+  return hipSuccess;
+}
+
 // FP8 pages with one column tile take the 64-key kernel; two tiles (8
 // heads, more than two rows) keep the 32-key one, whose registers already
 // hold two tiles' state.
 template <int D, int KIND, int G, int QN, bool F8>
-void launch_decode_one(const AttnParams& p, dim3 grid, hipStream_t s) {
-  if constexpr (F8 && G * QN <= 16)
+hipError_t launch_decode_one(const AttnParams& p, dim3 grid, hipStream_t s) {
+  if constexpr (F8 && G * QN <= 16) {
+    if (p.queue) {
+      hipError_t e = queue_grid(decode_fp8_kernel<D, KIND, G, QN>,
+                                (int64_t)p.num_seqs * p.n_splits * p.hkv, &grid.x);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((decode_fp8_kernel<D, KIND, G, QN>), grid, dim3(256), 0, s, p);
-  else
+  } else {
+    if (p.queue) {
+      hipError_t e = queue_grid(decode_kernel<D, KIND, G, QN, F8>,
+                                (int64_t)p.num_seqs * p.n_splits * p.hkv, &grid.x);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((decode_kernel<D, KIND, G, QN, F8>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
 }
 
 template <int D, int KIND, int QN, bool F8>
 hipError_t launch_decode_q(const AttnParams& p, hipStream_t s) {
   const int units = p.num_seqs * p.n_splits;
   dim3 grid((unsigned)(F8 && p.hkv % 2 == 0 ? idx::fp8_blocks(p.hkv, units) : units * p.hkv), 1);
-  switch (p.hq / p.hkv) {
-    case 1: launch_decode_one<D, KIND, 1, QN, F8>(p, grid, s); break;
-    case 2: launch_decode_one<D, KIND, 2, QN, F8>(p, grid, s); break;
-    case 4: launch_decode_one<D, KIND, 4, QN, F8>(p, grid, s); break;
-    default: launch_decode_one<D, KIND, 8, QN, F8>(p, grid, s); break;
+  if (p.queue) {
+    hipLaunchKernelGGL(decode_units_kernel, dim3(1), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipSuccess;
+  switch (p.hq / p.hkv) {
+    case 1: e = launch_decode_one<D, KIND, 1, QN, F8>(p, grid, s); break;
+    case 2: e = launch_decode_one<D, KIND, 2, QN, F8>(p, grid, s); break;
+    case 4: e = launch_decode_one<D, KIND, 4, QN, F8>(p, grid, s); break;
+    default: e = launch_decode_one<D, KIND, 8, QN, F8>(p, grid, s); break;
+  }
   if (e != hipSuccess || p.n_splits == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.num_seqs * QN, p.hq), dim3(D), 0, s, p,
                      QN);

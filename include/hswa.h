@@ -380,7 +380,10 @@ int hswa_prefill_chunk(const hswa_attn_args* args, void* stream);
  * hswa_decode_workspace_bytes(args) bytes (may be NULL when that is 0;
  * the size depends on kind, window, num_seqs, max(total_q, num_seqs), the
  * head counts, head_dim and max_seq_len, and no memory is read);
- * HSWA_E_INVAL if it is smaller. */
+ * HSWA_E_INVAL if it is smaller.  It receives the split partial states and
+ * the call's work list (which the call builds itself: the buffer needs no
+ * initialisation), so calls in flight at the same time need workspaces of
+ * their own. */
 int hswa_decode(const hswa_attn_args* args, void* workspace, size_t ws_bytes,
                 void* stream);
 size_t hswa_decode_workspace_bytes(const hswa_attn_args* args);
@@ -389,8 +392,8 @@ size_t hswa_decode_workspace_bytes(const hswa_attn_args* args);
  * or pass a workspace: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments, plan, kernels and
  * results (bitwise) as hswa_decode with a workspace of
- * hswa_decode_workspace_bytes(args) bytes; the split-K partial states go
- * instead to a device array of HSWA_DECODE_SCRATCH_BYTES that the library
+ * hswa_decode_workspace_bytes(args) bytes; the split-K partial states and
+ * work list go instead to a device array of HSWA_DECODE_SCRATCH_BYTES that the library
  * holds on each GPU it runs on until the process ends (its address is
  * looked up on the first call on a device).  No memory is allocated and
  * nothing in the array needs clearing between calls.  HSWA_E_INVAL, with

@@ -19,6 +19,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "index.h"  // csrc/index.h, found through the include path
@@ -231,6 +232,48 @@ int main() {
                 "blocks %d, %d", h, h + 1, u, b0, b1);
         }
     }
+  // Decode work queues: over the queues that blocks take items from (one
+  // unpaired, 8 paired) every (unit, head) item comes exactly once, a queue
+  // stays exhausted once it is, and paired heads 2j and 2j + 1 of a unit
+  // share a queue
+  for (int32_t hkv = 1; hkv <= 16; ++hkv)
+    for (int paired = 0; paired <= (hkv % 2 == 0 ? 1 : 0); ++paired)
+      for (int32_t units = 0; units <= 200; units += (units < 30 ? 1 : 17)) {
+        std::vector<int32_t> queue_of(units * hkv, -1);
+        std::vector<int32_t> used;
+        for (int32_t b = 0; b < 64; ++b) {
+          const int32_t q = queue_of_block(b, paired);
+          CHECK(q >= 0 && q < kQueues, "block %d takes queue %d", b, q);
+          if (std::find(used.begin(), used.end(), q) == used.end()) used.push_back(q);
+        }
+        CHECK((int)used.size() == (paired ? kQueues : 1), "%d queues in use (paired %d)",
+              (int)used.size(), paired);
+        for (int32_t q : used) {
+          bool done = false;
+          for (int32_t k = 0; k < units * hkv + 8; ++k) {
+            int32_t u = -1, h = -1;
+            const bool ok = queue_item(k, q, units, hkv, paired, &u, &h);
+            CHECK(!(done && ok), "queue %d item %d after the end (units %d hkv %d)", q, k,
+                  units, hkv);
+            if (!ok) {
+              done = true;
+              continue;
+            }
+            CHECK(u >= 0 && u < units && h >= 0 && h < hkv, "queue %d item %d -> (%d, %d)", q,
+                  k, u, h);
+            CHECK(queue_of[u * hkv + h] < 0, "item (%d, %d) in queues %d and %d", u, h,
+                  queue_of[u * hkv + h], q);
+            queue_of[u * hkv + h] = q;
+          }
+        }
+        for (int32_t x = 0; x < units * hkv; ++x)
+          CHECK(queue_of[x] >= 0, "item (%d, %d) in no queue (units %d hkv %d paired %d)",
+                x / hkv, x % hkv, units, hkv, paired);
+        if (paired)
+          for (int32_t x = 0; x < units * hkv; x += 2)
+            CHECK(queue_of[x] == queue_of[x + 1], "paired heads of unit %d in queues %d, %d",
+                  x / hkv, queue_of[x], queue_of[x + 1]);
+      }
   printf("index checks passed: %ld\n", g_checks);
   return 0;
 }

@@ -330,13 +330,22 @@ def test_multi_row_decode_validation_and_workspace():
     assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
     a = _args(n=2, total_q=2, max_q_len=0)
     assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
-    # the split-K workspace holds one partial state per (row, head, split)
+    # the split-K workspace holds one partial state per (row, head, split),
+    # then (256-byte aligned) the work queues: 8 counters of a 128-byte line,
+    # the unit count and a list of up to num_seqs * splits units.  Here 4
+    # sequences x 8 KV heads aim at 16,384 workgroups with pieces of at least
+    # 1,024 keys: 98 splits of 1,024 keys for 100,000.
     one = _args(kind=0, n=4, total_q=4, hq=64, hkv=8, d=128, max_seq_len=100000)
     four = _args(kind=0, n=4, total_q=16, max_q_len=4, hq=64, hkv=8, d=128,
                  max_seq_len=100000)
     b1 = lib.hswa_decode_workspace_bytes(C.byref(one))
     b4 = lib.hswa_decode_workspace_bytes(C.byref(four))
-    assert b1 > 0 and b4 == 4 * b1
+
+    def ws(rows, seqs=4, splits=98):
+        partial = rows * 64 * splits * (128 + 2) * 4
+        return -(-partial // 256) * 256 + (8 * 32 + 32 + seqs * splits) * 4
+
+    assert b1 == ws(4) and b4 == ws(16)
     assert H.hswa_decode_workspace_bytes(0, 128, 4, 64, 8, 128, 100000, total_q=16) == b4
     assert H.hswa_decode_workspace_bytes(0, 128, 4, 64, 8, 128, 100000) == b1
 

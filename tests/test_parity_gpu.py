@@ -322,6 +322,51 @@ def test_decode_small_heads_d64(gpu):
     _decode_scenario([1500, 90, 700], 3, 8, 2, 64, 128, 81)
 
 
+def test_decode_many_sequences_work_queue(gpu):
+    """600 sequences (the work-queue pre-pass scans 256 at a time) with
+    contexts from 1 to 6,000 keys: up to 6 splits of 1,024 keys, most of
+    them empty for the shorter sequences, so the queue holds a mix of
+    pieces of every length (and the bounds of a split: 1,023-1,025)."""
+    rng = np.random.default_rng(17)
+    ctxs = [int(x) for x in rng.integers(1, 6000, size=595)] + [1, 1023, 1024, 1025, 6000]
+    _decode_scenario(ctxs, 2, 16, 2, 64, 64, 171)
+
+
+def test_decode_skips_sequences_outside_the_pool(gpu):
+    """A seq_ids entry outside [0, max_seqs) gets no work (its output rows
+    and valid length stay as they were); the other sequences are exact,
+    through the split-K work queue and without it."""
+    hq, hkv, d, W = 16, 2, 64, 64
+    ctxs = [5000, 3000, 40]
+    seqs = make_seqs(ctxs, hq, hkv, d, 172)
+    B = len(ctxs)
+    maxp = max(ctxs) // 16 + 2
+    st = Setup(H.FULL, W, W, B, maxp, B * maxp + 8, hkv, d, 172)
+    ids = list(range(B))
+    H.hswa_pool_import(st.pool, ids, ctxs)
+    sid_all = torch.tensor(ids, dtype=torch.int32, device=dev())
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(ctxs)]), dtype=torch.int32, device=dev())
+    kf = torch.cat([s_.k[:c] for s_, c in zip(seqs, ctxs)]).to(dev())
+    vf = torch.cat([s_.v[:c] for s_, c in zip(seqs, ctxs)]).to(dev())
+    H.hswa_append_kv(H.FULL, kf, vf, sid_all, st.view, st.kc, st.vc, cu, max(ctxs))
+    pos = [c - 1 for c in ctxs]
+    q = torch.stack([s_.q[p_] for s_, p_ in zip(seqs, pos)]).to(dev())
+    for bad in (B, -1, 1 << 20):
+        sid = torch.tensor([0, bad, 2], dtype=torch.int32, device=dev())
+        for maxlen in (max(ctxs), 64):   # split-K (work queue), and one split
+            out = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device=dev())
+            vl = torch.full((B,), -7, dtype=torch.int32, device=dev())
+            nb = H.hswa_decode_workspace_bytes(H.FULL, W, B, hq, hkv, d, maxlen)
+            ws = torch.empty(max(nb // 4, 1), dtype=torch.float32, device=dev())
+            H.hswa_decode(H.FULL, W, q, None, None, sid, maxlen, st.view, st.kc, st.vc, out, ws, vl)
+            got = out.cpu().double().numpy()
+            for b in (0, 2):
+                exp = oracle_rows(seqs[b], [pos[b]], H.FULL, W)[0]
+                assert float(np.max(np.abs(got[b] - exp))) < TOL
+            assert np.isnan(got[1]).all()
+            assert vl.cpu().tolist() == [ctxs[0], -7, ctxs[2]]
+
+
 # ---------------------------------------------------------------------------
 # One GPU's share of an 8-way head split: Hq = 8, Hkv = 1, d = 128
 

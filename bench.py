@@ -67,6 +67,7 @@ import ctypes as C
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -95,12 +96,22 @@ def KV_TOKEN_BYTES(hkv, d):
 KERNEL_HEADERS = ("device.h", "internal.h", "index.h")
 
 
+def _code_only(text):
+    """C++ source without its comments, whitespace runs collapsed: a change
+    to comments or layout does not change the kernels (the sources hold no
+    string literal with comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha(fname):
-    """SHA-256 over a kernel source followed by the shared device headers."""
+    """SHA-256 over the code of a kernel source followed by the shared
+    device headers (comments and layout excluded)."""
     h = hashlib.sha256()
     for name in (fname,) + KERNEL_HEADERS:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

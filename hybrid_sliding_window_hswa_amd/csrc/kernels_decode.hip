@@ -10,10 +10,16 @@
 // one sequence are verified at once; they share every K/V byte read here.
 //
 // Design (gfx950):
-//  - One workgroup = 4 wavefronts per (sequence, KV head, split).  Full
-//    layers split a context of L keys into ceil(L / split_len) equal pieces
-//    (64-key multiples) so the grid fills 256 CUs without short tail
-//    pieces; pieces are merged by log-sum-exp in decode_combine_kernel.
+//  - One workgroup = 4 wavefronts works on one (sequence, KV head, split)
+//    at a time.  Full layers split a context of L keys into ceil(L /
+//    split_len) equal pieces (64-key multiples) of the plan's n_splits, so
+//    there is work for 256 CUs without short tail pieces; pieces are merged
+//    by log-sum-exp in decode_combine_kernel.  Shorter contexts leave some
+//    of the n_splits empty, so split-K calls run a work queue: a pre-pass
+//    lists the pieces that hold keys, longest first, and as many
+//    workgroups as the device holds take (piece, KV head) items from it,
+//    instead of one workgroup per (sequence, split, KV head) most of which
+//    would find nothing to do and still hold back dispatch.
 //  - The (row, head) pairs that share a KV head ride in the N dimension of
 //    16x16x32 MFMAs: S^T[key][col] = K[key][:] . Q[col][:], column
 //    col = row * G + head, in 16-column tiles.  Every K/V byte is read from

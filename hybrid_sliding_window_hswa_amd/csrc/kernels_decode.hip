@@ -771,16 +771,26 @@ __global__ void __launch_bounds__(256) decode_units_kernel(AttnParams p) {
 }
 
 // Workgroups of a queue grid: as many as the device holds at once (a
-// multiple of the 8 queues), at most one per item.
+// multiple of the 8 queues), at most one per item.  The count per device
+// and kernel is looked up once (`cache`, one slot per device).
+constexpr int kMaxQueueDevices = 64;
 template <typename K>
-hipError_t queue_grid(K kernel, int64_t items, unsigned* grid) {
-  int dev = 0, cus = 0, per_cu = 0;
+hipError_t queue_grid(K kernel, std::atomic<int> (&cache)[kMaxQueueDevices], int64_t items,
+                      unsigned* grid) {
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
   if (e != hipSuccess) return e;
+  int slots = dev >= 0 && dev < kMaxQueueDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (slots <= 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+    if (e != hipSuccess) return e;
+    slots = std::max(cus, 1) * std::max(per_cu, 1);
+    if (dev >= 0 && dev < kMaxQueueDevices) cache[dev].store(slots, std::memory_order_relaxed);
+  }
   const int64_t q = idx::kQueues;
-  int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1) / q * q;
+  int64_t g = (int64_t)slots / q * q;
   g = std::min<int64_t>(std::max<int64_t>(g, q), (items + q - 1) / q * q);
   *grid = (unsigned)g;
   return hipSuccess;
@@ -791,17 +801,17 @@ hipError_t queue_grid(K kernel, int64_t items, unsigned* grid) {
 // hold two tiles' state.
 template <int D, int KIND, int G, int QN, bool F8>
 hipError_t launch_decode_one(const AttnParams& p, dim3 grid, hipStream_t s) {
+  static std::atomic<int> slots[kMaxQueueDevices];  // per instantiation
+  const int64_t items = (int64_t)p.num_seqs * p.n_splits * p.hkv;
   if constexpr (F8 && G * QN <= 16) {
     if (p.queue) {
-      hipError_t e = queue_grid(decode_fp8_kernel<D, KIND, G, QN>,
-                                (int64_t)p.num_seqs * p.n_splits * p.hkv, &grid.x);
+      hipError_t e = queue_grid(decode_fp8_kernel<D, KIND, G, QN>, slots, items, &grid.x);
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((decode_fp8_kernel<D, KIND, G, QN>), grid, dim3(256), 0, s, p);
   } else {
     if (p.queue) {
-      hipError_t e = queue_grid(decode_kernel<D, KIND, G, QN, F8>,
-                                (int64_t)p.num_seqs * p.n_splits * p.hkv, &grid.x);
+      hipError_t e = queue_grid(decode_kernel<D, KIND, G, QN, F8>, slots, items, &grid.x);
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((decode_kernel<D, KIND, G, QN, F8>), grid, dim3(256), 0, s, p);

@@ -1288,7 +1288,7 @@ WORKLOADS = {
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     # after the setup's idle time the GPU takes about 15 chunked-prefill
     # steps (~18 ms) to reach its steady clock; 30 warm-up steps cover it
     ap.add_argument("--warmup", type=int, default=30)

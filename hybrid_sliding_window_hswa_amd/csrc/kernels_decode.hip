@@ -170,12 +170,12 @@ __device__ __forceinline__ bool decode_block(const AttnParams& p, int* unit, int
 constexpr float kDecLazy = 8.0f;
 
 // Split-K calls: the workgroup takes (unit, KV head) items from its queue
-// (idx::queue_item) until the queue is exhausted and runs body(unit, head)
-// on each; the pre-pass (decode_units_kernel) has listed the units that
-// hold keys and zeroed the counters.  Other calls: one item, from the block
-// index.  Every workgroup ends once its queue's counter passes the item
-// count, which no other workgroup waits on.
-// (SWA layers read one split and take the block-index path only.)
+// (idx::queue_of_block, idx::queue_item) until the queue is exhausted and
+// runs body(unit, head) on each; the pre-pass (decode_units_kernel) has
+// listed the units that hold keys and zeroed the counters.  Other calls,
+// and SWA layers (one split): one item, from the block index.  Every
+// workgroup ends once its queue's counter passes the item count; no
+// workgroup waits on another.
 template <int KIND, bool PAIRED, typename F>
 __device__ __forceinline__ void for_each_item(const AttnParams& p, F&& body) {
   const bool queued = KIND == 0 && p.queue;  // uniform

@@ -34,6 +34,9 @@ resident in HBM before the timed region starts):
       The mixed decode over FP8 pages (e4m3 codes with an fp32 scale per
       token and head, quantized by the append): half the K/V bytes per key.
       `value` = algorithmic HBM GB/s of the FP8 bytes.
+  swa_chunked_prefill_fp8
+      swa_chunked_prefill over FP8 pages: the appends quantize each chunk,
+      the attention reads codes and scales.  `value` = tokens/s.
   mtp_decode
       Multi-token decode: the mixed decode's 256 sequences with one token
       plus three draft tokens per step (rows of a sequence share every K/V
@@ -217,11 +220,12 @@ class ChunkedPrefill:
     layers see the same synthetic Q/K/V (an attention-only stack)."""
 
     def __init__(self, cx, lens, chunk, hq, hkv, d, W, seed, pattern="S", ring=None,
-                 out="f32", one_stream=False, combine_pool_ops=True):
+                 out="f32", one_stream=False, combine_pool_ops=True, fp8=False):
         torch, H = cx.torch, cx.H
         import synth
         self.cx = cx
         self.combine_pool_ops = combine_pool_ops
+        self.fp8 = fp8
         self.obytes = 2 if out == "f16" else 4
         self.lens, self.chunk, self.hq, self.hkv, self.d, self.W = lens, chunk, hq, hkv, d, W
         B = len(lens)
@@ -235,9 +239,14 @@ class ChunkedPrefill:
         self.pool = H.hswa_pool_create(W, C_, B, maxp, nfull, free, ringp, device=cx.dev)
         self.view = H.hswa_pool_get_view(self.pool)
         self.layers = []
+        self.scales = []  # FP8 pages: (k_scale, v_scale) per layer
         for kind in pattern:
             npages = nfull if kind == "F" else B * C_ // 16
-            kc, vc = H.kv_cache_alloc(npages, hkv, d, cx.dev, 0.0)
+            if fp8:
+                kc, vc, ks, vs = H.kv_cache_alloc_fp8(npages, hkv, d, cx.dev, 0)
+                self.scales.append((ks, vs))
+            else:
+                kc, vc = H.kv_cache_alloc(npages, hkv, d, cx.dev, 0.0)
             self.layers.append((H.FULL if kind == "F" else H.SWA, kc, vc))
         # inputs per sequence, generated on the device
         self.q, self.k, self.v = [], [], []
@@ -286,11 +295,16 @@ class ChunkedPrefill:
         for st in self.steps:
             T = st["q"].shape[0]
             st["args"] = []
-            for kind, kc, vc in self.layers:
+            for li, (kind, kc, vc) in enumerate(self.layers):
                 app = _attn_args(cx, kind, W, hkv, hkv, d, st["sid"], st["cu"], T, st["max_n"],
                                  0, self.view, None, st["k"], st["v"], kc, vc, None)
                 att = _attn_args(cx, kind, W, hq, hkv, d, st["sid"], st["cu"], T, st["max_n"],
                                  0, self.view, st["q"], None, None, kc, vc, self.out)
+                if fp8:
+                    ks, vs = self.scales[li]
+                    for a in (app, att):
+                        a.kv_dtype = H.HSWA_KV_FP8
+                        a.k_scale, a.v_scale = ks.data_ptr(), vs.data_ptr()
                 if "F" not in pattern:
                     app.q_pos = att.q_pos = st["qpos"].data_ptr()
                 st["args"].append((app, att))
@@ -335,7 +349,9 @@ class ChunkedPrefill:
         written (fp32), and the K/V of each key the chunk needs read once
         (SWA: the chunk plus its W-1 halo; Full: the whole prefix)."""
         T = st["q"].shape[0]
-        kvb = KV_TOKEN_BYTES(self.hkv, self.d)
+        # FP8 pages: one code per element plus an fp32 scale per token and
+        # head, for K and for V
+        kvb = 2 * self.hkv * (self.d + 4) if self.fp8 else KV_TOKEN_BYTES(self.hkv, self.d)
         if kind == self.cx.H.FULL:
             keys = sum(e for b, a, e in st["rows"])
         else:
@@ -901,6 +917,46 @@ def _sample_seqs(ctxs, n, seed):
     return ([lo, hi] + rest)[:n]
 
 
+def wl_swa_chunked_prefill_fp8(cx, args):
+    """The SWA chunked prefill over FP8 pages: the appends quantize each
+    chunk's K/V, the attention reads codes and scales."""
+    import synth
+    H = cx.H
+    wl = synth.C2
+    lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
+    cp = ChunkedPrefill(cx, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                        wl.window, wl.seed, out=args.out, one_stream=args.single_stream,
+                        combine_pool_ops=not args.separate_pool_ops, fp8=True)
+    cx.torch.cuda.synchronize()
+    sec = timed(cx, cp.run, args.steps, args.warmup)
+    ev = []
+    for _ in range(max(1, min(args.steps, 5))):
+        cp.run(ev)
+    cx.torch.cuda.synchronize()
+    ks = kernel_stats(cp, ev, H.SWA)
+    log(f"prefill fp8: {cp.tokens / sec:.4g} tok/s, {sec * 1e3:.3f} ms/step, kernel {ks}")
+    config = {"workload": "swa_chunked_prefill_fp8", "num_seqs": wl.num_seqs,
+              "seq_len_range": [wl.len_lo, wl.len_hi], "seq_lens": lens, "chunk": wl.chunk,
+              "window": wl.window, "num_q_heads": wl.num_q_heads,
+              "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+              "kv_dtype": "fp8 e4m3, fp32 scale per token and head",
+              "ring_slots": wl.window + wl.chunk, "output_dtype": ODT[args.out],
+              "seed": wl.seed}
+    rl = roofline("hbm", ks["gbs"], measured_traffic("prefill_swa_fp8", "kernels_prefill.hip")
+                  if args.out == "f32" else None)
+    line = base_line(args, round(cp.tokens / sec, 1), "tok/s", sec * 1e3, config, rl)
+    line["dtype"] = "fp8 K/V, bf16/fp16 MFMA"
+    line["precision"] = dict(line["precision"], k_pages="e4m3 + fp32 scale per token and head",
+                             v_pages="e4m3 + fp32 scale per token and head",
+                             qk_mfma="bf16 (exact e4m3 codes) x bf16 -> fp32, times the K scale",
+                             pv_mfma="fp16 (code x V scale, rounded) x fp16 weight -> fp32")
+    line["kernel"] = {"name": "prefill_kernel<128,SWA,FP8>", "avg_us": round(ks["avg_us"], 2),
+                      "launches_timed": ks["launches"], "tflops": round(ks["tflops"], 2),
+                      "mfma_frac": round(ks["tflops"] / MFMA_BF16_PEAK_TFS, 4)}
+    line["cpu_baseline"] = None
+    return line
+
+
 def wl_mixed_decode_fp8(cx, args):
     """The mixed decode over FP8 pages (e4m3 codes, fp32 scale per token and
     head): half the K/V bytes per key."""
@@ -1277,6 +1333,7 @@ WORKLOADS = {
     "tp8_share": wl_tp8_share,
     "mixed_decode": wl_mixed_decode,
     "mixed_decode_fp8": wl_mixed_decode_fp8,
+    "swa_chunked_prefill_fp8": wl_swa_chunked_prefill_fp8,
     "mtp_decode": wl_mtp_decode,
     "tier_transfer": wl_tier_transfer,
     "hybrid_stack": wl_hybrid_stack,

@@ -408,12 +408,14 @@ def _args(kind, window, q, k_new, v_new, seq_ids, cu_q, total_q, max_q_len, max_
 
 def hswa_prefill_chunk(kind: int, window: int, q, k_new, v_new, seq_ids, cu_q,
                        max_q_len: int, view, k_cache, v_cache, out, vlen=None,
-                       scale: float = 0.0, stream=None, q_pos=None) -> None:
+                       scale: float = 0.0, stream=None, q_pos=None, k_scale=None,
+                       v_scale=None) -> None:
     """q [T, Hq, d] bf16; k_new/v_new [T, Hkv, d] bf16 or None; seq_ids [B] and
     cu_q [B+1] int32 device tensors; out [T, Hq, d] fp32 or fp16; vlen [T]
-    int32; q_pos [B] int32 (optional): each sequence's first row position."""
+    int32; q_pos [B] int32 (optional): each sequence's first row position.
+    With ``k_scale``/``v_scale`` the pages are FP8 (kv_cache_alloc_fp8)."""
     a = _args(kind, window, q, k_new, v_new, seq_ids, cu_q, q.shape[0], max_q_len, 0, view,
-              k_cache, v_cache, out, vlen, scale, q_pos=q_pos)
+              k_cache, v_cache, out, vlen, scale, k_scale, v_scale, q_pos)
     _check(library().hswa_prefill_chunk(C.byref(a), _stream(stream)))
 
 

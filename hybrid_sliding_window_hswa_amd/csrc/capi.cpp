@@ -332,10 +332,6 @@ int hswa_prefill_chunk(const hswa_attn_args* a, void* stream) {
   hswa::AttnParams p;
   int rc = validate(a, false, true, &p);
   if (rc) return rc;
-  if (p.kv_fp8) {
-    hswa::set_error("prefill over FP8 pages is not built (decode and append are)");
-    return HSWA_E_UNSUPPORTED;
-  }
   if (p.num_seqs == 0 || p.total_q == 0) return HSWA_OK;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;

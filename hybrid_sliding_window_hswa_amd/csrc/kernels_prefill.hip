@@ -72,6 +72,13 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t
                "s"(sbase)
                : "memory", "m0");
 }
+// 4 bytes per lane from sbase + voff into LDS at lds_base + 4 * lane (the
+// lanes that execute it), as dma16.
+__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
 // Wait until at most N vector-memory operations of the wave are in flight
 // (they complete in issue order).
 template <int N>
@@ -79,7 +86,7 @@ __device__ __forceinline__ void wait_vm_at_most() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, int KIND, int G>
+template <int D, int KIND, int G, bool F8>
 __global__ void __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(3, 4)))
 prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   constexpr int HPW = G < kPreWaves ? G : kPreWaves;  // heads per workgroup
@@ -95,9 +102,16 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   constexpr int NI = SBYTES / 1024;                   // 1 KB transfers per step
   constexpr int NIW = NI / kPreWaves;                 // per wave
   static_assert(NI % kPreWaves == 0 && NIW >= 1, "a step's transfers split over the waves");
+  // FP8 pages: a wave moves its page block's e4m3 codes (half the bytes)
+  // into the second half of the block's bf16 / fp16 region, plus the
+  // block's 16 scales, then widens the codes in place before the barrier.
+  // The scales of a step sit after its V region: K of pages 0, 1, then V.
+  constexpr int NT8 = kPage * D / 1024;                 // 1 KB code transfers per block
+  constexpr int NWAIT = F8 ? NT8 + 1 : NIW;             // a wave's transfers per step
+  constexpr int SB = SBYTES + (F8 ? 4 * kPage * 4 : 0);  // bytes per step buffer
   constexpr int OROW = 64 * 4 + 16;  // LDS bytes per row of a 64-dim output piece (padded)
   constexpr int OBYTES = kPreWaves * 32 * OROW;
-  constexpr int LBYTES = kBufs * SBYTES > OBYTES ? kBufs * SBYTES : OBYTES;
+  constexpr int LBYTES = kBufs * SB > OBYTES ? kBufs * SB : OBYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LBYTES];
 
   const int t = blockIdx.x;
@@ -191,23 +205,94 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   auto issue = [&](int kp0, int buf) {
     const int32_t pg = kp0 + kPage * half <= wg_khi ? scalar_load_i32(prow, ipg) : 0;
     ipg = idx::prefill_next_entry(KIND, ipg, npr);
+    if constexpr (F8) {
+      const int64_t blk = (int64_t)(uint32_t)pg * hkv + kvh;  // (page, KV head) block
+      const uint8_t* codes = (const uint8_t*)(wave >= 2 ? p.v_cache : p.k_cache) + blk * kPage * D;
+      const uint32_t region = lds0 + buf * SB + (wave >= 2 ? KBYTES + half * VPAGE : half * VPAGE);
+      for (int x = 0; x < NT8; ++x) dma16(x * 1024 + 16 * lane, codes, region + kPage * D + x * 1024);
+      const float* sc = (wave >= 2 ? p.v_scale : p.k_scale) + blk * kPage;
+      if (lane < kPage)
+        dma4(4 * lane, sc, lds0 + buf * SB + SBYTES + (wave >= 2 ? 128 : 0) + 64 * half);
+      return;
+    }
     const uint16_t* src =
         (const uint16_t*)((const uint8_t*)tens + (uint64_t)(uint32_t)pg * pbytes);
-    const uint32_t base = lds0 + buf * SBYTES + wave * NIW * 1024;
+    const uint32_t base = lds0 + buf * SB + wave * NIW * 1024;
     for (int ii = 0; ii < NIW; ++ii) dma16(voff[ii], src, base + ii * 1024);
+  };
+
+  // FP8: this wave's block of buffer bc, codes -> the bf16 / fp16 layout the
+  // bf16 pages give, in place (all of a lane's reads come before its
+  // writes; the wave's LDS operations run in order, and only this wave
+  // touches the block).  K: exact bf16 codes, key kr in LDS row
+  // swap23(kr) with swizzled chunks; its scale multiplies the scores.  V:
+  // code * scale rounded to fp16, dim-major.
+  auto widen = [&](int bc) {
+    uint8_t* reg = lds + bc * SB + (wave >= 2 ? KBYTES + half * VPAGE : half * VPAGE);
+    const uint8_t* raw = reg + kPage * D;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recomputed here rather than held across the loop
+    if (wave < 2) {
+      constexpr int CL = D / 4;  // codes per lane: a quarter of key row ln / 4
+      const int kr = ln >> 2, q = ln & 3;
+      u32x4 c[CL / 16];
+      for (int t = 0; t < CL / 16; ++t) c[t] = *(const u32x4*)(raw + kr * D + q * CL + 16 * t);
+      asm volatile("" ::: "memory");  // no write moves above the reads
+      const int rr = ((kr >> 2) & 1) * 8 + ((kr >> 3) & 1) * 4 + (kr & 3);  // its LDS row
+      for (int t = 0; t < CL / 16; ++t)
+        for (int hh = 0; hh < 2; ++hh) {
+          const u32x2 a = e4m3x4_to_bf16x4(c[t][2 * hh]), b = e4m3x4_to_bf16x4(c[t][2 * hh + 1]);
+          const int j = (q * CL + 16 * t + 8 * hh) / 8;  // 16-byte chunk of the bf16 row
+          *(u32x4*)(reg + rr * (CPR * 16) + (j ^ (rr & (CPR - 1))) * 16) =
+              u32x4{a[0], a[1], b[0], b[1]};
+        }
+    } else {
+      constexpr int DL = D / 64;  // dims per lane, 16 codes (keys) each
+      u32x4 c[DL];
+      for (int t = 0; t < DL; ++t) c[t] = *(const u32x4*)(raw + (DL * ln + t) * kPage);
+      const float* vsc = (const float*)(lds + bc * SB + SBYTES + 128 + 64 * half);
+      f32x4 sc[4];
+      for (int x = 0; x < 4; ++x) sc[x] = *(const f32x4*)(vsc + 4 * x);
+      asm volatile("" ::: "memory");
+      for (int t = 0; t < DL; ++t) {
+        uint32_t w[8];  // fp16 pairs of keys 2m, 2m + 1
+        for (int x = 0; x < 4; ++x) {
+          // keys 4x .. 4x + 3 to fp32 (exact), two codes per conversion; the
+          // upper pair is shifted down rather than picked by the word select,
+          // which the compiler drops when the pair is widened like this
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(c[t][x], false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(c[t][x] >> 16, false);
+          w[2 * x] = pack_f16x2(lo[0] * sc[x][0], lo[1] * sc[x][1]);
+          w[2 * x + 1] = pack_f16x2(hi[0] * sc[x][2], hi[1] * sc[x][3]);
+        }
+        uint8_t* row = reg + (DL * ln + t) * (kPage * 2);
+        *(u32x4*)row = u32x4{w[0], w[1], w[2], w[3]};
+        *(u32x4*)(row + 16) = u32x4{w[4], w[5], w[6], w[7]};
+      }
+    }
   };
 
   // One 32-key step of scores, softmax and PV from LDS buffer `buf`.
   auto compute = [&](int buf, int kp0) {
     // does this wave have any unmasked key in the step?
     if (!(wave_on && kp0 <= w_pos_hi && kp0 + 31 >= w_klo)) return;
-    const uint8_t* kb = lds + buf * SBYTES;
+    const uint8_t* kb = lds + buf * SB;
     f32x16 sacc;
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
     for (int c = 0; c < NC; ++c) {
       const int pos = (2 * c + h2) ^ (qr & (CPR - 1));
       bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + qr * (CPR * 16) + pos * 16));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc, 0, 0, 0);
+    }
+    if constexpr (F8) {
+      // each score times its key's K scale (value r = 4j + i is in-page key
+      // 8*h2 + 4(j%2) + i of page j/2); a masked key's NaN scale is masked
+      // with its score below
+      const float* ksc = (const float*)(kb + SBYTES);
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 s = *(const f32x4*)(ksc + kPage * (j >> 1) + 8 * h2 + 4 * (j & 1));
+        for (int i = 0; i < 4; ++i) sacc[4 * j + i] *= s[i];
+      }
     }
     // every key of the step valid for every row of the wave?
     const bool interior = kp0 + 31 <= w_pos_lo && (KIND == 0 || kp0 > w_pos_hi - W);
@@ -277,13 +362,14 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
     const int kp0 = kstart + 32 * s;
     // this wave's part of step s (and, at s = 0, Q) has landed
     if (s + 1 < nsteps)
-      wait_vm_at_most<NIW>();
+      wait_vm_at_most<NWAIT>();
     else
       wait_vm_at_most<0>();
+    if constexpr (F8) widen(bc);
     __syncthreads();         // every part has; step s-1's buffer is free
     if (!(kp0 >= wg_klo && kp0 + 31 <= wg_khi)) {
       // keys of the step outside the workgroup's range: zero their V
-      uint8_t* vz = lds + bc * SBYTES + KBYTES;
+      uint8_t* vz = lds + bc * SB + KBYTES;
       for (int e = tid; e < 2 * D; e += kPreThreads) {  // (page block, dim) rows
         const int key0 = kp0 + 16 * (e / D);
         u32x4* rowp = (u32x4*)(vz + (e / D) * VPAGE + (e % D) * 32);
@@ -378,7 +464,7 @@ prefill_kernel(AttnParams p, int qblocks, int total_tiles) {
   }
 }
 
-template <int D, int KIND, int G>
+template <int D, int KIND, int G, bool F8>
 hipError_t launch_prefill_g(const AttnParams& p, hipStream_t s) {
   constexpr int HPW = G < kPreWaves ? G : kPreWaves;
   constexpr int QB = 32 * (kPreWaves / HPW);
@@ -386,19 +472,24 @@ hipError_t launch_prefill_g(const AttnParams& p, hipStream_t s) {
   const int64_t tiles = (int64_t)p.num_seqs * qblocks * p.hkv * (G / HPW);
   if (tiles > INT32_MAX - 8) return hipErrorInvalidValue;
   const int grid = (int)tiles;
-  hipLaunchKernelGGL((prefill_kernel<D, KIND, G>), dim3(grid), dim3(kPreThreads), 0, s, p,
+  hipLaunchKernelGGL((prefill_kernel<D, KIND, G, F8>), dim3(grid), dim3(kPreThreads), 0, s, p,
                      qblocks, (int)tiles);
   return hipGetLastError();
 }
 
+template <int D, int KIND, bool F8>
+hipError_t launch_prefill_f(const AttnParams& p, hipStream_t s) {
+  switch (p.hq / p.hkv) {
+    case 1: return launch_prefill_g<D, KIND, 1, F8>(p, s);
+    case 2: return launch_prefill_g<D, KIND, 2, F8>(p, s);
+    case 4: return launch_prefill_g<D, KIND, 4, F8>(p, s);
+    default: return launch_prefill_g<D, KIND, 8, F8>(p, s);
+  }
+}
+
 template <int D, int KIND>
 hipError_t launch_prefill_k(const AttnParams& p, hipStream_t s) {
-  switch (p.hq / p.hkv) {
-    case 1: return launch_prefill_g<D, KIND, 1>(p, s);
-    case 2: return launch_prefill_g<D, KIND, 2>(p, s);
-    case 4: return launch_prefill_g<D, KIND, 4>(p, s);
-    default: return launch_prefill_g<D, KIND, 8>(p, s);
-  }
+  return p.kv_fp8 ? launch_prefill_f<D, KIND, true>(p, s) : launch_prefill_f<D, KIND, false>(p, s);
 }
 
 }  // namespace

@@ -84,9 +84,9 @@ typedef enum hswa_layer_kind {
  * token) for K and for V.  A row x of d <= 128 elements is one tile:
  * scale = amax/448, codes of x * (448/amax) rounded to nearest (ties to an
  * even fraction), saturated at 448; the value of a code times the scale is
- * what attention reads.  Appends quantize and decode reads FP8 pages;
- * prefill over FP8 pages is HSWA_E_UNSUPPORTED, and the tier transfer moves
- * BF16 pages only (its buffers hold 16-bit words). */
+ * what attention reads.  Appends quantize, and decode and prefill read FP8
+ * pages; the tier transfer moves BF16 pages only (its buffers hold 16-bit
+ * words). */
 /* Element type of attention outputs.  fp32 keeps the kernels' fp32
  * accumulation; fp16 halves the bytes written (11 significant bits: within
  * 2^-11 relative of the fp32 result, e.g. <= 2e-3 absolute for |o| < 8;
@@ -363,7 +363,10 @@ typedef struct hswa_attn_args {
  * layers); then each row attends to its keys through the page tables.
  * Every needed key must be resident, which holds when the caller allocates
  * the chunk after evicting the previous one.  Output fp32 or fp16
- * (out_dtype). */
+ * (out_dtype).  FP8 pages (kv_dtype HSWA_KV_FP8, k_scale/v_scale set): the
+ * append quantizes the rows, and attention reads K as code values with
+ * each score times its key's K scale, and V as code * scale rounded to
+ * fp16. */
 int hswa_prefill_chunk(const hswa_attn_args* args, void* stream);
 
 /* Decode step of one layer ([MiMo] 1.2).  Without cu_q: one query row per

@@ -400,8 +400,8 @@ def test_fp8_argument_validation():
     assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
     a = _args(kv_dtype=H.HSWA_KV_FP8, k_scale=1 << 20, v_scale=(1 << 20) + 4)  # misaligned
     assert lib.hswa_decode(C.byref(a), None, 0, None) == H.HSWA_E_INVAL
-    a = _args(kv_dtype=H.HSWA_KV_FP8, k_scale=1 << 20, v_scale=1 << 20)
-    assert lib.hswa_prefill_chunk(C.byref(a), None) == H.HSWA_E_UNSUPPORTED
+    a = _args(kv_dtype=H.HSWA_KV_FP8, v_scale=1 << 20)     # prefill: K scales missing
+    assert lib.hswa_prefill_chunk(C.byref(a), None) == H.HSWA_E_INVAL
 
 
 def test_append_without_rows_is_a_noop():

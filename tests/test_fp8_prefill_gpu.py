@@ -10,7 +10,9 @@ bf16 rows (code value x scale).  Pools start with NaN codes (0x7F) and NaN
 scales, and the ring slots of evicted positions are set back to NaN after
 every chunk, so a read of a slot outside a row's keys shows up.  Cases: SWA
 and Full layers, d 64 and 128, 1 to 8 query heads per KV head, chunk starts
-on and off page boundaries, chunks of one row, and a ring of one page.
+on and off page boundaries, chunks of one row, a ring of one page, and 12
+seeded random configurations.  Every finite e4m3 code also comes back
+exactly through the prefill path.
 """
 import numpy as np
 import pytest
@@ -135,3 +137,25 @@ def test_prefill_reads_every_e4m3_code_exactly(gpu, kind):
     got = out.cpu().numpy()[0]
     assert np.array_equal(got.view(np.uint32) & 0x7FFFFFFF, want.view(np.uint32) & 0x7FFFFFFF) \
         and np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+def _random_case(seed):
+    import random
+    rnd = random.Random(7000 + seed)
+    kind = rnd.choice([H.SWA, H.FULL])
+    d = rnd.choice([64, 128])
+    hkv = rnd.choice([1, 2, 4])
+    g = rnd.choice([1, 2, 4, 8])
+    W = rnd.choice([1, 3, 16, 31, 64, 128, 200])
+    chunk = rnd.choice([1, 5, 16, 33, 64, 100])
+    C = 16 * (-(-(W - 1 + chunk) // 16) + rnd.choice([0, 0, 1]))
+    lens = [rnd.randint(1, 260) for _ in range(rnd.randint(1, 3))]
+    return (kind, W, d, g * hkv, hkv, lens, chunk, C)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fp8_chunked_prefill_random_configuration(gpu, seed):
+    """Seeded random shapes: SWA or Full, d, KV heads 1-4, GQA 1-8, windows
+    1-200, chunks 1-100 rows, rings from the smallest that holds W - 1 +
+    chunk (down to one page), 1-3 sequences of 1-260 tokens."""
+    _run(_random_case(seed), 980 + seed)

@@ -486,18 +486,26 @@ def hswa_pool_window_counts(pool: Pool, kind: int, seq_ids: Sequence[int]) -> np
 
 
 def _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache, buf_k, buf_v,
-               first_pos):
-    _expect("k_cache", k_cache, _BF16, (None, None, PAGE_SIZE, None))
+               first_pos, k_scale=None, v_scale=None, buf_k_scale=None, buf_v_scale=None):
+    fp8 = k_scale is not None
+    _expect("k_cache", k_cache, _U8 if fp8 else _BF16, (None, None, PAGE_SIZE, None))
     hkv, d = k_cache.shape[1], k_cache.shape[3]
-    _expect("v_cache", v_cache, _F16, (k_cache.shape[0], hkv, d, PAGE_SIZE))
+    _expect("v_cache", v_cache, _U8 if fp8 else _F16, (k_cache.shape[0], hkv, d, PAGE_SIZE))
+    _expect("k_scale", k_scale, _F32, (k_cache.shape[0], hkv, PAGE_SIZE))
+    _expect("v_scale", v_scale, _F32, (k_cache.shape[0], hkv, PAGE_SIZE))
+    scales = (v_scale, buf_k_scale, buf_v_scale)
+    if any((t is None) == fp8 for t in scales):
+        raise ValueError("FP8 pages need k_scale, v_scale, buf_k_scale and buf_v_scale; "
+                         "BF16 pages none of them")
     _expect("seq_ids", seq_ids, _I32, (None,))
     _expect("cu_tok", cu_tok, _I32, (seq_ids.shape[0] + 1,))
     _expect("first_pos", first_pos, _I32, (seq_ids.shape[0],))
     # the packed buffers may be pinned host memory; the library checks that
-    _expect("buf_k", buf_k, _BF16 + _F16 + ("torch.int16",), (None, hkv, d), total_tok,
-            device=False)
-    _expect("buf_v", buf_v, _BF16 + _F16 + ("torch.int16",), (None, hkv, d), total_tok,
-            device=False)
+    words = _U8 if fp8 else _BF16 + _F16 + ("torch.int16",)
+    _expect("buf_k", buf_k, words, (None, hkv, d), total_tok, device=False)
+    _expect("buf_v", buf_v, words, (None, hkv, d), total_tok, device=False)
+    _expect("buf_k_scale", buf_k_scale, _F32, (None, hkv), total_tok, device=False)
+    _expect("buf_v_scale", buf_v_scale, _F32, (None, hkv), total_tok, device=False)
     a = _capi.XferArgs()
     a.kind = kind
     a.num_kv_heads = k_cache.shape[1]
@@ -513,35 +521,49 @@ def _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache
     a.v_cache = _dptr(v_cache)
     a.buf_k = _dptr(buf_k)
     a.buf_v = _dptr(buf_v)
+    a.kv_dtype = HSWA_KV_FP8 if fp8 else HSWA_KV_BF16
+    a.k_scale, a.v_scale = _dptr(k_scale), _dptr(v_scale)
+    a.buf_k_scale, a.buf_v_scale = _dptr(buf_k_scale), _dptr(buf_v_scale)
     return a
 
 
 def hswa_kv_offload(kind: int, seq_ids, cu_tok, total_tok: int, max_tok: int, view, k_cache,
-                    v_cache, buf_k, buf_v, stream=None, first_pos=None) -> None:
+                    v_cache, buf_k, buf_v, stream=None, first_pos=None, k_scale=None,
+                    v_scale=None, buf_k_scale=None, buf_v_scale=None) -> None:
     """Copies n_i = cu_tok[i+1]-cu_tok[i] positions of each listed sequence
     (from first_pos[i], or its last n_i) from this layer's pages into buf_k
-    (bf16) / buf_v (fp16), [T, Hkv, d], pinned host or device tensors."""
+    (bf16) / buf_v (fp16), [T, Hkv, d], pinned host or device tensors.  FP8
+    pages (k_scale/v_scale given): buf_k/buf_v are uint8 codes [T, Hkv, d]
+    and buf_k_scale/buf_v_scale fp32 [T, Hkv]."""
     a = _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache, buf_k,
-                   buf_v, first_pos)
+                   buf_v, first_pos, k_scale, v_scale, buf_k_scale, buf_v_scale)
     _check(library().hswa_kv_offload(C.byref(a), _stream(stream)))
 
 
 def hswa_kv_restore(kind: int, seq_ids, cu_tok, total_tok: int, max_tok: int, view, k_cache,
-                    v_cache, buf_k, buf_v, stream=None, first_pos=None) -> None:
-    """Writes buf_k/buf_v back into this layer's pages at those positions."""
+                    v_cache, buf_k, buf_v, stream=None, first_pos=None, k_scale=None,
+                    v_scale=None, buf_k_scale=None, buf_v_scale=None) -> None:
+    """Writes buf_k/buf_v (and, for FP8 pages, the scale buffers) back into
+    this layer's pages at those positions."""
     a = _xfer_args(kind, seq_ids, cu_tok, total_tok, max_tok, view, k_cache, v_cache, buf_k,
-                   buf_v, first_pos)
+                   buf_v, first_pos, k_scale, v_scale, buf_k_scale, buf_v_scale)
     _check(library().hswa_kv_restore(C.byref(a), _stream(stream)))
 
 
 def hswa_kv_copy(kind: int, src_ids, dst_ids, first_pos, end_pos, max_tok: int, view, k_cache,
-                 v_cache, stream=None) -> None:
+                 v_cache, stream=None, k_scale=None, v_scale=None) -> None:
     """Copies this layer's K/V of positions [first_pos[i], end_pos[i]) from
     sequence src_ids[i] to dst_ids[i] (device int32 tensors), page to page,
-    e.g. after hswa_pool_fork."""
-    _expect("k_cache", k_cache, _BF16, (None, None, PAGE_SIZE, None))
+    e.g. after hswa_pool_fork.  With ``k_scale``/``v_scale`` the pages are
+    FP8 and each position's scales copy with its codes."""
+    fp8 = k_scale is not None
+    _expect("k_cache", k_cache, _U8 if fp8 else _BF16, (None, None, PAGE_SIZE, None))
     hkv, d = k_cache.shape[1], k_cache.shape[3]
-    _expect("v_cache", v_cache, _F16, (k_cache.shape[0], hkv, d, PAGE_SIZE))
+    _expect("v_cache", v_cache, _U8 if fp8 else _F16, (k_cache.shape[0], hkv, d, PAGE_SIZE))
+    _expect("k_scale", k_scale, _F32, (k_cache.shape[0], hkv, PAGE_SIZE))
+    _expect("v_scale", v_scale, _F32, (k_cache.shape[0], hkv, PAGE_SIZE))
+    if fp8 != (v_scale is not None):
+        raise ValueError("FP8 pages need both k_scale and v_scale")
     for name, t in (("src_ids", src_ids), ("dst_ids", dst_ids), ("first_pos", first_pos),
                     ("end_pos", end_pos)):
         _expect(name, t, _I32, (src_ids.shape[0],))
@@ -553,4 +575,6 @@ def hswa_kv_copy(kind: int, src_ids, dst_ids, first_pos, end_pos, max_tok: int, 
     a.max_tok = max_tok
     a.pool = view
     a.k_cache, a.v_cache = _dptr(k_cache), _dptr(v_cache)
+    a.kv_dtype = HSWA_KV_FP8 if fp8 else HSWA_KV_BF16
+    a.k_scale, a.v_scale = _dptr(k_scale), _dptr(v_scale)
     _check(library().hswa_kv_copy(C.byref(a), _stream(stream)))

@@ -115,6 +115,11 @@ class XferArgs(C.Structure):
         ("v_cache", C.c_void_p),
         ("buf_k", C.c_void_p),
         ("buf_v", C.c_void_p),
+        ("kv_dtype", C.c_int32),
+        ("k_scale", C.c_void_p),
+        ("v_scale", C.c_void_p),
+        ("buf_k_scale", C.c_void_p),
+        ("buf_v_scale", C.c_void_p),
     ]
 
 
@@ -132,6 +137,9 @@ class KvCopyArgs(C.Structure):
         ("pool", PoolView),
         ("k_cache", C.c_void_p),
         ("v_cache", C.c_void_p),
+        ("kv_dtype", C.c_int32),
+        ("k_scale", C.c_void_p),
+        ("v_scale", C.c_void_p),
     ]
 
 

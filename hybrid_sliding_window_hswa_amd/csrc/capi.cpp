@@ -38,6 +38,7 @@ int hip_fail(hipError_t e, const char* what) {
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // Query rows per sequence a decode call takes: one new token plus up to
 // three drafts of a multi-token verification step.
@@ -367,7 +368,7 @@ namespace {
 
 // Address the device uses for a transfer buffer: device memory as is, pinned
 // host memory through its device mapping; anything else is refused.
-int device_view(const void* ptr, const char* what, uint16_t** out) {
+int device_view(const void* ptr, const char* what, void** out) {
   hipPointerAttribute_t at;
   hipError_t e = hipPointerGetAttributes(&at, ptr);
   if (e != hipSuccess) {
@@ -376,7 +377,7 @@ int device_view(const void* ptr, const char* what, uint16_t** out) {
     return HSWA_E_INVAL;
   }
   if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
-    *out = (uint16_t*)ptr;
+    *out = const_cast<void*>(ptr);
     return HSWA_OK;
   }
   if (at.type == hipMemoryTypeHost) {
@@ -387,7 +388,7 @@ int device_view(const void* ptr, const char* what, uint16_t** out) {
       hswa::set_error("%s: pinned host memory without a device mapping", what);
       return HSWA_E_INVAL;
     }
-    *out = (uint16_t*)d;
+    *out = d;
     return HSWA_OK;
   }
   hswa::set_error("%s is neither device memory nor pinned host memory", what);
@@ -437,6 +438,20 @@ int xfer(const hswa_xfer_args* a, bool to_host, void* stream) {
       return HSWA_E_INVAL;
     }
   }
+  if (a->kv_dtype != HSWA_KV_BF16 && a->kv_dtype != HSWA_KV_FP8) {
+    hswa::set_error("kv_dtype must be HSWA_KV_BF16 or HSWA_KV_FP8 (got %d)", a->kv_dtype);
+    return HSWA_E_INVAL;
+  }
+  const bool fp8 = a->kv_dtype == HSWA_KV_FP8;
+  if (fp8 && (!a->k_scale || !a->v_scale || !a->buf_k_scale || !a->buf_v_scale)) {
+    hswa::set_error("FP8 pages need k_scale, v_scale, buf_k_scale and buf_v_scale");
+    return HSWA_E_INVAL;
+  }
+  if (fp8 && (!aligned4(a->k_scale) || !aligned4(a->v_scale) || !aligned4(a->buf_k_scale) ||
+              !aligned4(a->buf_v_scale))) {
+    hswa::set_error("scale buffers must be 4-byte aligned");
+    return HSWA_E_INVAL;
+  }
   hswa::XferParams p{};
   p.kind = a->kind;
   p.hkv = a->num_kv_heads;
@@ -455,10 +470,24 @@ int xfer(const hswa_xfer_args* a, bool to_host, void* stream) {
   p.t.max_pages = v.max_pages_per_seq;
   p.t.ring_slots = v.ring_slots;
   p.t.max_seqs = v.max_seqs;
-  int rc = device_view(a->buf_k, "buf_k", &p.buf_k);
+  void* dv = nullptr;
+  int rc = device_view(a->buf_k, "buf_k", &dv);
   if (rc) return rc;
-  rc = device_view(a->buf_v, "buf_v", &p.buf_v);
+  p.buf_k = (uint16_t*)dv;
+  rc = device_view(a->buf_v, "buf_v", &dv);
   if (rc) return rc;
+  p.buf_v = (uint16_t*)dv;
+  if (fp8) {
+    p.kv_fp8 = true;
+    p.k_scale = (float*)a->k_scale;
+    p.v_scale = (float*)a->v_scale;
+    rc = device_view(a->buf_k_scale, "buf_k_scale", &dv);
+    if (rc) return rc;
+    p.buf_k_scale = (float*)dv;
+    rc = device_view(a->buf_v_scale, "buf_v_scale", &dv);
+    if (rc) return rc;
+    p.buf_v_scale = (float*)dv;
+  }
   hipError_t e = hswa::launch_xfer(p, to_host, (hipStream_t)stream);
   return e == hipSuccess ? HSWA_OK : hswa::hip_fail(e, "transfer launch");
 }
@@ -508,7 +537,23 @@ int hswa_kv_copy(const hswa_kv_copy_args* a, void* stream) {
     hswa::set_error("k_cache and v_cache must be 16-byte aligned");
     return HSWA_E_INVAL;
   }
+  if (a->kv_dtype != HSWA_KV_BF16 && a->kv_dtype != HSWA_KV_FP8) {
+    hswa::set_error("kv_dtype must be HSWA_KV_BF16 or HSWA_KV_FP8 (got %d)", a->kv_dtype);
+    return HSWA_E_INVAL;
+  }
+  const bool fp8 = a->kv_dtype == HSWA_KV_FP8;
+  if (fp8 && (!a->k_scale || !a->v_scale)) {
+    hswa::set_error("FP8 pages need k_scale and v_scale");
+    return HSWA_E_INVAL;
+  }
+  if (fp8 && (!aligned4(a->k_scale) || !aligned4(a->v_scale))) {
+    hswa::set_error("k_scale and v_scale must be 4-byte aligned");
+    return HSWA_E_INVAL;
+  }
   hswa::CopyParams p{};
+  p.kv_fp8 = fp8;
+  p.k_scale = fp8 ? (float*)a->k_scale : nullptr;
+  p.v_scale = fp8 ? (float*)a->v_scale : nullptr;
   p.kind = a->kind;
   p.hkv = a->num_kv_heads;
   p.d = a->head_dim;

@@ -124,6 +124,13 @@ struct XferParams {
   Tables t;
   uint16_t* buf_k;         // device-usable address of the packed buffers
   uint16_t* buf_v;
+  // FP8 pages: codes move as bytes ([token][Hkv][d] in the buffers, V too)
+  // and the fp32 scales of each (token, head) beside them
+  bool kv_fp8;
+  float* k_scale;          // page scales [page][Hkv][16]
+  float* v_scale;
+  float* buf_k_scale;      // device-usable [total_tok][Hkv]
+  float* buf_v_scale;
 };
 
 // Copy of one layer's K/V between two sequences of a pool, page to page.
@@ -139,6 +146,9 @@ struct CopyParams {
   uint16_t* k_cache;
   uint16_t* v_cache;
   Tables t;
+  bool kv_fp8;             // FP8 pages: byte codes plus these fp32 scales
+  float* k_scale;          // [page][Hkv][16]
+  float* v_scale;
 };
 
 hipError_t launch_append(const AttnParams& p, hipStream_t stream);

@@ -329,12 +329,80 @@ __global__ void __launch_bounds__(256) copy_kernel(CopyParams p, int tiles_per_p
   }
 }
 
+// The same copy over FP8 pages: K rows of D code bytes, V columns of 16
+// code bytes (one per token), and each copied token's K and V scale.
+template <int D, int KIND>
+__global__ void __launch_bounds__(256) copy8_kernel(CopyParams p, int tiles_per_pair) {
+  constexpr int CPR = D / 16;  // 16-byte chunks per K row
+  const int i = blockIdx.x / tiles_per_pair;
+  const int t = blockIdx.x % tiles_per_pair;
+  const int a = p.src_ids[i], b = p.dst_ids[i];
+  if (a < 0 || a >= p.t.max_seqs || b < 0 || b >= p.t.max_seqs || a == b) return;
+  const int La = p.t.seq_len[a], Lb = p.t.seq_len[b];
+  int p0 = p.first_pos[i];
+  int p1 = min(p.end_pos[i], min(La, Lb));
+  if (KIND != 0)
+    p0 = max(p0, max(idx::ring_oldest(La, p.t.ring_slots), idx::ring_oldest(Lb, p.t.ring_slots)));
+  p0 = max(p0, 0);
+  if (p1 - p0 > p.max_tok) p1 = p0 + p.max_tok;
+  const int tile_pos = idx::tile_pos(p0, t);
+  if (p0 >= p1 || tile_pos >= p1) return;
+  const int lo = max(tile_pos, p0), hi = min(tile_pos + kPage, p1);
+  const int32_t pa = page_of<KIND>(p.t.fpt, p.t.rpt, a, tile_pos, p.t.max_pages, p.t.ring_slots);
+  const int32_t pb = page_of<KIND>(p.t.fpt, p.t.rpt, b, tile_pos, p.t.max_pages, p.t.ring_slots);
+  if (pa < 0 || pb < 0) return;
+  const int hkv = p.hkv;
+  const int tid = threadIdx.x;
+  const bool whole = lo == tile_pos && hi == tile_pos + kPage;
+  const int64_t bytes = (int64_t)hkv * kPage * D;  // code bytes of one page, K or V
+  const uint8_t* ksrc = (const uint8_t*)p.k_cache + pa * bytes;
+  uint8_t* kdst = (uint8_t*)p.k_cache + pb * bytes;
+  const uint8_t* vsrc = (const uint8_t*)p.v_cache + pa * bytes;
+  uint8_t* vdst = (uint8_t*)p.v_cache + pb * bytes;
+  // K rows: (head, token, chunk)
+  for (int e = tid; e < hkv * kPage * CPR; e += blockDim.x) {
+    const int tok = (e / CPR) % kPage;
+    if (tile_pos + tok < lo || tile_pos + tok >= hi) continue;
+    *(u32x4*)(kdst + (int64_t)e * 16) = *(const u32x4*)(ksrc + (int64_t)e * 16);
+  }
+  // V columns: (head, dim), 16 tokens each
+  for (int e = tid; e < hkv * D; e += blockDim.x) {
+    if (whole) {
+      *(u32x4*)(vdst + (int64_t)e * 16) = *(const u32x4*)(vsrc + (int64_t)e * 16);
+    } else {
+      for (int j = lo - tile_pos; j < hi - tile_pos; ++j)
+        vdst[(int64_t)e * 16 + j] = vsrc[(int64_t)e * 16 + j];
+    }
+  }
+  // scales: (head, token)
+  for (int e = tid; e < hkv * kPage; e += blockDim.x) {
+    const int tok = e % kPage;
+    if (tile_pos + tok < lo || tile_pos + tok >= hi) continue;
+    p.k_scale[((int64_t)pb * hkv) * kPage + e] = p.k_scale[((int64_t)pa * hkv) * kPage + e];
+    p.v_scale[((int64_t)pb * hkv) * kPage + e] = p.v_scale[((int64_t)pa * hkv) * kPage + e];
+  }
+}
+
 hipError_t launch_copy(const CopyParams& p, hipStream_t s) {
   if (p.num_seqs <= 0 || p.max_tok <= 0) return hipSuccess;
   const int tiles = idx::tiles_for(p.max_tok);
   const int64_t blocks = (int64_t)p.num_seqs * tiles;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks);
+  if (p.kv_fp8) {
+    if (p.d == 128) {
+      if (p.kind == 0)
+        hipLaunchKernelGGL((copy8_kernel<128, 0>), grid, dim3(256), 0, s, p, tiles);
+      else
+        hipLaunchKernelGGL((copy8_kernel<128, 1>), grid, dim3(256), 0, s, p, tiles);
+    } else {
+      if (p.kind == 0)
+        hipLaunchKernelGGL((copy8_kernel<64, 0>), grid, dim3(256), 0, s, p, tiles);
+      else
+        hipLaunchKernelGGL((copy8_kernel<64, 1>), grid, dim3(256), 0, s, p, tiles);
+    }
+    return hipGetLastError();
+  }
   if (p.d == 128) {
     if (p.kind == 0)
       hipLaunchKernelGGL((copy_kernel<128, 0>), grid, dim3(256), 0, s, p, tiles);
@@ -461,12 +529,131 @@ __global__ void __launch_bounds__(256) xfer_kernel(XferParams p, int tiles_per_s
   }
 }
 
+// The same transfer over FP8 pages.  The buffers hold code bytes
+// [token][Hkv][d] for K and for V and the fp32 scales [token][Hkv] of each;
+// V goes through LDS between the page's 16-byte token columns and the
+// buffer's rows.
+template <int D, int KIND, bool TO_HOST>
+__global__ void __launch_bounds__(256) xfer8_kernel(XferParams p, int tiles_per_seq) {
+  constexpr int CPR = D / 16;  // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kPage][kXferHeads][D + 16];
+  const int i = blockIdx.x / tiles_per_seq;
+  const int t = blockIdx.x % tiles_per_seq;
+  const int sid = p.seq_ids[i];
+  if (sid < 0 || sid >= p.t.max_seqs) return;
+  const int tok0 = p.cu_tok[i];
+  const int n = p.cu_tok[i + 1] - tok0;
+  const int L = p.t.seq_len[sid];
+  const int p0 = p.first_pos ? p.first_pos[i] : L - n;
+  if (n <= 0 || p0 < 0 || p0 > L - n) return;
+  if (tok0 < 0 || tok0 + n > p.total_tok) return;
+  const int tile_pos = idx::tile_pos(p0, t);
+  if (tile_pos >= p0 + n) return;
+  const int lo = max(max(tile_pos, p0), KIND == 0 ? 0 : idx::ring_oldest(L, p.t.ring_slots));
+  const int hi = min(tile_pos + kPage, p0 + n);
+  if (lo >= hi) return;
+  const int32_t page = page_of<KIND>(p.t.fpt, p.t.rpt, sid, tile_pos, p.t.max_pages,
+                                     p.t.ring_slots);
+  if (page < 0) return;
+  const int hkv = p.hkv;
+  const int tid = threadIdx.x;
+  const int64_t bytes = (int64_t)hkv * kPage * D;  // code bytes of one page, K or V
+  uint8_t* kpg = (uint8_t*)p.k_cache + page * bytes;
+  uint8_t* vpg = (uint8_t*)p.v_cache + page * bytes;
+  uint8_t* bk = (uint8_t*)p.buf_k;
+  uint8_t* bv = (uint8_t*)p.buf_v;
+  // buffer token index of the tile's first position
+  const int64_t b0 = (int64_t)tok0 + tile_pos - p0;
+
+  // K rows: (token, head, chunk)
+  for (int e = tid; e < kPage * hkv * CPR; e += blockDim.x) {
+    const int tok = e / (hkv * CPR);
+    const int h = (e / CPR) % hkv;
+    const int c = e % CPR;
+    const int pos = tile_pos + tok;
+    if (pos < lo || pos >= hi) continue;
+    u32x4* pg = (u32x4*)(kpg + ((int64_t)h * kPage + tok) * D + c * 16);
+    u32x4* bf = (u32x4*)(bk + ((b0 + tok) * hkv + h) * D + c * 16);
+    if (TO_HOST)
+      *bf = *pg;
+    else
+      *pg = *bf;
+  }
+  // scales: (token, head)
+  for (int e = tid; e < kPage * hkv; e += blockDim.x) {
+    const int tok = e / hkv;
+    const int h = e % hkv;
+    const int pos = tile_pos + tok;
+    if (pos < lo || pos >= hi) continue;
+    const int64_t ps = ((int64_t)page * hkv + h) * kPage + tok;
+    const int64_t bs = (b0 + tok) * hkv + h;
+    if (TO_HOST) {
+      p.buf_k_scale[bs] = p.k_scale[ps];
+      p.buf_v_scale[bs] = p.v_scale[ps];
+    } else {
+      p.k_scale[ps] = p.buf_k_scale[bs];
+      p.v_scale[ps] = p.buf_v_scale[bs];
+    }
+  }
+  // V, kXferHeads heads at a time through LDS
+  const bool whole = lo == tile_pos && hi == tile_pos + kPage;
+  for (int h0 = 0; h0 < hkv; h0 += kXferHeads) {
+    const int nh = min(kXferHeads, hkv - h0);
+    if (TO_HOST) {
+      // page column (head, dim e) of 16 tokens -> LDS [token][head][dim]
+      for (int e = tid; e < nh * D; e += blockDim.x) {
+        const int hh = e / D, dim = e % D;
+        const u32x4 w = *(const u32x4*)(vpg + ((int64_t)(h0 + hh) * D + dim) * kPage);
+        for (int j = 0; j < kPage; ++j)
+          vt[j][hh][dim] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+      }
+      __syncthreads();
+      for (int e = tid; e < kPage * nh * CPR; e += blockDim.x) {
+        const int tok = e / (nh * CPR);
+        const int hh = (e / CPR) % nh;
+        const int c = e % CPR;
+        const int pos = tile_pos + tok;
+        if (pos >= lo && pos < hi)
+          *(u32x4*)(bv + ((b0 + tok) * hkv + h0 + hh) * D + c * 16) =
+              *(const u32x4*)(&vt[tok][hh][c * 16]);
+      }
+    } else {
+      for (int e = tid; e < kPage * nh * CPR; e += blockDim.x) {
+        const int tok = e / (nh * CPR);
+        const int hh = (e / CPR) % nh;
+        const int c = e % CPR;
+        const int pos = tile_pos + tok;
+        if (pos >= lo && pos < hi)
+          *(u32x4*)(&vt[tok][hh][c * 16]) =
+              *(const u32x4*)(bv + ((b0 + tok) * hkv + h0 + hh) * D + c * 16);
+      }
+      __syncthreads();
+      for (int e = tid; e < nh * D; e += blockDim.x) {
+        const int hh = e / D, dim = e % D;
+        uint8_t* dst = vpg + ((int64_t)(h0 + hh) * D + dim) * kPage;
+        if (whole) {
+          u32x4 w = {0u, 0u, 0u, 0u};
+          for (int j = 0; j < kPage; ++j) w[j >> 2] |= (uint32_t)vt[j][hh][dim] << (8 * (j & 3));
+          *(u32x4*)dst = w;
+        } else {
+          for (int j = lo - tile_pos; j < hi - tile_pos; ++j) dst[j] = vt[j][hh][dim];
+        }
+      }
+    }
+    __syncthreads();  // LDS free for the next head group
+  }
+}
+
 hipError_t launch_xfer(const XferParams& p, bool to_host, hipStream_t s) {
   if (p.num_seqs <= 0) return hipSuccess;
   const int tiles = idx::tiles_for(p.max_tok);
   dim3 grid((unsigned)(p.num_seqs * tiles));
 #define HSWA_XFER(D_, K_)                                                                   \
-  if (to_host)                                                                              \
+  if (p.kv_fp8 && to_host)                                                                  \
+    hipLaunchKernelGGL((xfer8_kernel<D_, K_, true>), grid, dim3(256), 0, s, p, tiles);      \
+  else if (p.kv_fp8)                                                                        \
+    hipLaunchKernelGGL((xfer8_kernel<D_, K_, false>), grid, dim3(256), 0, s, p, tiles);     \
+  else if (to_host)                                                                         \
     hipLaunchKernelGGL((xfer_kernel<D_, K_, true>), grid, dim3(256), 0, s, p, tiles);       \
   else                                                                                      \
     hipLaunchKernelGGL((xfer_kernel<D_, K_, false>), grid, dim3(256), 0, s, p, tiles);

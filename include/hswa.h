@@ -84,9 +84,9 @@ typedef enum hswa_layer_kind {
  * token) for K and for V.  A row x of d <= 128 elements is one tile:
  * scale = amax/448, codes of x * (448/amax) rounded to nearest (ties to an
  * even fraction), saturated at 448; the value of a code times the scale is
- * what attention reads.  Appends quantize, and decode and prefill read FP8
- * pages; the tier transfer moves BF16 pages only (its buffers hold 16-bit
- * words). */
+ * what attention reads.  Appends quantize, decode and prefill read FP8
+ * pages, and the copy and the tier transfer move their codes and scales
+ * verbatim. */
 /* Element type of attention outputs.  fp32 keeps the kernels' fp32
  * accumulation; fp16 halves the bytes written (11 significant bits: within
  * 2^-11 relative of the fp32 result, e.g. <= 2e-3 absolute for |o| < 8;
@@ -464,13 +464,25 @@ typedef struct hswa_xfer_args {
                                bf16; pinned host memory (hipHostMalloc, or a
                                torch pin_memory tensor) or device memory     */
   void* buf_v;              /* same layout, V as fp16 (the pool's format)    */
+  int32_t kv_dtype;         /* hswa_kv_dtype of the pages; HSWA_KV_FP8: buf_k
+                               and buf_v hold [total_tok][Hkv][head_dim] e4m3
+                               code bytes (V token-major too) ...            */
+  void* k_scale;            /* ... the pages' device fp32 scales
+                               [num_pages][Hkv][16] of K and of V (NULL for
+                               BF16 pages) ...                               */
+  void* v_scale;
+  void* buf_k_scale;        /* ... and [total_tok][Hkv] fp32 scales of K and
+                               of V, pinned host or device memory like the
+                               code buffers; 4-byte aligned                   */
+  void* buf_v_scale;
 } hswa_xfer_args;
 
 /* Offload: copies the listed positions' K/V from the layer's pages into
  * buf_k/buf_v (sequences in the order listed, positions ascending).  The
  * copy is asynchronous on `stream`; read the buffers after it completes.
- * HSWA_E_INVAL for a bad argument or a buffer that is neither device memory
- * nor pinned host memory. */
+ * FP8 pages move their code bytes and each position's K and V scales.
+ * HSWA_E_INVAL for a bad argument (FP8 without all four scale arrays) or a
+ * buffer that is neither device memory nor pinned host memory. */
 int hswa_kv_offload(const hswa_xfer_args* args, void* stream);
 
 /* Restore: writes buf_k/buf_v into the pages at the listed positions' slots
@@ -498,8 +510,12 @@ typedef struct hswa_kv_copy_args {
   int32_t max_tok;          /* ... host hint >= every end_pos - first_pos;
                                SWA: at most ring_slots                        */
   hswa_pool_view pool;      /* from hswa_pool_get_view                        */
-  void* k_cache;            /* this layer's K pages (bf16, layout above)      */
-  void* v_cache;            /* this layer's V pages (fp16)                    */
+  void* k_cache;            /* this layer's K pages (layout above)            */
+  void* v_cache;            /* this layer's V pages                           */
+  int32_t kv_dtype;         /* hswa_kv_dtype of the pages                     */
+  void* k_scale;            /* HSWA_KV_FP8: device fp32 [num_pages][Hkv][16]  */
+  void* v_scale;            /* scales of K and V, copied with the codes; else
+                               NULL                                          */
 } hswa_kv_copy_args;
 
 /* Copies, for every listed pair, the K and V of positions [first_pos,
@@ -510,8 +526,9 @@ typedef struct hswa_kv_copy_args {
  * SWA layers, positions older than length - ring_slots of either sequence
  * (their slots hold newer positions); a pair with equal ids copies nothing.
  * Asynchronous on `stream`, ordered after the hswa_pool_fork that gave the
- * destination its slots.  HSWA_E_INVAL for a bad argument or an SWA max_tok
- * above ring_slots; BF16 pages only. */
+ * destination its slots.  FP8 pages copy each position's codes and its K
+ * and V scales.  HSWA_E_INVAL for a bad argument (FP8 without both scale
+ * arrays) or an SWA max_tok above ring_slots. */
 int hswa_kv_copy(const hswa_kv_copy_args* args, void* stream);
 
 #ifdef __cplusplus

@@ -19,12 +19,19 @@ Readings taken where the pages leave a step open:
   ascending, each token [Hkv][d] for K and for V.  It holds what the pool
   holds: K as the bf16 input, V as the fp16 value of the bf16 input (the
   pool's V format), so a restore puts back the same bits.
+* FP8 pages (Baidu Day0 hybrid-attention article, Layered quantization,
+  point 2) cross the link as they are stored: each token's e4m3 codes
+  [Hkv][d] for K and for V (V token-major like K) and its fp32 scale per
+  (token, head) for each, so the same mask moves 2 bytes per element plus
+  8 bytes per (token, head).
 """
 from __future__ import annotations
 
 from typing import Iterable, List, Sequence, Tuple
 
 import numpy as np
+
+from oracle import fp8
 
 FULL = 0
 SWA = 1
@@ -52,6 +59,13 @@ def transfer_bytes(kind: int, lengths: Sequence[int], window: int, hkv: int, d: 
     return sum(transfer_counts(kind, lengths, window)) * hkv * d * 4
 
 
+def transfer_bytes_fp8(kind: int, lengths: Sequence[int], window: int, hkv: int,
+                       d: int) -> int:
+    """Bytes a window-masked transfer of FP8 pages moves: a code byte of K
+    and of V per element, and an fp32 K and V scale per (token, head)."""
+    return sum(transfer_counts(kind, lengths, window)) * hkv * (2 * d + 8)
+
+
 def host_image(kind: int, window: int, seqs: Iterable[Tuple[np.ndarray, np.ndarray]]):
     """Packed host buffers a transfer of these sequences holds.
 
@@ -72,3 +86,28 @@ def host_image(kind: int, window: int, seqs: Iterable[Tuple[np.ndarray, np.ndarr
     if not ks:
         return np.zeros((0,), np.uint16), np.zeros((0,), np.uint16)
     return np.concatenate(ks), np.concatenate(vs)
+
+
+def host_image_fp8(kind: int, window: int, seqs: Iterable[Tuple[np.ndarray, np.ndarray]]):
+    """Packed buffers a transfer of FP8 pages holds.
+
+    seqs yields, per sequence in listed order, (k, v): the full inputs
+    [L, Hkv, d] as fp32 values (bf16 inputs convert exactly).  Each moved
+    token holds what the quantizing append stored for it (one tile per
+    (token, head) row).  Returns (codes_k, codes_v) uint8 [tokens, Hkv, d]
+    and (scale_k, scale_v) float32 [tokens, Hkv].
+    """
+    out = [[], [], [], []]
+    for k, v in seqs:
+        k = np.asarray(k, dtype=np.float32)
+        v = np.asarray(v, dtype=np.float32)
+        pos = transfer_positions(kind, k.shape[0], window)
+        sel = slice(pos.start, pos.stop)
+        ck, sk = fp8.quantize_rows(k[sel])
+        cv, sv = fp8.quantize_rows(v[sel])
+        for lst, x in zip(out, (ck, cv, sk, sv)):
+            lst.append(x)
+    if not out[0]:
+        return (np.zeros((0,), np.uint8), np.zeros((0,), np.uint8),
+                np.zeros((0,), np.float32), np.zeros((0,), np.float32))
+    return tuple(np.concatenate(lst) for lst in out)

@@ -467,3 +467,48 @@ def test_kv_copy_validation():
     a.head_dim, a.num_seqs = 128, 0
     assert lib.hswa_kv_copy(C.byref(a), None) == H.HSWA_OK         # nothing to copy
     assert lib.hswa_kv_copy(None, None) == H.HSWA_E_INVAL
+
+
+def _fake_view(a):
+    fake = 1 << 20  # never dereferenced: every case below fails validation
+    a.pool.seq_len = a.pool.fpt = a.pool.rpt = a.pool.map = fake
+    a.pool.max_seqs, a.pool.max_pages_per_seq = 4, 4
+    a.pool.ring_slots, a.pool.window = 32, 16
+    return fake
+
+
+def test_fp8_copy_and_transfer_validation():
+    """FP8 pages need their scale arrays (copy: K and V page scales;
+    transfer: those and the buffers' scales), aligned to 4 bytes, and
+    kv_dtype must name a format; each is E_INVAL before any launch."""
+    from hybrid_sliding_window_hswa_amd import _capi
+    lib = _capi.load()
+    a = _capi.KvCopyArgs()
+    a.kind, a.num_kv_heads, a.head_dim, a.num_seqs, a.max_tok = 1, 2, 128, 1, 16
+    fake = _fake_view(a)
+    a.src_ids = a.dst_ids = a.first_pos = a.end_pos = a.k_cache = a.v_cache = fake
+    a.kv_dtype = 7
+    assert lib.hswa_kv_copy(C.byref(a), None) == H.HSWA_E_INVAL
+    assert "kv_dtype" in H.hswa_last_error()
+    a.kv_dtype, a.k_scale = H.HSWA_KV_FP8, fake
+    assert lib.hswa_kv_copy(C.byref(a), None) == H.HSWA_E_INVAL     # V scales missing
+    assert "scale" in H.hswa_last_error()
+    a.v_scale = fake + 2
+    assert lib.hswa_kv_copy(C.byref(a), None) == H.HSWA_E_INVAL     # misaligned
+    assert "aligned" in H.hswa_last_error()
+
+    x = _capi.XferArgs()
+    x.kind, x.num_kv_heads, x.head_dim, x.num_seqs = 1, 2, 128, 1
+    x.total_tok, x.max_tok = 16, 16
+    fake = _fake_view(x)
+    x.seq_ids = x.cu_tok = x.k_cache = x.v_cache = x.buf_k = x.buf_v = fake
+    x.kv_dtype = -1
+    assert lib.hswa_kv_offload(C.byref(x), None) == H.HSWA_E_INVAL
+    assert "kv_dtype" in H.hswa_last_error()
+    x.kv_dtype, x.k_scale, x.v_scale = H.HSWA_KV_FP8, fake, fake
+    for fn in (lib.hswa_kv_offload, lib.hswa_kv_restore):
+        assert fn(C.byref(x), None) == H.HSWA_E_INVAL               # buffer scales missing
+        assert "buf_k_scale" in H.hswa_last_error()
+    x.buf_k_scale, x.buf_v_scale = fake, fake + 1
+    assert lib.hswa_kv_restore(C.byref(x), None) == H.HSWA_E_INVAL  # misaligned
+    assert "aligned" in H.hswa_last_error()

@@ -186,6 +186,15 @@ CASES = [
     ("v_left_in_bf16", "test_oracle_transfer",
      "vs.append(v32.astype(np.float16).view(np.uint16))", "vs.append(v[sel])",
      [("test_v_conversion_matches_binary16_definition", {})]),
+    ("fp8_bytes_without_scales", "test_oracle_transfer",
+     "* hkv * (2 * d + 8)", "* hkv * 2 * d",
+     [("test_fp8_byte_counts_closed_form", {})]),
+    ("fp8_v_quantized_from_k", "test_oracle_transfer",
+     "cv, sv = fp8.quantize_rows(v[sel])", "cv, sv = fp8.quantize_rows(k[sel])",
+     [("test_host_image_fp8_packs_windows_in_order", {})]),
+    ("fp8_image_whole_sequence", "test_oracle_transfer",
+     "ck, sk = fp8.quantize_rows(k[sel])", "ck, sk = fp8.quantize_rows(k[:len(pos)])",
+     [("test_host_image_fp8_packs_windows_in_order", {})]),
     ("sequences_packed_in_reverse", "test_oracle_transfer",
      "return np.concatenate(ks), np.concatenate(vs)",
      "return np.concatenate(ks[::-1]), np.concatenate(vs[::-1])",

@@ -8,6 +8,11 @@
 * The V format conversion (bf16 -> fp16, round to nearest even) against an
   fp16 encoder written from the IEEE 754 binary16 definition, including
   subnormal results and exact ties.
+* FP8 pages: byte counts against the closed form (2 code bytes per element
+  plus 8 scale bytes per (token, head)); the packed codes times their scales
+  give back every moved input within the e4m3 rounding bound (half a unit
+  of the 3-bit fraction, or half the subnormal step 2^-9 of the tile's
+  scale), K from K and V from V, in sequence and position order.
 """
 import math
 import random
@@ -107,3 +112,38 @@ def test_host_image_packs_windows_in_order():
     assert np.array_equal(hk, np.concatenate([a[7:10], b[0:3]]))
     hk, _ = T.host_image(T.FULL, 4, [(a, a), (b, b)])
     assert np.array_equal(hk, np.concatenate([a, b]))
+
+
+def test_fp8_byte_counts_closed_form():
+    lens = [0, 1, 5, 127, 128, 129, 4096]
+    W, hkv = 128, 8
+    for d in (64, 128):
+        per_tok = hkv * d * 2 + hkv * 8
+        assert T.transfer_bytes_fp8(T.SWA, lens, W, hkv, d) == \
+            sum(min(L, 127) for L in lens) * per_tok
+        assert T.transfer_bytes_fp8(T.FULL, lens, W, hkv, d) == sum(lens) * per_tok
+
+
+def test_host_image_fp8_packs_windows_in_order():
+    rng = np.random.default_rng(3)
+    lens, W, hkv, d = [10, 3, 0, 25], 4, 2, 16
+    ks = [rng.standard_normal((L, hkv, d)).astype(np.float32) for L in lens]
+    vs = [(3 * rng.standard_normal((L, hkv, d))).astype(np.float32) for L in lens]
+    for kind in (T.FULL, T.SWA):
+        ck, cv, sk, sv = T.host_image_fp8(kind, W, zip(ks, vs))
+        sel = [T.transfer_positions(kind, L, W) for L in lens]
+        want_k = np.concatenate([k[r.start:r.stop] for k, r in zip(ks, sel)])
+        want_v = np.concatenate([v[r.start:r.stop] for v, r in zip(vs, sel)])
+        n = sum(len(r) for r in sel)
+        assert ck.shape == cv.shape == (n, hkv, d) and sk.shape == sv.shape == (n, hkv)
+        for codes, scale, want in ((ck, sk, want_k), (cv, sv, want_v)):
+            # e4m3 value of each code: sign, 4-bit exponent (bias 7), 3-bit
+            # fraction; exponent field 0 is subnormal, units of 2^-9
+            c = codes.astype(np.int64)
+            e, f = (c >> 3) & 15, c & 7
+            mag = np.where(e == 0, f * 2.0 ** -9, (1 + f / 8) * 2.0 ** (e - 7))
+            got = np.where(c & 0x80, -mag, mag) * scale[..., None].astype(np.float64)
+            bound = np.abs(want) * 2.0 ** -4 + scale[..., None] * 2.0 ** -10
+            assert np.all(np.abs(got - want) <= bound * (1 + 1e-6) + 1e-30), kind
+            # the largest element of each row maps to the largest code
+            assert np.all(np.max(mag, axis=-1) == 448.0), kind

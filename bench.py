@@ -48,6 +48,10 @@ resident in HBM before the timed region starts):
       layers move only their W-1-token windows.  `value` = restore GB/s over
       PCIe; also offload GB/s and restore + first decode step, serial versus
       pulled layer by layer on a second stream.
+  tier_transfer_fp8
+      tier_transfer over FP8 pages: the buffers hold code bytes and the fp32
+      scale of each (token, head), 2 * Hkv * (d + 4) bytes per token instead
+      of 4 * Hkv * d.  `value` = restore GB/s of those bytes.
   swa_single_chunk
       One SWA layer, one 1024-token sequence (8 query / 2 KV heads, head_dim
       64) prefilled in one chunk, then 16 decode steps.  `value` = tok/s.
@@ -1022,10 +1026,11 @@ def wl_mtp_decode(cx, args):
     return line
 
 
-def wl_tier_transfer(cx, args):
+def wl_tier_transfer(cx, args, fp8=False):
     """Window-masked offload/restore of a 14-layer hybrid stack through pinned
     host memory, and restore + first decode step, serial and pulled layer by
-    layer on a second stream."""
+    layer on a second stream.  fp8: the pages are FP8, and the buffers hold
+    code bytes and per-(token, head) fp32 scales."""
     import synth
     from hybrid_sliding_window_hswa_amd import _capi
     torch, H, lib = cx.torch, cx.H, cx.lib
@@ -1033,8 +1038,9 @@ def wl_tier_transfer(cx, args):
     ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
     hq, hkv, d, W = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window
     B, ids = len(ctxs), list(range(len(ctxs)))
-    src = Decode(cx, ctxs, wl.pattern, hq, hkv, d, W, wl.ring_slots, wl.seed, 8)
-    dst = Decode(cx, ctxs, wl.pattern, hq, hkv, d, W, wl.ring_slots, wl.seed + 1, 8, fill=False)
+    src = Decode(cx, ctxs, wl.pattern, hq, hkv, d, W, wl.ring_slots, wl.seed, 8, fp8=fp8)
+    dst = Decode(cx, ctxs, wl.pattern, hq, hkv, d, W, wl.ring_slots, wl.seed + 1, 8, fill=False,
+                 fp8=fp8)
     plan = {}
     for kind in (H.FULL, H.SWA):
         cnt = [int(x) for x in H.hswa_pool_window_counts(src.pool, kind, ids)]
@@ -1044,9 +1050,16 @@ def wl_tier_transfer(cx, args):
     for li, (kind, kc, vc) in enumerate(src.layers):
         cnt, cu, first = plan[kind]
         T = sum(cnt)
-        bk = torch.empty((T, hkv, d), dtype=torch.bfloat16, pin_memory=True)
-        bv = torch.empty((T, hkv, d), dtype=torch.float16, pin_memory=True)
-        bufs.append((bk, bv))
+        if fp8:
+            bk = torch.empty((T, hkv, d), dtype=torch.uint8, pin_memory=True)
+            bv = torch.empty((T, hkv, d), dtype=torch.uint8, pin_memory=True)
+            bks = torch.empty((T, hkv), dtype=torch.float32, pin_memory=True)
+            bvs = torch.empty((T, hkv), dtype=torch.float32, pin_memory=True)
+        else:
+            bk = torch.empty((T, hkv, d), dtype=torch.bfloat16, pin_memory=True)
+            bv = torch.empty((T, hkv, d), dtype=torch.float16, pin_memory=True)
+            bks = bvs = None
+        bufs.append((bk, bv, bks, bvs))
         for dc, lst in ((src, a_off), (dst, a_res)):
             a = _capi.XferArgs()
             a.kind, a.num_kv_heads, a.head_dim, a.num_seqs = kind, hkv, d, B
@@ -1055,8 +1068,14 @@ def wl_tier_transfer(cx, args):
             a.pool = dc.view
             a.k_cache, a.v_cache = dc.layers[li][1].data_ptr(), dc.layers[li][2].data_ptr()
             a.buf_k, a.buf_v = bk.data_ptr(), bv.data_ptr()
+            if fp8:
+                a.kv_dtype = H.HSWA_KV_FP8
+                a.k_scale = dc.scales[li][0].data_ptr()
+                a.v_scale = dc.scales[li][1].data_ptr()
+                a.buf_k_scale, a.buf_v_scale = bks.data_ptr(), bvs.data_ptr()
             lst.append(a)
-    kvb = KV_TOKEN_BYTES(hkv, d)
+    # bytes per moved token: codes and scales of K and V for FP8 pages
+    kvb = 2 * hkv * (d + 4) if fp8 else KV_TOKEN_BYTES(hkv, d)
     masked = sum(sum(plan[kind][0]) for kind, _, _ in src.layers) * kvb
     unmasked = len(src.layers) * sum(ctxs) * kvb
     swa_bytes = sum(sum(plan[kind][0]) for kind, _, _ in src.layers if kind == H.SWA) * kvb
@@ -1122,13 +1141,21 @@ def wl_tier_transfer(cx, args):
     t_pull = timed(cx, pulled, steps, warm)
     torch.cuda.synchronize()
     res_gbs = masked / t_res / 1e9
-    config = {"workload": "tier_transfer", "num_seqs": B, "ctx_range": [wl.ctx_lo, wl.ctx_hi],
+    config = {"workload": "tier_transfer_fp8" if fp8 else "tier_transfer", "num_seqs": B,
+              "ctx_range": [wl.ctx_lo, wl.ctx_hi],
               "layers": len(wl.pattern), "pattern": "6 SWA then 1 Full, x2",
               "num_kv_heads": hkv, "head_dim": d, "window": W, "host_buffers": "pinned",
+              "kv_dtype": "fp8 e4m3, fp32 scale per token and head" if fp8 else "bf16/fp16",
               "seed": wl.seed}
     line = base_line(args, round(res_gbs, 2), "GB/s", t_res * 1e3, config,
                      roofline("pcie", res_gbs, None))
     line["steps"] = steps
+    if fp8:
+        line["dtype"] = "fp8 K/V, bf16/fp16 MFMA"
+        line["precision"] = dict(line["precision"],
+                                 k_pages="e4m3 + fp32 scale per token and head",
+                                 v_pages="e4m3 + fp32 scale per token and head",
+                                 host_buffers="e4m3 codes + fp32 scales, moved verbatim")
     line["offload_gbs"] = round(masked / t_off / 1e9, 2)
     line["offload_ms"] = round(t_off * 1e3, 3)
     line["restore_full_layer_gbs"] = round(per_kind[H.FULL][0] / per_kind[H.FULL][1] / 1e9, 2)
@@ -1336,6 +1363,7 @@ WORKLOADS = {
     "swa_chunked_prefill_fp8": wl_swa_chunked_prefill_fp8,
     "mtp_decode": wl_mtp_decode,
     "tier_transfer": wl_tier_transfer,
+    "tier_transfer_fp8": lambda cx, args: wl_tier_transfer(cx, args, fp8=True),
     "hybrid_stack": wl_hybrid_stack,
     "long_decode": wl_long_decode,
     "swa_single_chunk": wl_swa_single_chunk,

@@ -17,6 +17,8 @@ prefix).
   both ends, a whole tile, ranges cut by either sequence's length or ring,
   a pair with equal ids), the destination slots of the copied positions
   hold the source's bits and every other byte of the layer is unchanged.
+* Seeded random configurations of both (KV heads 1-12, d 64 and 128,
+  windows 1-200, rings from one page up).
 """
 import numpy as np
 import pytest
@@ -87,20 +89,17 @@ def test_fp8_offload_matches_oracle_image(gpu, pinned, d, hkv):
         assert np.array_equal(_u32(bufs[3][:T]), sv.view(np.uint32)), kind
 
 
-def test_fp8_round_trip_into_other_pages(gpu):
-    lens = [1500, 90, 3, 128, 4100]
-    hq, hkv, d, W = 64, 8, 128, 128
-    k, v = _contexts(lens, hkv, d, 33)
-    src = Fp8Pool(lens, hkv, d, W, 11)
-    src.append_context(k, v, lens)
-    dst = Fp8Pool(lens, hkv, d, W, 12)        # other page orders; codes 0x7F, NaN scales
-    sentinel = {kind: [t.clone() for t in dst.bufs(kind)] for kind in (H.FULL, H.SWA)}
+def _round_trip(src, dst, lens, W, pinned=True):
+    """Offload every layer kind of src and restore it into dst (its own page
+    orders): dst's restored slots hold src's codes and scales bit for bit,
+    every other byte of dst keeps what it held."""
+    sentinel = {kind: [t.cpu() for t in dst.bufs(kind)] for kind in (H.FULL, H.SWA)}
     for kind in (H.FULL, H.SWA):
-        bufs, _ = _move(src, kind, lens, True)
+        bufs, _ = _move(src, kind, lens, True, pinned=pinned)
         _move(dst, kind, lens, False, bufs=bufs, explicit=True)
         s_all = [t.cpu() for t in src.bufs(kind)]
         d_all = [t.cpu() for t in dst.bufs(kind)]
-        want = [t.cpu() for t in sentinel[kind]]
+        want = sentinel[kind]
         for b, L in enumerate(lens):
             for pos in OT.transfer_positions(kind, L, W):
                 a, c = src.slot(kind, b, pos), dst.slot(kind, b, pos)
@@ -114,6 +113,16 @@ def test_fp8_round_trip_into_other_pages(gpu):
             if g.dtype == np.float32:
                 g, w = g.view(np.uint32), w.view(np.uint32)
             assert np.array_equal(g, w), (kind, i)
+
+
+def test_fp8_round_trip_into_other_pages(gpu):
+    lens = [1500, 90, 3, 128, 4100]
+    hq, hkv, d, W = 64, 8, 128, 128
+    k, v = _contexts(lens, hkv, d, 33)
+    src = Fp8Pool(lens, hkv, d, W, 11)
+    src.append_context(k, v, lens)
+    dst = Fp8Pool(lens, hkv, d, W, 12)        # other page orders; codes 0x7F, NaN scales
+    _round_trip(src, dst, lens, W)
     # decode one new token over both pools: identical outputs, oracle-close
     B = len(lens)
     q = synth.bf16_normal((B, hq, d), 33, 5, 0, synth.ROLE_Q)
@@ -147,6 +156,36 @@ def test_fp8_round_trip_into_other_pages(gpu):
             exp = OA.attend(synth.to_f64(q[b:b + 1]), [L], kk, vv, kind, W)
             err = float(np.max(np.abs(got[b:b + 1].double().numpy() - exp)))
             assert err < TOL, (kind, b, err)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_fp8_transfer_random_configuration(gpu, case):
+    """Seeded random shapes: KV heads 1-12, d, window 1-200 (rings down to
+    one page), 1-6 sequences of 0-2,000 tokens, pinned or device buffers.
+    The packed image of both layer kinds equals the oracle's bit for bit,
+    and restoring it into a pool with other page orders puts back the same
+    bits and nothing else."""
+    import random
+    rnd = random.Random(9700 + case)
+    hkv, d = rnd.choice([1, 2, 3, 8, 12]), rnd.choice([64, 128])
+    W = rnd.choice([1, 2, 5, 16, 33, 128, 200])
+    lens = [rnd.randint(0, 2000) for _ in range(rnd.randint(1, 6))]
+    pinned = rnd.random() < 0.5
+    print(f"case {case}: hkv {hkv} d {d} W {W} lens {lens} pinned {pinned}", flush=True)
+    k, v = _contexts(lens, hkv, d, 830 + case)
+    src = Fp8Pool(lens, hkv, d, W, 40 + case)
+    src.append_context(k, v, lens)
+    for kind in (H.FULL, H.SWA):
+        bufs, cnt = _move(src, kind, lens, True, pinned=pinned)
+        assert cnt == OT.transfer_counts(kind, lens, W)
+        ck, cv, sk, sv = OT.host_image_fp8(kind, W, [(k[b].float().numpy(), v[b].float().numpy())
+                                                     for b in src.ids])
+        T = sum(cnt)
+        assert np.array_equal(bufs[0][:T].cpu().numpy().reshape(-1), ck.reshape(-1)), kind
+        assert np.array_equal(bufs[1][:T].cpu().numpy().reshape(-1), cv.reshape(-1)), kind
+        assert np.array_equal(_u32(bufs[2][:T]).reshape(-1), sk.view(np.uint32).reshape(-1))
+        assert np.array_equal(_u32(bufs[3][:T]).reshape(-1), sv.view(np.uint32).reshape(-1))
+    _round_trip(src, Fp8Pool(lens, hkv, d, W, 60 + case), lens, W, pinned)
 
 
 def test_fp8_transfer_rejects_missing_buffer_scales(gpu):
@@ -186,6 +225,8 @@ class CopyPool:
         for kind, bufs in self.layers.items():
             cnt = H.hswa_pool_window_counts(self.pool, kind, ids).tolist()
             live = [b for b in ids if cnt[b] > 0]
+            if not live:                 # W = 1: no SWA layer rows to append
+                continue
             cu = torch.tensor(np.concatenate([[0], np.cumsum([cnt[b] for b in live])]),
                               dtype=torch.int32, device=dev())
             sc = dict(k_scale=bufs[2], v_scale=bufs[3]) if fp8 else {}
@@ -217,12 +258,44 @@ def test_copy_moves_exactly_the_listed_positions(gpu, fp8, d, hkv):
     lens = [300, 77, 45, 260, 100, 45, 20]
     # (source, destination, first, end)
     pairs = [(0, 3, 37, 290), (1, 4, 0, 500), (2, 5, 16, 32), (6, 6, 0, 20)]
-    P = CopyPool(lens, hkv, d, W, C, 70 + d + hkv, fp8)
+    _check_copy(lens, pairs, hkv, d, W, C, 70 + d + hkv, fp8)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_copy_random_configuration(gpu, case):
+    """Seeded random copies: FP8 or BF16 pages, KV heads 1-8, d, windows
+    1-200 with rings of the window or up to three pages more, 2-4 disjoint
+    pairs whose destination is about as long as the source, with ranges
+    from 0, from the window start, from inside the ring or anywhere, to
+    the shared end, past it, or a few positions on (some empty)."""
+    import random
+    rnd = random.Random(9900 + case)
+    fp8 = case % 2 == 0
+    hkv, d = rnd.choice([1, 2, 3, 8]), rnd.choice([64, 128])
+    W = rnd.choice([1, 2, 5, 16, 33, 128, 200])
+    C = 16 * (-(-W // 16) + rnd.choice([0, 0, 1, 3]))
+    n = rnd.randint(2, 4)
+    src = [rnd.randint(1, 700) for _ in range(n)]
+    dst = [max(1, L + rnd.choice([-20, 0, 0, 5, 100])) for L in src]
+    lens = src + dst
+    pairs = []
+    for i in range(n):
+        m = min(src[i], dst[i])
+        first = rnd.choice([0, max(0, m - W + 1), max(0, m - rnd.randint(1, C)),
+                            rnd.randint(0, m)])
+        end = rnd.choice([m, m + 50, first + rnd.choice([0, 1, 15, 16, 17])])
+        pairs.append((i, n + i, first, end))
+    print(f"case {case}: fp8 {fp8} hkv {hkv} d {d} W {W} C {C} lens {lens} pairs {pairs}",
+          flush=True)
+    _check_copy(lens, pairs, hkv, d, W, C, 90 + case, fp8)
+
+
+def _check_copy(lens, pairs, hkv, d, W, C, seed, fp8):
+    P = CopyPool(lens, hkv, d, W, C, seed, fp8)
     i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=dev())
     for kind, bufs in P.layers.items():
         before = [t.cpu().clone() for t in bufs]
         want = [t.clone() for t in before]
-        longest = 0
         for a, b, first, end in pairs:
             if a == b:
                 continue
@@ -231,7 +304,6 @@ def test_copy_moves_exactly_the_listed_positions(gpu, fp8, d, hkv):
             if kind == H.SWA:
                 p0 = max(p0, lens[a] - C, lens[b] - C)
             p0 = max(p0, 0)
-            longest = max(longest, p1 - p0)
             for pos in range(p0, p1):
                 s, t = P.slot(kind, a, pos), P.slot(kind, b, pos)
                 for i, x in enumerate(want):
@@ -239,9 +311,8 @@ def test_copy_moves_exactly_the_listed_positions(gpu, fp8, d, hkv):
                         x[t // 16, :, :, t % 16] = before[i][s // 16, :, :, s % 16]
                     else:
                         x[t // 16, :, t % 16] = before[i][s // 16, :, s % 16]
-        assert longest > 0
         cols = list(zip(*pairs))
-        max_tok = C if kind == H.SWA else max(e - f for _, _, f, e in pairs)
+        max_tok = C if kind == H.SWA else max(1, max(e - f for _, _, f, e in pairs))
         sc = dict(k_scale=bufs[2], v_scale=bufs[3]) if fp8 else {}
         H.hswa_kv_copy(kind, i32(cols[0]), i32(cols[1]), i32(cols[2]), i32(cols[3]), max_tok,
                        P.view, bufs[0], bufs[1], **sc)

@@ -51,7 +51,7 @@ class Setup:
     """A pool with device tables plus one layer's K/V buffers."""
 
     def __init__(self, kind, window, ring_slots, max_seqs, max_pages, num_full_pages, hkv, d,
-                 seed, poison=True):
+                 seed, poison=True, fp8=False):
         self.kind, self.W, self.C = kind, window, ring_slots
         self.hkv, self.d = hkv, d
         free = synth.permutation(num_full_pages, seed, 1)
@@ -60,9 +60,22 @@ class Setup:
                                        free, ring, device=dev())
         self.view = H.hswa_pool_get_view(self.pool)
         npages = num_full_pages if kind == H.FULL else max_seqs * ring_slots // 16
-        self.kc, self.vc = H.kv_cache_alloc(npages, hkv, d, dev(),
-                                            float("nan") if poison else 0.0)
+        self.fp8 = fp8
+        if fp8:   # codes 0x7F (NaN) and NaN scales, or zeros
+            self.kc, self.vc, self.ks, self.vs = H.kv_cache_alloc_fp8(
+                npages, hkv, d, dev(), 0x7F if poison else 0)
+            if not poison:
+                self.ks.zero_()
+                self.vs.zero_()
+        else:
+            self.kc, self.vc = H.kv_cache_alloc(npages, hkv, d, dev(),
+                                                float("nan") if poison else 0.0)
+            self.ks = self.vs = None
         self.ring_pages = ring.reshape(max_seqs, ring_slots // 16)
+
+    def scales(self):
+        """Keyword arguments naming the FP8 scale arrays (none for BF16)."""
+        return dict(k_scale=self.ks, v_scale=self.vs) if self.fp8 else {}
 
     def poison_ring_positions(self, b, positions):
         """NaN into the ring slots of positions that just left the window."""
@@ -71,8 +84,14 @@ class Setup:
         r = np.asarray(positions) % self.C
         pages = torch.as_tensor(self.ring_pages[b][r // 16].astype(np.int64), device=dev())
         offs = torch.as_tensor((r % 16).astype(np.int64), device=dev())
-        self.kc[pages, :, offs, :] = float("nan")
-        self.vc[pages, :, :, offs] = float("nan")
+        if self.fp8:
+            self.kc[pages, :, offs, :] = 0x7F
+            self.vc[pages, :, :, offs] = 0x7F
+            self.ks[pages, :, offs] = float("nan")
+            self.vs[pages, :, offs] = float("nan")
+        else:
+            self.kc[pages, :, offs, :] = float("nan")
+            self.vc[pages, :, :, offs] = float("nan")
 
 
 def chunked_prefill(setup: Setup, seqs: List[SeqData], chunk: int, hq: int,

@@ -8,7 +8,8 @@ window halo ends, the longest and shortest sequences, and seeded random
 rows.  Pool results are checked in full: the slots handed out and the
 eviction sets against the oracle's pool simulator (prefill) or against the
 slot formulas applied to the slots the pool returned (decode), and every
-valid-window length the kernels report.
+valid-window length the kernels report.  The chunked prefill also runs over
+FP8 pages, against the oracle on the dequantized K/V.
 """
 import numpy as np
 import pytest
@@ -17,6 +18,7 @@ import torch
 import hybrid_sliding_window_hswa_amd as H
 import synth
 from oracle import attention as OA
+from oracle import fp8 as F8
 from oracle.pool import PoolSim
 
 from harness import TOL, Setup, dev
@@ -30,15 +32,29 @@ def _draw(shape, seed, layer, b, role):
 
 class _Host:
     """fp64 copies of one sequence's K/V rows from position `lo` on (moved
-    from the device once)."""
+    from the device once); with fp8, the values FP8 pages hold for them (the
+    oracle's quantization, code times scale)."""
 
-    def __init__(self, k, v, lo=0):
-        self.k, self.v, self.lo = synth.to_f64(k), synth.to_f64(v), lo
+    def __init__(self, k, v, lo=0, fp8=False):
+        self.fp8, self.lo = fp8, lo
+        if fp8:   # quantized on demand, per row (each row is its own tile)
+            self.kf, self.vf = k.float().cpu().numpy(), v.float().cpu().numpy()
+        else:
+            self.k, self.v = synth.to_f64(k), synth.to_f64(v)
 
     def attend(self, q, positions, kind, W):
         # rows before `lo` are outside every window asked for (SWA only)
         assert self.lo == 0 or all(p - W + 1 >= self.lo for p in positions)
-        return OA.attend(q, [p - self.lo for p in positions], self.k, self.v, kind, W)
+        if not self.fp8:
+            return OA.attend(q, [p - self.lo for p in positions], self.k, self.v, kind, W)
+        # FP8 pages hold each (token, head) row's own quantization, so the
+        # rows of the sampled windows quantize alone to the same values.
+        # Each window [p - W + 1, p] lies whole in the union of the windows,
+        # so in the union's compact order it is again the W rows up to p.
+        assert self.lo == 0 and kind == OA.SWA
+        rows = np.unique(np.concatenate([np.arange(max(0, p - W + 1), p + 1) for p in positions]))
+        k, v = (F8.dequantize_rows(*F8.quantize_rows(x[rows])) for x in (self.kf, self.vf))
+        return OA.attend(q, [int(j) for j in np.searchsorted(rows, positions)], k, v, kind, W)
 
 
 def _sample_chunk_rows(a, e, W, rng, k_random):
@@ -49,17 +65,18 @@ def _sample_chunk_rows(a, e, W, rng, k_random):
     return sorted(p for p in cand if a <= p < e)
 
 
-def _prefill_fullsize(kind, lens, chunk, hq, hkv, d, W, C, seed, rows_per_chunk, layer=0):
+def _prefill_fullsize(kind, lens, chunk, hq, hkv, d, W, C, seed, rows_per_chunk, layer=0,
+                      fp8=False):
     B = len(lens)
     maxp = max(lens) // 16 + 2
     nfull = B * maxp + 16
-    su = Setup(kind, W, C, B, maxp, nfull, hkv, d, seed)
+    su = Setup(kind, W, C, B, maxp, nfull, hkv, d, seed, fp8=fp8)
     sim = PoolSim(W, C, B, maxp, nfull, synth.permutation(nfull, seed, 1),
                   synth.permutation(B * C // 16, seed, 2))
     Q = [_draw((L, hq, d), seed, layer, b, synth.ROLE_Q) for b, L in enumerate(lens)]
     K = [_draw((L, hkv, d), seed, layer, b, synth.ROLE_K) for b, L in enumerate(lens)]
     V = [_draw((L, hkv, d), seed, layer, b, synth.ROLE_V) for b, L in enumerate(lens)]
-    host = [_Host(k, v) for k, v in zip(K, V)]
+    host = [_Host(k, v, fp8=fp8) for k, v in zip(K, V)]
     rng = np.random.default_rng(seed + 17)
     done = [0] * B
     worst, checked = 0.0, 0
@@ -77,11 +94,11 @@ def _prefill_fullsize(kind, lens, chunk, hq, hkv, d, W, C, seed, rows_per_chunk,
         vn = torch.cat([V[b][a:e] for b, a, e in rows])
         cu = torch.tensor(np.concatenate([[0], np.cumsum(n)]), dtype=torch.int32, device=dev())
         sid = torch.tensor(act, dtype=torch.int32, device=dev())
-        H.hswa_append_kv(kind, kn, vn, sid, su.view, su.kc, su.vc, cu, max(n))
+        H.hswa_append_kv(kind, kn, vn, sid, su.view, su.kc, su.vc, cu, max(n), **su.scales())
         out = torch.full((q.shape[0], hq, d), float("nan"), dtype=torch.float32, device=dev())
         vl = torch.full((q.shape[0],), -7, dtype=torch.int32, device=dev())
         H.hswa_prefill_chunk(kind, W, q, None, None, sid, cu, max(n), su.view, su.kc, su.vc,
-                             out, vl)
+                             out, vl, **su.scales())
         ev, cnt = H.hswa_pool_evict(su.pool, act)
         eev, ecnt = sim.evict(act)
         assert list(cnt) == list(ecnt) and np.array_equal(ev, eev)
@@ -118,6 +135,18 @@ def test_swa_chunked_prefill_fullsize(gpu):
     worst, n = _prefill_fullsize(H.SWA, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads,
                                  wl.head_dim, wl.window, wl.window + wl.chunk, wl.seed, 12)
     print(f"C2 full size: {n} rows checked, worst max-abs {worst:.3e}")
+
+
+def test_swa_chunked_prefill_fp8_fullsize(gpu):
+    """The same workload over FP8 pages: the appends quantize each chunk and
+    the prefill reads codes and scales; sampled rows against the oracle on
+    the dequantized K/V."""
+    wl = synth.C2
+    lens = synth.uniform_lengths(wl.num_seqs, wl.len_lo, wl.len_hi, wl.seed)
+    worst, n = _prefill_fullsize(H.SWA, lens, wl.chunk, wl.num_q_heads, wl.num_kv_heads,
+                                 wl.head_dim, wl.window, wl.window + wl.chunk, wl.seed, 3,
+                                 fp8=True)
+    print(f"C2 full size, FP8 pages: {n} rows checked, worst max-abs {worst:.3e}")
 
 
 @pytest.mark.parametrize("kind", [H.FULL, H.SWA])

@@ -41,10 +41,16 @@ def make_seqs(lengths, hq, hkv, d, seed, layer=0) -> List[SeqData]:
     return out
 
 
-def oracle_rows(s: SeqData, positions, kind, window, scale=None):
+def oracle_rows(s: SeqData, positions, kind, window, scale=None, fp8=False):
+    """The oracle's rows at `positions`; fp8: over the values FP8 pages hold
+    for the sequence's K/V (each row quantized, code times scale)."""
     q = synth.to_f64(s.q[positions])
-    return OA.attend(q, positions, synth.to_f64(s.k), synth.to_f64(s.v),
-                     kind, window, scale)
+    if fp8:
+        from oracle import fp8 as F8
+        k, v = (F8.dequantize_rows(*F8.quantize_rows(x.float().numpy())) for x in (s.k, s.v))
+    else:
+        k, v = synth.to_f64(s.k), synth.to_f64(s.v)
+    return OA.attend(q, positions, k, v, kind, window, scale)
 
 
 class Setup:
@@ -123,7 +129,7 @@ def chunked_prefill(setup: Setup, seqs: List[SeqData], chunk: int, hq: int,
         out = torch.full((q.shape[0], hq, d), float("nan"), dtype=out_dtype, device=dev())
         vl = torch.full((q.shape[0],), -7, dtype=torch.int32, device=dev())
         H.hswa_prefill_chunk(setup.kind, setup.W, q, kn, vn, sid, cu, max(n), setup.view,
-                             setup.kc, setup.vc, out, vl, scale)
+                             setup.kc, setup.vc, out, vl, scale, **setup.scales())
         ev, cnt = H.hswa_pool_evict(setup.pool, [ids[b] for b in act])
         log["evict"].append((ev, cnt))
         torch.cuda.synchronize()

@@ -3,7 +3,8 @@ group, KV heads, window, chunk, ring slack, lengths, softmax scale and output
 type are drawn per case; each case runs a chunked prefill of every sequence
 and then multi-row decode steps (1-4 rows per sequence, ragged) with eviction
 after each, and compares every output row with the fp64 oracle and every
-valid length with its definition."""
+valid length with its definition.  32 more cases run over FP8 pages, against
+the oracle on the dequantized K/V."""
 import random
 
 import numpy as np
@@ -20,8 +21,8 @@ pytestmark = pytest.mark.gpu
 CASES = 128
 
 
-def _draw(case):
-    rnd = random.Random(7000 + case)
+def _draw(case, base=7000):
+    rnd = random.Random(base + case)
     c = dict(
         kind=rnd.choice([H.SWA, H.FULL]),
         d=rnd.choice([64, 128]),
@@ -46,18 +47,29 @@ def _tau(scale, d):
 
 @pytest.mark.parametrize("case", range(CASES))
 def test_random_configuration(gpu, case):
-    c = _draw(case)
+    _run(_draw(case), case, fp8=False)
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_random_configuration_fp8_pages(gpu, case):
+    """The same scenarios over FP8 pages (the appends quantize, prefill and
+    decode read codes and scales), against the oracle on the dequantized
+    K/V."""
+    _run(_draw(case, base=7200), case, fp8=True)
+
+
+def _run(c, case, fp8):
     kind, d, hkv, W = c["kind"], c["d"], c["hkv"], c["W"]
     hq = c["g"] * hkv
     lens, B = c["lens"], len(c["lens"])
     grow = [sum(r[b] for r in c["rows"]) for b in range(B)]
     total = [L + k for L, k in zip(lens, grow)]
-    print(f"case {case}: {c}", flush=True)
+    print(f"case {case}: fp8 {fp8} {c}", flush=True)
     seqs = make_seqs(total, hq, hkv, d, c["seed"])
     # the ring holds the W - 1 resident positions plus the largest append
     C = -(-(W - 1 + max(c["chunk"], 4)) // 16) * 16 + c["slack"]
     maxp = max(total) // 16 + 2
-    st = Setup(kind, W, C, B, maxp, B * maxp + 3, hkv, d, c["seed"])
+    st = Setup(kind, W, C, B, maxp, B * maxp + 3, hkv, d, c["seed"], fp8=fp8)
     tau = _tau(c["scale"], d)
 
     # chunked prefill of the first lens[b] positions
@@ -66,7 +78,7 @@ def test_random_configuration(gpu, case):
                                      out_dtype=c["out"])
     for b, s in enumerate(pre):
         got = outs[b].double().numpy()
-        exp = oracle_rows(s, list(range(lens[b])), kind, W, tau)
+        exp = oracle_rows(s, list(range(lens[b])), kind, W, tau, fp8)
         assert np.all(np.isfinite(got)), f"prefill: non-finite output in sequence {b}"
         err = float(np.max(np.abs(got - exp)))
         assert err < TOL, f"prefill sequence {b}: max-abs error {err:.3e}"
@@ -91,11 +103,11 @@ def test_random_configuration(gpu, case):
         out = torch.full((T, hq, d), float("nan"), dtype=c["out"], device=dev())
         vl = torch.full((T,), -1, dtype=torch.int32, device=dev())
         H.hswa_decode(kind, W, q, kn, vn, sid, maxlen, st.view, st.kc, st.vc, out, ws, vl,
-                      scale=c["scale"], cu_q=cu, max_q_len=max(n))
+                      scale=c["scale"], cu_q=cu, max_q_len=max(n), **st.scales())
         got = out.cpu().double().numpy()
         o = 0
         for b in range(B):
-            exp = oracle_rows(seqs[b], pos[b], kind, W, tau)
+            exp = oracle_rows(seqs[b], pos[b], kind, W, tau, fp8)
             err = float(np.max(np.abs(got[o:o + n[b]] - exp)))
             assert err < TOL, f"decode step {t} sequence {b}: max-abs error {err:.3e}"
             o += n[b]

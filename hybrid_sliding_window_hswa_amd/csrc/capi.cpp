@@ -447,9 +447,9 @@ int xfer(const hswa_xfer_args* a, bool to_host, void* stream) {
     hswa::set_error("FP8 pages need k_scale, v_scale, buf_k_scale and buf_v_scale");
     return HSWA_E_INVAL;
   }
-  if (fp8 && (!aligned4(a->k_scale) || !aligned4(a->v_scale) || !aligned4(a->buf_k_scale) ||
+  if (fp8 && (!aligned16(a->k_scale) || !aligned16(a->v_scale) || !aligned4(a->buf_k_scale) ||
               !aligned4(a->buf_v_scale))) {
-    hswa::set_error("scale buffers must be 4-byte aligned");
+    hswa::set_error("k_scale and v_scale must be 16-byte aligned, the buffer scales 4-byte");
     return HSWA_E_INVAL;
   }
   hswa::XferParams p{};
@@ -546,8 +546,8 @@ int hswa_kv_copy(const hswa_kv_copy_args* a, void* stream) {
     hswa::set_error("FP8 pages need k_scale and v_scale");
     return HSWA_E_INVAL;
   }
-  if (fp8 && (!aligned4(a->k_scale) || !aligned4(a->v_scale))) {
-    hswa::set_error("k_scale and v_scale must be 4-byte aligned");
+  if (fp8 && (!aligned16(a->k_scale) || !aligned16(a->v_scale))) {
+    hswa::set_error("k_scale and v_scale must be 16-byte aligned");
     return HSWA_E_INVAL;
   }
   hswa::CopyParams p{};

@@ -473,7 +473,8 @@ typedef struct hswa_xfer_args {
   void* v_scale;
   void* buf_k_scale;        /* ... and [total_tok][Hkv] fp32 scales of K and
                                of V, pinned host or device memory like the
-                               code buffers; 4-byte aligned                   */
+                               code buffers; 4-byte aligned (all other
+                               buffers 16-byte)                              */
   void* buf_v_scale;
 } hswa_xfer_args;
 

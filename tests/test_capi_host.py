@@ -479,8 +479,9 @@ def _fake_view(a):
 
 def test_fp8_copy_and_transfer_validation():
     """FP8 pages need their scale arrays (copy: K and V page scales;
-    transfer: those and the buffers' scales), aligned to 4 bytes, and
-    kv_dtype must name a format; each is E_INVAL before any launch."""
+    transfer: those and the buffers' scales), the page scales aligned to 16
+    bytes like every device buffer, the buffer scales to 4, and kv_dtype
+    must name a format; each is E_INVAL before any launch."""
     from hybrid_sliding_window_hswa_amd import _capi
     lib = _capi.load()
     a = _capi.KvCopyArgs()
@@ -512,3 +513,6 @@ def test_fp8_copy_and_transfer_validation():
     x.buf_k_scale, x.buf_v_scale = fake, fake + 1
     assert lib.hswa_kv_restore(C.byref(x), None) == H.HSWA_E_INVAL  # misaligned
     assert "aligned" in H.hswa_last_error()
+    x.buf_v_scale, x.k_scale = fake + 4, fake + 4   # buffer scales need 4, page scales 16
+    assert lib.hswa_kv_offload(C.byref(x), None) == H.HSWA_E_INVAL
+    assert "16-byte" in H.hswa_last_error()

@@ -260,9 +260,11 @@ static_assert(HSWA_DECODE_SCRATCH_BYTES == hswa::kDecodeScratchBytes,
 namespace hswa {
 
 // Split-K plan for a decode call.  FULL layers cut each sequence's context
-// into chunks of split_len keys (a multiple of 64) so that the grid has
-// enough workgroups for 256 CUs while the partial results stay small next
-// to the KV bytes; SWA layers read at most W keys and use one split.
+// into pieces of split_len keys (a multiple of 64, between 1,024 and about
+// 20K): enough (sequence, KV head, piece) work items for 256 CUs, but no
+// more, since every piece pays a Q load, a partial-state store and its share
+// of the combine.  Pieces of 8K-20K keys measured fastest on 4K-256K
+// contexts.  SWA layers read at most W keys and use one split.
 DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t rows, int32_t hq, int32_t hkv,
                        int32_t d, int32_t window, int32_t max_seq_len) {
   DecodePlan pl{1, 0, 0};
@@ -272,9 +274,12 @@ DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t rows, int32_t hq,
     return pl;
   }
   const int64_t min_split = 1024;
-  const int64_t target_units = 16384;  // (sequence, kv head, split) workgroups
+  const int64_t max_split = 20480;
+  const int64_t target_units = 4096;  // (sequence, kv head, split) work items
   int64_t units = (int64_t)num_seqs * hkv;
   int64_t want = (target_units + units - 1) / units;
+  const int64_t by_max = (max_seq_len + max_split - 1) / max_split;
+  if (want < by_max) want = by_max;
   int64_t max_by_len = (max_seq_len + min_split - 1) / min_split;
   int64_t n = want < max_by_len ? want : max_by_len;
   if (n < 1) n = 1;

@@ -333,7 +333,7 @@ def test_multi_row_decode_validation_and_workspace():
     # the split-K workspace holds one partial state per (row, head, split),
     # then (256-byte aligned) the work queues: 8 counters of a 128-byte line,
     # the unit count and a list of up to num_seqs * splits units.  Here 4
-    # sequences x 8 KV heads aim at 16,384 workgroups with pieces of at least
+    # sequences x 8 KV heads aim at 4,096 work items with pieces of at least
     # 1,024 keys: 98 splits of 1,024 keys for 100,000.
     one = _args(kind=0, n=4, total_q=4, hq=64, hkv=8, d=128, max_seq_len=100000)
     four = _args(kind=0, n=4, total_q=16, max_q_len=4, hq=64, hkv=8, d=128,

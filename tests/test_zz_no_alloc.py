@@ -128,10 +128,10 @@ def test_noalloc_decode_matches_workspace_decode(gpu):
 
 
 def test_noalloc_decode_refuses_plans_beyond_the_scratch(gpu):
-    """1,024 rows (256 sequences x 4) of 64 heads over 32K-token contexts
-    need more split-K state than the scratch holds: HSWA_E_INVAL, and the
-    output is untouched."""
-    B, rows, maxlen = 256, 4, 32768
+    """1,024 rows (256 sequences x 4) of 64 heads over 128K-token contexts
+    (7 splits) need more split-K state than the scratch holds: HSWA_E_INVAL,
+    and the output is untouched."""
+    B, rows, maxlen = 256, 4, 131072
     nb = H.hswa_decode_workspace_bytes(H.FULL, W, B, HQ, HKV, D, maxlen, B * rows)
     assert nb > H.DECODE_SCRATCH_BYTES
     st = Setup(H.FULL, W, W + 16, B, 4, B * 4, HKV, D, seed=153, poison=False)

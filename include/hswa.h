@@ -402,10 +402,10 @@ size_t hswa_decode_workspace_bytes(const hswa_attn_args* args);
  * nothing in the array needs clearing between calls.  HSWA_E_INVAL, with
  * nothing launched, when the call needs more than the array holds
  * (hswa_decode_workspace_bytes(args) > HSWA_DECODE_SCRATCH_BYTES, e.g.
- * 1,024 rows of 64 heads at d = 128 over 8 splits).  Every call on one GPU
- * shares the array: calls whose device work overlaps (other streams, other
- * host threads) race and give undefined results, so issue them in order on
- * one stream. */
+ * 1,024 rows of 64 heads at d = 128 over 128K-token contexts, 7 splits).
+ * Every call on one GPU shares the array: calls whose device work overlaps
+ * (other streams, other host threads) race and give undefined results, so
+ * issue them in order on one stream. */
 #define HSWA_DECODE_SCRATCH_BYTES ((size_t)128 << 20)
 int hswa_decode_noalloc(const hswa_attn_args* args, void* stream);
 

@@ -516,3 +516,22 @@ def test_fp8_copy_and_transfer_validation():
     x.buf_v_scale, x.k_scale = fake + 4, fake + 4   # buffer scales need 4, page scales 16
     assert lib.hswa_kv_offload(C.byref(x), None) == H.HSWA_E_INVAL
     assert "16-byte" in H.hswa_last_error()
+
+
+@pytest.mark.parametrize("seqs,hkv,max_len,splits", [
+    (256, 8, 32769, 2),     # the mixed decode: two pieces of 16,448 keys
+    (64, 8, 262145, 13),    # long contexts: pieces of at most 20,480 keys
+    (256, 1, 32769, 16),    # one KV head: more pieces for parallelism
+    (1, 8, 32769, 33),      # one sequence: pieces of 1,024 keys (the floor)
+    (4, 8, 1000, 1),        # short contexts: no split
+])
+def test_decode_split_plan(seqs, hkv, max_len, splits):
+    """Full-layer decode plans about 4,096 (sequence, KV head, piece) work
+    items with pieces of 1,024 to about 20K keys; the workspace holds one
+    partial state per (row, head, piece) and the work list."""
+    b = H.hswa_decode_workspace_bytes(0, 128, seqs, 8 * hkv, hkv, 128, max_len)
+    if splits == 1:
+        assert b == 0
+        return
+    partial = seqs * 8 * hkv * splits * (128 + 2) * 4
+    assert b == -(-partial // 256) * 256 + (8 * 32 + 32 + seqs * splits) * 4

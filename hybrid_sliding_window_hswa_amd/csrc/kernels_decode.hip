@@ -93,8 +93,9 @@ __device__ __forceinline__ void store_out(const AttnParams& p, int64_t idx, floa
 // Merges the four waves' partial states of a workgroup (fixed order), one
 // column tile at a time, and stores the result (one split) or the partial
 // state for decode_combine_kernel (several splits).  Column 16t + c of tile
-// t is (row, head) = ((16t + c) / G, (16t + c) % G).
-template <int D, int G, int NT, int CT>
+// t is (row, head) = ((16t + c) / G, (16t + c) % G) of KV head kvh; with
+// NCH > 0 the columns cover KV heads 2 kvh and 2 kvh + 1, NCH each.
+template <int D, int G, int NT, int CT, int NCH = 0>
 __device__ __forceinline__ void merge_store(const AttnParams& p, float (&red_o)[kDecWaves][CT][D],
                                             float (&red_ml)[kDecWaves][CT][2],
                                             const f32x4 (&o)[NT][D / 16], const float (&m)[NT],
@@ -106,7 +107,7 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, float (&red_o)[
   const int col = lane & 15;
   const int q4 = lane >> 4;
   const int hq = p.hq;
-  const int hq_base = kvh * G;
+  const int hq_base = (NCH > 0 ? 2 * kvh : kvh) * G;
   for (int t = 0; t < NT; ++t) {
     float ls = lsum[t];
     ls += xor_lane(ls, 16);
@@ -124,7 +125,9 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, float (&red_o)[
     for (int idx = threadIdx.x; idx < CT * D; idx += blockDim.x) {
       const int c = idx / D;
       const int d = idx % D;
-      const int g = 16 * t + c;
+      const int g0 = 16 * t + c;
+      const int mem = NCH > 0 ? g0 / NCH : 0;  // which KV head of the pair
+      const int g = NCH > 0 ? g0 % NCH : g0;
       const int r = g / G;
       if (r >= nr) continue;
       float M = -INFINITY;
@@ -136,7 +139,7 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, float (&red_o)[
         num += sc * red_o[w][c][d];
         den += sc * red_ml[w][c][1];
       }
-      const int64_t hrow = (int64_t)(row0 + r) * hq + hq_base + g % G;
+      const int64_t hrow = (int64_t)(row0 + r) * hq + hq_base + mem * G + g % G;
       if (p.n_splits == 1) {
         store_out(p, hrow * D + d, num / den);
       } else {
@@ -494,17 +497,28 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
 // contiguous quarter of the row (d in [q4 * D/4, (q4 + 1) * D/4)); Q takes
 // the same order of the reduction.  A wave then keeps 16.5 KB in flight per
 // step, as much as the bf16 path, at two waves per SIMD.
-template <int D, int KIND, int G, int QN>
+//
+// PAIR (Full layers, G * QN <= 8): the unit covers KV heads 2 kvh and
+// 2 kvh + 1 in 32-key steps over two pages.  Row group a = 4a + r of a score
+// tile is (page a >> 1, head a & 1), so each wave reads the two heads'
+// adjacent code blocks of a page, 4 KB in a run, and their scales as one
+// 128-byte line.  The 16 columns are the two heads' G * QN (row, head)
+// pairs; a lane whose rows belong to the other head of its column gets
+// -inf scores, so it adds nothing to the column's max, sum or output.
+template <int D, int KIND, int G, int QN, bool PAIR>
 __device__ __forceinline__ void decode_fp8_unit(const AttnParams& p, const int unit,
                                                 const int kvh) {
   constexpr int NB = D / 16;                  // 16-row d blocks of O^T
   constexpr int NC = D / 32;                  // 32-wide chunks of the QK reduction
   constexpr int DQ = D / 4;                   // contiguous K bytes of a lane per row
   constexpr int KV4 = DQ / 16;                // 16-byte loads per row and lane
-  constexpr int NCOL = G * QN;
+  constexpr int NCH = G * QN;                 // columns per KV head
+  constexpr int NCOL = PAIR ? 2 * NCH : NCH;
   constexpr int CT = NCOL;                    // one tile
   static_assert(NCOL <= 16, "one column tile");
-  constexpr int SK = 64;                      // keys per step
+  static_assert(!PAIR || KIND == 0, "head pairs serve Full layers");
+  constexpr int SK = PAIR ? 32 : 64;          // keys per step
+  constexpr int NPG = SK / kPage;             // pages per step
   __shared__ __attribute__((aligned(16))) float red_o[kDecWaves][CT][D];
   __shared__ float red_ml[kDecWaves][CT][2];
 
@@ -537,12 +551,19 @@ __device__ __forceinline__ void decode_fp8_unit(const AttnParams& p, const int u
   const int hkv = p.hkv;
   const int W = p.window;
 
-  const int crow = col / G;
+  // column col: KV head h0 + mem, row crow, query head (h0 + mem) G + c2 % G
+  const int h0 = PAIR ? 2 * kvh : kvh;
+  const int mem = PAIR ? col / NCH : 0;
+  const int c2 = PAIR ? col % NCH : col;
+  const int crow = c2 / G;
   const bool con = col < CT && crow < nr;
   const int cpos = L - n + crow;
+  // PAIR: this lane's score rows belong to its column's KV head
+  const bool lane_head = !PAIR || (q4 & 1) == mem;
   bf16x8 qf[1][NC];  // lane holds Q[col][q4 * DQ + 8c .. +8]
   {
-    const uint16_t* qrow = p.q + ((int64_t)(row0 + (con ? crow : 0)) * hq + kvh * G + col % G) * D;
+    const uint16_t* qrow =
+        p.q + ((int64_t)(row0 + (con ? crow : 0)) * hq + (h0 + (con ? mem : 0)) * G + c2 % G) * D;
     for (int c = 0; c < NC; ++c) {
       u32x4 w = con ? *(const u32x4*)(qrow + q4 * DQ + 8 * c) : u32x4{0, 0, 0, 0};
       qf[0][c] = __builtin_bit_cast(bf16x8, w);
@@ -570,17 +591,21 @@ __device__ __forceinline__ void decode_fp8_unit(const AttnParams& p, const int u
     int64_t sc;        // scales of page q4
   };
   auto step_pages = [&](int kp0) {
-    int32_t pg[4];
-    for (int x = 0; x < 4; ++x) {
+    int32_t pg[NPG];
+    for (int x = 0; x < NPG; ++x) {
       // a page with no key of [klo, khi): a page of the step that has one
       // (masked keys); a missing page (skipped alloc): page 0 of the pool
       const int32_t v = page_at(idx::decode_page_pos(kp0, x, klo, khi));
       pg[x] = v < 0 ? 0 : v;
     }
-    const int32_t pk = pg[col >> 2], pv = pg[q4];
-    return Ptrs{kbase + ((int64_t)pk * hkv + kvh) * blk + (col & 3) * D + q4 * DQ,
-                vbase + ((int64_t)pv * hkv + kvh) * blk + col * kPage,
-                ((int64_t)pv * hkv + kvh) * kPage};
+    // row group a = col >> 2 (K rows) or q4 (scores, V, scales): page a, or
+    // with PAIR page a >> 1 of KV head h0 + (a & 1)
+    const int ak = col >> 2;
+    const int32_t pk = PAIR ? pg[ak >> 1] : pg[ak], pv = PAIR ? pg[q4 >> 1] : pg[q4];
+    const int hk = PAIR ? h0 + (ak & 1) : kvh, hv = PAIR ? h0 + (q4 & 1) : kvh;
+    return Ptrs{kbase + ((int64_t)pk * hkv + hk) * blk + (col & 3) * D + q4 * DQ,
+                vbase + ((int64_t)pv * hkv + hv) * blk + col * kPage,
+                ((int64_t)pv * hkv + hv) * kPage};
   };
   u32x4 kr[4][KV4], vr[NB], sc[8];  // sc: K scales 0-3, V scales 4-7
   auto load_k = [&](const Ptrs& pt) {
@@ -620,17 +645,19 @@ __device__ __forceinline__ void decode_fp8_unit(const AttnParams& p, const int u
       s4[kt] = acc;
     }
     if (more) load_k(ptn);
-    // lane value (kt, r) is key kp0 + 16*q4 + 4kt + r, in-page index 4kt + r
+    // lane value (kt, r) is key kp0 + 16*page + 4kt + r, in-page index 4kt + r,
+    // page = q4 (PAIR: q4 >> 1)
+    const int page16 = 16 * (PAIR ? q4 >> 1 : q4);
     unsigned valid = 0;
     for (int j = 0; j < 16; ++j) {
-      const int kp = kp0 + 16 * q4 + j;
+      const int kp = kp0 + page16 + j;
       valid |= (unsigned)(kp >= klo && kp < khi) << j;
     }
     float mx = -INFINITY;
     float sv[16];
     for (int j = 0; j < 16; ++j) {
-      const int kp = kp0 + 16 * q4 + j;
-      bool ok = (valid >> j) & 1u;
+      const int kp = kp0 + page16 + j;
+      bool ok = lane_head && ((valid >> j) & 1u);
       if (QN > 1) ok = ok && kp <= cpos && (KIND == 0 || kp > cpos - W);
       const float ks = __uint_as_float(sc[j >> 2][j & 3]);
       const float x = ok ? s4[j >> 2][j & 3] * (ks * sl2) : -INFINITY;
@@ -670,7 +697,7 @@ __device__ __forceinline__ void decode_fp8_unit(const AttnParams& p, const int u
     pt = ptn;
   }
   for (int nb = 0; nb < NB; ++nb) o[0][nb] *= 0.00390625f;  // the weights carried 2^8
-  merge_store<D, G, 1, CT>(p, red_o, red_ml, o, m, lsum, kvh, split, row0, nr);
+  merge_store<D, G, 1, CT, PAIR ? NCH : 0>(p, red_o, red_ml, o, m, lsum, kvh, split, row0, nr);
   if (p.vlen && split == 0 && kvh == 0 && (int)threadIdx.x < nr) {
     const int pos = L - n + threadIdx.x;
     p.vlen[row0 + threadIdx.x] = KIND == 0 ? pos + 1 : min(pos + 1, W);
@@ -681,7 +708,29 @@ __device__ __forceinline__ void decode_fp8_unit(const AttnParams& p, const int u
 template <int D, int KIND, int G, int QN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4)))
 decode_fp8_kernel(AttnParams p) {
-  for_each_item<KIND, true>(p, [&](int unit, int kvh) { decode_fp8_unit<D, KIND, G, QN>(p, unit, kvh); });
+  for_each_item<KIND, true>(p, [&](int unit, int kvh) {
+    decode_fp8_unit<D, KIND, G, QN, false>(p, unit, kvh);
+  });
+}
+
+// Full layers with an even KV head count and a split-K plan: items are
+// (unit, KV head pair) from one queue, both heads in one workgroup.
+template <int D, int G, int QN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4)))
+decode_fp8_pair_kernel(AttnParams p) {
+  __shared__ int s_k;
+  const int pairs = p.hkv / 2;
+  for (;;) {
+    if (threadIdx.x == 0)
+      s_k = __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int k = s_k;
+    __syncthreads();  // every wave has read s_k before it is written again
+    const int units = min(p.queue[idx::kQueueCount], p.num_seqs * p.n_splits);
+    int a, pair;
+    if (!idx::queue_item(k, 0, units, pairs, false, &a, &pair)) return;
+    decode_fp8_unit<D, 0, G, QN, true>(p, p.queue[idx::kQueueList + a], pair);
+  }
 }
 
 // Log-sum-exp merge of the split partial states of one (query row, head).
@@ -803,6 +852,15 @@ template <int D, int KIND, int G, int QN, bool F8>
 hipError_t launch_decode_one(const AttnParams& p, dim3 grid, hipStream_t s) {
   static std::atomic<int> slots[kMaxQueueDevices];  // per instantiation
   const int64_t items = (int64_t)p.num_seqs * p.n_splits * p.hkv;
+  if constexpr (F8 && KIND == 0 && G * QN <= 8) {
+    if (p.queue && p.hkv % 2 == 0) {
+      static std::atomic<int> pair_slots[kMaxQueueDevices];
+      hipError_t e = queue_grid(decode_fp8_pair_kernel<D, G, QN>, pair_slots, items / 2, &grid.x);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((decode_fp8_pair_kernel<D, G, QN>), grid, dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if constexpr (F8 && G * QN <= 16) {
     if (p.queue) {
       hipError_t e = queue_grid(decode_fp8_kernel<D, KIND, G, QN>, slots, items, &grid.x);

@@ -193,14 +193,26 @@ def test_fp8_multi_row_decode(gpu):
     _fp8_decode_scenario([3000, 40, 129, 9000], 3, 64, 8, 128, 128, 53, max_rows=4)
 
 
-@pytest.mark.parametrize("kind", [H.FULL, H.SWA])
-def test_decode_reads_every_e4m3_code_exactly(gpu, kind):
+@pytest.mark.parametrize("g,rows", [(2, 4), (4, 2), (1, 4), (8, 1)])
+def test_fp8_head_pairs_multi_row(gpu, g, rows):
+    """Full layers with split-K and an even KV head count decode both heads
+    of a pair in one workgroup; these shapes (G x rows <= 8) cover every
+    column layout of that path, with ragged rows and contexts that cross
+    splits."""
+    _fp8_decode_scenario([5000, 40, 2100, 1, 3333], 2, g * 4, 4, 128, 128, 70 + g,
+                         max_rows=rows)
+
+
+@pytest.mark.parametrize("kind,hint", [(H.FULL, 2), (H.FULL, 4096), (H.SWA, 2)])
+def test_decode_reads_every_e4m3_code_exactly(gpu, kind, hint):
     """Every finite e4m3 code, through the decode path, comes back as its
     exact value.  One stored key's V codes are all 254 finite codes (two KV
     heads x 128 dims) with V scale 1; its K codes are 448 and Q is all ones,
     so its score exceeds the new token's (K = 0) by thousands and its weight
     is 1 while the new token's is 0.  The output is then that key's V, code
-    by code, bit for bit (the fp16 weight 2^8 and the final 2^-8 are exact)."""
+    by code, bit for bit (the fp16 weight 2^8 and the final 2^-8 are exact).
+    The Full layer with a length hint of 4,096 takes split-K over both KV
+    heads at once, with the combine."""
     hkv, d, W = 2, 128, 128
     P = Fp8Pool([1], hkv, d, W, 61)
     codes = np.arange(256, dtype=np.uint8).reshape(hkv, d)
@@ -216,9 +228,10 @@ def test_decode_reads_every_e4m3_code_exactly(gpu, kind):
     q = torch.ones((1, hkv, d), dtype=torch.bfloat16, device=dev())
     zero = torch.zeros((1, hkv, d), dtype=torch.bfloat16, device=dev())
     out = torch.full((1, hkv, d), float("nan"), dtype=torch.float32, device=dev())
-    nb = H.hswa_decode_workspace_bytes(kind, W, 1, hkv, hkv, d, 2)
+    nb = H.hswa_decode_workspace_bytes(kind, W, 1, hkv, hkv, d, hint)
+    assert (nb > 0) == (hint > 2)
     ws = torch.empty(max(nb // 4, 1), dtype=torch.float32, device=dev())
-    H.hswa_decode(kind, W, q, zero, zero, P.sid, 2, P.view, kc, vc, out, ws,
+    H.hswa_decode(kind, W, q, zero, zero, P.sid, hint, P.view, kc, vc, out, ws,
                   k_scale=ks, v_scale=vs)
     want = F8.E4M3_TABLE[codes].astype(np.float32)
     got = out.cpu().numpy()[0]

@@ -499,10 +499,10 @@ __attribute__((amdgpu_waves_per_eu(G * QN > 16 ? 2 : 3, 4))) decode_kernel(AttnP
 // step, as much as the bf16 path, at two waves per SIMD.
 //
 // PAIR (Full layers, G * QN <= 8): the unit covers KV heads 2 kvh and
-// 2 kvh + 1 in 32-key steps over two pages.  Row group a = 4a + r of a score
-// tile is (page a >> 1, head a & 1), so each wave reads the two heads'
-// adjacent code blocks of a page, 4 KB in a run, and their scales as one
-// 128-byte line.  The 16 columns are the two heads' G * QN (row, head)
+// 2 kvh + 1 in 32-key steps over two pages.  Rows 4a .. 4a + 3 of a score
+// tile (row group a) belong to page a >> 1 and head a & 1, so each wave
+// reads the two heads' adjacent code blocks of a page, 4 KB in a run, and
+// their scales as one 128-byte line.  The 16 columns are the two heads' G * QN (row, head)
 // pairs; a lane whose rows belong to the other head of its column gets
 // -inf scores, so it adds nothing to the column's max, sum or output.
 template <int D, int KIND, int G, int QN, bool PAIR>
@@ -586,9 +586,9 @@ __device__ __forceinline__ void decode_fp8_unit(const AttnParams& p, const int u
   const uint8_t* kbase = (const uint8_t*)p.k_cache;
   const uint8_t* vbase = (const uint8_t*)p.v_cache;
   struct Ptrs {
-    const uint8_t* k;  // this lane's K row (page col/4, row col%4), its d quarter
-    const uint8_t* v;  // page q4, dim col
-    int64_t sc;        // scales of page q4
+    const uint8_t* k;  // this lane's K row (row group col/4, row col%4), its d quarter
+    const uint8_t* v;  // row group q4, dim col
+    int64_t sc;        // scales of row group q4
   };
   auto step_pages = [&](int kp0) {
     int32_t pg[NPG];

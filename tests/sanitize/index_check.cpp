@@ -76,9 +76,10 @@ static void prefill_walk(int kind, int32_t L, int32_t n, int32_t W, int32_t C, i
   }
 }
 
-// The decode kernels' page walk: bf16 pages in 32-key steps (pages kp0 and
-// kp0 + 16), FP8 pages in 64-key steps (four pages), over the splits of a
-// Full layer or the window of a SWA layer; n rows end at position L - 1.
+// The decode kernels' page walk: bf16 pages and FP8 KV-head pairs in 32-key
+// steps (pages kp0 and kp0 + 16), FP8 pages of one head in 64-key steps (four
+// pages), over the splits of a Full layer or the window of a SWA layer; n
+// rows end at position L - 1.
 static void decode_walk(int kind, int32_t L, int32_t n, int32_t W, int32_t C, int32_t n_splits,
                         int32_t split_len, int step_keys) {
   const int32_t rl = row_len(kind, L, C);

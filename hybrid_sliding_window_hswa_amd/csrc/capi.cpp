@@ -261,9 +261,9 @@ namespace hswa {
 
 // Split-K plan for a decode call.  FULL layers cut each sequence's context
 // into pieces of split_len keys (a multiple of 64, between 1,024 and about
-// 20K): enough (sequence, KV head, piece) work items for 256 CUs, but no
+// 20K): about 2K (sequence, KV head, piece) work items for 256 CUs, but no
 // more, since every piece pays a Q load, a partial-state store and its share
-// of the combine.  Pieces of 8K-20K keys measured fastest on 4K-256K
+// of the combine.  Pieces of 4K-20K keys measured fastest on 4K-256K
 // contexts.  SWA layers read at most W keys and use one split.
 DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t rows, int32_t hq, int32_t hkv,
                        int32_t d, int32_t window, int32_t max_seq_len) {
@@ -275,7 +275,7 @@ DecodePlan plan_decode(int32_t kind, int32_t num_seqs, int32_t rows, int32_t hq,
   }
   const int64_t min_split = 1024;
   const int64_t max_split = 20480;
-  const int64_t target_units = 4096;  // (sequence, kv head, split) work items
+  const int64_t target_units = 2048;  // (sequence, kv head, split) work items
   int64_t units = (int64_t)num_seqs * hkv;
   int64_t want = (target_units + units - 1) / units;
   const int64_t by_max = (max_seq_len + max_split - 1) / max_split;

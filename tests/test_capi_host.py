@@ -333,15 +333,15 @@ def test_multi_row_decode_validation_and_workspace():
     # the split-K workspace holds one partial state per (row, head, split),
     # then (256-byte aligned) the work queues: 8 counters of a 128-byte line,
     # the unit count and a list of up to num_seqs * splits units.  Here 4
-    # sequences x 8 KV heads aim at 4,096 work items with pieces of at least
-    # 1,024 keys: 98 splits of 1,024 keys for 100,000.
+    # sequences x 8 KV heads aim at 2,048 work items with pieces of at least
+    # 1,024 keys: 63 splits of 1,600 keys for 100,000.
     one = _args(kind=0, n=4, total_q=4, hq=64, hkv=8, d=128, max_seq_len=100000)
     four = _args(kind=0, n=4, total_q=16, max_q_len=4, hq=64, hkv=8, d=128,
                  max_seq_len=100000)
     b1 = lib.hswa_decode_workspace_bytes(C.byref(one))
     b4 = lib.hswa_decode_workspace_bytes(C.byref(four))
 
-    def ws(rows, seqs=4, splits=98):
+    def ws(rows, seqs=4, splits=63):
         partial = rows * 64 * splits * (128 + 2) * 4
         return -(-partial // 256) * 256 + (8 * 32 + 32 + seqs * splits) * 4
 
@@ -521,12 +521,12 @@ def test_fp8_copy_and_transfer_validation():
 @pytest.mark.parametrize("seqs,hkv,max_len,splits", [
     (256, 8, 32769, 2),     # the mixed decode: two pieces of 16,448 keys
     (64, 8, 262145, 13),    # long contexts: pieces of at most 20,480 keys
-    (256, 1, 32769, 16),    # one KV head: more pieces for parallelism
+    (256, 1, 32769, 8),     # one KV head: more pieces for parallelism
     (1, 8, 32769, 33),      # one sequence: pieces of 1,024 keys (the floor)
     (4, 8, 1000, 1),        # short contexts: no split
 ])
 def test_decode_split_plan(seqs, hkv, max_len, splits):
-    """Full-layer decode plans about 4,096 (sequence, KV head, piece) work
+    """Full-layer decode plans about 2,048 (sequence, KV head, piece) work
     items with pieces of 1,024 to about 20K keys; the workspace holds one
     partial state per (row, head, piece) and the work list."""
     b = H.hswa_decode_workspace_bytes(0, 128, seqs, 8 * hkv, hkv, 128, max_len)

@@ -324,11 +324,11 @@ def test_decode_small_heads_d64(gpu):
 
 def test_decode_many_sequences_work_queue(gpu):
     """600 sequences (the work-queue pre-pass scans 256 at a time) with
-    contexts from 1 to 6,000 keys: up to 4 splits of 1,536 keys, most of
-    them empty for the shorter sequences, so the queue holds a mix of
-    pieces of every length (and the bounds of a split: 1,535-1,537)."""
+    contexts from 1 to 6,000 keys: 2 splits of 3,008 keys, the second
+    empty for the shorter sequences, so the queue holds a mix of pieces of
+    every length (and the bounds of a split: 3,007-3,009)."""
     rng = np.random.default_rng(17)
-    ctxs = [int(x) for x in rng.integers(1, 6000, size=595)] + [1, 1535, 1536, 1537, 6000]
+    ctxs = [int(x) for x in rng.integers(1, 6000, size=595)] + [1, 3007, 3008, 3009, 6000]
     _decode_scenario(ctxs, 2, 16, 2, 64, 64, 171)
 
 

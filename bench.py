@@ -42,6 +42,9 @@ resident in HBM before the timed region starts):
       plus three draft tokens per step (rows of a sequence share every K/V
       byte read); the step keeps a seeded accepted prefix (truncate) before
       evicting.  `value` = algorithmic HBM GB/s.
+  mtp_decode_fp8
+      mtp_decode over FP8 pages (32 (row, head) columns per KV head: the
+      two-tile kernel).  `value` = algorithmic HBM GB/s of the FP8 bytes.
   tier_transfer
       Window-masked offload and restore of a 14-layer hybrid stack's KV
       (16 sequences, contexts 4096-32768) through pinned host memory: SWA
@@ -997,28 +1000,35 @@ def wl_mixed_decode_fp8(cx, args):
     return line
 
 
-def wl_mtp_decode(cx, args):
+def wl_mtp_decode(cx, args, fp8=False):
     """Multi-token decode: one token plus three drafts per sequence per step
-    over one Full and one SWA layer, accepted prefix kept."""
+    over one Full and one SWA layer, accepted prefix kept; fp8: over FP8
+    pages."""
     import synth
     wl = synth.MTP
     ctxs = synth.uniform_lengths(wl.num_seqs, wl.ctx_lo, wl.ctx_hi, wl.seed)
     steps, warm = args.decode_steps, 4
     rows = wl.drafts + 1
     dc = Decode(cx, ctxs, "FS", wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window,
-                wl.ring_slots, wl.seed, steps + warm + 8, rows=rows, out=args.out)
+                wl.ring_slots, wl.seed, steps + warm + 8, rows=rows, fp8=fp8, out=args.out)
     r = run_decode(cx, dc, "FS", steps, warm)
-    log(f"mtp decode: {r}")
-    config = {"workload": "mtp_decode", "num_seqs": wl.num_seqs,
+    log(f"mtp decode{' fp8' if fp8 else ''}: {r}")
+    config = {"workload": "mtp_decode_fp8" if fp8 else "mtp_decode", "num_seqs": wl.num_seqs,
               "ctx_range": [wl.ctx_lo, wl.ctx_hi], "rows_per_seq": rows,
               "accepted_rows": [1, rows], "layers": "1 Full + 1 SWA",
               "output_dtype": ODT[args.out],
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "window": wl.window, "ring_slots": wl.ring_slots,
               "seed": wl.seed}
+    if fp8:
+        config["kv_dtype"] = "fp8 e4m3, fp32 scale per token and head"
     rl = roofline("hbm", r["full_gbs"],
-                  measured_traffic("decode_full_mtp", "kernels_decode.hip"))
+                  None if fp8 else measured_traffic("decode_full_mtp", "kernels_decode.hip"))
     line = base_line(args, round(r["gbs"], 1), "GB/s", r["ms_per_step"], config, rl)
+    if fp8:
+        line["dtype"] = "fp8 K/V, bf16/fp16 MFMA"
+        line["precision"] = dict(line["precision"], k_pages="e4m3 + fp32 scale per token and head",
+                                 v_pages="e4m3 + fp32 scale per token and head")
     line["step_frac_of_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
     line["accepted_tok_per_s"] = round(r["tok_per_s"], 1)
     line["full_call_us"] = round(r["full_call_us"], 1)
@@ -1362,6 +1372,7 @@ WORKLOADS = {
     "mixed_decode_fp8": wl_mixed_decode_fp8,
     "swa_chunked_prefill_fp8": wl_swa_chunked_prefill_fp8,
     "mtp_decode": wl_mtp_decode,
+    "mtp_decode_fp8": lambda cx, args: wl_mtp_decode(cx, args, fp8=True),
     "tier_transfer": wl_tier_transfer,
     "tier_transfer_fp8": lambda cx, args: wl_tier_transfer(cx, args, fp8=True),
     "hybrid_stack": wl_hybrid_stack,

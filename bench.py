@@ -55,6 +55,11 @@ resident in HBM before the timed region starts):
       tier_transfer over FP8 pages: the buffers hold code bytes and the fp32
       scale of each (token, head), 2 * Hkv * (d + 4) bytes per token instead
       of 4 * Hkv * d.  `value` = restore GB/s of those bytes.
+  tp8_share
+      One GPU's share of an 8-way KV-head split: the default run's prefill
+      and mixed decode with 8 query heads and 1 KV head (the same lengths,
+      chunk, W and contexts).  `value` = prefill tokens/s of the share; the
+      decode under "decode".
   swa_single_chunk
       One SWA layer, one 1024-token sequence (8 query / 2 KV heads, head_dim
       64) prefilled in one chunk, then 16 decode steps.  `value` = tok/s.
